@@ -1,0 +1,341 @@
+"""Pins for the CPU oracle: each check compares it with something other than
+itself -- torch's float64 SDPA/autograd/rms_norm (library routines for the
+textbook definitions), central finite differences, closed forms, brute-force
+counts, a complex-multiplication RoPE and hand-worked golden fixtures.
+
+The last group plants plausible mistakes in copies of oracle functions and
+checks that the pins catch each one.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+rng = np.random.default_rng(12345)
+
+
+def sdpa_ref(q, k, v, W, scale=None):
+    """torch float64 SDPA with an explicit inclusive-window causal mask and GQA."""
+    qt = torch.from_numpy(q).permute(0, 2, 1, 3)
+    kt = torch.from_numpy(k).permute(0, 2, 1, 3)
+    vt = torch.from_numpy(v).permute(0, 2, 1, 3)
+    T = q.shape[1]
+    i = torch.arange(T)[:, None]
+    j = torch.arange(T)[None, :]
+    mask = j <= i
+    if W >= 0:
+        mask = mask & (i - j <= W)
+    o = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=scale,
+                                       enable_gqa=q.shape[2] != k.shape[2])
+    return o.permute(0, 2, 1, 3).numpy()
+
+
+def rand(*shape):
+    return rng.standard_normal(shape)
+
+
+# ----------------------------------------------------------------- RMSNorm
+
+def test_rmsnorm_matches_torch_rms_norm():
+    x = rand(3, 5, 2, 64)
+    got = oracle.rms_norm(x, eps=1e-6)
+    ref = F.rms_norm(torch.from_numpy(x), (64,), eps=1e-6).numpy()
+    np.testing.assert_allclose(got, ref, rtol=1e-13, atol=1e-13)
+
+
+def test_rmsnorm_closed_forms():
+    x = rand(4, 128)
+    eps, g = 1e-6, math.sqrt(1.2)
+    y = oracle.rms_norm(x, eps=eps, gain=g)
+    m = np.mean(x * x, axis=-1)
+    np.testing.assert_allclose(np.sqrt(np.mean(y * y, axis=-1)), g * np.sqrt(m / (m + eps)), rtol=1e-12)
+    # constant row c * 1 -> g * sign(c) * 1 (up to eps)
+    c = np.full((1, 64), -3.5)
+    np.testing.assert_allclose(oracle.rms_norm(c, eps=0.0, gain=g), -g * np.ones((1, 64)), rtol=1e-14)
+    # scale invariance for c > 0 (eps = 0)
+    np.testing.assert_allclose(oracle.rms_norm(7.0 * x, eps=0.0), oracle.rms_norm(x, eps=0.0), rtol=1e-13)
+
+
+# ----------------------------------------------------------------- RoPE
+
+def test_rope_golden_hand_values():
+    g = json.load(open(os.path.join(GOLDEN, "rope_hand.json")))
+    for case in g["cases"]:
+        x = np.array(case["x"], dtype=np.float64).reshape(1, 1, 1, 4)
+        pos = np.array([[case["pos"]]], dtype=np.float64)
+        got = oracle.apply_rope(x, pos, g["base"]).reshape(-1)
+        np.testing.assert_allclose(got, case["expect"], rtol=0, atol=1e-14, err_msg=case["why"])
+
+
+def test_rope_equals_complex_multiplication():
+    # independent formulation: z_j = x_j + i x_{j+D/2}, z_j <- z_j * exp(i pos w_j)
+    B, T, Hh, D, base = 2, 9, 3, 64, 100000.0
+    x = rand(B, T, Hh, D)
+    pos = rng.integers(0, 9000, size=(B, T)).astype(np.float64)
+    w = np.array([base ** (-(2.0 * j) / D) for j in range(D // 2)])
+    z = x[..., : D // 2] + 1j * x[..., D // 2:]
+    z = z * np.exp(1j * pos[:, :, None, None] * w)
+    ref = np.concatenate([z.real, z.imag], axis=-1)
+    np.testing.assert_allclose(oracle.apply_rope(x, pos, base), ref, rtol=1e-12, atol=1e-12)
+
+
+def test_rope_invariants():
+    D, base = 128, 100000.0
+    x = rand(1, 6, 2, D)
+    pos = np.arange(6, dtype=np.float64)[None] * 1000.0
+    y = oracle.apply_rope(x, pos, base)
+    np.testing.assert_allclose(np.linalg.norm(y, axis=-1), np.linalg.norm(x, axis=-1), rtol=1e-13)
+    np.testing.assert_allclose(oracle.apply_rope(x, 0 * pos, base), x, rtol=0, atol=0)
+    # R(a) R(b) = R(a + b)
+    a = oracle.apply_rope(oracle.apply_rope(x, pos, base), pos + 17.0, base)
+    np.testing.assert_allclose(a, oracle.apply_rope(x, 2 * pos + 17.0, base), atol=1e-10)
+    # relative position: <R(q, m), R(k, n)> depends only on n - m
+    qv, kv = rand(1, 1, 1, D), rand(1, 1, 1, D)
+    d1 = np.sum(oracle.apply_rope(qv, np.array([[5.0]]), base) * oracle.apply_rope(kv, np.array([[12.0]]), base))
+    d2 = np.sum(oracle.apply_rope(qv, np.array([[105.0]]), base) * oracle.apply_rope(kv, np.array([[112.0]]), base))
+    assert abs(d1 - d2) < 1e-11
+
+
+def test_qknorm_rope_commutes_and_offsets():
+    q, k = rand(2, 5, 4, 64), rand(2, 5, 2, 64)
+    off = np.array([0, 300])
+    qn, kn = oracle.qknorm_rope(q, k, off, base=10000.0, eps=1e-6, gain=1.0)
+    pos = off[:, None] + np.arange(5)[None]
+    # RoPE then norm gives the same result (norm and rotation commute)
+    alt = oracle.rms_norm(oracle.apply_rope(q, pos, 10000.0), 1e-6)
+    np.testing.assert_allclose(qn, alt, atol=1e-13)
+    np.testing.assert_allclose(kn[1, 2], oracle.apply_rope(oracle.rms_norm(k, 1e-6), pos, 10000.0)[1, 2], atol=1e-14)
+
+
+# ----------------------------------------------------------------- forward
+
+@pytest.mark.parametrize("T,H,KV,D,W", [(16, 2, 2, 8, -1), (16, 4, 2, 8, 3), (33, 6, 2, 16, 0),
+                                        (33, 3, 1, 16, 7), (20, 2, 2, 8, 19), (1, 2, 1, 8, -1)])
+def test_fwd_matches_torch_sdpa(T, H, KV, D, W):
+    q, k, v = rand(2, T, H, D), rand(2, T, KV, D), rand(2, T, KV, D)
+    o, lse = oracle.attn_fwd(q, k, v, W)
+    np.testing.assert_allclose(o, sdpa_ref(q, k, v, W), rtol=1e-12, atol=1e-12)
+    # LSE against torch.logsumexp of the masked scores
+    G = H // KV
+    qt = torch.from_numpy(q).permute(0, 2, 1, 3)
+    kt = torch.from_numpy(k).permute(0, 2, 1, 3).repeat_interleave(G, dim=1)
+    s = qt @ kt.transpose(-1, -2) / math.sqrt(D)
+    i, j = torch.arange(T)[:, None], torch.arange(T)[None, :]
+    vis = (j <= i) & ((i - j <= W) if W >= 0 else torch.ones_like(j <= i))
+    ref_lse = torch.logsumexp(s.masked_fill(~vis, float("-inf")), dim=-1).numpy()
+    np.testing.assert_allclose(lse, ref_lse, rtol=1e-12, atol=1e-12)
+
+
+def test_fwd_closed_forms():
+    T, H, D = 24, 2, 16
+    q, k, v = rand(1, T, H, D), rand(1, T, H, D), rand(1, T, H, D)
+    # W = 0: every query sees only itself
+    o, lse = oracle.attn_fwd(q, k, v, 0)
+    np.testing.assert_allclose(o, v, atol=1e-14)
+    np.testing.assert_allclose(lse, np.einsum("bthd,bthd->bht", q, k) / math.sqrt(D), atol=1e-13)
+    # q = 0: O_i is the mean of the visible v_j and LSE_i = log(n_visible(i))
+    W = 5
+    o, lse = oracle.attn_fwd(np.zeros_like(q), k, v, W)
+    for i in range(T):
+        lo = max(0, i - W)
+        np.testing.assert_allclose(o[0, i], v[0, lo:i + 1].mean(axis=0), atol=1e-13)
+        np.testing.assert_allclose(lse[0, :, i], math.log(i + 1 - lo), atol=1e-13)
+    # W >= T - 1 equals full causal exactly
+    a, _ = oracle.attn_fwd(q, k, v, T - 1)
+    b, _ = oracle.attn_fwd(q, k, v, -1)
+    np.testing.assert_array_equal(a, b)
+    # T = 1 => O = v
+    o1, _ = oracle.attn_fwd(q[:, :1], k[:, :1], v[:, :1], -1)
+    np.testing.assert_allclose(o1, v[:, :1], atol=1e-15)
+
+
+def test_fwd_gqa_equals_mha_on_repeated_kv():
+    q, k, v = rand(2, 12, 6, 8), rand(2, 12, 2, 8), rand(2, 12, 2, 8)
+    a, la = oracle.attn_fwd(q, k, v, 4)
+    b, lb = oracle.attn_fwd(q, np.repeat(k, 3, axis=2), np.repeat(v, 3, axis=2), 4)
+    np.testing.assert_allclose(a, b, atol=1e-14)
+    np.testing.assert_allclose(la, lb, atol=1e-14)
+
+
+def test_pair_count_brute_force():
+    for T in (1, 2, 7, 64, 130):
+        for W in (-1, 0, 1, 5, 63, 129, 500):
+            brute = sum(1 for i in range(T) for j in range(T) if j <= i and (W < 0 or i - j <= W))
+            assert oracle.n_visible_pairs(T, W) == brute == int(oracle.visible_mask(T, W).sum())
+    assert oracle.n_visible_pairs(2048, -1) == 2048 * 2049 // 2
+    # closed form for W < T: W+1 keys for the T-W rows past the ramp, 1..W for the ramp
+    assert oracle.n_visible_pairs(2048, 1024) == (2048 - 1024) * 1025 + 1024 * 1025 // 2
+    fwd, bwd = oracle.attn_flops(8, 2048, 6, 128, 1024)
+    assert (fwd, bwd) == (4 * 128 * 1574400 * 48, 8 * 128 * 1574400 * 48)
+
+
+def test_window_schedule_golden():
+    g = json.load(open(os.path.join(GOLDEN, "window_schedule.json")))
+    for c in g["cases"]:
+        got = oracle.window_sizes(c["pattern"], c["n_layer"], c["short"])
+        assert [list(t) for t in got] == c["expect"], c
+
+
+# ----------------------------------------------------------------- backward
+
+def _loss(q, k, v, do, W):
+    return float(np.sum(oracle.attn_fwd(q, k, v, W)[0] * do))
+
+
+@pytest.mark.parametrize("H,KV,W", [(2, 2, -1), (4, 2, 3), (3, 1, 0)])
+def test_bwd_matches_finite_differences(H, KV, W):
+    T, D, h = 7, 4, 1e-6
+    q, k, v, do = rand(1, T, H, D), rand(1, T, KV, D), rand(1, T, KV, D), rand(1, T, H, D)
+    dq, dk, dv = oracle.attn_bwd(q, k, v, do, W)
+    for x, g in ((q, dq), (k, dk), (v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            old = x[idx]
+            x[idx] = old + h
+            lp = _loss(q, k, v, do, W)
+            x[idx] = old - h
+            lm = _loss(q, k, v, do, W)
+            x[idx] = old
+            num[idx] = (lp - lm) / (2 * h)
+        np.testing.assert_allclose(g, num, atol=2e-8, rtol=1e-6)
+
+
+@pytest.mark.parametrize("T,H,KV,D,W", [(40, 4, 2, 16, -1), (40, 6, 2, 16, 9), (17, 2, 2, 8, 0)])
+def test_bwd_matches_torch_autograd(T, H, KV, D, W):
+    q, k, v, do = rand(2, T, H, D), rand(2, T, KV, D), rand(2, T, KV, D), rand(2, T, H, D)
+    qt, kt, vt = (torch.from_numpy(x).clone().requires_grad_(True) for x in (q, k, v))
+    i, j = torch.arange(T)[:, None], torch.arange(T)[None, :]
+    mask = (j <= i) & ((i - j <= W) if W >= 0 else torch.ones(T, T, dtype=torch.bool))
+    o = F.scaled_dot_product_attention(qt.permute(0, 2, 1, 3), kt.permute(0, 2, 1, 3), vt.permute(0, 2, 1, 3),
+                                       attn_mask=mask, enable_gqa=H != KV).permute(0, 2, 1, 3)
+    (o * torch.from_numpy(do)).sum().backward()
+    dq, dk, dv = oracle.attn_bwd(q, k, v, do, W)
+    np.testing.assert_allclose(dq, qt.grad.numpy(), atol=1e-11)
+    np.testing.assert_allclose(dk, kt.grad.numpy(), atol=1e-11)
+    np.testing.assert_allclose(dv, vt.grad.numpy(), atol=1e-11)
+
+
+def test_bwd_invariants_and_closed_forms():
+    T, H, KV, D = 30, 4, 2, 8
+    q, k, v, do = rand(1, T, H, D), rand(1, T, KV, D), rand(1, T, KV, D), rand(1, T, H, D)
+    dq, dk, dv = oracle.attn_bwd(q, k, v, do, 6)
+    # shifting every key by a constant vector leaves O unchanged: sum_j dK_j = 0
+    np.testing.assert_allclose(dk.sum(axis=1), 0.0, atol=1e-12)
+    # rows of P sum to one: sum_j dV_j = sum over the group's heads of sum_i dO_i
+    np.testing.assert_allclose(dv.sum(axis=1), do.reshape(1, T, KV, 2, D).sum(axis=(1, 3)), atol=1e-12)
+    # W = 0: dQ = dK = 0 and dV_i = sum over the group of dO_i
+    dq, dk, dv = oracle.attn_bwd(q, k, v, do, 0)
+    np.testing.assert_allclose(dq, 0.0, atol=1e-15)
+    np.testing.assert_allclose(dk, 0.0, atol=1e-15)
+    np.testing.assert_allclose(dv, do.reshape(1, T, KV, 2, D).sum(axis=3), atol=1e-14)
+
+
+# ----------------------------------------------------------------- decode
+
+@pytest.mark.parametrize("W", [-1, 0, 3, 50])
+def test_decode_equals_sdpa_last_row(W):
+    B, H, KV, D, Tm = 3, 4, 2, 16, 40
+    lens = np.array([0, 17, 38])
+    q, kn, vn = rand(B, 1, H, D), rand(B, 1, KV, D), rand(B, 1, KV, D)
+    kc, vc = rand(B, Tm, KV, D), rand(B, Tm, KV, D)
+    for b in range(B):
+        kc[b, lens[b]:] = np.nan
+        vc[b, lens[b]:] = np.nan
+    o, lse, kc2, vc2 = oracle.decode(q, kn, vn, kc, vc, lens, W)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    for b in range(B):
+        s = lens[b]
+        # slot s written, everything else untouched (bitwise)
+        np.testing.assert_array_equal(kc2[b, s], kn[b, 0])
+        np.testing.assert_array_equal(vc2[b, s], vn[b, 0])
+        keep = np.ones(Tm, bool)
+        keep[s] = False
+        np.testing.assert_array_equal(np.isnan(kc2[b, keep]), np.isnan(kc[b, keep]))
+        np.testing.assert_array_equal(np.nan_to_num(kc2[b, keep]), np.nan_to_num(kc[b, keep]))
+        # the decode row equals the last row of torch SDPA over the full prefix
+        kf = np.concatenate([kc[b, :s], kn[b]], axis=0)[None]
+        vf = np.concatenate([vc[b, :s], vn[b]], axis=0)[None]
+        qf = np.zeros((1, s + 1, H, D))
+        qf[0, s] = q[b, 0]
+        ref = sdpa_ref(qf, kf, vf, W)[0, s]
+        np.testing.assert_allclose(o[b, 0], ref, atol=1e-12)
+    if W == 0:
+        np.testing.assert_allclose(o[:, 0], np.repeat(vn[:, 0], H // KV, axis=1), atol=1e-15)
+
+
+# ----------------------------------------------------------------- planted mistakes
+
+def test_planted_mistakes_are_caught(monkeypatch):
+    """Each mutant of the oracle must fail at least one pin above."""
+    import oracle.attention as A
+
+    T, H, KV, D = 9, 4, 2, 8
+    q, k, v, do = rand(1, T, H, D), rand(1, T, KV, D), rand(1, T, KV, D), rand(1, T, H, D)
+
+    def fwd_pin(f):
+        o, _ = f(q, k, v, 3)
+        return np.allclose(o, sdpa_ref(q, k, v, 3), atol=1e-10)
+
+    # 1. exclusive window (i - j < W) instead of inclusive
+    def mask_exclusive(T_, W):
+        i, j = np.arange(T_)[:, None], np.arange(T_)[None, :]
+        return (j <= i) & ((i - j < W) if W >= 0 else True)
+    monkeypatch.setattr(A, "visible_mask", mask_exclusive)
+    assert not fwd_pin(A.attn_fwd)
+    monkeypatch.undo()
+
+    # 2. wrong GQA mapping (kv head h % KV instead of h // G)
+    def fwd_bad_gqa(q_, k_, v_, W):
+        kk = np.stack([k_[:, :, h % KV] for h in range(H)], axis=2)
+        vv = np.stack([v_[:, :, h % KV] for h in range(H)], axis=2)
+        return A.attn_fwd(q_, kk, vv, W)
+    assert not fwd_pin(fwd_bad_gqa)
+
+    # 3. backward with the softmax-Jacobian term dropped: finite differences catch it
+    def bwd_dropped(q_, k_, v_, do_, W):
+        Bq, Tq, Hq, Dq = q_.shape
+        scale = 1 / np.sqrt(Dq)
+        vis = A.visible_mask(Tq, W)
+        dq = np.zeros_like(q_)
+        for h in range(Hq):
+            kh = h // (Hq // k_.shape[2])
+            s = np.where(vis, scale * q_[0, :, h] @ k_[0, :, kh].T, -np.inf)
+            p = np.exp(s - s.max(1, keepdims=True))
+            p /= p.sum(1, keepdims=True)
+            dp = do_[0, :, h] @ v_[0, :, kh].T
+            dq[0, :, h] = scale * (p * dp) @ k_[0, :, kh]
+        return dq
+    dq_ref = oracle.attn_bwd(q, k, v, do, 3)[0]
+    assert not np.allclose(bwd_dropped(q, k, v, do, 3), dq_ref, atol=1e-6)
+
+    # 4. RoPE rotating by -theta fails the hand-worked golden values
+    g = json.load(open(os.path.join(GOLDEN, "rope_hand.json")))
+    c = g["cases"][1]
+    x = np.array(c["x"]).reshape(1, 1, 1, 4)
+    bad = A.apply_rope(x, np.array([[-float(c["pos"])]]), g["base"]).reshape(-1)
+    assert not np.allclose(bad, c["expect"], atol=1e-12)
+
+    # 5. interleaved RoPE pairing fails the complex-multiplication pin
+    def rope_interleaved(x_, pos, base):
+        Dd = x_.shape[-1]
+        th = A.rope_angles(pos, Dd, base)[:, :, None, :]
+        a, b = x_[..., 0::2], x_[..., 1::2]
+        out = np.empty_like(x_)
+        out[..., 0::2] = a * np.cos(th) - b * np.sin(th)
+        out[..., 1::2] = a * np.sin(th) + b * np.cos(th)
+        return out
+    xx = rand(1, 3, 1, 8)
+    pos = np.array([[1.0, 2.0, 3.0]])
+    w = np.array([10000.0 ** (-(2.0 * j) / 8) for j in range(4)])
+    z = (xx[..., :4] + 1j * xx[..., 4:]) * np.exp(1j * pos[:, :, None, None] * w)
+    ref = np.concatenate([z.real, z.imag], axis=-1)
+    assert np.allclose(A.apply_rope(xx, pos, 10000.0), ref, atol=1e-12)
+    assert not np.allclose(rope_interleaved(xx, pos, 10000.0), ref, atol=1e-6)
