@@ -1,0 +1,148 @@
+/*
+ * ncattn -- QK-norm + RoPE + causal sliding-window grouped-query attention
+ * (forward, backward, single-token decode) for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (page titles and sections of the sources):
+ *   - "nanochat Admin & Developer Guide", section 3 "The GPT Model (Internals)":
+ *     rotary embeddings (base 100000 there), QK-norm = weightless RMSNorm of q and
+ *     k (optionally followed by a logit gain), grouped-query attention
+ *     (n_kv_head <= n_head), per-layer sliding windows given as (left, right).
+ *   - same page, section 6 "Attention: FA3 with SDPA Fallback": full-context
+ *     training attention, single-token decode over the window, GQA.
+ *   - same page, section 7 "The Inference Engine & Tool Use", "KV cache": the
+ *     cache is (B, T, H, D) per layer with per-sequence int32 cache_seqlens and
+ *     the new token is written into it in place.
+ *   - "nanoGPT Administrator & Developer Guide", section 8, model.py
+ *     CausalSelfAttention: softmax(q k^T / sqrt(d_k) + causal mask) v.
+ *   - "nanochat (Python)" catalog, AI / Model & kernels / Backward pass: the
+ *     backward is the exact gradient (autograd) of that forward.
+ *
+ * Conventions shared by every call:
+ *   - Tensor pointers are DEVICE pointers owned by the caller; tensors are
+ *     contiguous and row-major in the layouts given per argument, and 16-byte
+ *     aligned.  bf16 is IEEE bfloat16 (stored as uint16), f32 is IEEE float.
+ *   - Calls enqueue kernels on `stream` (a hipStream_t; NULL = the default
+ *     stream) and return without synchronising.  The library never allocates
+ *     device memory: scratch space is passed in as `workspace`.
+ *   - Key j is visible to query i iff j <= i and (window_left < 0 or
+ *     i - j <= window_left): the inclusive (left, right) = (W, 0) convention.
+ *     window_right must be 0.
+ *   - softmax_scale <= 0 selects 1 / sqrt(head_dim).
+ *   - Query head h reads kv head h / (n_head / n_kv_head).
+ *   - Return value: NCATTN_OK, or a negative ncattn_status_t.  Arguments are
+ *     validated on the host before anything is launched; on error nothing is
+ *     enqueued and ncattn_last_error() (thread-local) describes the problem.
+ *     No C++ exception crosses this interface.
+ *   - Outputs must not alias inputs, except where a call says it works in place.
+ *   - Apart from the thread-local error string the library keeps no mutable
+ *     global state; calls on different streams may run concurrently.
+ *
+ * Supported: dtype NCATTN_BF16 (fp32 accumulation, bf16 MFMA contractions) with
+ * head_dim 128; dtype NCATTN_F32 (fp32 throughout) with head_dim 64 or 128.
+ * Decode is bf16 only.  Anything else returns NCATTN_EUNSUPPORTED.
+ */
+#ifndef NCATTN_H
+#define NCATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { NCATTN_BF16 = 0, NCATTN_F32 = 1 } ncattn_dtype_t;
+
+typedef enum {
+  NCATTN_OK = 0,
+  NCATTN_EINVAL = -1,       /* bad argument (NULL, non-positive size, misaligned, ...) */
+  NCATTN_EUNSUPPORTED = -2, /* valid but not implemented (head_dim, dtype combination) */
+  NCATTN_EWORKSPACE = -3,   /* workspace missing or smaller than *_workspace_bytes()   */
+  NCATTN_EHIP = -4          /* the HIP runtime reported an error at launch             */
+} ncattn_status_t;
+
+/*
+ * QK-norm + RoPE, in place ("nanochat Admin & Developer Guide", section 3).
+ * For every row x (one head of one token) of q [B][T][n_head][head_dim] and of
+ * k [B][T][n_kv_head][head_dim]:
+ *     x <- qk_gain * x / sqrt(mean_d(x_d^2) + eps)
+ *     (x_j, x_{j+D/2}) <- (x_j cos a - x_{j+D/2} sin a, x_j sin a + x_{j+D/2} cos a),
+ *     a = pos * rope_base^(-2j/D), pos = pos_offset[b] + t   (j < D/2)
+ * pos_offset: device int32 [B], or NULL for 0 (decode passes cache_seqlens).
+ * Arithmetic is fp32 with the angle reduced in fp64; storage stays in `dtype`.
+ * v is not touched.  q and k are read and written in place.
+ */
+int ncattn_qknorm_rope(void *q, void *k, int B, int T, int n_head, int n_kv_head, int head_dim,
+                       const int32_t *pos_offset, float rope_base, float eps, float qk_gain,
+                       int dtype, void *stream);
+
+/*
+ * Attention forward ("nanoGPT Administrator & Developer Guide" section 8;
+ * "nanochat Admin & Developer Guide" sections 3 and 6).
+ *   q [B][T][n_head][D], k, v [B][T][n_kv_head][D]          (dtype)
+ *   o [B][T][n_head][D]                                      (dtype, written)
+ *   lse [B][n_head][T] fp32, natural-log logsumexp of the scaled visible
+ *   scores of each query row (written; every row has at least its own key).
+ * Tiles of keys outside every row's window are skipped.
+ */
+int ncattn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+               int B, int T, int n_head, int n_kv_head, int head_dim,
+               int window_left, int window_right, float softmax_scale, int dtype, void *stream);
+
+/* Bytes of workspace ncattn_bwd needs (the per-row fp32 D_i = sum_d dO*O). */
+size_t ncattn_bwd_workspace_bytes(int B, int T, int n_head, int n_kv_head, int head_dim, int dtype);
+
+/*
+ * Attention backward: the exact gradient of sum(O * dO) ("nanochat (Python)"
+ * catalog, Backward pass = autograd of the forward).
+ *   inputs q, k, v, o (as from ncattn_fwd), lse [B][n_head][T] fp32 from
+ *   ncattn_fwd, dout [B][T][n_head][D]; outputs dq [B][T][n_head][D],
+ *   dk, dv [B][T][n_kv_head][D] (dtype; fp32 accumulation).  dk and dv of a kv
+ *   head are summed over the query heads of its group.  Deterministic: no
+ *   atomics, the same inputs give the same bits.
+ *   workspace: device memory of at least ncattn_bwd_workspace_bytes(...) bytes,
+ *   overwritten.
+ */
+int ncattn_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
+               const void *dout, void *dq, void *dk, void *dv,
+               int B, int T, int n_head, int n_kv_head, int head_dim,
+               int window_left, int window_right, float softmax_scale, int dtype,
+               void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace ncattn_decode needs (split-KV partial results). */
+size_t ncattn_decode_workspace_bytes(int B, int T_max, int n_head, int n_kv_head, int head_dim,
+                                     int window_left);
+
+/*
+ * Single-token decode against a KV cache ("nanochat Admin & Developer Guide",
+ * sections 6 and 7).  For every sequence b with s = cache_seqlens[b]:
+ *   1. k_new[b], v_new[b] are written into cache slot s (in place);
+ *   2. o[b] = softmax(scale * q[b] . K[j]) V[j] over j in [max(0, s - W), s]
+ *      (all of [0, s] when window_left < 0), key s being the new one.
+ *   q [B][1][n_head][D], k_new, v_new [B][1][n_kv_head][D],
+ *   k_cache, v_cache [B][T_max][n_kv_head][D] (bf16), cache_seqlens device
+ *   int32 [B] (NOT advanced: the caller owns the position),
+ *   o [B][1][n_head][D] bf16, lse [B][n_head] fp32 or NULL.
+ *   Precondition 0 <= cache_seqlens[b] < T_max (not checkable on the host
+ *   without a sync): a row that breaks it is skipped, its cache is left
+ *   untouched and o[b] (and lse[b]) are set to NaN.
+ *   workspace: at least ncattn_decode_workspace_bytes(...) bytes, overwritten.
+ */
+int ncattn_decode(const void *q, const void *k_new, const void *v_new,
+                  void *k_cache, void *v_cache, const int32_t *cache_seqlens,
+                  void *o, float *lse,
+                  int B, int T_max, int n_head, int n_kv_head, int head_dim,
+                  int window_left, float softmax_scale, int dtype,
+                  void *workspace, size_t workspace_bytes, void *stream);
+
+/* Thread-local description of the last non-OK return on this thread ("" if none). */
+const char *ncattn_last_error(void);
+
+/* Library version string. */
+const char *ncattn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NCATTN_H */

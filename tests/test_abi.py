@@ -1,0 +1,133 @@
+"""CPU-side checks of the C-ABI library: it loads, exports every function that
+include/ncattn.h declares, and rejects bad arguments on the host with the right
+status code before anything is launched (so these run without a GPU)."""
+
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+import transformer_attention_qknorm_amd as nc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ncattn.h")
+
+EINVAL, EUNSUP, EWS = -1, -2, -3
+P = 4096          # a fake, 16-byte-aligned, non-NULL "device pointer": never dereferenced
+MIS = 4096 + 8    # misaligned
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(nc.LIB_PATH):
+        from transformer_attention_qknorm_amd._build import build
+        build()
+    return nc.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ncattn_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert {"ncattn_qknorm_rope", "ncattn_fwd", "ncattn_bwd", "ncattn_decode"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), f"libncattn.so does not export {n}"
+    # and the shared object's dynamic symbol table agrees
+    import subprocess
+    syms = subprocess.run(["nm", "-D", "--defined-only", nc.LIB_PATH], capture_output=True, text=True).stdout
+    for n in names:
+        assert re.search(rf"\bT {n}\b", syms), n
+
+
+def test_version_and_empty_error(L):
+    assert L.ncattn_version().decode().startswith("ncattn")
+    assert isinstance(L.ncattn_last_error(), bytes)
+
+
+def fwd(L, q=P, k=P, v=P, o=P + 16, lse=P + 32, B=1, T=64, H=2, KV=2, D=128, wl=-1, wr=0, scale=0.0, dt=0):
+    return L.ncattn_fwd(q, k, v, o, lse, B, T, H, KV, D, wl, wr, scale, dt, None)
+
+
+def test_fwd_validation(L):
+    assert fwd(L, q=None) == EINVAL
+    assert "q is NULL" in L.ncattn_last_error().decode()
+    assert fwd(L, k=MIS) == EINVAL
+    assert "aligned" in L.ncattn_last_error().decode()
+    assert fwd(L, B=0) == EINVAL
+    assert fwd(L, T=-3) == EINVAL
+    assert fwd(L, H=6, KV=4) == EINVAL
+    assert fwd(L, wl=-2) == EINVAL
+    assert fwd(L, wr=1) == EINVAL
+    assert fwd(L, dt=7) == EINVAL
+    assert fwd(L, D=64) == EUNSUP          # bf16 MFMA path is head_dim 128
+    assert fwd(L, D=96, dt=1) == EUNSUP
+    assert fwd(L, o=P) == EINVAL            # o aliases q
+    assert fwd(L, scale=float("nan")) == EINVAL
+
+
+def test_qknorm_rope_validation(L):
+    f = L.ncattn_qknorm_rope
+    assert f(None, P, 1, 4, 2, 2, 128, None, 1e5, 1e-6, 1.0, 0, None) == EINVAL
+    assert f(P, P + 16, 1, 4, 2, 2, 96, None, 1e5, 1e-6, 1.0, 0, None) == EUNSUP
+    assert f(P, P + 16, 1, 4, 2, 2, 128, None, 0.5, 1e-6, 1.0, 0, None) == EINVAL
+    assert f(P, P + 16, 1, 4, 2, 2, 128, None, 1e5, -1.0, 1.0, 0, None) == EINVAL
+    assert f(P, P + 16, 1, 4, 2, 2, 128, P + 2, 1e5, 1e-6, 1.0, 0, None) == EINVAL  # pos_offset misaligned
+    assert f(P, P + 16, 1, 4, 3, 2, 128, None, 1e5, 1e-6, 1.0, 0, None) == EINVAL
+
+
+def test_bwd_validation_and_workspace(L):
+    need = L.ncattn_bwd_workspace_bytes(2, 100, 4, 2, 128, 0)
+    assert need == 2 * 4 * 100 * 4
+    args = [P, P + 16, P + 32, P + 48, P + 64, P + 80, P + 96, P + 112, P + 128, 2, 100, 4, 2, 128, -1, 0, 0.0, 0]
+    assert L.ncattn_bwd(*args, None, 0, None) == EWS
+    assert L.ncattn_bwd(*args, P + 256, need - 1, None) == EWS
+    bad = list(args)
+    bad[6] = P  # dq aliases q
+    assert L.ncattn_bwd(*bad, P + 256, need, None) == EINVAL
+    bad = list(args)
+    bad[7] = bad[8]  # dk == dv
+    assert L.ncattn_bwd(*bad, P + 256, need, None) == EINVAL
+    bad = list(args)
+    bad[14] = -5
+    assert L.ncattn_bwd(*bad, P + 256, need, None) == EINVAL
+
+
+def test_decode_validation_and_workspace(L):
+    n_full = L.ncattn_decode_workspace_bytes(64, 8320, 10, 10, 128, -1)
+    n_win = L.ncattn_decode_workspace_bytes(64, 8320, 10, 10, 128, 1024)
+    assert n_full > n_win > 0
+    assert L.ncattn_decode_workspace_bytes(0, 8320, 10, 10, 128, -1) == 0
+    base = [P, P + 16, P + 32, P + 48, P + 64, P + 80, P + 96, None, 4, 512, 2, 2, 128, -1, 0.0]
+    ws = L.ncattn_decode_workspace_bytes(4, 512, 2, 2, 128, -1)
+    assert L.ncattn_decode(*base, 1, P + 256, ws, None) == EUNSUP       # fp32 decode
+    assert L.ncattn_decode(*base, 0, None, 0, None) == EWS
+    bad = list(base)
+    bad[5] = P + 82                                                    # seqlens misaligned
+    assert L.ncattn_decode(*bad, 0, P + 256, ws, None) == EINVAL
+    bad = list(base)
+    bad[4] = bad[3]                                                    # k_cache == v_cache
+    assert L.ncattn_decode(*bad, 0, P + 256, ws, None) == EINVAL
+    bad = list(base)
+    bad[12] = 64
+    assert L.ncattn_decode(*bad, 0, P + 256, ws, None) == EUNSUP
+
+
+def test_window_sizes_binding_golden():
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "window_schedule.json")))
+    for c in g["cases"]:
+        assert [list(t) for t in nc.window_sizes(c["pattern"], c["n_layer"], c["short"])] == c["expect"]
+    with pytest.raises(ValueError):
+        nc.window_sizes("SXL", 4, 128)
+
+
+def test_binding_fails_loudly_without_gpu_tensors():
+    import torch
+    x = torch.zeros(1, 4, 2, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        nc.fwd(x, x, x)

@@ -1,0 +1,202 @@
+"""GPU parity of every hot-path call against the CPU oracle, element by element,
+at sizes the oracle finishes in seconds that still span several tiles and a
+ragged tail, plus the edge cases: T = 1, windows 0 / 1 / tile-1 / tile / tile+1 /
+T-1 / larger than T, GQA groups, empty and full caches, invalid cache lengths,
+NaN-poisoned cache slots, and run-twice determinism."""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import transformer_attention_qknorm_amd as nc
+from parity_util import LSE_TOL, TOL, check, check_lse, f64
+from workloads import attn_inputs, decode_inputs
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def to_dev(*ts):
+    return [t.to(DEV) for t in ts]
+
+
+# ------------------------------------------------------------------ QK-norm + RoPE
+
+@pytest.mark.parametrize("dtype,B,T,H,KV,D,base,gain,offset", [
+    ("f32", 1, 64, 2, 2, 64, 10000.0, 1.0, False),
+    ("f32", 2, 37, 4, 2, 128, 100000.0, math.sqrt(1.2), True),
+    ("bf16", 3, 130, 6, 6, 128, 100000.0, 1.0, False),
+    ("bf16", 64, 1, 10, 10, 128, 100000.0, 1.0, True),     # decode: one token at pos = cache length
+    ("bf16", 2, 50, 12, 4, 64, 10000.0, math.sqrt(1.2), True),
+])
+def test_qknorm_rope(dtype, B, T, H, KV, D, base, gain, offset):
+    say(f"qknorm_rope {dtype} B={B} T={T} H={H} KV={KV} D={D}")
+    q, k, v, _ = attn_inputs(B, T, H, KV, D, dtype, seed=11)
+    pos = torch.from_numpy(np.random.default_rng(3).integers(0, 8192, size=B).astype(np.int32)) if offset else None
+    ref_q, ref_k = oracle.qknorm_rope(f64(q), f64(k), None if pos is None else pos.numpy(), base, 1e-6, gain)
+    qd, kd, vd = to_dev(q, k, v)
+    v_before = vd.clone()
+    nc.qknorm_rope_(qd, kd, None if pos is None else pos.to(DEV), rope_base=base, eps=1e-6, qk_gain=gain)
+    torch.cuda.synchronize()
+    check(qd, ref_q, dtype, "q")
+    check(kd, ref_k, dtype, "k")
+    assert torch.equal(vd, v_before)
+
+
+# ------------------------------------------------------------------ forward / backward
+
+FWD_CASES = [
+    # dtype, B, T, H, KV, D, W
+    ("bf16", 2, 200, 4, 2, 128, -1),
+    ("bf16", 2, 200, 4, 2, 128, 0),
+    ("bf16", 2, 200, 4, 2, 128, 1),
+    ("bf16", 2, 200, 4, 2, 128, 63),
+    ("bf16", 2, 200, 4, 2, 128, 64),
+    ("bf16", 2, 200, 4, 2, 128, 65),
+    ("bf16", 2, 200, 4, 2, 128, 127),
+    ("bf16", 2, 200, 4, 2, 128, 128),
+    ("bf16", 2, 200, 4, 2, 128, 199),
+    ("bf16", 2, 200, 4, 2, 128, 5000),
+    ("bf16", 1, 1, 2, 1, 128, -1),
+    ("bf16", 1, 64, 2, 2, 128, -1),
+    ("bf16", 1, 129, 3, 1, 128, 20),
+    ("bf16", 3, 520, 2, 2, 128, -1),
+    ("bf16", 1, 777, 6, 2, 128, 256),
+    ("f32", 1, 64, 2, 2, 64, -1),
+    ("f32", 2, 100, 4, 2, 64, 17),
+    ("f32", 1, 150, 2, 1, 128, -1),
+    ("f32", 1, 150, 3, 3, 128, 40),
+]
+
+
+def _ids(c):
+    return "-".join(str(x) for x in c)
+
+
+@pytest.mark.parametrize("case", FWD_CASES, ids=[_ids(c) for c in FWD_CASES])
+def test_fwd_bwd(case):
+    dtype, B, T, H, KV, D, W = case
+    say(f"fwd/bwd {case}")
+    q, k, v, do = attn_inputs(B, T, H, KV, D, dtype, seed=100 + T + W)
+    ro, rlse = oracle.attn_fwd(f64(q), f64(k), f64(v), W)
+    rdq, rdk, rdv = oracle.attn_bwd(f64(q), f64(k), f64(v), f64(do), W)
+    qd, kd, vd, dod = to_dev(q, k, v, do)
+    o, lse = nc.fwd(qd, kd, vd, window=(W, 0))
+    torch.cuda.synchronize()
+    check(o, ro, dtype, "o")
+    check_lse(lse, rlse, dtype, "lse")
+    dq, dk, dv = nc.bwd(qd, kd, vd, o, lse, dod, window=(W, 0))
+    torch.cuda.synchronize()
+    check(dq, rdq, dtype, "dq")
+    check(dk, rdk, dtype, "dk")
+    check(dv, rdv, dtype, "dv")
+
+
+def test_fwd_bwd_closed_forms_on_gpu():
+    """W = 0 gives O = v, dQ = dK = 0, dV = sum of the group's dO (exact up to rounding)."""
+    q, k, v, do = to_dev(*attn_inputs(2, 300, 4, 2, 128, "bf16", seed=9))
+    o, lse = nc.fwd(q, k, v, window=(0, 0))
+    torch.cuda.synchronize()
+    assert torch.equal(o, v.repeat_interleave(2, dim=2))
+    dq, dk, dv = nc.bwd(q, k, v, o, lse, do, window=(0, 0))
+    torch.cuda.synchronize()
+    assert float(dq.abs().max()) == 0.0 and float(dk.abs().max()) == 0.0
+    ref = f64(do).reshape(2, 300, 2, 2, 128).sum(axis=3)
+    check(dv, ref, "bf16", "dv(W=0)")
+
+
+def test_determinism():
+    q, k, v, do = to_dev(*attn_inputs(2, 700, 6, 2, 128, "bf16", seed=5))
+    for W in (-1, 100):
+        o1, l1 = nc.fwd(q, k, v, window=(W, 0))
+        o2, l2 = nc.fwd(q, k, v, window=(W, 0))
+        g1 = nc.bwd(q, k, v, o1, l1, do, window=(W, 0))
+        g2 = nc.bwd(q, k, v, o1, l1, do, window=(W, 0))
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+        for a, b in zip(g1, g2):
+            assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------------ decode
+
+@pytest.mark.parametrize("W", [-1, 0, 1, 100, 127, 128, 129, 400])
+def test_decode_small(W):
+    say(f"decode small W={W}")
+    B, H, KV, D, Tm = 6, 4, 2, 128, 300
+    q, kn, vn, kc, vc, lens = decode_inputs(B, H, KV, D, 1, 290, Tm, seed=21, poison=False)
+    lens = torch.tensor([0, 1, 127, 128, 129, 299], dtype=torch.int32)
+    # poison every slot from each sequence's length on (the oracle never reads them)
+    for b in range(B):
+        kc[b, int(lens[b]):] = float("nan")
+        vc[b, int(lens[b]):] = float("nan")
+    ro, rlse, rkc, rvc = oracle.decode(f64(q), f64(kn), f64(vn), f64(kc), f64(vc), lens.numpy(), W)
+    qd, knd, vnd, kcd, vcd, ld = to_dev(q, kn, vn, kc, vc, lens)
+    o, lse = nc.decode(qd, knd, vnd, kcd, vcd, ld, window=W, return_lse=True)
+    torch.cuda.synchronize()
+    check(o, ro, "bf16", "o")
+    check_lse(lse, rlse, "bf16", "lse")
+    # the new slot is written bit-exactly, every other slot is untouched (NaNs included)
+    kc_after, vc_after = kcd.cpu(), vcd.cpu()
+    for b in range(B):
+        s = int(lens[b])
+        assert torch.equal(kc_after[b, s], kn[b, 0]) and torch.equal(vc_after[b, s], vn[b, 0])
+    mask = torch.ones(B, Tm, dtype=torch.bool)
+    mask[torch.arange(B), lens.long()] = False
+    for a, b_ in ((kc_after, kc), (vc_after, vc)):
+        x, y = a[mask].view(torch.int16), b_[mask].view(torch.int16)
+        assert torch.equal(x, y)
+
+
+def test_decode_matches_fwd_row():
+    """Decode at position s equals row s of the forward over the prefix (the
+    incremental computation equals the full one)."""
+    B, T, H, KV, D = 3, 333, 6, 2, 128
+    q, k, v, _ = attn_inputs(B, T, H, KV, D, "bf16", seed=8)
+    qd, kd, vd = to_dev(q, k, v)
+    for W in (-1, 64):
+        o_full, lse_full = nc.fwd(qd, kd, vd, window=(W, 0))
+        s = T - 1
+        kc = torch.zeros(B, T + 5, KV, D, dtype=torch.bfloat16, device=DEV)
+        vc = torch.zeros_like(kc)
+        kc[:, :s] = kd[:, :s]
+        vc[:, :s] = vd[:, :s]
+        lens = torch.full((B,), s, dtype=torch.int32, device=DEV)
+        o, lse = nc.decode(qd[:, s:s + 1].contiguous(), kd[:, s:s + 1].contiguous(), vd[:, s:s + 1].contiguous(),
+                           kc, vc, lens, window=W, return_lse=True)
+        torch.cuda.synchronize()
+        d = (o.float() - o_full[:, s:s + 1].float()).abs().max().item()
+        assert d <= 1.6e-2, d
+        assert (lse - lse_full[:, :, s]).abs().max().item() <= 1e-3
+
+
+def test_decode_invalid_lengths_give_nan_and_leave_cache():
+    B, H, KV, D, Tm = 3, 2, 2, 128, 64
+    q, kn, vn, kc, vc, _ = decode_inputs(B, H, KV, D, 1, 10, Tm, seed=2, poison=False)
+    lens = torch.tensor([-1, 5, Tm], dtype=torch.int32)
+    qd, knd, vnd, kcd, vcd, ld = to_dev(q, kn, vn, kc, vc, lens)
+    o, lse = nc.decode(qd, knd, vnd, kcd, vcd, ld, return_lse=True)
+    torch.cuda.synchronize()
+    o, lse = o.cpu(), lse.cpu()
+    assert torch.isnan(o[0]).all() and torch.isnan(o[2]).all() and torch.isfinite(o[1]).all()
+    assert torch.isnan(lse[0]).all() and torch.isnan(lse[2]).all()
+    kca = kcd.cpu()
+    assert torch.equal(kca[0], kc[0]) and torch.equal(kca[2], kc[2])
+    assert torch.equal(kca[1, 5], kn[1, 0])
+
+
+def test_decode_deterministic():
+    q, kn, vn, kc, vc, lens = to_dev(*decode_inputs(8, 4, 4, 128, 256, 2000, 2048, seed=4, poison=False))
+    for W in (-1, 1024):
+        o1 = nc.decode(q, kn, vn, kc, vc, lens, window=W)
+        o2 = nc.decode(q, kn, vn, kc, vc, lens, window=W)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2)

@@ -1,0 +1,210 @@
+"""ncattn: QK-norm + RoPE + causal sliding-window GQA attention for MI355X (gfx950).
+
+Thin Python binding over the C-ABI library ``libncattn.so`` (declared in
+``include/ncattn.h``).  This module only marshals arguments: it checks tensor
+dtypes/devices/shapes, allocates outputs and workspace with torch, and passes
+raw device pointers plus torch's current HIP stream to the library.  Every step
+of the computation runs in the library's HIP kernels; there is no fallback.
+If the library is missing or cannot be loaded every call raises.
+
+Functions (names follow the C ABI):
+    qknorm_rope_(q, k, pos_offset=None, rope_base=1e5, eps=1e-6, qk_gain=1.0)
+    fwd(q, k, v, window=(-1, 0), softmax_scale=None) -> (o, lse)
+    bwd(q, k, v, o, lse, do, window=(-1, 0), softmax_scale=None) -> (dq, dk, dv)
+    decode(q, k_new, v_new, k_cache, v_cache, cache_seqlens, window=-1,
+           softmax_scale=None, return_lse=False) -> o  (or (o, lse))
+    window_sizes(pattern, n_layer, short_window, long_window=-1) -> [(left, 0), ...]
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["qknorm_rope_", "fwd", "bwd", "decode", "window_sizes", "lib", "NcattnError", "LIB_PATH",
+           "BF16", "F32", "STATUS"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libncattn.so")
+BF16, F32 = 0, 1
+STATUS = {0: "OK", -1: "EINVAL", -2: "EUNSUPPORTED", -3: "EWORKSPACE", -4: "EHIP"}
+
+_lib = None
+
+
+class NcattnError(RuntimeError):
+    def __init__(self, fn, code, msg):
+        super().__init__(f"{fn} failed with {STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+def lib():
+    """The loaded ctypes handle of libncattn.so (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"ncattn: {LIB_PATH} is not built; run "
+                          f"`python -m transformer_attention_qknorm_amd._build` (hipcc, gfx950)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.ncattn_qknorm_rope.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, f32, f32, f32, i32, vp]
+    L.ncattn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp]
+    L.ncattn_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+    L.ncattn_bwd_workspace_bytes.restype = sz
+    L.ncattn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32,
+                             vp, sz, vp]
+    L.ncattn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+    L.ncattn_decode_workspace_bytes.restype = sz
+    L.ncattn_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp, sz, vp]
+    L.ncattn_last_error.restype = ctypes.c_char_p
+    L.ncattn_version.restype = ctypes.c_char_p
+    for fn in ("ncattn_qknorm_rope", "ncattn_fwd", "ncattn_bwd", "ncattn_decode"):
+        getattr(L, fn).restype = i32
+    _lib = L
+    return L
+
+
+def _check(fn, rc):
+    if rc != 0:
+        raise NcattnError(fn, rc, lib().ncattn_last_error().decode())
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"ncattn: unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _dev(*ts):
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("ncattn: tensors must live on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("ncattn: tensors must be contiguous")
+    dev = ts[0].device
+    if any(t.device != dev for t in ts):
+        raise ValueError("ncattn: tensors must share one device")
+    return dev
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream(dev):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _window(window):
+    if isinstance(window, int):
+        return window, 0
+    wl, wr = window
+    return int(wl), int(wr)
+
+
+def _scale(softmax_scale):
+    return 0.0 if softmax_scale is None else float(softmax_scale)
+
+
+def qknorm_rope_(q, k, pos_offset=None, rope_base=100000.0, eps=1e-6, qk_gain=1.0):
+    """In-place QK-norm + RoPE of q [B][T][H][D] and k [B][T][KV][D]; returns (q, k)."""
+    dev = _dev(q, k)
+    if q.dtype != k.dtype or q.dim() != 4 or k.dim() != 4:
+        raise ValueError("ncattn.qknorm_rope_: q and k must be 4-D tensors of one dtype")
+    B, T, H, D = q.shape
+    if k.shape[0] != B or k.shape[1] != T or k.shape[3] != D:
+        raise ValueError("ncattn.qknorm_rope_: k must be [B][T][n_kv_head][D] matching q")
+    if pos_offset is not None:
+        _dev(pos_offset)
+        if pos_offset.dtype != torch.int32 or pos_offset.numel() != B:
+            raise ValueError("ncattn.qknorm_rope_: pos_offset must be int32 [B]")
+    with torch.cuda.device(dev):
+        rc = lib().ncattn_qknorm_rope(_ptr(q), _ptr(k), B, T, H, k.shape[2], D, _ptr(pos_offset),
+                                      float(rope_base), float(eps), float(qk_gain), _dtype_code(q), _stream(dev))
+    _check("ncattn_qknorm_rope", rc)
+    return q, k
+
+
+def fwd(q, k, v, window=(-1, 0), softmax_scale=None):
+    """Attention forward: returns (o [B][T][H][D], lse [B][H][T] fp32)."""
+    dev = _dev(q, k, v)
+    B, T, H, D = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[1] != T or k.shape[3] != D or q.dtype != k.dtype \
+            or q.dtype != v.dtype:
+        raise ValueError("ncattn.fwd: k, v must be [B][T][n_kv_head][D] of q's dtype")
+    wl, wr = _window(window)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    with torch.cuda.device(dev):
+        rc = lib().ncattn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, T, H, k.shape[2], D, wl, wr,
+                              _scale(softmax_scale), _dtype_code(q), _stream(dev))
+    _check("ncattn_fwd", rc)
+    return o, lse
+
+
+def bwd(q, k, v, o, lse, do, window=(-1, 0), softmax_scale=None):
+    """Attention backward: returns (dq, dk, dv)."""
+    dev = _dev(q, k, v, o, lse, do)
+    B, T, H, D = q.shape
+    KV = k.shape[2]
+    if o.shape != q.shape or do.shape != q.shape or lse.shape != (B, H, T) or lse.dtype != torch.float32:
+        raise ValueError("ncattn.bwd: o, do must match q and lse must be fp32 [B][H][T]")
+    if k.shape != v.shape or q.dtype != k.dtype or q.dtype != v.dtype or q.dtype != o.dtype or q.dtype != do.dtype:
+        raise ValueError("ncattn.bwd: inconsistent shapes or dtypes")
+    wl, wr = _window(window)
+    dt = _dtype_code(q)
+    L = lib()
+    nws = L.ncattn_bwd_workspace_bytes(B, T, H, KV, D, dt)
+    ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    with torch.cuda.device(dev):
+        rc = L.ncattn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv),
+                          B, T, H, KV, D, wl, wr, _scale(softmax_scale), dt, _ptr(ws), ws.numel(), _stream(dev))
+    _check("ncattn_bwd", rc)
+    return dq, dk, dv
+
+
+def decode(q, k_new, v_new, k_cache, v_cache, cache_seqlens, window=-1, softmax_scale=None, return_lse=False):
+    """Single-token decode; writes k_new/v_new into cache slot cache_seqlens[b] in place.
+
+    q [B][1][H][D], k_new/v_new [B][1][KV][D], caches [B][T_max][KV][D] (bf16),
+    cache_seqlens int32 [B] (not advanced).  Returns o [B][1][H][D] (and lse [B][H]).
+    """
+    dev = _dev(q, k_new, v_new, k_cache, v_cache, cache_seqlens)
+    B, one, H, D = q.shape
+    T_max, KV = k_cache.shape[1], k_cache.shape[2]
+    if one != 1 or k_new.shape != (B, 1, KV, D) or v_new.shape != (B, 1, KV, D) \
+            or k_cache.shape != v_cache.shape or k_cache.shape[0] != B or k_cache.shape[3] != D:
+        raise ValueError("ncattn.decode: inconsistent shapes")
+    if cache_seqlens.dtype != torch.int32 or cache_seqlens.numel() != B:
+        raise ValueError("ncattn.decode: cache_seqlens must be int32 [B]")
+    wl = window if isinstance(window, int) else _window(window)[0]
+    dt = _dtype_code(q)
+    L = lib()
+    nws = L.ncattn_decode_workspace_bytes(B, T_max, H, KV, D, wl)
+    ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H), dtype=torch.float32, device=dev) if return_lse else None
+    with torch.cuda.device(dev):
+        rc = L.ncattn_decode(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(cache_seqlens),
+                             _ptr(o), _ptr(lse), B, T_max, H, KV, D, wl, _scale(softmax_scale), dt, _ptr(ws),
+                             ws.numel(), _stream(dev))
+    _check("ncattn_decode", rc)
+    return (o, lse) if return_lse else o
+
+
+def window_sizes(pattern, n_layer, short_window, long_window=-1):
+    """Per-layer (left, right) windows from a pattern of 'S'/'L' tiled over the
+    layers, the final layer always 'L' ("nanochat Admin & Developer Guide",
+    section 3, "Sliding-window attention"); -1 means unbounded."""
+    p = str(pattern).upper()
+    if not p or set(p) - {"S", "L"}:
+        raise ValueError("window pattern must be a non-empty string over {'S', 'L'}")
+    sizes = [short_window if p[i % len(p)] == "S" else long_window for i in range(n_layer)]
+    if n_layer:
+        sizes[-1] = long_window
+    return [(w, 0) for w in sizes]

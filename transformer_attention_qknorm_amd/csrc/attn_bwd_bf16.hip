@@ -1,0 +1,379 @@
+// Attention backward, bf16 in/out, fp32 accumulation, head_dim 128, gfx950 MFMA.
+//
+// The exact gradient of sum(O * dO) through the forward ("nanochat (Python)"
+// catalog, AI / Model & kernels / Backward pass: autograd of the forward).  With
+// P_ij = exp(scale q_i.k_j - LSE_i) on visible pairs and D_i = sum_d dO_i O_i:
+//   dV_j = sum_i P_ij dO_i            dP_ij = dO_i . v_j
+//   dS_ij = P_ij (dP_ij - D_i)        dQ_i = scale sum_j dS_ij k_j
+//   dK_j = scale sum_i dS_ij q_i      (dK, dV summed over the G heads of a group)
+// (D_i equals sum_j P_ij dP_ij, the softmax-Jacobian term, because O_i = sum_j P_ij v_j.)
+//
+// Three kernels, no atomics (deterministic):
+//   1. bwd_delta: D_i per (b, h, i) into the workspace.
+//   2. bwd_dkdv: one workgroup per (b, kv head, 128-key block), wave w owns keys
+//      32w..32w+31 and keeps K, V for them in registers; it walks 64-row query
+//      tiles (Q, dO, LSE, D staged in LDS, double-buffered) for every query head of
+//      the group, computing S = Q K^T, dP = dO V^T (queries as MFMA rows, the
+//      wave's keys as columns), then dV^T += dO^T P and dK^T += Q^T dS with
+//      transposing LDS reads of dO and Q.
+//   3. bwd_dq: one workgroup per (b, h, 128-row query block), like the forward:
+//      S^T = K Q^T and dP^T = V dO^T with Q, dO in registers, dQ^T += K^T dS^T.
+// Tiles with no visible pair are skipped; masks only on straddling tiles.
+#include "attn_tiles.hpp"
+#include "internal.hpp"
+
+namespace ncattn {
+
+namespace {
+
+constexpr int kBlockM = 128;  // query rows per dq workgroup
+constexpr int kBlockN = 128;  // keys per dkdv workgroup
+
+// ---------------------------------------------------------------- D_i = dO . O
+__global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t *__restrict__ O,
+                                                        const uint16_t *__restrict__ dO, float *__restrict__ delta,
+                                                        int B, int T, int H) {
+  // 16 lanes per (token, head) row, 16 rows per block
+  const long long row = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int part = threadIdx.x & 15;
+  const long long nrows = (long long)B * T * H;
+  float s = 0.f;
+  if (row < nrows) {
+    const u32x4 a = *(const u32x4 *)(O + row * kD + part * 8);
+    const u32x4 g = *(const u32x4 *)(dO + row * kD + part * 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s += lo_bf16(a[i]) * lo_bf16(g[i]) + hi_bf16(a[i]) * hi_bf16(g[i]);
+  }
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) s += shfl_xor(s, m);
+  if (row < nrows && part == 0) {
+    const long long tok = row / H;
+    const int h = (int)(row % H);
+    const int b = (int)(tok / T);
+    const int t = (int)(tok % T);
+    delta[((long long)b * H + h) * T + t] = s;
+  }
+}
+
+// ---------------------------------------------------------------- dK, dV
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__restrict__ Q,
+                                                          const uint16_t *__restrict__ K,
+                                                          const uint16_t *__restrict__ V,
+                                                          const uint16_t *__restrict__ dO,
+                                                          const float *__restrict__ LSE,
+                                                          const float *__restrict__ delta, uint16_t *__restrict__ dK,
+                                                          uint16_t *__restrict__ dV, int B, int T, int H, int KV,
+                                                          int W, float scale) {
+  // [buf][Q | dO] tiles + [buf][lse2 | delta] rows
+  __shared__ __attribute__((aligned(16))) char smem[4 * kTileBytes];
+  __shared__ float srow[2][2][kTileN];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int hh = lane >> 5;
+  const int G = H / KV;
+  const int nkb = (T + kBlockN - 1) / kBlockN;
+  const int BKV = B * KV;
+  // key blocks near the start of the sequence see the most queries: schedule them first
+  const int kblk = (int)(blockIdx.x / BKV);
+  const int bk = (int)(blockIdx.x % BKV);
+  const int b = bk / KV;
+  const int kvh = bk % KV;
+  const int k0 = kblk * kBlockN;
+  const int kw0 = k0 + 32 * wave;
+  const int key_lane = kw0 + (lane & 31);  // the key column this lane holds
+  const float c = scale * kLog2e;
+  (void)nkb;
+
+  const long long q_stride = (long long)H * kD;
+  const long long kv_stride = (long long)KV * kD;
+
+  // K, V rows of this wave's keys as MFMA B operands: lane holds key key_lane,
+  // d = 16 s + 8 hh + [0, 8).
+  bf16x8 kreg[8], vreg[8];
+  {
+    const bool valid = key_lane < T;
+    const long long off = ((long long)b * T + (valid ? key_lane : 0)) * kv_stride + (long long)kvh * kD + 8 * hh;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      u32x4 wk = valid ? *(const u32x4 *)(K + off + 16 * s) : u32x4{0u, 0u, 0u, 0u};
+      u32x4 wv = valid ? *(const u32x4 *)(V + off + 16 * s) : u32x4{0u, 0u, 0u, 0u};
+      kreg[s] = __builtin_bit_cast(bf16x8, wk);
+      vreg[s] = __builtin_bit_cast(bf16x8, wv);
+    }
+  }
+
+  // Query tiles that can see any key of the block.
+  const int k_last_blk = min(k0 + kBlockN - 1, T - 1);
+  const int q_hi = W < 0 ? T - 1 : min(T - 1, k_last_blk + W);
+  const int qt0 = k0 / kTileN;
+  const int qt1 = q_hi / kTileN;
+  const int nq = qt1 - qt0 + 1;
+  const int n_iter = nq * G;  // (query tile, head) pairs
+  const int kw_last = min(kw0 + 31, T - 1);
+  const bool wave_active = kw0 < T;
+
+  f32x16 dkacc[4], dvacc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    dkacc[i] = f32x16{};
+    dvacc[i] = f32x16{};
+  }
+
+  TileRegs qr, dor;
+  float lse_r = 0.f, del_r = 0.f;
+  auto load_iter = [&](int it) {
+    const int qt = qt0 + it / G;
+    const int h = kvh * G + it % G;
+    const uint16_t *Qb = Q + (long long)b * T * q_stride + (long long)h * kD;
+    const uint16_t *dOb = dO + (long long)b * T * q_stride + (long long)h * kD;
+    tile_load(qr, Qb, q_stride, qt * kTileN, T, tid);
+    tile_load(dor, dOb, q_stride, qt * kTileN, T, tid);
+    if (tid < kTileN) {
+      const int qi = qt * kTileN + tid;
+      const long long ri = ((long long)b * H + h) * T + qi;
+      // rows past T get P = 0 through an infinite LSE
+      lse_r = qi < T ? LSE[ri] * kLog2e : INFINITY;
+      del_r = qi < T ? delta[ri] : 0.f;
+    }
+  };
+  auto store_iter = [&](int buf) {
+    char *base = smem + buf * 2 * kTileBytes;
+    tile_store_lds(base, qr, tid);
+    tile_store_lds(base + kTileBytes, dor, tid);
+    if (tid < kTileN) {
+      srow[buf][0][tid] = lse_r;
+      srow[buf][1][tid] = del_r;
+    }
+  };
+
+  load_iter(0);
+  store_iter(0);
+  __syncthreads();
+
+  for (int it = 0; it < n_iter; ++it) {
+    const int buf = it & 1;
+    const char *Qs = smem + buf * 2 * kTileBytes;
+    const char *dOs = Qs + kTileBytes;
+    const bool has_next = it + 1 < n_iter;
+    if (has_next) load_iter(it + 1);
+    const int qtile0 = (qt0 + it / G) * kTileN;
+    const int qtile_last = qtile0 + kTileN - 1;
+    const bool skip = !wave_active || qtile_last < kw0 || (W >= 0 && qtile0 - kw_last > W);
+    if (!skip) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const int qr0 = qtile0 + 32 * qb;  // first query row of this 32-row block
+        const bool blk_skip = qr0 + 31 < kw0 || (W >= 0 && qr0 - kw_last > W);
+        if (blk_skip) continue;
+        const bool need_mask = !(qr0 >= kw_last && (W < 0 || qr0 + 31 - kw0 <= W));
+        // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys.
+        f32x16 sacc = f32x16{}, dpacc = f32x16{};
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          sacc = mfma32(lds_row_operand(Qs, 32 * qb, s, lane), kreg[s], sacc);
+          dpacc = mfma32(lds_row_operand(dOs, 32 * qb, s, lane), vreg[s], dpacc);
+        }
+        // P = exp2(S c - LSE log2 e);  dS = P (dP - D)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int r = 32 * qb + 8 * (e >> 2) + 4 * hh + (e & 3);  // row within the tile
+          float p = fast_exp2(__builtin_fmaf(sacc[e], c, -srow[buf][0][r]));
+          if (need_mask) {
+            const int qi = qtile0 + r;
+            const bool vis = key_lane <= qi && (W < 0 || qi - key_lane <= W);
+            if (!vis) p = 0.f;
+          }
+          sacc[e] = p;
+          dpacc[e] = p * (dpacc[e] - srow[buf][1][r]);
+        }
+        // dV^T += dO^T P and dK^T += Q^T dS, contraction over the 32 query rows.
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+          const bf16x8 pb = acc_to_operand(sacc, c2);
+          const bf16x8 db_ = acc_to_operand(dpacc, c2);
+          const int cs = 2 * qb + c2;
+#pragma unroll
+          for (int db = 0; db < 4; ++db) {
+            dvacc[db] = mfma32(lds_col_operand(dOs, 32 * db, cs, lane), pb, dvacc[db]);
+            dkacc[db] = mfma32(lds_col_operand(Qs, 32 * db, cs, lane), db_, dkacc[db]);
+          }
+        }
+      }
+    }
+    if (has_next) store_iter(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (!wave_active || key_lane >= T) return;
+  const long long off = ((long long)b * T + key_lane) * kv_stride + (long long)kvh * kD;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int d = 32 * db + 8 * i + 4 * hh;
+      u32x2 wk, wv;
+      wk[0] = pack_bf16x2(dkacc[db][4 * i + 0] * scale, dkacc[db][4 * i + 1] * scale);
+      wk[1] = pack_bf16x2(dkacc[db][4 * i + 2] * scale, dkacc[db][4 * i + 3] * scale);
+      wv[0] = pack_bf16x2(dvacc[db][4 * i + 0], dvacc[db][4 * i + 1]);
+      wv[1] = pack_bf16x2(dvacc[db][4 * i + 2], dvacc[db][4 * i + 3]);
+      *(u32x2 *)(dK + off + d) = wk;
+      *(u32x2 *)(dV + off + d) = wv;
+    }
+}
+
+// ---------------------------------------------------------------- dQ
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t *__restrict__ Q,
+                                                        const uint16_t *__restrict__ K,
+                                                        const uint16_t *__restrict__ V,
+                                                        const uint16_t *__restrict__ dO,
+                                                        const float *__restrict__ LSE,
+                                                        const float *__restrict__ delta, uint16_t *__restrict__ dQ,
+                                                        int B, int T, int H, int KV, int W, float scale) {
+  __shared__ __attribute__((aligned(16))) char smem[4 * kTileBytes];  // [buf][K|V]
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int nqb = (T + kBlockM - 1) / kBlockM;
+  const int BH = B * H;
+  const int qblk = nqb - 1 - (int)(blockIdx.x / BH);
+  const int bh = (int)(blockIdx.x % BH);
+  const int b = bh / H;
+  const int h = bh % H;
+  const int kvh = h / (H / KV);
+  const int q0 = qblk * kBlockM;
+  const int qw0 = q0 + 32 * wave;
+  const int q_lane = qw0 + (lane & 31);
+  const int hh = lane >> 5;
+  const float c = scale * kLog2e;
+
+  const long long q_stride = (long long)H * kD;
+  const long long kv_stride = (long long)KV * kD;
+  const uint16_t *Kb = K + (long long)b * T * kv_stride + (long long)kvh * kD;
+  const uint16_t *Vb = V + (long long)b * T * kv_stride + (long long)kvh * kD;
+
+  bf16x8 qreg[8], doreg[8];
+  const bool valid = q_lane < T;
+  {
+    const long long off = ((long long)b * T + (valid ? q_lane : 0)) * q_stride + (long long)h * kD + 8 * hh;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      u32x4 wq = valid ? *(const u32x4 *)(Q + off + 16 * s) : u32x4{0u, 0u, 0u, 0u};
+      u32x4 wd = valid ? *(const u32x4 *)(dO + off + 16 * s) : u32x4{0u, 0u, 0u, 0u};
+      qreg[s] = __builtin_bit_cast(bf16x8, wq);
+      doreg[s] = __builtin_bit_cast(bf16x8, wd);
+    }
+  }
+  const long long ri = ((long long)b * H + h) * T + (valid ? q_lane : 0);
+  const float lse2 = valid ? LSE[ri] * kLog2e : INFINITY;
+  const float del = valid ? delta[ri] : 0.f;
+
+  const int q_last_blk = min(q0 + kBlockM - 1, T - 1);
+  const int k_lo = W < 0 ? 0 : max(0, q0 - W);
+  const int t0 = k_lo / kTileN;
+  const int t1 = q_last_blk / kTileN;
+  const int qw_last = min(qw0 + 31, T - 1);
+  const bool wave_active = qw0 < T;
+
+  f32x16 dqacc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dqacc[i] = f32x16{};
+
+  TileRegs kr, vr;
+  tile_load(kr, Kb, kv_stride, t0 * kTileN, T, tid);
+  tile_load(vr, Vb, kv_stride, t0 * kTileN, T, tid);
+  tile_store_lds(smem, kr, tid);
+  tile_store_lds(smem + kTileBytes, vr, tid);
+  __syncthreads();
+
+  for (int t = t0; t <= t1; ++t) {
+    const int buf = (t - t0) & 1;
+    const char *Ks = smem + buf * 2 * kTileBytes;
+    const char *Vs = Ks + kTileBytes;
+    const bool has_next = t < t1;
+    if (has_next) {
+      tile_load(kr, Kb, kv_stride, (t + 1) * kTileN, T, tid);
+      tile_load(vr, Vb, kv_stride, (t + 1) * kTileN, T, tid);
+    }
+    const int k0 = t * kTileN;
+    const bool skip = !wave_active || k0 > qw_last || (W >= 0 && qw0 - (k0 + kTileN - 1) > W);
+    if (!skip) {
+      const bool need_mask = !(k0 + kTileN - 1 <= qw0 && (W < 0 || qw_last - k0 <= W));
+      f32x16 sacc[2], dpacc[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        f32x16 a = f32x16{}, g = f32x16{};
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          a = mfma32(lds_row_operand(Ks, 32 * kb, s, lane), qreg[s], a);
+          g = mfma32(lds_row_operand(Vs, 32 * kb, s, lane), doreg[s], g);
+        }
+        sacc[kb] = a;
+        dpacc[kb] = g;
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          float p = fast_exp2(__builtin_fmaf(sacc[kb][e], c, -lse2));
+          if (need_mask) {
+            const int key = k0 + 32 * kb + 8 * (e >> 2) + 4 * hh + (e & 3);
+            const bool vis = key <= q_lane && (W < 0 || q_lane - key <= W);
+            if (!vis) p = 0.f;
+          }
+          dpacc[kb][e] = p * (dpacc[kb][e] - del);
+        }
+      // dQ^T += K^T dS^T
+#pragma unroll
+      for (int cs = 0; cs < 4; ++cs) {
+        const bf16x8 dsb = acc_to_operand(dpacc[cs >> 1], cs & 1);
+#pragma unroll
+        for (int db = 0; db < 4; ++db) dqacc[db] = mfma32(lds_col_operand(Ks, 32 * db, cs, lane), dsb, dqacc[db]);
+      }
+    }
+    if (has_next) {
+      char *nxt = smem + (buf ^ 1) * 2 * kTileBytes;
+      tile_store_lds(nxt, kr, tid);
+      tile_store_lds(nxt + kTileBytes, vr, tid);
+    }
+    __syncthreads();
+  }
+
+  if (!wave_active || !valid) return;
+  uint16_t *dqp = dQ + ((long long)b * T + q_lane) * q_stride + (long long)h * kD;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int d = 32 * db + 8 * i + 4 * hh;
+      u32x2 w;
+      w[0] = pack_bf16x2(dqacc[db][4 * i + 0] * scale, dqacc[db][4 * i + 1] * scale);
+      w[1] = pack_bf16x2(dqacc[db][4 * i + 2] * scale, dqacc[db][4 * i + 3] * scale);
+      *(u32x2 *)(dqp + d) = w;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_bwd_bf16(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                           const void *dout, void *dq, void *dk, void *dv, float *delta, const AttnShape &sh,
+                           hipStream_t s) {
+  const long long rows = (long long)sh.B * sh.T * sh.H;
+  const long long dblocks = (rows + 15) / 16;
+  const long long nkb = (sh.T + kBlockN - 1) / kBlockN;
+  const long long nqb = (sh.T + kBlockM - 1) / kBlockM;
+  const long long kvblocks = nkb * sh.B * sh.KV;
+  const long long qblocks = nqb * sh.B * sh.H;
+  if (dblocks > 0x7fffffffLL || kvblocks > 0x7fffffffLL || qblocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(bwd_delta_kernel, dim3((unsigned)dblocks), dim3(256), 0, s, (const uint16_t *)o,
+                     (const uint16_t *)dout, delta, sh.B, sh.T, sh.H);
+  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)kvblocks), dim3(256), 0, s, (const uint16_t *)q,
+                     (const uint16_t *)k, (const uint16_t *)v, (const uint16_t *)dout, lse, delta, (uint16_t *)dk,
+                     (uint16_t *)dv, sh.B, sh.T, sh.H, sh.KV, sh.window, sh.scale);
+  hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)qblocks), dim3(256), 0, s, (const uint16_t *)q,
+                     (const uint16_t *)k, (const uint16_t *)v, (const uint16_t *)dout, lse, delta, (uint16_t *)dq,
+                     sh.B, sh.T, sh.H, sh.KV, sh.window, sh.scale);
+  return hipGetLastError();
+}
+
+}  // namespace ncattn

@@ -1,0 +1,206 @@
+// Single-token decode against a KV cache, bf16, head_dim 128 (HBM-bound).
+//
+// "nanochat Admin & Developer Guide", section 6 (the fallback's single-token
+// decode attends over the window of the cache) and section 7 "KV cache" (cache
+// (B, T, H, D) per layer, per-sequence int32 cache_seqlens, the new token written
+// into the cache in place).  For sequence b with s = cache_seqlens[b]:
+//   cache[b, s] <- (k_new[b], v_new[b]);
+//   o[b, h] = softmax_j(scale q[b, h] . k_j) v_j over j in [max(0, s - W), s].
+//
+// Split-KV: the visible keys of each (b, kv head) are cut into chunks of 128.
+// decode_split: one workgroup per (b, kv head, chunk); 16 groups of 16 lanes,
+// each group owning 8 keys (16 B per lane per K or V row, so every load
+// instruction covers four whole 256-byte rows).  All K and V loads of the chunk
+// are issued up front; scores are reduced over the 16 lanes with DPP, the softmax
+// statistics over the groups through LDS, and each query head of the group reuses
+// the K/V registers.  The chunk that holds key s takes it from k_new/v_new and
+// writes it into the cache; no other chunk touches slot s, and slots past s are
+// never read (they may hold anything, NaN included).
+// decode_combine: one workgroup per (b, h) merges the chunk partials
+// (max, sum, unnormalised output) into o and lse.
+#include "device_common.hpp"
+#include "internal.hpp"
+
+namespace ncattn {
+
+namespace {
+
+constexpr int kDD = 128;   // head_dim
+constexpr int kCH = 128;   // keys per chunk
+constexpr int kPerGroup = kCH / 16;
+
+int n_chunks_max(int T_max, int window) {
+  const int span = (window < 0 || window + 1 > T_max) ? T_max : window + 1;
+  return (span + kCH - 1) / kCH;
+}
+
+__global__ __launch_bounds__(256) void decode_split_kernel(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kn, const uint16_t *__restrict__ Vn,
+    uint16_t *__restrict__ Kc, uint16_t *__restrict__ Vc, const int32_t *__restrict__ seqlens,
+    float *__restrict__ ws_o, float *__restrict__ ws_m, float *__restrict__ ws_l, int B, int T_max, int H, int KV,
+    int W, float c, int C_max) {
+  __shared__ float red[16];
+  __shared__ float obuf[16][kDD + 4];
+  const int tid = threadIdx.x;
+  const int grp = tid >> 4;
+  const int p16 = tid & 15;
+  const int chunk = (int)(blockIdx.x % C_max);
+  const int bk = (int)(blockIdx.x / C_max);
+  const int b = bk / KV;
+  const int kvh = bk % KV;
+  const int G = H / KV;
+  const int s = seqlens[b];
+  if (s < 0 || s >= T_max) return;
+  const int lo = W < 0 ? 0 : max(0, s - W);
+  const int j0 = lo + chunk * kCH;
+  if (j0 > s) return;
+
+  const long long row_stride = (long long)KV * kDD;
+  const long long cache_base = (long long)b * T_max * row_stride + (long long)kvh * kDD + p16 * 8;
+  const long long new_off = ((long long)b * KV + kvh) * kDD + p16 * 8;
+
+  u32x4 kreg[kPerGroup], vreg[kPerGroup];
+#pragma unroll
+  for (int it = 0; it < kPerGroup; ++it) {
+    const int j = j0 + grp + 16 * it;
+    if (j < s) {
+      kreg[it] = *(const u32x4 *)(Kc + cache_base + (long long)j * row_stride);
+      vreg[it] = *(const u32x4 *)(Vc + cache_base + (long long)j * row_stride);
+    } else if (j == s) {
+      kreg[it] = *(const u32x4 *)(Kn + new_off);
+      vreg[it] = *(const u32x4 *)(Vn + new_off);
+      *(u32x4 *)(Kc + cache_base + (long long)j * row_stride) = kreg[it];
+      *(u32x4 *)(Vc + cache_base + (long long)j * row_stride) = vreg[it];
+    } else {
+      kreg[it] = u32x4{0u, 0u, 0u, 0u};
+      vreg[it] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  for (int g = 0; g < G; ++g) {
+    const int h = kvh * G + g;
+    float qv[8];
+    {
+      const u32x4 w = *(const u32x4 *)(Q + ((long long)b * H + h) * kDD + p16 * 8);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        qv[2 * i] = lo_bf16(w[i]);
+        qv[2 * i + 1] = hi_bf16(w[i]);
+      }
+    }
+    float sc[kPerGroup];
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int it = 0; it < kPerGroup; ++it) {
+      float part = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        part = __builtin_fmaf(qv[2 * i], lo_bf16(kreg[it][i]), part);
+        part = __builtin_fmaf(qv[2 * i + 1], hi_bf16(kreg[it][i]), part);
+      }
+      const float tot = row16_sum(part) * c;  // log2-domain score
+      const int j = j0 + grp + 16 * it;
+      sc[it] = j <= s ? tot : -INFINITY;
+      mloc = fmaxf(mloc, sc[it]);
+    }
+    if (p16 == 0) red[grp] = mloc;
+    __syncthreads();
+    float m = red[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) m = fmaxf(m, red[i]);
+    __syncthreads();
+    float lsum = 0.f;
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int it = 0; it < kPerGroup; ++it) {
+      const float p = fast_exp2(sc[it] - m);  // the chunk always holds key j0 <= s, so m is finite
+      lsum += p;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] = __builtin_fmaf(p, lo_bf16(vreg[it][i]), acc[2 * i]);
+        acc[2 * i + 1] = __builtin_fmaf(p, hi_bf16(vreg[it][i]), acc[2 * i + 1]);
+      }
+    }
+    if (p16 == 0) red[grp] = lsum;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) obuf[grp][p16 * 8 + i] = acc[i];
+    __syncthreads();
+    const long long pidx = ((long long)b * H + h) * C_max + chunk;
+    if (tid < kDD) {
+      float o = 0.f;
+#pragma unroll
+      for (int gg = 0; gg < 16; ++gg) o += obuf[gg][tid];
+      ws_o[pidx * kDD + tid] = o;
+    }
+    if (tid == 0) {
+      float l = 0.f;
+#pragma unroll
+      for (int gg = 0; gg < 16; ++gg) l += red[gg];
+      ws_m[pidx] = m;
+      ws_l[pidx] = l;
+    }
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(128) void decode_combine_kernel(const float *__restrict__ ws_o,
+                                                             const float *__restrict__ ws_m,
+                                                             const float *__restrict__ ws_l,
+                                                             const int32_t *__restrict__ seqlens,
+                                                             uint16_t *__restrict__ O, float *__restrict__ LSE,
+                                                             int B, int T_max, int H, int W, int C_max) {
+  const int bh = blockIdx.x;
+  const int b = bh / H;
+  const int d = threadIdx.x;
+  const int s = seqlens[b];
+  if (s < 0 || s >= T_max) {
+    O[(long long)bh * kDD + d] = 0x7fc0;  // bf16 quiet NaN
+    if (LSE != nullptr && d == 0) LSE[bh] = __builtin_nanf("");
+    return;
+  }
+  const int lo = W < 0 ? 0 : max(0, s - W);
+  const int nc = (s - lo + 1 + kCH - 1) / kCH;
+  const long long base = (long long)bh * C_max;
+  float M = -INFINITY;
+  for (int ci = 0; ci < nc; ++ci) M = fmaxf(M, ws_m[base + ci]);
+  float L = 0.f, o = 0.f;
+  for (int ci = 0; ci < nc; ++ci) {
+    const float a = fast_exp2(ws_m[base + ci] - M);
+    L = __builtin_fmaf(ws_l[base + ci], a, L);
+    o = __builtin_fmaf(ws_o[(base + ci) * kDD + d], a, o);
+  }
+  O[(long long)bh * kDD + d] = __builtin_bit_cast(uint16_t, (__bf16)(o / L));
+  if (LSE != nullptr && d == 0) LSE[bh] = (M + log2f(L)) * kLn2;
+}
+
+}  // namespace
+
+size_t decode_workspace_bytes(int B, int T_max, int H, int KV, int D, int window) {
+  (void)KV;
+  (void)D;
+  const size_t parts = (size_t)B * H * n_chunks_max(T_max, window);
+  return parts * (kDD + 2) * sizeof(float) + 256;
+}
+
+hipError_t launch_decode_bf16(const void *q, const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                              const int32_t *seqlens, void *o, float *lse, int B, int T_max, int H, int KV, int D,
+                              int window, float scale, void *workspace, hipStream_t s) {
+  (void)D;
+  const int C_max = n_chunks_max(T_max, window);
+  const size_t parts = (size_t)B * H * C_max;
+  float *ws_o = (float *)workspace;
+  float *ws_m = ws_o + parts * kDD;
+  float *ws_l = ws_m + parts;
+  const long long blocks = (long long)B * KV * C_max;
+  if (blocks > 0x7fffffffLL || (long long)B * H > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(decode_split_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (const uint16_t *)q,
+                     (const uint16_t *)k_new, (const uint16_t *)v_new, (uint16_t *)k_cache, (uint16_t *)v_cache,
+                     seqlens, ws_o, ws_m, ws_l, B, T_max, H, KV, window, scale * kLog2e, C_max);
+  hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)(B * H)), dim3(kDD), 0, s, ws_o, ws_m, ws_l, seqlens,
+                     (uint16_t *)o, lse, B, T_max, H, window, C_max);
+  return hipGetLastError();
+}
+
+}  // namespace ncattn

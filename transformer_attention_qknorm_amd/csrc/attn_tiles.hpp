@@ -1,0 +1,99 @@
+// Tile-level building blocks of the bf16 MFMA attention kernels (head_dim 128).
+//
+// Data layout in LDS: a tile of 64 rows x 128 bf16 (256 B per row) is stored
+// with its 16-byte chunks permuted per row, chunk' = chunk ^ f(row) with
+// f(row) = ((row & 3) << 2) | ((row >> 2) & 3).  Two read patterns hit such a
+// tile and both are free of bank conflicts under this permutation:
+//   * straight 16-byte reads of one chunk column by 16 consecutive rows
+//     (MFMA operands whose contraction index runs along the row), and
+//   * 8-byte transposing reads (ds_read_b64_tr_b16) that gather 4 rows x 4
+//     chunks per 16-lane group (MFMA operands whose contraction index runs
+//     down the rows).
+#pragma once
+
+#include "device_common.hpp"
+
+namespace ncattn {
+
+constexpr int kD = 128;          // head_dim of the MFMA path
+constexpr int kRowBytes = kD * 2;  // one bf16 row of a tile
+constexpr int kTileN = 64;         // rows of a K/V (or Q/dO) tile
+constexpr int kTileBytes = kTileN * kRowBytes;
+
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return row * kRowBytes + ((chunk ^ (((row & 3) << 2) | ((row >> 2) & 3))) << 4);
+}
+
+// Cooperative copy of a 64 x 128 bf16 tile from global rows (stride in elements)
+// into registers: 256 threads, 4 chunks of 16 B each.  Rows at or past `nrows`
+// are zero-filled.
+struct TileRegs {
+  u32x4 c[4];
+};
+
+__device__ __forceinline__ void tile_load(TileRegs &r, const uint16_t *__restrict__ base, long long row_stride,
+                                          int row0, int nrows, int tid) {
+  const int chunk = tid & 15;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = (tid >> 4) + 16 * i;
+    if (row0 + row < nrows)
+      r.c[i] = *(const u32x4 *)(base + (long long)(row0 + row) * row_stride + chunk * 8);
+    else
+      r.c[i] = u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+__device__ __forceinline__ void tile_store_lds(char *lds, const TileRegs &r, int tid) {
+  const int chunk = tid & 15;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = (tid >> 4) + 16 * i;
+    *(u32x4 *)(lds + swz(row, chunk)) = r.c[i];
+  }
+}
+
+// A/B operand of a 32x32x16 MFMA whose contraction index is the column (d) of a
+// row-major tile: lane l gets row (row0 + l%32), columns 16*s + 8*(l/32) + [0,8).
+__device__ __forceinline__ bf16x8 lds_row_operand(const char *lds, int row0, int s, int lane) {
+  const int row = row0 + (lane & 31);
+  const int chunk = 2 * s + (lane >> 5);
+  return *(const bf16x8 *)(lds + swz(row, chunk));
+}
+
+// A/B operand of a 32x32x16 MFMA whose contraction index runs down the rows of a
+// tile, in the permuted row order that matches a 32x32 accumulator used as the
+// other operand (see acc_to_operand): lane l gets column d = col0 + l%32 of the 8
+// rows {16c + 4h + k, 16c + 8 + 4h + k : k = 0..3}, h = l/32.
+__device__ __forceinline__ bf16x8 lds_col_operand(const char *lds, int col0, int c, int lane) {
+  const int g = lane >> 4;             // 16-lane group
+  const int r = lane & 15;
+  const int h = g >> 1;
+  const int d = col0 + ((g & 1) << 4) + 4 * (r & 3);
+  const int row = 16 * c + 4 * h + (r >> 2);
+  const int off_in_chunk = (d & 7) * 2;
+  i16x4 lo = lds_read_tr16(lds + swz(row, d >> 3) + off_in_chunk);
+  i16x4 hi = lds_read_tr16(lds + swz(row + 8, d >> 3) + off_in_chunk);
+  bf16x8 out;
+  out[0] = __builtin_bit_cast(__bf16, lo[0]);
+  out[1] = __builtin_bit_cast(__bf16, lo[1]);
+  out[2] = __builtin_bit_cast(__bf16, lo[2]);
+  out[3] = __builtin_bit_cast(__bf16, lo[3]);
+  out[4] = __builtin_bit_cast(__bf16, hi[0]);
+  out[5] = __builtin_bit_cast(__bf16, hi[1]);
+  out[6] = __builtin_bit_cast(__bf16, hi[2]);
+  out[7] = __builtin_bit_cast(__bf16, hi[3]);
+  return out;
+}
+
+// Operand of a 32x32x16 MFMA taken from a 32x32 fp32 accumulator block (rows =
+// contraction index): step c2 (0 or 1) of the block uses rows {16c2 + 4h + k,
+// 16c2 + 8 + 4h + k}, i.e. accumulator elements 8c2 + k and 8c2 + 4 + k of lane l.
+__device__ __forceinline__ bf16x8 acc_to_operand(const f32x16 &acc, int c2) {
+  bf16x8 out;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) out[k] = (__bf16)acc[8 * c2 + k];
+  return out;
+}
+
+}  // namespace ncattn

@@ -1,0 +1,44 @@
+// Internal launch functions behind the C ABI (include/ncattn.h).  Each one
+// assumes arguments were validated by ncattn_api.hip and only sizes the grid and
+// enqueues kernels on the given stream; it returns hipGetLastError() afterwards.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ncattn {
+
+struct AttnShape {
+  int B, T, H, KV, D;
+  int window;   // window_left, -1 = unbounded
+  float scale;  // resolved softmax scale (> 0)
+};
+
+// QK-norm + RoPE in place; inv_freq[j] = base^(-2j/D) computed on the host in fp64.
+hipError_t launch_qknorm_rope(void *q, void *k, int B, int T, int H, int KV, int D,
+                              const int32_t *pos_offset, const double *inv_freq_host, float eps,
+                              float gain, bool bf16, hipStream_t s);
+
+// bf16, head_dim 128, MFMA kernels.
+hipError_t launch_fwd_bf16(const void *q, const void *k, const void *v, void *o, float *lse,
+                           const AttnShape &sh, hipStream_t s);
+hipError_t launch_bwd_bf16(const void *q, const void *k, const void *v, const void *o,
+                           const float *lse, const void *dout, void *dq, void *dk, void *dv,
+                           float *delta, const AttnShape &sh, hipStream_t s);
+
+// fp32 reference-precision kernels (head_dim 64 or 128).
+hipError_t launch_fwd_f32(const float *q, const float *k, const float *v, float *o, float *lse,
+                          const AttnShape &sh, hipStream_t s);
+hipError_t launch_bwd_f32(const float *q, const float *k, const float *v, const float *o,
+                          const float *lse, const float *dout, float *dq, float *dk, float *dv,
+                          float *delta, const AttnShape &sh, hipStream_t s);
+
+// Split-KV decode, bf16, head_dim 128.
+size_t decode_workspace_bytes(int B, int T_max, int H, int KV, int D, int window);
+hipError_t launch_decode_bf16(const void *q, const void *k_new, const void *v_new, void *k_cache,
+                              void *v_cache, const int32_t *seqlens, void *o, float *lse, int B,
+                              int T_max, int H, int KV, int D, int window, float scale,
+                              void *workspace, hipStream_t s);
+
+}  // namespace ncattn

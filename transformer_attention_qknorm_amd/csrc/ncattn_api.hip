@@ -1,0 +1,222 @@
+// C ABI of ncattn: host-side validation, workspace sizing and dispatch.
+// Every argument is checked before anything is enqueued; errors come back as
+// status codes with a thread-local message (include/ncattn.h).
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <new>
+
+#include "../../include/ncattn.h"
+#include "internal.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return NCATTN_OK;
+}
+
+int hip_status(hipError_t e, const char *what) {
+  if (e != hipSuccess) return fail(NCATTN_EHIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Shape checks common to every attention call.
+int check_heads(const char *fn, int B, int T, int H, int KV, int D) {
+  if (B <= 0 || T <= 0 || H <= 0 || KV <= 0 || D <= 0)
+    return fail(NCATTN_EINVAL, "%s: sizes must be positive (B=%d T=%d n_head=%d n_kv_head=%d head_dim=%d)", fn, B,
+                T, H, KV, D);
+  if (H % KV != 0) return fail(NCATTN_EINVAL, "%s: n_head (%d) must be a multiple of n_kv_head (%d)", fn, H, KV);
+  // every index used by the kernels is formed in 64-bit, but per-tensor element
+  // counts must still fit the int64 address arithmetic comfortably
+  if ((double)B * T * H * D > 4.0e15) return fail(NCATTN_EINVAL, "%s: tensor too large", fn);
+  return NCATTN_OK;
+}
+
+int check_dtype(const char *fn, int dtype) {
+  if (dtype != NCATTN_BF16 && dtype != NCATTN_F32) return fail(NCATTN_EINVAL, "%s: unknown dtype %d", fn, dtype);
+  return NCATTN_OK;
+}
+
+int check_attn_support(const char *fn, int dtype, int D) {
+  if (dtype == NCATTN_BF16 && D != 128)
+    return fail(NCATTN_EUNSUPPORTED, "%s: bf16 attention supports head_dim 128 only (got %d)", fn, D);
+  if (dtype == NCATTN_F32 && D != 64 && D != 128)
+    return fail(NCATTN_EUNSUPPORTED, "%s: fp32 attention supports head_dim 64 or 128 (got %d)", fn, D);
+  return NCATTN_OK;
+}
+
+int check_window(const char *fn, int wl, int wr) {
+  if (wl < -1) return fail(NCATTN_EINVAL, "%s: window_left must be >= -1 (got %d)", fn, wl);
+  if (wr != 0) return fail(NCATTN_EINVAL, "%s: window_right must be 0 (causal), got %d", fn, wr);
+  return NCATTN_OK;
+}
+
+#define NC_TRY(expr)            \
+  do {                          \
+    int _rc = (expr);           \
+    if (_rc != NCATTN_OK) return _rc; \
+  } while (0)
+
+#define NC_PTR(p, fn)                                                                \
+  do {                                                                               \
+    if ((p) == nullptr) return fail(NCATTN_EINVAL, "%s: %s is NULL", fn, #p);        \
+    if (!aligned16(p)) return fail(NCATTN_EINVAL, "%s: %s is not 16-byte aligned", fn, #p); \
+  } while (0)
+
+float resolve_scale(float s, int D) { return s > 0.f ? s : (float)(1.0 / sqrt((double)D)); }
+
+}  // namespace
+
+extern "C" {
+
+const char *ncattn_last_error(void) { return g_err; }
+
+const char *ncattn_version(void) { return "ncattn 0.1.0 (gfx950)"; }
+
+int ncattn_qknorm_rope(void *q, void *k, int B, int T, int n_head, int n_kv_head, int head_dim,
+                       const int32_t *pos_offset, float rope_base, float eps, float qk_gain, int dtype,
+                       void *stream) {
+  const char *fn = "ncattn_qknorm_rope";
+  NC_PTR(q, fn);
+  NC_PTR(k, fn);
+  NC_TRY(check_heads(fn, B, T, n_head, n_kv_head, head_dim));
+  NC_TRY(check_dtype(fn, dtype));
+  if (head_dim != 64 && head_dim != 128)
+    return fail(NCATTN_EUNSUPPORTED, "%s: head_dim must be 64 or 128 (got %d)", fn, head_dim);
+  if (pos_offset != nullptr && ((uintptr_t)pos_offset & 3u))
+    return fail(NCATTN_EINVAL, "%s: pos_offset is not 4-byte aligned", fn);
+  if (!(rope_base > 1.0f) || !isfinite(rope_base)) return fail(NCATTN_EINVAL, "%s: rope_base must be > 1", fn);
+  if (!(eps >= 0.0f) || !isfinite(eps)) return fail(NCATTN_EINVAL, "%s: eps must be >= 0", fn);
+  if (!isfinite(qk_gain)) return fail(NCATTN_EINVAL, "%s: qk_gain must be finite", fn);
+  double inv_freq[64];
+  for (int j = 0; j < head_dim / 2; ++j) inv_freq[j] = pow((double)rope_base, -2.0 * j / head_dim);
+  return hip_status(ncattn::launch_qknorm_rope(q, k, B, T, n_head, n_kv_head, head_dim, pos_offset, inv_freq, eps,
+                                               qk_gain, dtype == NCATTN_BF16, (hipStream_t)stream),
+                    fn);
+}
+
+int ncattn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int T, int n_head,
+               int n_kv_head, int head_dim, int window_left, int window_right, float softmax_scale, int dtype,
+               void *stream) {
+  const char *fn = "ncattn_fwd";
+  NC_PTR(q, fn);
+  NC_PTR(k, fn);
+  NC_PTR(v, fn);
+  NC_PTR(o, fn);
+  NC_PTR(lse, fn);
+  NC_TRY(check_heads(fn, B, T, n_head, n_kv_head, head_dim));
+  NC_TRY(check_dtype(fn, dtype));
+  NC_TRY(check_window(fn, window_left, window_right));
+  NC_TRY(check_attn_support(fn, dtype, head_dim));
+  if (!isfinite(softmax_scale)) return fail(NCATTN_EINVAL, "%s: softmax_scale must be finite", fn);
+  if (o == q || o == k || o == v) return fail(NCATTN_EINVAL, "%s: o must not alias an input", fn);
+  ncattn::AttnShape sh{B, T, n_head, n_kv_head, head_dim, window_left, resolve_scale(softmax_scale, head_dim)};
+  hipError_t e = dtype == NCATTN_BF16
+                     ? ncattn::launch_fwd_bf16(q, k, v, o, lse, sh, (hipStream_t)stream)
+                     : ncattn::launch_fwd_f32((const float *)q, (const float *)k, (const float *)v, (float *)o, lse,
+                                              sh, (hipStream_t)stream);
+  return hip_status(e, fn);
+}
+
+size_t ncattn_bwd_workspace_bytes(int B, int T, int n_head, int n_kv_head, int head_dim, int dtype) {
+  (void)n_kv_head;
+  (void)head_dim;
+  (void)dtype;
+  if (B <= 0 || T <= 0 || n_head <= 0) return 0;
+  return (size_t)B * n_head * T * sizeof(float);
+}
+
+int ncattn_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse, const void *dout,
+               void *dq, void *dk, void *dv, int B, int T, int n_head, int n_kv_head, int head_dim, int window_left,
+               int window_right, float softmax_scale, int dtype, void *workspace, size_t workspace_bytes,
+               void *stream) {
+  const char *fn = "ncattn_bwd";
+  NC_PTR(q, fn);
+  NC_PTR(k, fn);
+  NC_PTR(v, fn);
+  NC_PTR(o, fn);
+  NC_PTR(lse, fn);
+  NC_PTR(dout, fn);
+  NC_PTR(dq, fn);
+  NC_PTR(dk, fn);
+  NC_PTR(dv, fn);
+  NC_TRY(check_heads(fn, B, T, n_head, n_kv_head, head_dim));
+  NC_TRY(check_dtype(fn, dtype));
+  NC_TRY(check_window(fn, window_left, window_right));
+  NC_TRY(check_attn_support(fn, dtype, head_dim));
+  if (!isfinite(softmax_scale)) return fail(NCATTN_EINVAL, "%s: softmax_scale must be finite", fn);
+  const void *ins[] = {q, k, v, o, lse, dout};
+  void *outs[] = {dq, dk, dv};
+  for (void *x : outs)
+    for (const void *y : ins)
+      if (x == y) return fail(NCATTN_EINVAL, "%s: gradients must not alias an input", fn);
+  if (dq == dk || dq == dv || dk == dv) return fail(NCATTN_EINVAL, "%s: dq, dk, dv must be distinct", fn);
+  size_t need = ncattn_bwd_workspace_bytes(B, T, n_head, n_kv_head, head_dim, dtype);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(NCATTN_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
+  if (!aligned16(workspace)) return fail(NCATTN_EINVAL, "%s: workspace is not 16-byte aligned", fn);
+  ncattn::AttnShape sh{B, T, n_head, n_kv_head, head_dim, window_left, resolve_scale(softmax_scale, head_dim)};
+  hipError_t e =
+      dtype == NCATTN_BF16
+          ? ncattn::launch_bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, (float *)workspace, sh, (hipStream_t)stream)
+          : ncattn::launch_bwd_f32((const float *)q, (const float *)k, (const float *)v, (const float *)o, lse,
+                                   (const float *)dout, (float *)dq, (float *)dk, (float *)dv, (float *)workspace, sh,
+                                   (hipStream_t)stream);
+  return hip_status(e, fn);
+}
+
+size_t ncattn_decode_workspace_bytes(int B, int T_max, int n_head, int n_kv_head, int head_dim, int window_left) {
+  if (B <= 0 || T_max <= 0 || n_head <= 0 || n_kv_head <= 0 || head_dim <= 0 || window_left < -1) return 0;
+  return ncattn::decode_workspace_bytes(B, T_max, n_head, n_kv_head, head_dim, window_left);
+}
+
+int ncattn_decode(const void *q, const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                  const int32_t *cache_seqlens, void *o, float *lse, int B, int T_max, int n_head, int n_kv_head,
+                  int head_dim, int window_left, float softmax_scale, int dtype, void *workspace,
+                  size_t workspace_bytes, void *stream) {
+  const char *fn = "ncattn_decode";
+  NC_PTR(q, fn);
+  NC_PTR(k_new, fn);
+  NC_PTR(v_new, fn);
+  NC_PTR(k_cache, fn);
+  NC_PTR(v_cache, fn);
+  NC_PTR(o, fn);
+  if (cache_seqlens == nullptr) return fail(NCATTN_EINVAL, "%s: cache_seqlens is NULL", fn);
+  if ((uintptr_t)cache_seqlens & 3u) return fail(NCATTN_EINVAL, "%s: cache_seqlens is not 4-byte aligned", fn);
+  if (lse != nullptr && ((uintptr_t)lse & 3u)) return fail(NCATTN_EINVAL, "%s: lse is not 4-byte aligned", fn);
+  NC_TRY(check_heads(fn, B, T_max, n_head, n_kv_head, head_dim));
+  NC_TRY(check_dtype(fn, dtype));
+  if (window_left < -1) return fail(NCATTN_EINVAL, "%s: window_left must be >= -1 (got %d)", fn, window_left);
+  if (dtype != NCATTN_BF16) return fail(NCATTN_EUNSUPPORTED, "%s: decode supports bf16 only", fn);
+  if (head_dim != 128) return fail(NCATTN_EUNSUPPORTED, "%s: decode supports head_dim 128 only (got %d)", fn, head_dim);
+  if (!isfinite(softmax_scale)) return fail(NCATTN_EINVAL, "%s: softmax_scale must be finite", fn);
+  if (k_cache == v_cache) return fail(NCATTN_EINVAL, "%s: k_cache and v_cache must differ", fn);
+  if (o == q || o == k_cache || o == v_cache || o == k_new || o == v_new)
+    return fail(NCATTN_EINVAL, "%s: o must not alias an input", fn);
+  size_t need = ncattn::decode_workspace_bytes(B, T_max, n_head, n_kv_head, head_dim, window_left);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(NCATTN_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
+  if (!aligned16(workspace)) return fail(NCATTN_EINVAL, "%s: workspace is not 16-byte aligned", fn);
+  hipError_t e = ncattn::launch_decode_bf16(q, k_new, v_new, k_cache, v_cache, cache_seqlens, o, lse, B, T_max,
+                                            n_head, n_kv_head, head_dim, window_left,
+                                            resolve_scale(softmax_scale, head_dim), workspace, (hipStream_t)stream);
+  return hip_status(e, fn);
+}
+
+}  // extern "C"
