@@ -1,0 +1,269 @@
+"""Benchmark of the attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+One step = the training-side hot path of a nanochat d12-shaped model's attention
+(B=8, T=2048, n_head=n_kv_head=6, head_dim=128, bf16) over its four SSSL layers
+(windows 1024, 1024, 1024, full causal): per layer QK-norm + RoPE, attention
+forward, attention backward.  Inputs are seeded synthetic N(0, 1) tensors
+already resident in HBM, one distinct set per layer.  The engine-decode row (64
+sequences, cache lengths U[256, 8192], 10 heads, head_dim 128) is timed in the
+same run at the full-causal and 1024 windows and reported under "decode".
+
+Prints ONE JSON line.  ``value`` = unmasked attention FLOPs of a step (fwd 4*D
+and bwd 8*D per visible (query, key) pair and head) / wall time of the step
+(QK-norm included in the time).  ``roofline`` is for the kernel with the largest
+share of the step, timed with HIP events on the stream it runs on; ``traffic``
+comes from the committed rocprofv3 counter summary in profiles/ when it was
+taken on the current kernel source, else null.  ``cpu_baseline`` times the CPU
+oracle on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 FLOP/clk)
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+METRIC = "attn fwd+bwd TFLOP/s (unmasked FLOPs) & % bf16 MFMA peak; decode GB/s"
+
+
+def visible_pairs(T, W):
+    """Visible (query, key) pairs of one head: sum_i min(i + 1, W + 1)."""
+    if W < 0 or W >= T - 1:
+        return T * (T + 1) // 2
+    return (W + 1) * (W + 2) // 2 + (T - W - 1) * (W + 1)
+
+
+def kernel_source_hash(name):
+    p = os.path.join(ROOT, "transformer_attention_qknorm_amd", "csrc", name)
+    h = hashlib.sha256()
+    for f in sorted([p, os.path.join(os.path.dirname(p), "attn_tiles.hpp"),
+                     os.path.join(os.path.dirname(p), "device_common.hpp")]):
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SOURCES = {"fwd": "attn_fwd_bf16.hip", "bwd_dkdv": "attn_bwd_bf16.hip", "bwd_dq": "attn_bwd_bf16.hip",
+                  "bwd_delta": "attn_bwd_bf16.hip", "qknorm_rope": "qknorm_rope.hip",
+                  "decode_split": "attn_decode.hip"}
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch from the committed counter summary, if it matches the source."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+        e = d["kernels"][kernel]
+        if e.get("source_hash") != kernel_source_hash(KERNEL_SOURCES[kernel]):
+            return None
+        return e["bytes_per_launch"]
+    except (KeyError, ValueError, TypeError):
+        return None
+
+
+def cpu_baseline(cfg, budget_s=12.0):
+    """Time the CPU oracle (fwd + bwd of one (b, head) slice at a time, S and L
+    windows alternately) on the same seeded inputs until ~budget_s has passed."""
+    import numpy as np
+    import oracle
+    from workloads import config_inputs
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    q, k, v, do = config_inputs(cfg)
+    f = lambda t: t.double().numpy()
+    flops, t_used, slices = 0, 0.0, []
+    i = 0
+    while t_used < budget_s and i < 2 * cfg.B * cfg.H:
+        W = cfg.windows[0] if i % 2 == 0 else -1
+        b, h = (i // 2) % cfg.B, (i // 2) % cfg.H
+        sq, sk, sv, sdo = (f(x[b:b + 1, :, h:h + 1]) for x in (q, k, v, do))
+        t0 = time.perf_counter()
+        oracle.attn_fwd(sq, sk, sv, W)
+        oracle.attn_bwd(sq, sk, sv, sdo, W)
+        t_used += time.perf_counter() - t0
+        flops += 12 * cfg.D * visible_pairs(cfg.T, W)
+        slices.append((b, h, W))
+        i += 1
+    return {"value": flops / t_used / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{len(slices)} (b, head) slices of the d12 workload (T=2048, D=128), alternating "
+                      f"window 1024 and full causal, fwd+bwd in float64 numpy; {t_used:.1f} s of CPU work"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-iters", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build measures one GPU only (the attention path needs no collective); "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import transformer_attention_qknorm_amd as nc
+    from workloads import D12, DECODE, config_inputs, decode_inputs
+
+    nc.lib()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = D12
+    B, T, H, KV, D = cfg.B, cfg.T, cfg.H, cfg.KV, cfg.D
+    q0, k0, v0, do0 = config_inputs(cfg)
+    layers = []
+    for W in cfg.windows:
+        L = dict(W=W, q=q0.to(dev), k=k0.to(dev), v=v0.to(dev), do=do0.to(dev))
+        L["o"] = torch.empty_like(L["q"])
+        L["lse"] = torch.empty(B, H, T, dtype=torch.float32, device=dev)
+        L["dq"], L["dk"], L["dv"] = torch.empty_like(L["q"]), torch.empty_like(L["k"]), torch.empty_like(L["v"])
+        layers.append(L)
+    ws = nc.bwd_workspace(layers[0]["q"], layers[0]["k"])
+    names = ["qknorm_rope", "fwd", "bwd_delta", "bwd_dkdv", "bwd_dq"]
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        for li, L in enumerate(layers):
+            def rec(i):
+                if ev is not None:
+                    ev[li][i].record(stream)
+            rec(0)
+            nc.qknorm_rope_(L["q"], L["k"], None, rope_base=cfg.rope_base, eps=1e-6)
+            rec(1)
+            nc.fwd(L["q"], L["k"], L["v"], window=(L["W"], 0), out=(L["o"], L["lse"]))
+            rec(2)
+            for si, st in enumerate(("preprocess", "dkdv", "dq")):
+                nc.bwd(L["q"], L["k"], L["v"], L["o"], L["lse"], L["do"], window=(L["W"], 0),
+                       out=(L["dq"], L["dk"], L["dv"]), workspace=ws, stage=st)
+                rec(3 + si)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in layers] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    # per-kernel durations (ms), per layer, averaged over steps
+    dur = {n: [0.0] * len(layers) for n in names}
+    for s in range(args.steps):
+        for li in range(len(layers)):
+            e = events[s][li]
+            for i, n in enumerate(names):
+                dur[n][li] += e[i].elapsed_time(e[i + 1]) / args.steps
+    pairs = [visible_pairs(T, L["W"]) * B * H for L in layers]
+    f_fwd = [4 * D * p for p in pairs]
+    f_bwd = [8 * D * p for p in pairs]
+    flops_step = sum(f_fwd) + sum(f_bwd)
+    value = flops_step / (ms_per_step * 1e-3) / 1e12
+    t_attn = sum(sum(dur[n]) for n in names[1:])
+    totals = {n: sum(dur[n]) for n in names}
+    dominant = max(totals, key=totals.get)
+    # algorithmic work attributed per kernel: fwd 4D/pair; dkdv computes dV, dP, dK
+    # (6D/pair); dq computes dQ (2D/pair); the S/dP recomputations are not counted
+    share = {"fwd": 4, "bwd_dkdv": 6, "bwd_dq": 2}
+    if dominant in share:
+        work = sum(share[dominant] * D * p for p in pairs)
+        achieved = work / (totals[dominant] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "kernel": dominant}
+    else:
+        nbytes = (B * T * (H + KV) * D * 2 * 2) if dominant == "qknorm_rope" else (B * T * H * D * 2 * 2 + B * H * T * 4)
+        achieved = nbytes * len(layers) / (totals[dominant] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBPS, 4), "kernel": dominant}
+    tr = measured_traffic(dominant)
+    roof["traffic"] = None if tr is None else tr
+    roof["avg_launch_us"] = round(totals[dominant] * 1e3 / len(layers), 2)
+
+    per_layer = []
+    for li, L in enumerate(layers):
+        tf = dur["fwd"][li]
+        tb = dur["bwd_delta"][li] + dur["bwd_dkdv"][li] + dur["bwd_dq"][li]
+        per_layer.append({"window": L["W"], "fwd_us": round(tf * 1e3, 1), "bwd_us": round(tb * 1e3, 1),
+                          "fwd_tflops": round(f_fwd[li] / (tf * 1e-3) / 1e12, 1),
+                          "bwd_tflops": round(f_bwd[li] / (tb * 1e-3) / 1e12, 1),
+                          "qknorm_rope_us": round(dur["qknorm_rope"][li] * 1e3, 1),
+                          "dkdv_us": round(dur["bwd_dkdv"][li] * 1e3, 1), "dq_us": round(dur["bwd_dq"][li] * 1e3, 1)})
+    qk_bytes = B * T * (H + KV) * D * 2 * 2
+    detail = {
+        "fwd_bwd_tflops_kernels_only": round(flops_step / (t_attn * 1e-3) / 1e12, 1),
+        "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "qknorm_rope_gbps": round(qk_bytes * len(layers) / (totals["qknorm_rope"] * 1e-3) / 1e9, 1),
+        "kernel_ms_per_step": {n: round(totals[n], 4) for n in names},
+        "layers": per_layer,
+        "algorithmic_gflop_per_step": round(flops_step / 1e9, 2),
+    }
+
+    decode = None
+    if not args.no_decode:
+        c = DECODE
+        qd, knd, vnd, kcd, vcd, lens = (x.to(dev) for x in decode_inputs(c.B, c.H, c.KV, c.D, c.min_len, c.max_len,
+                                                                           c.T_max, seed=c.seed, poison=False))
+        sets = [(kcd, vcd)] + [(kcd.clone(), vcd.clone()) for _ in range(3)]  # rotate past the 256 MB MALL
+        od = torch.empty_like(qd)
+        decode = {}
+        lens_h = lens.cpu().tolist()
+        for W in c.windows:
+            wsd = nc.decode_workspace(qd, kcd, W)
+            for i in range(3):
+                kc, vc = sets[i % 4]
+                nc.decode(qd, knd, vnd, kc, vc, lens, window=W, out=od, workspace=wsd)
+            torch.cuda.synchronize()
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.decode_iters)]
+            for i in range(args.decode_iters):
+                kc, vc = sets[i % 4]
+                evs[i][0].record(stream)
+                nc.decode(qd, knd, vnd, kc, vc, lens, window=W, out=od, workspace=wsd)
+                evs[i][1].record(stream)
+            torch.cuda.synchronize()
+            us = sum(a.elapsed_time(b) for a, b in evs) * 1e3 / len(evs)
+            KV_row = c.KV * c.D * 2
+            n_cached = sum(s - (0 if W < 0 else max(0, s - W)) for s in lens_h)
+            nbytes = n_cached * 2 * KV_row + c.B * 4 * KV_row + c.B * 2 * c.H * c.D * 2
+            gbps = nbytes / (us * 1e-6) / 1e9
+            decode["L" if W < 0 else "S"] = {"window": W, "us": round(us, 2), "GBps": round(gbps, 1),
+                                             "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4),
+                                             "algorithmic_bytes": nbytes}
+        del sets
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg.name, "global_batch": B, "seq_len": T, "n_head": H, "n_kv_head": KV,
+                   "head_dim": D, "windows": list(cfg.windows), "parallelism": "single GPU"},
+        "roofline": roof,
+        "decode": decode,
+        "detail": detail,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -109,6 +109,31 @@ int ncattn_bwd(const void *q, const void *k, const void *v, const void *o, const
                int window_left, int window_right, float softmax_scale, int dtype,
                void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * The three stages of ncattn_bwd, callable one at a time with the same
+ * arguments and checks: ncattn_bwd_preprocess writes D_i = sum_d dO_i O_i into
+ * the workspace, ncattn_bwd_dkdv then writes dk and dv, ncattn_bwd_dq writes dq.
+ * Enqueuing the three in this order on one stream is exactly ncattn_bwd (the dkdv
+ * and dq stages only read the workspace, so they may also run concurrently on two
+ * streams once the preprocess stage has completed).  Useful for timing and for
+ * overlapping the dq stage with other work.
+ */
+int ncattn_bwd_preprocess(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                          const void *dout, void *dq, void *dk, void *dv,
+                          int B, int T, int n_head, int n_kv_head, int head_dim,
+                          int window_left, int window_right, float softmax_scale, int dtype,
+                          void *workspace, size_t workspace_bytes, void *stream);
+int ncattn_bwd_dkdv(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                    const void *dout, void *dq, void *dk, void *dv,
+                    int B, int T, int n_head, int n_kv_head, int head_dim,
+                    int window_left, int window_right, float softmax_scale, int dtype,
+                    void *workspace, size_t workspace_bytes, void *stream);
+int ncattn_bwd_dq(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                  const void *dout, void *dq, void *dk, void *dv,
+                  int B, int T, int n_head, int n_kv_head, int head_dim,
+                  int window_left, int window_right, float softmax_scale, int dtype,
+                  void *workspace, size_t workspace_bytes, void *stream);
+
 /* Bytes of workspace ncattn_decode needs (split-KV partial results). */
 size_t ncattn_decode_workspace_bytes(int B, int T_max, int n_head, int n_kv_head, int head_dim,
                                      int window_left);

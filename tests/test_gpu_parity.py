@@ -108,7 +108,8 @@ def test_fwd_bwd_closed_forms_on_gpu():
     assert torch.equal(o, v.repeat_interleave(2, dim=2))
     dq, dk, dv = nc.bwd(q, k, v, o, lse, do, window=(0, 0))
     torch.cuda.synchronize()
-    assert float(dq.abs().max()) == 0.0 and float(dk.abs().max()) == 0.0
+    # dS = P (dP - D) vanishes exactly in exact arithmetic; fp32 rounding of dP and D leaves ~1e-6
+    assert float(dq.abs().max()) <= 1e-5 and float(dk.abs().max()) <= 1e-5
     ref = f64(do).reshape(2, 300, 2, 2, 128).sum(axis=3)
     check(dv, ref, "bf16", "dv(W=0)")
 

@@ -17,7 +17,7 @@ import torch
 
 import oracle
 import transformer_attention_qknorm_amd as nc
-from parity_util import check, check_lse, f64, group_slice
+from parity_util import check, check_lse, f64, group_slice, lse_tol_after_bf16_inputs
 from workloads import D12, D20, DECODE, GQA, TINY, config_inputs, decode_inputs
 
 pytestmark = pytest.mark.gpu
@@ -81,7 +81,8 @@ def test_workload_layers(cfg):
             rdq, rdk, rdv = oracle.attn_bwd(xq, xk, f64(sv), f64(sdo), W)
             hs = slice(g * G, (g + 1) * G)
             check(o[b:b + 1, :, hs], ro, "bf16", f"o W={W}")
-            check_lse(lse[b:b + 1, hs], rlse, "bf16", f"lse W={W}")
+            check_lse(lse[b:b + 1, hs], rlse, "bf16", f"lse W={W}",
+                      tol=None if cfg.pre_normed else lse_tol_after_bf16_inputs(cfg.D))
             check(dq[b:b + 1, :, hs], rdq, "bf16", f"dq W={W}")
             check(dk[b:b + 1, :, g:g + 1], rdk, "bf16", f"dk W={W}")
             check(dv[b:b + 1, :, g:g + 1], rdv, "bf16", f"dv W={W}")

@@ -24,7 +24,7 @@ import os
 import torch
 
 __all__ = ["qknorm_rope_", "fwd", "bwd", "decode", "window_sizes", "lib", "NcattnError", "LIB_PATH",
-           "BF16", "F32", "STATUS"]
+           "BF16", "F32", "STATUS", "bwd_workspace", "decode_workspace", "BWD_STAGES"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libncattn.so")
 BF16, F32 = 0, 1
@@ -55,6 +55,9 @@ def lib():
     L.ncattn_bwd_workspace_bytes.restype = sz
     L.ncattn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32,
                              vp, sz, vp]
+    for fn in ("ncattn_bwd_preprocess", "ncattn_bwd_dkdv", "ncattn_bwd_dq"):
+        getattr(L, fn).argtypes = L.ncattn_bwd.argtypes
+        getattr(L, fn).restype = i32
     L.ncattn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     L.ncattn_decode_workspace_bytes.restype = sz
     L.ncattn_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp, sz, vp]
@@ -129,16 +132,23 @@ def qknorm_rope_(q, k, pos_offset=None, rope_base=100000.0, eps=1e-6, qk_gain=1.
     return q, k
 
 
-def fwd(q, k, v, window=(-1, 0), softmax_scale=None):
-    """Attention forward: returns (o [B][T][H][D], lse [B][H][T] fp32)."""
+def fwd(q, k, v, window=(-1, 0), softmax_scale=None, out=None):
+    """Attention forward: returns (o [B][T][H][D], lse [B][H][T] fp32).
+    ``out=(o, lse)`` reuses preallocated outputs."""
     dev = _dev(q, k, v)
     B, T, H, D = q.shape
     if k.shape != v.shape or k.shape[0] != B or k.shape[1] != T or k.shape[3] != D or q.dtype != k.dtype \
             or q.dtype != v.dtype:
         raise ValueError("ncattn.fwd: k, v must be [B][T][n_kv_head][D] of q's dtype")
     wl, wr = _window(window)
-    o = torch.empty_like(q)
-    lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    if out is None:
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    else:
+        o, lse = out
+        _dev(o, lse)
+        if o.shape != q.shape or o.dtype != q.dtype or lse.shape != (B, H, T) or lse.dtype != torch.float32:
+            raise ValueError("ncattn.fwd: out must be (o like q, lse fp32 [B][H][T])")
     with torch.cuda.device(dev):
         rc = lib().ncattn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, T, H, k.shape[2], D, wl, wr,
                               _scale(softmax_scale), _dtype_code(q), _stream(dev))
@@ -146,8 +156,23 @@ def fwd(q, k, v, window=(-1, 0), softmax_scale=None):
     return o, lse
 
 
-def bwd(q, k, v, o, lse, do, window=(-1, 0), softmax_scale=None):
-    """Attention backward: returns (dq, dk, dv)."""
+BWD_STAGES = {None: "ncattn_bwd", "preprocess": "ncattn_bwd_preprocess", "dkdv": "ncattn_bwd_dkdv",
+              "dq": "ncattn_bwd_dq"}
+
+
+def bwd_workspace(q, k):
+    """A workspace tensor large enough for bwd() on these shapes."""
+    B, T, H, D = q.shape
+    n = lib().ncattn_bwd_workspace_bytes(B, T, H, k.shape[2], D, _dtype_code(q))
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=q.device)
+
+
+def bwd(q, k, v, o, lse, do, window=(-1, 0), softmax_scale=None, out=None, workspace=None, stage=None):
+    """Attention backward: returns (dq, dk, dv).
+
+    ``out=(dq, dk, dv)`` and ``workspace`` reuse preallocated buffers; ``stage``
+    ("preprocess", "dkdv" or "dq") enqueues only that stage of the backward (the
+    three in that order, with one workspace, equal the full call)."""
     dev = _dev(q, k, v, o, lse, do)
     B, T, H, D = q.shape
     KV = k.shape[2]
@@ -155,20 +180,36 @@ def bwd(q, k, v, o, lse, do, window=(-1, 0), softmax_scale=None):
         raise ValueError("ncattn.bwd: o, do must match q and lse must be fp32 [B][H][T]")
     if k.shape != v.shape or q.dtype != k.dtype or q.dtype != v.dtype or q.dtype != o.dtype or q.dtype != do.dtype:
         raise ValueError("ncattn.bwd: inconsistent shapes or dtypes")
+    if stage not in BWD_STAGES:
+        raise ValueError(f"ncattn.bwd: unknown stage {stage!r}")
     wl, wr = _window(window)
     dt = _dtype_code(q)
-    L = lib()
-    nws = L.ncattn_bwd_workspace_bytes(B, T, H, KV, D, dt)
-    ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=dev)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = bwd_workspace(q, k) if workspace is None else workspace
+    if out is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    else:
+        dq, dk, dv = out
+        _dev(dq, dk, dv, ws)
+        if dq.shape != q.shape or dk.shape != k.shape or dv.shape != v.shape:
+            raise ValueError("ncattn.bwd: out must be (dq like q, dk like k, dv like v)")
+    fn = getattr(lib(), BWD_STAGES[stage])
     with torch.cuda.device(dev):
-        rc = L.ncattn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv),
-                          B, T, H, KV, D, wl, wr, _scale(softmax_scale), dt, _ptr(ws), ws.numel(), _stream(dev))
-    _check("ncattn_bwd", rc)
+        rc = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv),
+                B, T, H, KV, D, wl, wr, _scale(softmax_scale), dt, _ptr(ws), ws.numel(), _stream(dev))
+    _check(BWD_STAGES[stage], rc)
     return dq, dk, dv
 
 
-def decode(q, k_new, v_new, k_cache, v_cache, cache_seqlens, window=-1, softmax_scale=None, return_lse=False):
+def decode_workspace(q, k_cache, window=-1):
+    """A workspace tensor large enough for decode() on these shapes and window."""
+    B, _, H, D = q.shape
+    wl = window if isinstance(window, int) else _window(window)[0]
+    n = lib().ncattn_decode_workspace_bytes(B, k_cache.shape[1], H, k_cache.shape[2], D, wl)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=q.device)
+
+
+def decode(q, k_new, v_new, k_cache, v_cache, cache_seqlens, window=-1, softmax_scale=None, return_lse=False,
+           out=None, workspace=None):
     """Single-token decode; writes k_new/v_new into cache slot cache_seqlens[b] in place.
 
     q [B][1][H][D], k_new/v_new [B][1][KV][D], caches [B][T_max][KV][D] (bf16),
@@ -185,10 +226,15 @@ def decode(q, k_new, v_new, k_cache, v_cache, cache_seqlens, window=-1, softmax_
     wl = window if isinstance(window, int) else _window(window)[0]
     dt = _dtype_code(q)
     L = lib()
-    nws = L.ncattn_decode_workspace_bytes(B, T_max, H, KV, D, wl)
-    ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=dev)
-    o = torch.empty_like(q)
-    lse = torch.empty((B, H), dtype=torch.float32, device=dev) if return_lse else None
+    ws = decode_workspace(q, k_cache, wl) if workspace is None else workspace
+    if out is None:
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev) if return_lse else None
+    else:
+        o, lse = out if isinstance(out, tuple) else (out, None)
+        _dev(o)
+        if o.shape != q.shape or o.dtype != q.dtype:
+            raise ValueError("ncattn.decode: out must be like q")
     with torch.cuda.device(dev):
         rc = L.ncattn_decode(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(cache_seqlens),
                              _ptr(o), _ptr(lse), B, T_max, H, KV, D, wl, _scale(softmax_scale), dt, _ptr(ws),

@@ -357,7 +357,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t *__restri
 
 hipError_t launch_bwd_bf16(const void *q, const void *k, const void *v, const void *o, const float *lse,
                            const void *dout, void *dq, void *dk, void *dv, float *delta, const AttnShape &sh,
-                           hipStream_t s) {
+                           int stages, hipStream_t s) {
   const long long rows = (long long)sh.B * sh.T * sh.H;
   const long long dblocks = (rows + 15) / 16;
   const long long nkb = (sh.T + kBlockN - 1) / kBlockN;
@@ -365,12 +365,15 @@ hipError_t launch_bwd_bf16(const void *q, const void *k, const void *v, const vo
   const long long kvblocks = nkb * sh.B * sh.KV;
   const long long qblocks = nqb * sh.B * sh.H;
   if (dblocks > 0x7fffffffLL || kvblocks > 0x7fffffffLL || qblocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(bwd_delta_kernel, dim3((unsigned)dblocks), dim3(256), 0, s, (const uint16_t *)o,
+  if (stages & kBwdDelta)
+    hipLaunchKernelGGL(bwd_delta_kernel, dim3((unsigned)dblocks), dim3(256), 0, s, (const uint16_t *)o,
                      (const uint16_t *)dout, delta, sh.B, sh.T, sh.H);
-  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)kvblocks), dim3(256), 0, s, (const uint16_t *)q,
+  if (stages & kBwdDkDv)
+    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)kvblocks), dim3(256), 0, s, (const uint16_t *)q,
                      (const uint16_t *)k, (const uint16_t *)v, (const uint16_t *)dout, lse, delta, (uint16_t *)dk,
                      (uint16_t *)dv, sh.B, sh.T, sh.H, sh.KV, sh.window, sh.scale);
-  hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)qblocks), dim3(256), 0, s, (const uint16_t *)q,
+  if (stages & kBwdDq)
+    hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)qblocks), dim3(256), 0, s, (const uint16_t *)q,
                      (const uint16_t *)k, (const uint16_t *)v, (const uint16_t *)dout, lse, delta, (uint16_t *)dq,
                      sh.B, sh.T, sh.H, sh.KV, sh.window, sh.scale);
   return hipGetLastError();

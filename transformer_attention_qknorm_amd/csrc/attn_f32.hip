@@ -242,17 +242,20 @@ hipError_t fwd_f32(const float *q, const float *k, const float *v, float *o, flo
 template <int D>
 hipError_t bwd_f32(const float *q, const float *k, const float *v, const float *o, const float *lse,
                    const float *dout, float *dq, float *dk, float *dv, float *delta, const AttnShape &sh,
-                   hipStream_t s) {
+                   int stages, hipStream_t s) {
   const long long rows = (long long)sh.B * sh.T * sh.H;
   const long long nqb = (sh.T + kRows - 1) / kRows;
   const long long dblocks = (rows + kRows - 1) / kRows;
   const long long qblocks = nqb * sh.B * sh.H, kblocks = nqb * sh.B * sh.KV;
   if (dblocks > 0x7fffffffLL || qblocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(delta_f32_kernel<D>, dim3((unsigned)dblocks), dim3(256), 0, s, o, dout, delta, sh.B, sh.T,
+  if (stages & kBwdDelta)
+    hipLaunchKernelGGL(delta_f32_kernel<D>, dim3((unsigned)dblocks), dim3(256), 0, s, o, dout, delta, sh.B, sh.T,
                      sh.H);
-  hipLaunchKernelGGL(dkdv_f32_kernel<D>, dim3((unsigned)kblocks), dim3(256), 0, s, q, k, v, dout, lse, delta, dk, dv,
+  if (stages & kBwdDkDv)
+    hipLaunchKernelGGL(dkdv_f32_kernel<D>, dim3((unsigned)kblocks), dim3(256), 0, s, q, k, v, dout, lse, delta, dk, dv,
                      sh.B, sh.T, sh.H, sh.KV, sh.window, sh.scale);
-  hipLaunchKernelGGL(dq_f32_kernel<D>, dim3((unsigned)qblocks), dim3(256), 0, s, q, k, v, dout, lse, delta, dq, sh.B,
+  if (stages & kBwdDq)
+    hipLaunchKernelGGL(dq_f32_kernel<D>, dim3((unsigned)qblocks), dim3(256), 0, s, q, k, v, dout, lse, delta, dq, sh.B,
                      sh.T, sh.H, sh.KV, sh.window, sh.scale);
   return hipGetLastError();
 }
@@ -266,9 +269,9 @@ hipError_t launch_fwd_f32(const float *q, const float *k, const float *v, float 
 
 hipError_t launch_bwd_f32(const float *q, const float *k, const float *v, const float *o, const float *lse,
                           const float *dout, float *dq, float *dk, float *dv, float *delta, const AttnShape &sh,
-                          hipStream_t s) {
-  return sh.D == 64 ? bwd_f32<64>(q, k, v, o, lse, dout, dq, dk, dv, delta, sh, s)
-                    : bwd_f32<128>(q, k, v, o, lse, dout, dq, dk, dv, delta, sh, s);
+                          int stages, hipStream_t s) {
+  return sh.D == 64 ? bwd_f32<64>(q, k, v, o, lse, dout, dq, dk, dv, delta, sh, stages, s)
+                    : bwd_f32<128>(q, k, v, o, lse, dout, dq, dk, dv, delta, sh, stages, s);
 }
 
 }  // namespace ncattn

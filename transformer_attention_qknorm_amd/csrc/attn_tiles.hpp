@@ -72,28 +72,19 @@ __device__ __forceinline__ bf16x8 lds_col_operand(const char *lds, int col0, int
   const int d = col0 + ((g & 1) << 4) + 4 * (r & 3);
   const int row = 16 * c + 4 * h + (r >> 2);
   const int off_in_chunk = (d & 7) * 2;
-  i16x4 lo = lds_read_tr16(lds + swz(row, d >> 3) + off_in_chunk);
-  i16x4 hi = lds_read_tr16(lds + swz(row + 8, d >> 3) + off_in_chunk);
-  bf16x8 out;
-  out[0] = __builtin_bit_cast(__bf16, lo[0]);
-  out[1] = __builtin_bit_cast(__bf16, lo[1]);
-  out[2] = __builtin_bit_cast(__bf16, lo[2]);
-  out[3] = __builtin_bit_cast(__bf16, lo[3]);
-  out[4] = __builtin_bit_cast(__bf16, hi[0]);
-  out[5] = __builtin_bit_cast(__bf16, hi[1]);
-  out[6] = __builtin_bit_cast(__bf16, hi[2]);
-  out[7] = __builtin_bit_cast(__bf16, hi[3]);
-  return out;
+  const u32x2 lo = __builtin_bit_cast(u32x2, lds_read_tr16(lds + swz(row, d >> 3) + off_in_chunk));
+  const u32x2 hi = __builtin_bit_cast(u32x2, lds_read_tr16(lds + swz(row + 8, d >> 3) + off_in_chunk));
+  const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
+  return __builtin_bit_cast(bf16x8, w);
 }
 
 // Operand of a 32x32x16 MFMA taken from a 32x32 fp32 accumulator block (rows =
 // contraction index): step c2 (0 or 1) of the block uses rows {16c2 + 4h + k,
 // 16c2 + 8 + 4h + k}, i.e. accumulator elements 8c2 + k and 8c2 + 4 + k of lane l.
 __device__ __forceinline__ bf16x8 acc_to_operand(const f32x16 &acc, int c2) {
-  bf16x8 out;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) out[k] = (__bf16)acc[8 * c2 + k];
-  return out;
+  const u32x4 w = {pack_bf16x2(acc[8 * c2 + 0], acc[8 * c2 + 1]), pack_bf16x2(acc[8 * c2 + 2], acc[8 * c2 + 3]),
+                   pack_bf16x2(acc[8 * c2 + 4], acc[8 * c2 + 5]), pack_bf16x2(acc[8 * c2 + 6], acc[8 * c2 + 7])};
+  return __builtin_bit_cast(bf16x8, w);
 }
 
 }  // namespace ncattn

@@ -20,19 +20,22 @@ hipError_t launch_qknorm_rope(void *q, void *k, int B, int T, int H, int KV, int
                               const int32_t *pos_offset, const double *inv_freq_host, float eps,
                               float gain, bool bf16, hipStream_t s);
 
+// Backward stages (bit mask): D_i = dO.O, then dK/dV, then dQ.
+constexpr int kBwdDelta = 1, kBwdDkDv = 2, kBwdDq = 4, kBwdAll = 7;
+
 // bf16, head_dim 128, MFMA kernels.
 hipError_t launch_fwd_bf16(const void *q, const void *k, const void *v, void *o, float *lse,
                            const AttnShape &sh, hipStream_t s);
 hipError_t launch_bwd_bf16(const void *q, const void *k, const void *v, const void *o,
                            const float *lse, const void *dout, void *dq, void *dk, void *dv,
-                           float *delta, const AttnShape &sh, hipStream_t s);
+                           float *delta, const AttnShape &sh, int stages, hipStream_t s);
 
 // fp32 reference-precision kernels (head_dim 64 or 128).
 hipError_t launch_fwd_f32(const float *q, const float *k, const float *v, float *o, float *lse,
                           const AttnShape &sh, hipStream_t s);
 hipError_t launch_bwd_f32(const float *q, const float *k, const float *v, const float *o,
                           const float *lse, const float *dout, float *dq, float *dk, float *dv,
-                          float *delta, const AttnShape &sh, hipStream_t s);
+                          float *delta, const AttnShape &sh, int stages, hipStream_t s);
 
 // Split-KV decode, bf16, head_dim 128.
 size_t decode_workspace_bytes(int B, int T_max, int H, int KV, int D, int window);

@@ -140,11 +140,14 @@ size_t ncattn_bwd_workspace_bytes(int B, int T, int n_head, int n_kv_head, int h
   return (size_t)B * n_head * T * sizeof(float);
 }
 
-int ncattn_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse, const void *dout,
-               void *dq, void *dk, void *dv, int B, int T, int n_head, int n_kv_head, int head_dim, int window_left,
-               int window_right, float softmax_scale, int dtype, void *workspace, size_t workspace_bytes,
-               void *stream) {
-  const char *fn = "ncattn_bwd";
+}  // extern "C"
+
+namespace {
+
+int bwd_common(const char *fn, int stages, const void *q, const void *k, const void *v, const void *o,
+               const float *lse, const void *dout, void *dq, void *dk, void *dv, int B, int T, int n_head,
+               int n_kv_head, int head_dim, int window_left, int window_right, float softmax_scale, int dtype,
+               void *workspace, size_t workspace_bytes, void *stream) {
   NC_PTR(q, fn);
   NC_PTR(k, fn);
   NC_PTR(v, fn);
@@ -173,12 +176,32 @@ int ncattn_bwd(const void *q, const void *k, const void *v, const void *o, const
   ncattn::AttnShape sh{B, T, n_head, n_kv_head, head_dim, window_left, resolve_scale(softmax_scale, head_dim)};
   hipError_t e =
       dtype == NCATTN_BF16
-          ? ncattn::launch_bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, (float *)workspace, sh, (hipStream_t)stream)
+          ? ncattn::launch_bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, (float *)workspace, sh, stages,
+                                    (hipStream_t)stream)
           : ncattn::launch_bwd_f32((const float *)q, (const float *)k, (const float *)v, (const float *)o, lse,
                                    (const float *)dout, (float *)dq, (float *)dk, (float *)dv, (float *)workspace, sh,
-                                   (hipStream_t)stream);
+                                   stages, (hipStream_t)stream);
   return hip_status(e, fn);
 }
+
+}  // namespace
+
+extern "C" {
+
+#define NC_BWD_ARGS                                                                                          \
+  q, k, v, o, lse, dout, dq, dk, dv, B, T, n_head, n_kv_head, head_dim, window_left, window_right, softmax_scale, \
+      dtype, workspace, workspace_bytes, stream
+#define NC_BWD_PARAMS                                                                                        \
+  const void *q, const void *k, const void *v, const void *o, const float *lse, const void *dout, void *dq,    \
+      void *dk, void *dv, int B, int T, int n_head, int n_kv_head, int head_dim, int window_left,             \
+      int window_right, float softmax_scale, int dtype, void *workspace, size_t workspace_bytes, void *stream
+
+int ncattn_bwd(NC_BWD_PARAMS) { return bwd_common("ncattn_bwd", ncattn::kBwdAll, NC_BWD_ARGS); }
+int ncattn_bwd_preprocess(NC_BWD_PARAMS) {
+  return bwd_common("ncattn_bwd_preprocess", ncattn::kBwdDelta, NC_BWD_ARGS);
+}
+int ncattn_bwd_dkdv(NC_BWD_PARAMS) { return bwd_common("ncattn_bwd_dkdv", ncattn::kBwdDkDv, NC_BWD_ARGS); }
+int ncattn_bwd_dq(NC_BWD_PARAMS) { return bwd_common("ncattn_bwd_dq", ncattn::kBwdDq, NC_BWD_ARGS); }
 
 size_t ncattn_decode_workspace_bytes(int B, int T_max, int n_head, int n_kv_head, int head_dim, int window_left) {
   if (B <= 0 || T_max <= 0 || n_head <= 0 || n_kv_head <= 0 || head_dim <= 0 || window_left < -1) return 0;
