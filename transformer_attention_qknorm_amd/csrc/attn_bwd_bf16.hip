@@ -56,6 +56,82 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t *__restri
 }
 
 // ---------------------------------------------------------------- dK, dV
+// Per-lane LDS offsets of the two operand patterns used on a 64 x 128 tile.
+struct TileLane {
+  int roff[8];     // row operand (rows l%32, chunk 2s + l/32), s = 0..7; +32 rows = +8192 B
+  int coff[4][2];  // transposed operand, d-block db, rows (16c + x) and (16c + x + 8); +16 rows = +4096 B
+};
+
+__device__ __forceinline__ TileLane make_tile_lane(int lane) {
+  TileLane L;
+  const int h = lane >> 5;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) L.roff[s] = swz(lane & 31, 2 * s + h);
+  const int g = lane >> 4, r = lane & 15;
+  const int x = 4 * (g >> 1) + (r >> 2);
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    const int d = 32 * db + ((g & 1) << 4) + 4 * (r & 3);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) L.coff[db][half] = swz(x + 8 * half, d >> 3) + (d & 7) * 2;
+  }
+  return L;
+}
+
+__device__ __forceinline__ bf16x8 col_operand(const char *t, const TileLane &L, int db, int cs) {
+  const u32x2 lo = __builtin_bit_cast(u32x2, lds_read_tr16(t + L.coff[db][0] + cs * 16 * kRowBytes));
+  const u32x2 hi = __builtin_bit_cast(u32x2, lds_read_tr16(t + L.coff[db][1] + cs * 16 * kRowBytes));
+  const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+constexpr int kQBuf = 2 * kTileBytes + 2 * kTileN * 4;  // Q tile, dO tile, lse2[64], delta[64]
+
+// One 32-query block (rows 32 qb.. of the staged tile) against this wave's 32 keys.
+template <bool kMask>
+__device__ __forceinline__ void dkdv_block(f32x16 (&dkacc)[4], f32x16 (&dvacc)[4], const char *qs, const char *dos,
+                                           const float *lse2, const float *dl, const TileLane &L,
+                                           const bf16x8 (&kreg)[8], const bf16x8 (&vreg)[8], int qb, int qtile0,
+                                           int key_lane, int T, int W, float c, int hh) {
+  f32x16 sacc = f32x16{}, dpacc = f32x16{};
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    sacc = mfma32(*(const bf16x8 *)(qs + L.roff[s] + qb * 32 * kRowBytes), kreg[s], sacc);
+    dpacc = mfma32(*(const bf16x8 *)(dos + L.roff[s] + qb * 32 * kRowBytes), vreg[s], dpacc);
+  }
+  // rows of this lane's accumulator elements: 32 qb + 8 i + 4 hh + j
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r0 = 32 * qb + 8 * i + 4 * hh;
+    const f32x4 l4 = *(const f32x4 *)(lse2 + r0);
+    const f32x4 d4 = *(const f32x4 *)(dl + r0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = 4 * i + j;
+      float p = fast_exp2(__builtin_fmaf(sacc[e], c, -l4[j]));
+      if constexpr (kMask) {
+        const int qi = qtile0 + r0 + j;
+        const bool vis = qi < T && key_lane <= qi && (W < 0 || qi - key_lane <= W);
+        if (!vis) p = 0.f;
+      }
+      sacc[e] = p;
+      dpacc[e] = p * (dpacc[e] - d4[j]);
+    }
+  }
+  // dV^T += dO^T P and dK^T += Q^T dS, contraction over the 32 query rows.
+#pragma unroll
+  for (int c2 = 0; c2 < 2; ++c2) {
+    const bf16x8 pb = acc_to_operand(sacc, c2);
+    const bf16x8 dsb = acc_to_operand(dpacc, c2);
+    const int cs = 2 * qb + c2;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      dvacc[db] = mfma32(col_operand(dos, L, db, cs), pb, dvacc[db]);
+      dkacc[db] = mfma32(col_operand(qs, L, db, cs), dsb, dkacc[db]);
+    }
+  }
+}
+
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__restrict__ Q,
                                                           const uint16_t *__restrict__ K,
                                                           const uint16_t *__restrict__ V,
@@ -64,15 +140,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__rest
                                                           const float *__restrict__ delta, uint16_t *__restrict__ dK,
                                                           uint16_t *__restrict__ dV, int B, int T, int H, int KV,
                                                           int W, float scale) {
-  // [buf][Q | dO] tiles + [buf][lse2 | delta] rows
-  __shared__ __attribute__((aligned(16))) char smem[4 * kTileBytes];
-  __shared__ float srow[2][2][kTileN];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kQBuf];  // [buf][Q | dO | lse2 | delta]
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int hh = lane >> 5;
   const int G = H / KV;
-  const int nkb = (T + kBlockN - 1) / kBlockN;
   const int BKV = B * KV;
   // key blocks near the start of the sequence see the most queries: schedule them first
   const int kblk = (int)(blockIdx.x / BKV);
@@ -83,33 +156,48 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__rest
   const int kw0 = k0 + 32 * wave;
   const int key_lane = kw0 + (lane & 31);  // the key column this lane holds
   const float c = scale * kLog2e;
-  (void)nkb;
 
   const long long q_stride = (long long)H * kD;
   const long long kv_stride = (long long)KV * kD;
+  const TileLoader tl = make_tile_loader(q_stride, tid);
 
-  // K, V rows of this wave's keys as MFMA B operands: lane holds key key_lane,
-  // d = 16 s + 8 hh + [0, 8).
-  bf16x8 kreg[8], vreg[8];
-  {
-    const bool valid = key_lane < T;
-    const long long off = ((long long)b * T + (valid ? key_lane : 0)) * kv_stride + (long long)kvh * kD + 8 * hh;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      u32x4 wk = valid ? *(const u32x4 *)(K + off + 16 * s) : u32x4{0u, 0u, 0u, 0u};
-      u32x4 wv = valid ? *(const u32x4 *)(V + off + 16 * s) : u32x4{0u, 0u, 0u, 0u};
-      kreg[s] = __builtin_bit_cast(bf16x8, wk);
-      vreg[s] = __builtin_bit_cast(bf16x8, wv);
-    }
-  }
-
-  // Query tiles that can see any key of the block.
+  // Query tiles that can see any key of the block, times the G heads of the group.
   const int k_last_blk = min(k0 + kBlockN - 1, T - 1);
   const int q_hi = W < 0 ? T - 1 : min(T - 1, k_last_blk + W);
   const int qt0 = k0 / kTileN;
-  const int qt1 = q_hi / kTileN;
-  const int nq = qt1 - qt0 + 1;
-  const int n_iter = nq * G;  // (query tile, head) pairs
+  const int nq = q_hi / kTileN - qt0 + 1;
+  const int n_iter = nq * G;
+
+  auto stage = [&](int it, int buf) {
+    const int qt = qt0 + it / G;
+    const int h = kvh * G + it % G;
+    char *base = smem + buf * kQBuf;
+    const long long hoff = (long long)b * T * q_stride + (long long)h * kD;
+    tile_load_lds(base, Q + hoff, tl, qt * kTileN, T);
+    tile_load_lds(base + kTileBytes, dO + hoff, tl, qt * kTileN, T);
+    if (tid < 128) {  // waves 0, 1: 64 lse rows and 64 delta rows, 4 bytes per lane
+      const int qi = min(qt * kTileN + lane, T - 1);
+      const float *src = (tid < 64 ? LSE : delta) + ((long long)b * H + h) * T + qi;
+      typedef __attribute__((address_space(3))) void lds_void;
+      typedef __attribute__((address_space(1))) const void glb_void;
+      __builtin_amdgcn_global_load_lds((glb_void *)src, (lds_void *)(base + 2 * kTileBytes + (tid >> 6) * kTileN * 4),
+                                       4, 0, 0);
+    }
+  };
+
+  stage(0, 0);
+
+  bf16x8 kreg[8], vreg[8];
+  {
+    const int kr = min(key_lane, T - 1);
+    const long long off = ((long long)b * T + kr) * kv_stride + (long long)kvh * kD + 8 * hh;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      kreg[s] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(K + off + 16 * s));
+      vreg[s] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(V + off + 16 * s));
+    }
+  }
+  const TileLane L = make_tile_lane(lane);
   const int kw_last = min(kw0 + 31, T - 1);
   const bool wave_active = kw0 < T;
 
@@ -120,89 +208,33 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__rest
     dvacc[i] = f32x16{};
   }
 
-  TileRegs qr, dor;
-  float lse_r = 0.f, del_r = 0.f;
-  auto load_iter = [&](int it) {
-    const int qt = qt0 + it / G;
-    const int h = kvh * G + it % G;
-    const uint16_t *Qb = Q + (long long)b * T * q_stride + (long long)h * kD;
-    const uint16_t *dOb = dO + (long long)b * T * q_stride + (long long)h * kD;
-    tile_load(qr, Qb, q_stride, qt * kTileN, T, tid);
-    tile_load(dor, dOb, q_stride, qt * kTileN, T, tid);
-    if (tid < kTileN) {
-      const int qi = qt * kTileN + tid;
-      const long long ri = ((long long)b * H + h) * T + qi;
-      // rows past T get P = 0 through an infinite LSE
-      lse_r = qi < T ? LSE[ri] * kLog2e : INFINITY;
-      del_r = qi < T ? delta[ri] : 0.f;
-    }
-  };
-  auto store_iter = [&](int buf) {
-    char *base = smem + buf * 2 * kTileBytes;
-    tile_store_lds(base, qr, tid);
-    tile_store_lds(base + kTileBytes, dor, tid);
-    if (tid < kTileN) {
-      srow[buf][0][tid] = lse_r;
-      srow[buf][1][tid] = del_r;
-    }
-  };
-
-  load_iter(0);
-  store_iter(0);
-  __syncthreads();
+  lds_loads_done_barrier();
 
   for (int it = 0; it < n_iter; ++it) {
     const int buf = it & 1;
-    const char *Qs = smem + buf * 2 * kTileBytes;
-    const char *dOs = Qs + kTileBytes;
-    const bool has_next = it + 1 < n_iter;
-    if (has_next) load_iter(it + 1);
+    const char *qs = smem + buf * kQBuf;
+    const char *dos = qs + kTileBytes;
+    float *lse2 = (float *)(qs + 2 * kTileBytes);
+    float *dl = lse2 + kTileN;
+    if (it + 1 < n_iter) stage(it + 1, buf ^ 1);
     const int qtile0 = (qt0 + it / G) * kTileN;
-    const int qtile_last = qtile0 + kTileN - 1;
-    const bool skip = !wave_active || qtile_last < kw0 || (W >= 0 && qtile0 - kw_last > W);
+    // the staged lse is natural-log; scale it to log2 units in place once per tile
+    if (tid < kTileN) lse2[tid] *= kLog2e;
+    __syncthreads();
+    const bool skip = !wave_active || qtile0 + kTileN - 1 < kw0 || (W >= 0 && qtile0 - kw_last > W);
     if (!skip) {
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        const int qr0 = qtile0 + 32 * qb;  // first query row of this 32-row block
-        const bool blk_skip = qr0 + 31 < kw0 || (W >= 0 && qr0 - kw_last > W);
-        if (blk_skip) continue;
-        const bool need_mask = !(qr0 >= kw_last && (W < 0 || qr0 + 31 - kw0 <= W));
-        // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys.
-        f32x16 sacc = f32x16{}, dpacc = f32x16{};
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          sacc = mfma32(lds_row_operand(Qs, 32 * qb, s, lane), kreg[s], sacc);
-          dpacc = mfma32(lds_row_operand(dOs, 32 * qb, s, lane), vreg[s], dpacc);
-        }
-        // P = exp2(S c - LSE log2 e);  dS = P (dP - D)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int r = 32 * qb + 8 * (e >> 2) + 4 * hh + (e & 3);  // row within the tile
-          float p = fast_exp2(__builtin_fmaf(sacc[e], c, -srow[buf][0][r]));
-          if (need_mask) {
-            const int qi = qtile0 + r;
-            const bool vis = key_lane <= qi && (W < 0 || qi - key_lane <= W);
-            if (!vis) p = 0.f;
-          }
-          sacc[e] = p;
-          dpacc[e] = p * (dpacc[e] - srow[buf][1][r]);
-        }
-        // dV^T += dO^T P and dK^T += Q^T dS, contraction over the 32 query rows.
-#pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2) {
-          const bf16x8 pb = acc_to_operand(sacc, c2);
-          const bf16x8 db_ = acc_to_operand(dpacc, c2);
-          const int cs = 2 * qb + c2;
-#pragma unroll
-          for (int db = 0; db < 4; ++db) {
-            dvacc[db] = mfma32(lds_col_operand(dOs, 32 * db, cs, lane), pb, dvacc[db]);
-            dkacc[db] = mfma32(lds_col_operand(Qs, 32 * db, cs, lane), db_, dkacc[db]);
-          }
-        }
+        const int qr0 = qtile0 + 32 * qb;
+        if (qr0 + 31 < kw0 || (W >= 0 && qr0 - kw_last > W)) continue;
+        const bool need_mask = !(qr0 >= kw_last && (W < 0 || qr0 + 31 - kw0 <= W) && qr0 + 31 < T);
+        if (need_mask)
+          dkdv_block<true>(dkacc, dvacc, qs, dos, lse2, dl, L, kreg, vreg, qb, qtile0, key_lane, T, W, c, hh);
+        else
+          dkdv_block<false>(dkacc, dvacc, qs, dos, lse2, dl, L, kreg, vreg, qb, qtile0, key_lane, T, W, c, hh);
       }
     }
-    if (has_next) store_iter(buf ^ 1);
-    __syncthreads();
+    lds_loads_done_barrier();
   }
 
   if (!wave_active || key_lane >= T) return;
