@@ -56,48 +56,18 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t *__restri
 }
 
 // ---------------------------------------------------------------- dK, dV
-// Per-lane LDS offsets of the two operand patterns used on a 64 x 128 tile.
-struct TileLane {
-  int roff[8];     // row operand (rows l%32, chunk 2s + l/32), s = 0..7; +32 rows = +8192 B
-  int coff[4][2];  // transposed operand, d-block db, rows (16c + x) and (16c + x + 8); +16 rows = +4096 B
-};
-
-__device__ __forceinline__ TileLane make_tile_lane(int lane) {
-  TileLane L;
-  const int h = lane >> 5;
-#pragma unroll
-  for (int s = 0; s < 8; ++s) L.roff[s] = swz(lane & 31, 2 * s + h);
-  const int g = lane >> 4, r = lane & 15;
-  const int x = 4 * (g >> 1) + (r >> 2);
-#pragma unroll
-  for (int db = 0; db < 4; ++db) {
-    const int d = 32 * db + ((g & 1) << 4) + 4 * (r & 3);
-#pragma unroll
-    for (int half = 0; half < 2; ++half) L.coff[db][half] = swz(x + 8 * half, d >> 3) + (d & 7) * 2;
-  }
-  return L;
-}
-
-__device__ __forceinline__ bf16x8 col_operand(const char *t, const TileLane &L, int db, int cs) {
-  const u32x2 lo = __builtin_bit_cast(u32x2, lds_read_tr16(t + L.coff[db][0] + cs * 16 * kRowBytes));
-  const u32x2 hi = __builtin_bit_cast(u32x2, lds_read_tr16(t + L.coff[db][1] + cs * 16 * kRowBytes));
-  const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
-  return __builtin_bit_cast(bf16x8, w);
-}
-
 constexpr int kQBuf = 2 * kTileBytes + 2 * kTileN * 4;  // Q tile, dO tile, lse2[64], delta[64]
 
 // One 32-query block (rows 32 qb.. of the staged tile) against this wave's 32 keys.
-template <bool kMask>
-__device__ __forceinline__ void dkdv_block(f32x16 (&dkacc)[4], f32x16 (&dvacc)[4], const char *qs, const char *dos,
+__device__ __forceinline__ void dkdv_block(bool need_mask, f32x16 (&dkacc)[4], f32x16 (&dvacc)[4], const char *qs, const char *dos,
                                            const float *lse2, const float *dl, const TileLane &L,
                                            const bf16x8 (&kreg)[8], const bf16x8 (&vreg)[8], int qb, int qtile0,
                                            int key_lane, int T, int W, float c, int hh) {
   f32x16 sacc = f32x16{}, dpacc = f32x16{};
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
-    sacc = mfma32(*(const bf16x8 *)(qs + L.roff[s] + qb * 32 * kRowBytes), kreg[s], sacc);
-    dpacc = mfma32(*(const bf16x8 *)(dos + L.roff[s] + qb * 32 * kRowBytes), vreg[s], dpacc);
+    sacc = mfma32(row_operand(qs, L, s, qb), kreg[s], sacc);
+    dpacc = mfma32(row_operand(dos, L, s, qb), vreg[s], dpacc);
   }
   // rows of this lane's accumulator elements: 32 qb + 8 i + 4 hh + j
 #pragma unroll
@@ -109,7 +79,7 @@ __device__ __forceinline__ void dkdv_block(f32x16 (&dkacc)[4], f32x16 (&dvacc)[4
     for (int j = 0; j < 4; ++j) {
       const int e = 4 * i + j;
       float p = fast_exp2(__builtin_fmaf(sacc[e], c, -l4[j]));
-      if constexpr (kMask) {
+      if (need_mask) {
         const int qi = qtile0 + r0 + j;
         const bool vis = qi < T && key_lane <= qi && (W < 0 || qi - key_lane <= W);
         if (!vis) p = 0.f;
@@ -140,7 +110,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__rest
                                                           const float *__restrict__ delta, uint16_t *__restrict__ dK,
                                                           uint16_t *__restrict__ dV, int B, int T, int H, int KV,
                                                           int W, float scale) {
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kQBuf];  // [buf][Q | dO | lse2 | delta]
+  // Two separate LDS objects for the double buffer (Q | dO | lse2 | delta each),
+  // so the compiler can tell the copy into one from the reads of the other.
+  __shared__ __attribute__((aligned(1024))) char buf0[kQBuf];
+  __shared__ __attribute__((aligned(1024))) char buf1[kQBuf];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -168,10 +141,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__rest
   const int nq = q_hi / kTileN - qt0 + 1;
   const int n_iter = nq * G;
 
-  auto stage = [&](int it, int buf) {
+  auto stage = [&](int it, char *base) {
     const int qt = qt0 + it / G;
     const int h = kvh * G + it % G;
-    char *base = smem + buf * kQBuf;
     const long long hoff = (long long)b * T * q_stride + (long long)h * kD;
     tile_load_lds(base, Q + hoff, tl, qt * kTileN, T);
     tile_load_lds(base + kTileBytes, dO + hoff, tl, qt * kTileN, T);
@@ -185,7 +157,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__rest
     }
   };
 
-  stage(0, 0);
+  stage(0, buf0);
 
   bf16x8 kreg[8], vreg[8];
   {
@@ -210,31 +182,32 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__rest
 
   lds_loads_done_barrier();
 
-  for (int it = 0; it < n_iter; ++it) {
-    const int buf = it & 1;
-    const char *qs = smem + buf * kQBuf;
-    const char *dos = qs + kTileBytes;
-    float *lse2 = (float *)(qs + 2 * kTileBytes);
-    float *dl = lse2 + kTileN;
-    if (it + 1 < n_iter) stage(it + 1, buf ^ 1);
+  auto step = [&](char *cur, char *nxt, int it) {
+    const char *qs = cur;
+    const char *dos = cur + kTileBytes;
+    float *lse2 = (float *)(cur + 2 * kTileBytes);
+    const float *dl = lse2 + kTileN;
+    if (it + 1 < n_iter) stage(it + 1, nxt);
     const int qtile0 = (qt0 + it / G) * kTileN;
     // the staged lse is natural-log; scale it to log2 units in place once per tile
     if (tid < kTileN) lse2[tid] *= kLog2e;
     __syncthreads();
     const bool skip = !wave_active || qtile0 + kTileN - 1 < kw0 || (W >= 0 && qtile0 - kw_last > W);
     if (!skip) {
-#pragma unroll
+#pragma unroll 1
       for (int qb = 0; qb < 2; ++qb) {
         const int qr0 = qtile0 + 32 * qb;
         if (qr0 + 31 < kw0 || (W >= 0 && qr0 - kw_last > W)) continue;
         const bool need_mask = !(qr0 >= kw_last && (W < 0 || qr0 + 31 - kw0 <= W) && qr0 + 31 < T);
-        if (need_mask)
-          dkdv_block<true>(dkacc, dvacc, qs, dos, lse2, dl, L, kreg, vreg, qb, qtile0, key_lane, T, W, c, hh);
-        else
-          dkdv_block<false>(dkacc, dvacc, qs, dos, lse2, dl, L, kreg, vreg, qb, qtile0, key_lane, T, W, c, hh);
+        dkdv_block(need_mask, dkacc, dvacc, qs, dos, lse2, dl, L, kreg, vreg, qb, qtile0, key_lane, T, W, c, hh);
       }
     }
     lds_loads_done_barrier();
+  };
+  for (int it = 0; it < n_iter; it += 2) {
+    step(buf0, buf1, it);
+    if (it + 1 >= n_iter) break;
+    step(buf1, buf0, it + 1);
   }
 
   if (!wave_active || key_lane >= T) return;
@@ -255,14 +228,56 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__rest
 }
 
 // ---------------------------------------------------------------- dQ
-__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t *__restrict__ Q,
+struct DqState {
+  f32x16 dqacc[4];
+};
+
+// One 64-key tile: S^T = K Q^T, dP^T = V dO^T, dS^T = P^T (dP^T - D), dQ^T += K^T dS^T.
+template <bool kMask>
+__device__ __forceinline__ void dq_tile(DqState &st, const char *ks, const char *vs, const TileLane &L,
+                                        const bf16x8 (&qreg)[8], const bf16x8 (&doreg)[8], int k0, int q_lane,
+                                        int W, float c, float lse2, float del, int hh) {
+  f32x16 sacc[2], dpacc[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    f32x16 a = f32x16{}, g = f32x16{};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      a = mfma32(row_operand(ks, L, s, kb), qreg[s], a);
+      g = mfma32(row_operand(vs, L, s, kb), doreg[s], g);
+    }
+    sacc[kb] = a;
+    dpacc[kb] = g;
+  }
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      float p = fast_exp2(__builtin_fmaf(sacc[kb][e], c, -lse2));
+      if constexpr (kMask) {
+        const int key = k0 + 32 * kb + 8 * (e >> 2) + 4 * hh + (e & 3);
+        const bool vis = key <= q_lane && (W < 0 || q_lane - key <= W);
+        if (!vis) p = 0.f;
+      }
+      dpacc[kb][e] = p * (dpacc[kb][e] - del);
+    }
+#pragma unroll
+  for (int cs = 0; cs < 4; ++cs) {
+    const bf16x8 dsb = acc_to_operand(dpacc[cs >> 1], cs & 1);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) st.dqacc[db] = mfma32(col_operand(ks, L, db, cs), dsb, st.dqacc[db]);
+  }
+}
+
+__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(const uint16_t *__restrict__ Q,
                                                         const uint16_t *__restrict__ K,
                                                         const uint16_t *__restrict__ V,
                                                         const uint16_t *__restrict__ dO,
                                                         const float *__restrict__ LSE,
                                                         const float *__restrict__ delta, uint16_t *__restrict__ dQ,
                                                         int B, int T, int H, int KV, int W, float scale) {
-  __shared__ __attribute__((aligned(16))) char smem[4 * kTileBytes];  // [buf][K|V]
+  __shared__ __attribute__((aligned(1024))) char buf0[2 * kTileBytes];  // K | V, double buffer
+  __shared__ __attribute__((aligned(1024))) char buf1[2 * kTileBytes];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -283,92 +298,60 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t *__restri
   const long long kv_stride = (long long)KV * kD;
   const uint16_t *Kb = K + (long long)b * T * kv_stride + (long long)kvh * kD;
   const uint16_t *Vb = V + (long long)b * T * kv_stride + (long long)kvh * kD;
-
-  bf16x8 qreg[8], doreg[8];
-  const bool valid = q_lane < T;
-  {
-    const long long off = ((long long)b * T + (valid ? q_lane : 0)) * q_stride + (long long)h * kD + 8 * hh;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      u32x4 wq = valid ? *(const u32x4 *)(Q + off + 16 * s) : u32x4{0u, 0u, 0u, 0u};
-      u32x4 wd = valid ? *(const u32x4 *)(dO + off + 16 * s) : u32x4{0u, 0u, 0u, 0u};
-      qreg[s] = __builtin_bit_cast(bf16x8, wq);
-      doreg[s] = __builtin_bit_cast(bf16x8, wd);
-    }
-  }
-  const long long ri = ((long long)b * H + h) * T + (valid ? q_lane : 0);
-  const float lse2 = valid ? LSE[ri] * kLog2e : INFINITY;
-  const float del = valid ? delta[ri] : 0.f;
+  const TileLoader tl = make_tile_loader(kv_stride, tid);
 
   const int q_last_blk = min(q0 + kBlockM - 1, T - 1);
   const int k_lo = W < 0 ? 0 : max(0, q0 - W);
   const int t0 = k_lo / kTileN;
   const int t1 = q_last_blk / kTileN;
+
+  tile_load_lds(buf0, Kb, tl, t0 * kTileN, T);
+  tile_load_lds(buf0 + kTileBytes, Vb, tl, t0 * kTileN, T);
+
+  const bool valid = q_lane < T;
+  bf16x8 qreg[8], doreg[8];
+  {
+    const int qr = min(q_lane, T - 1);
+    const long long off = ((long long)b * T + qr) * q_stride + (long long)h * kD + 8 * hh;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      qreg[s] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(Q + off + 16 * s));
+      doreg[s] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(dO + off + 16 * s));
+    }
+  }
+  const long long ri = ((long long)b * H + h) * T + min(q_lane, T - 1);
+  const float lse2 = valid ? LSE[ri] * kLog2e : INFINITY;  // rows past T get P = 0
+  const float del = valid ? delta[ri] : 0.f;
+  const TileLane L = make_tile_lane(lane);
   const int qw_last = min(qw0 + 31, T - 1);
   const bool wave_active = qw0 < T;
 
-  f32x16 dqacc[4];
+  DqState st;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) dqacc[i] = f32x16{};
+  for (int i = 0; i < 4; ++i) st.dqacc[i] = f32x16{};
 
-  TileRegs kr, vr;
-  tile_load(kr, Kb, kv_stride, t0 * kTileN, T, tid);
-  tile_load(vr, Vb, kv_stride, t0 * kTileN, T, tid);
-  tile_store_lds(smem, kr, tid);
-  tile_store_lds(smem + kTileBytes, vr, tid);
-  __syncthreads();
+  lds_loads_done_barrier();
 
-  for (int t = t0; t <= t1; ++t) {
-    const int buf = (t - t0) & 1;
-    const char *Ks = smem + buf * 2 * kTileBytes;
-    const char *Vs = Ks + kTileBytes;
-    const bool has_next = t < t1;
-    if (has_next) {
-      tile_load(kr, Kb, kv_stride, (t + 1) * kTileN, T, tid);
-      tile_load(vr, Vb, kv_stride, (t + 1) * kTileN, T, tid);
+  auto step = [&](const char *cur, char *nxt, int t) {
+    if (t < t1) {
+      tile_load_lds(nxt, Kb, tl, (t + 1) * kTileN, T);
+      tile_load_lds(nxt + kTileBytes, Vb, tl, (t + 1) * kTileN, T);
     }
     const int k0 = t * kTileN;
     const bool skip = !wave_active || k0 > qw_last || (W >= 0 && qw0 - (k0 + kTileN - 1) > W);
     if (!skip) {
       const bool need_mask = !(k0 + kTileN - 1 <= qw0 && (W < 0 || qw_last - k0 <= W));
-      f32x16 sacc[2], dpacc[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        f32x16 a = f32x16{}, g = f32x16{};
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          a = mfma32(lds_row_operand(Ks, 32 * kb, s, lane), qreg[s], a);
-          g = mfma32(lds_row_operand(Vs, 32 * kb, s, lane), doreg[s], g);
-        }
-        sacc[kb] = a;
-        dpacc[kb] = g;
-      }
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          float p = fast_exp2(__builtin_fmaf(sacc[kb][e], c, -lse2));
-          if (need_mask) {
-            const int key = k0 + 32 * kb + 8 * (e >> 2) + 4 * hh + (e & 3);
-            const bool vis = key <= q_lane && (W < 0 || q_lane - key <= W);
-            if (!vis) p = 0.f;
-          }
-          dpacc[kb][e] = p * (dpacc[kb][e] - del);
-        }
-      // dQ^T += K^T dS^T
-#pragma unroll
-      for (int cs = 0; cs < 4; ++cs) {
-        const bf16x8 dsb = acc_to_operand(dpacc[cs >> 1], cs & 1);
-#pragma unroll
-        for (int db = 0; db < 4; ++db) dqacc[db] = mfma32(lds_col_operand(Ks, 32 * db, cs, lane), dsb, dqacc[db]);
-      }
+      if (need_mask)
+        dq_tile<true>(st, cur, cur + kTileBytes, L, qreg, doreg, k0, q_lane, W, c, lse2, del, hh);
+      else
+        dq_tile<false>(st, cur, cur + kTileBytes, L, qreg, doreg, k0, q_lane, W, c, lse2, del, hh);
     }
-    if (has_next) {
-      char *nxt = smem + (buf ^ 1) * 2 * kTileBytes;
-      tile_store_lds(nxt, kr, tid);
-      tile_store_lds(nxt + kTileBytes, vr, tid);
-    }
-    __syncthreads();
+    lds_loads_done_barrier();
+  };
+  for (int t = t0; t <= t1; t += 2) {
+    step(buf0, buf1, t);
+    if (t + 1 > t1) break;
+    step(buf1, buf0, t + 1);
   }
 
   if (!wave_active || !valid) return;
@@ -379,8 +362,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t *__restri
     for (int i = 0; i < 4; ++i) {
       const int d = 32 * db + 8 * i + 4 * hh;
       u32x2 w;
-      w[0] = pack_bf16x2(dqacc[db][4 * i + 0] * scale, dqacc[db][4 * i + 1] * scale);
-      w[1] = pack_bf16x2(dqacc[db][4 * i + 2] * scale, dqacc[db][4 * i + 3] * scale);
+      w[0] = pack_bf16x2(st.dqacc[db][4 * i + 0] * scale, st.dqacc[db][4 * i + 1] * scale);
+      w[1] = pack_bf16x2(st.dqacc[db][4 * i + 2] * scale, st.dqacc[db][4 * i + 3] * scale);
       *(u32x2 *)(dqp + d) = w;
     }
 }

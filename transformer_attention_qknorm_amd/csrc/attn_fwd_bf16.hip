@@ -30,35 +30,6 @@ constexpr int kBlockM = 128;
 constexpr int kBufBytes = 2 * kTileBytes;  // K tile + V tile
 constexpr float kRescaleThreshold = 8.0f;  // log2 units: rescale O only when the max grows by > 2^8
 
-struct FwdLane {
-  int koff[8];     // K row-operand offsets for d-step s (kb adds 32 rows)
-  int voff[4][2];  // V transposed-operand offsets for d-block db, rows (16c + x) and (16c + x + 8)
-};
-
-__device__ __forceinline__ FwdLane make_fwd_lane(int lane) {
-  FwdLane L;
-  const int h = lane >> 5;
-  const int r32 = lane & 31;
-#pragma unroll
-  for (int s = 0; s < 8; ++s) L.koff[s] = swz(r32, 2 * s + h);
-  const int g = lane >> 4, r = lane & 15;
-  const int x = 4 * (g >> 1) + (r >> 2);
-#pragma unroll
-  for (int db = 0; db < 4; ++db) {
-    const int d = 32 * db + ((g & 1) << 4) + 4 * (r & 3);
-#pragma unroll
-    for (int half = 0; half < 2; ++half) L.voff[db][half] = swz(x + 8 * half, d >> 3) + (d & 7) * 2;
-  }
-  return L;
-}
-
-__device__ __forceinline__ bf16x8 v_operand(const char *vs, const FwdLane &L, int db, int cs) {
-  const u32x2 lo = __builtin_bit_cast(u32x2, lds_read_tr16(vs + L.voff[db][0] + cs * 16 * kRowBytes));
-  const u32x2 hi = __builtin_bit_cast(u32x2, lds_read_tr16(vs + L.voff[db][1] + cs * 16 * kRowBytes));
-  const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
-  return __builtin_bit_cast(bf16x8, w);
-}
-
 struct FwdState {
   f32x16 oacc[4];
   float m_run;  // running reference max of raw scores (both half-waves agree)
@@ -67,7 +38,7 @@ struct FwdState {
 
 // One 64-key tile: S^T, online softmax, O^T += V^T P^T.
 template <bool kMask>
-__device__ __forceinline__ void fwd_tile(FwdState &st, const char *ks, const char *vs, const FwdLane &L,
+__device__ __forceinline__ void fwd_tile(FwdState &st, const char *ks, const char *vs, const TileLane &L,
                                          const bf16x8 (&qreg)[8], int k0, int q_lane, int W, float c, int hh) {
   f32x16 sacc[2];
 #pragma unroll
@@ -75,7 +46,7 @@ __device__ __forceinline__ void fwd_tile(FwdState &st, const char *ks, const cha
     f32x16 acc = f32x16{};
 #pragma unroll
     for (int s = 0; s < 8; ++s)
-      acc = mfma32(*(const bf16x8 *)(ks + L.koff[s] + kb * 32 * kRowBytes), qreg[s], acc);
+      acc = mfma32(row_operand(ks, L, s, kb), qreg[s], acc);
     sacc[kb] = acc;
   }
   if constexpr (kMask) {
@@ -124,7 +95,7 @@ __device__ __forceinline__ void fwd_tile(FwdState &st, const char *ks, const cha
   for (int cs = 0; cs < 4; ++cs) {
     const bf16x8 pb = acc_to_operand(sacc[cs >> 1], cs & 1);
 #pragma unroll
-    for (int db = 0; db < 4; ++db) st.oacc[db] = mfma32(v_operand(vs, L, db, cs), pb, st.oacc[db]);
+    for (int db = 0; db < 4; ++db) st.oacc[db] = mfma32(col_operand(vs, L, db, cs), pb, st.oacc[db]);
   }
 }
 
@@ -133,7 +104,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const uint16_t *_
                                                                const uint16_t *__restrict__ V,
                                                                uint16_t *__restrict__ O, float *__restrict__ LSE,
                                                                int B, int T, int H, int KV, int W, float scale) {
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kBufBytes];  // [buf][K | V]
+  // Two separate LDS objects for the double buffer, so that the compiler can tell
+  // the direct-to-LDS copy into one from the reads of the other and does not
+  // wait for the copy before reading.
+  __shared__ __attribute__((aligned(1024))) char buf0[kBufBytes];  // K | V
+  __shared__ __attribute__((aligned(1024))) char buf1[kBufBytes];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -161,8 +136,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const uint16_t *_
   const int t0 = k_lo / kTileN;
   const int t1 = q_last_blk / kTileN;
 
-  tile_load_lds(smem, Kb, tl, t0 * kTileN, T);
-  tile_load_lds(smem + kTileBytes, Vb, tl, t0 * kTileN, T);
+  tile_load_lds(buf0, Kb, tl, t0 * kTileN, T);
+  tile_load_lds(buf0 + kTileBytes, Vb, tl, t0 * kTileN, T);
 
   // Q^T operand in registers: lane holds q row q_lane, d = 16 s + 8 hh + [0, 8).
   bf16x8 qreg[8];
@@ -172,7 +147,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const uint16_t *_
 #pragma unroll
     for (int s = 0; s < 8; ++s) qreg[s] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qp + 16 * s));
   }
-  const FwdLane L = make_fwd_lane(lane);
+  const TileLane L = make_tile_lane(lane);
   const int qw_last = min(qw0 + 31, T - 1);
   const bool wave_active = qw0 < T;
 
@@ -184,12 +159,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const uint16_t *_
 
   lds_loads_done_barrier();
 
-  for (int t = t0; t <= t1; ++t) {
-    const int buf = (t - t0) & 1;
-    const char *ks = smem + buf * kBufBytes;
-    const char *vs = ks + kTileBytes;
+  // One tile of work on `cur` while the next tile is copied into `nxt`.
+  auto step = [&](const char *cur, char *nxt, int t) {
     if (t < t1) {
-      char *nxt = smem + (buf ^ 1) * kBufBytes;
       tile_load_lds(nxt, Kb, tl, (t + 1) * kTileN, T);
       tile_load_lds(nxt + kTileBytes, Vb, tl, (t + 1) * kTileN, T);
     }
@@ -198,11 +170,16 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const uint16_t *_
     if (!skip) {
       const bool need_mask = !(k0 + kTileN - 1 <= qw0 && (W < 0 || qw_last - k0 <= W));
       if (need_mask)
-        fwd_tile<true>(st, ks, vs, L, qreg, k0, q_lane, W, c, hh);
+        fwd_tile<true>(st, cur, cur + kTileBytes, L, qreg, k0, q_lane, W, c, hh);
       else
-        fwd_tile<false>(st, ks, vs, L, qreg, k0, q_lane, W, c, hh);
+        fwd_tile<false>(st, cur, cur + kTileBytes, L, qreg, k0, q_lane, W, c, hh);
     }
     lds_loads_done_barrier();
+  };
+  for (int t = t0; t <= t1; t += 2) {
+    step(buf0, buf1, t);
+    if (t + 1 > t1) break;
+    step(buf1, buf0, t + 1);
   }
 
   if (!wave_active) return;

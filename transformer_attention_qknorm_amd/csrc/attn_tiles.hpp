@@ -69,58 +69,38 @@ __device__ __forceinline__ void lds_loads_done_barrier() {
   __syncthreads();
 }
 
-// Cooperative copy of a 64 x 128 bf16 tile from global rows (stride in elements)
-// into registers: 256 threads, 4 chunks of 16 B each.  Rows at or past `nrows`
-// are zero-filled.
-struct TileRegs {
-  u32x4 c[4];
+// Per-lane LDS offsets of the two operand patterns used on a 64 x 128 tile,
+// computed once per kernel (row and chunk permutations are lane constants).
+struct TileLane {
+  int roff[8];     // row operand (rows l%32, chunk 2s + l/32), s = 0..7; +32 rows = +8192 B
+  int coff[4][2];  // transposed operand, d-block db, rows (16c + x) and (16c + x + 8); +16 rows = +4096 B
 };
 
-__device__ __forceinline__ void tile_load(TileRegs &r, const uint16_t *__restrict__ base, long long row_stride,
-                                          int row0, int nrows, int tid) {
-  const int chunk = tid & 15;
+__device__ __forceinline__ TileLane make_tile_lane(int lane) {
+  TileLane L;
+  const int h = lane >> 5;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = (tid >> 4) + 16 * i;
-    if (row0 + row < nrows)
-      r.c[i] = *(const u32x4 *)(base + (long long)(row0 + row) * row_stride + chunk * 8);
-    else
-      r.c[i] = u32x4{0u, 0u, 0u, 0u};
-  }
-}
-
-__device__ __forceinline__ void tile_store_lds(char *lds, const TileRegs &r, int tid) {
-  const int chunk = tid & 15;
+  for (int s = 0; s < 8; ++s) L.roff[s] = swz(lane & 31, 2 * s + h);
+  const int g = lane >> 4, r = lane & 15;
+  const int x = 4 * (g >> 1) + (r >> 2);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = (tid >> 4) + 16 * i;
-    *(u32x4 *)(lds + swz(row, chunk)) = r.c[i];
+  for (int db = 0; db < 4; ++db) {
+    const int d = 32 * db + ((g & 1) << 4) + 4 * (r & 3);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) L.coff[db][half] = swz(x + 8 * half, d >> 3) + (d & 7) * 2;
   }
+  return L;
 }
 
-// A/B operand of a 32x32x16 MFMA whose contraction index is the column (d) of a
-// row-major tile: lane l gets row (row0 + l%32), columns 16*s + 8*(l/32) + [0,8).
-__device__ __forceinline__ bf16x8 lds_row_operand(const char *lds, int row0, int s, int lane) {
-  const int row = row0 + (lane & 31);
-  const int chunk = 2 * s + (lane >> 5);
-  return *(const bf16x8 *)(lds + swz(row, chunk));
-}
-
-// A/B operand of a 32x32x16 MFMA whose contraction index runs down the rows of a
-// tile, in the permuted row order that matches a 32x32 accumulator used as the
-// other operand (see acc_to_operand): lane l gets column d = col0 + l%32 of the 8
-// rows {16c + 4h + k, 16c + 8 + 4h + k : k = 0..3}, h = l/32.
-__device__ __forceinline__ bf16x8 lds_col_operand(const char *lds, int col0, int c, int lane) {
-  const int g = lane >> 4;             // 16-lane group
-  const int r = lane & 15;
-  const int h = g >> 1;
-  const int d = col0 + ((g & 1) << 4) + 4 * (r & 3);
-  const int row = 16 * c + 4 * h + (r >> 2);
-  const int off_in_chunk = (d & 7) * 2;
-  const u32x2 lo = __builtin_bit_cast(u32x2, lds_read_tr16(lds + swz(row, d >> 3) + off_in_chunk));
-  const u32x2 hi = __builtin_bit_cast(u32x2, lds_read_tr16(lds + swz(row + 8, d >> 3) + off_in_chunk));
+__device__ __forceinline__ bf16x8 col_operand(const char *t, const TileLane &L, int db, int cs) {
+  const u32x2 lo = __builtin_bit_cast(u32x2, lds_read_tr16(t + L.coff[db][0] + cs * 16 * kRowBytes));
+  const u32x2 hi = __builtin_bit_cast(u32x2, lds_read_tr16(t + L.coff[db][1] + cs * 16 * kRowBytes));
   const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
   return __builtin_bit_cast(bf16x8, w);
+}
+
+__device__ __forceinline__ bf16x8 row_operand(const char *t, const TileLane &L, int s, int rowblk) {
+  return *(const bf16x8 *)(t + L.roff[s] + rowblk * 32 * kRowBytes);
 }
 
 // Operand of a 32x32x16 MFMA taken from a 32x32 fp32 accumulator block (rows =
