@@ -135,7 +135,7 @@ def main():
         L["lse"] = torch.empty(B, H, T, dtype=torch.float32, device=dev)
         L["dq"], L["dk"], L["dv"] = torch.empty_like(L["q"]), torch.empty_like(L["k"]), torch.empty_like(L["v"])
         layers.append(L)
-    ws = nc.bwd_workspace(layers[0]["q"], layers[0]["k"])
+    ws = nc.bwd_workspace(layers[0]["q"], layers[0]["k"], (-1, 0))  # the full-causal band is the largest
     names = ["qknorm_rope", "fwd", "bwd_delta", "bwd_dkdv", "bwd_dq"]
     stream = torch.cuda.current_stream(dev)
 

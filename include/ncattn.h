@@ -89,8 +89,14 @@ int ncattn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
                int B, int T, int n_head, int n_kv_head, int head_dim,
                int window_left, int window_right, float softmax_scale, int dtype, void *stream);
 
-/* Bytes of workspace ncattn_bwd needs (the per-row fp32 D_i = sum_d dO*O). */
-size_t ncattn_bwd_workspace_bytes(int B, int T, int n_head, int n_kv_head, int head_dim, int dtype);
+/*
+ * Bytes of workspace ncattn_bwd needs for this shape and window: the per-row
+ * fp32 D_i = sum_d dO_i O_i and, for bf16, the bf16 dS = P (dP - D) tiles of the
+ * window band that the dk/dv stage hands to the dq stage (64 x 64 tiles, about
+ * 2 bytes per visible (query, key) pair and head).  0 for invalid sizes.
+ */
+size_t ncattn_bwd_workspace_bytes(int B, int T, int n_head, int n_kv_head, int head_dim, int window_left,
+                                  int dtype);
 
 /*
  * Attention backward: the exact gradient of sum(O * dO) ("nanochat (Python)"
@@ -112,11 +118,10 @@ int ncattn_bwd(const void *q, const void *k, const void *v, const void *o, const
 /*
  * The three stages of ncattn_bwd, callable one at a time with the same
  * arguments and checks: ncattn_bwd_preprocess writes D_i = sum_d dO_i O_i into
- * the workspace, ncattn_bwd_dkdv then writes dk and dv, ncattn_bwd_dq writes dq.
- * Enqueuing the three in this order on one stream is exactly ncattn_bwd (the dkdv
- * and dq stages only read the workspace, so they may also run concurrently on two
- * streams once the preprocess stage has completed).  Useful for timing and for
- * overlapping the dq stage with other work.
+ * the workspace, ncattn_bwd_dkdv then writes dk and dv (and, for bf16, dS into
+ * the workspace), ncattn_bwd_dq writes dq from the workspace.  Enqueuing the three
+ * in this order on one stream, with one workspace, is exactly ncattn_bwd; each
+ * stage needs the previous one to have completed.  Useful for timing each stage.
  */
 int ncattn_bwd_preprocess(const void *q, const void *k, const void *v, const void *o, const float *lse,
                           const void *dout, void *dq, void *dk, void *dv,

@@ -51,7 +51,7 @@ def lib():
     vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     L.ncattn_qknorm_rope.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, f32, f32, f32, i32, vp]
     L.ncattn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp]
-    L.ncattn_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+    L.ncattn_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
     L.ncattn_bwd_workspace_bytes.restype = sz
     L.ncattn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32,
                              vp, sz, vp]
@@ -160,10 +160,10 @@ BWD_STAGES = {None: "ncattn_bwd", "preprocess": "ncattn_bwd_preprocess", "dkdv":
               "dq": "ncattn_bwd_dq"}
 
 
-def bwd_workspace(q, k):
-    """A workspace tensor large enough for bwd() on these shapes."""
+def bwd_workspace(q, k, window=(-1, 0)):
+    """A workspace tensor large enough for bwd() on these shapes and window."""
     B, T, H, D = q.shape
-    n = lib().ncattn_bwd_workspace_bytes(B, T, H, k.shape[2], D, _dtype_code(q))
+    n = lib().ncattn_bwd_workspace_bytes(B, T, H, k.shape[2], D, _window(window)[0], _dtype_code(q))
     return torch.empty(max(n, 16), dtype=torch.uint8, device=q.device)
 
 
@@ -184,7 +184,7 @@ def bwd(q, k, v, o, lse, do, window=(-1, 0), softmax_scale=None, out=None, works
         raise ValueError(f"ncattn.bwd: unknown stage {stage!r}")
     wl, wr = _window(window)
     dt = _dtype_code(q)
-    ws = bwd_workspace(q, k) if workspace is None else workspace
+    ws = bwd_workspace(q, k, (wl, wr)) if workspace is None else workspace
     if out is None:
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     else:

@@ -59,10 +59,12 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t *__restri
 constexpr int kQBuf = 2 * kTileBytes + 2 * kTileN * 4;  // Q tile, dO tile, lse2[64], delta[64]
 
 // One 32-query block (rows 32 qb.. of the staged tile) against this wave's 32 keys.
-__device__ __forceinline__ void dkdv_block(bool need_mask, f32x16 (&dkacc)[4], f32x16 (&dvacc)[4], const char *qs, const char *dos,
-                                           const float *lse2, const float *dl, const TileLane &L,
+// dS of the block also goes to `ds_tile` (the [key][query] bf16 64 x 64 tile of
+// this query tile and key tile; this wave's keys are rows kofs..kofs+31).
+__device__ __forceinline__ void dkdv_block(bool need_mask, f32x16 (&dkacc)[4], f32x16 (&dvacc)[4], const char *qs,
+                                           const char *dos, const float *lse2, const float *dl, const TileLane &L,
                                            const bf16x8 (&kreg)[8], const bf16x8 (&vreg)[8], int qb, int qtile0,
-                                           int key_lane, int T, int W, float c, int hh) {
+                                           int key_lane, int T, int W, float c, int hh, uint16_t *ds_row) {
   f32x16 sacc = f32x16{}, dpacc = f32x16{};
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
@@ -87,6 +89,11 @@ __device__ __forceinline__ void dkdv_block(bool need_mask, f32x16 (&dkacc)[4], f
       sacc[e] = p;
       dpacc[e] = p * (dpacc[e] - d4[j]);
     }
+    // dS^T row of this lane's key, query columns r0 .. r0+3
+    u32x2 w;
+    w[0] = pack_bf16x2(dpacc[4 * i + 0], dpacc[4 * i + 1]);
+    w[1] = pack_bf16x2(dpacc[4 * i + 2], dpacc[4 * i + 3]);
+    *(u32x2 *)(ds_row + r0) = w;
   }
   // dV^T += dO^T P and dK^T += Q^T dS, contraction over the 32 query rows.
 #pragma unroll
@@ -108,8 +115,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__rest
                                                           const uint16_t *__restrict__ dO,
                                                           const float *__restrict__ LSE,
                                                           const float *__restrict__ delta, uint16_t *__restrict__ dK,
-                                                          uint16_t *__restrict__ dV, int B, int T, int H, int KV,
-                                                          int W, float scale) {
+                                                          uint16_t *__restrict__ dV, uint16_t *__restrict__ dsband,
+                                                          int B, int T, int H, int KV, int W, float scale, int nqt,
+                                                          int nbw) {
   // Two separate LDS objects for the double buffer (Q | dO | lse2 | delta each),
   // so the compiler can tell the copy into one from the reads of the other.
   __shared__ __attribute__((aligned(1024))) char buf0[kQBuf];
@@ -128,6 +136,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__rest
   const int k0 = kblk * kBlockN;
   const int kw0 = k0 + 32 * wave;
   const int key_lane = kw0 + (lane & 31);  // the key column this lane holds
+  const int kt = kw0 / kTileN;              // key tile of this wave's keys, and their first row in it
+  const int kofs = kw0 % kTileN;
   const float c = scale * kLog2e;
 
   const long long q_stride = (long long)H * kD;
@@ -199,7 +209,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__rest
         const int qr0 = qtile0 + 32 * qb;
         if (qr0 + 31 < kw0 || (W >= 0 && qr0 - kw_last > W)) continue;
         const bool need_mask = !(qr0 >= kw_last && (W < 0 || qr0 + 31 - kw0 <= W) && qr0 + 31 < T);
-        dkdv_block(need_mask, dkacc, dvacc, qs, dos, lse2, dl, L, kreg, vreg, qb, qtile0, key_lane, T, W, c, hh);
+        const int qt = qtile0 / kTileN;
+        const int h = kvh * G + it % G;
+        const long long tile = (((long long)b * H + h) * nqt + qt) * nbw + (kt - ds_kt_lo(qt, W));
+        uint16_t *ds_row = dsband + tile * (kTileN * kTileN) + (kofs + (lane & 31)) * kTileN;
+        dkdv_block(need_mask, dkacc, dvacc, qs, dos, lse2, dl, L, kreg, vreg, qb, qtile0, key_lane, T, W, c, hh,
+                   ds_row);
       }
     }
     lds_loads_done_barrier();
@@ -228,56 +243,34 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__rest
 }
 
 // ---------------------------------------------------------------- dQ
-struct DqState {
-  f32x16 dqacc[4];
-};
+// dQ = scale dS K from the dS tiles the dK/dV stage stored: one GEMM per tile.
+// A dS^T tile ([key][query], 64 x 64 bf16, 128-byte rows) is staged with its
+// 16-byte chunks permuted per row, chunk' = chunk ^ (4 ((row >> 1) & 1)), which
+// keeps the transposing reads below free of bank conflicts.
+__device__ __forceinline__ int ds_swz(int row, int chunk) { return row * 128 + ((chunk ^ (((row >> 1) & 1) << 2)) << 4); }
 
-// One 64-key tile: S^T = K Q^T, dP^T = V dO^T, dS^T = P^T (dP^T - D), dQ^T += K^T dS^T.
-template <bool kMask>
-__device__ __forceinline__ void dq_tile(DqState &st, const char *ks, const char *vs, const TileLane &L,
-                                        const bf16x8 (&qreg)[8], const bf16x8 (&doreg)[8], int k0, int q_lane,
-                                        int W, float c, float lse2, float del, int hh) {
-  f32x16 sacc[2], dpacc[2];
+// Direct global -> LDS copy of one dS^T tile (8 KB) by the 4 waves: wave w,
+// instruction i fills rows 16 w + 8 i + [0, 8), lane l row + l/8, position l%8.
+__device__ __forceinline__ void ds_tile_load(char *lds_tile, const uint16_t *src_tile, int tid) {
+  const int lane = tid & 63, w = tid >> 6;
+  typedef __attribute__((address_space(3))) void lds_void;
+  typedef __attribute__((address_space(1))) const void glb_void;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    f32x16 a = f32x16{}, g = f32x16{};
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      a = mfma32(row_operand(ks, L, s, kb), qreg[s], a);
-      g = mfma32(row_operand(vs, L, s, kb), doreg[s], g);
-    }
-    sacc[kb] = a;
-    dpacc[kb] = g;
-  }
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      float p = fast_exp2(__builtin_fmaf(sacc[kb][e], c, -lse2));
-      if constexpr (kMask) {
-        const int key = k0 + 32 * kb + 8 * (e >> 2) + 4 * hh + (e & 3);
-        const bool vis = key <= q_lane && (W < 0 || q_lane - key <= W);
-        if (!vis) p = 0.f;
-      }
-      dpacc[kb][e] = p * (dpacc[kb][e] - del);
-    }
-#pragma unroll
-  for (int cs = 0; cs < 4; ++cs) {
-    const bf16x8 dsb = acc_to_operand(dpacc[cs >> 1], cs & 1);
-#pragma unroll
-    for (int db = 0; db < 4; ++db) st.dqacc[db] = mfma32(col_operand(ks, L, db, cs), dsb, st.dqacc[db]);
+  for (int i = 0; i < 2; ++i) {
+    const int row = 16 * w + 8 * i + (lane >> 3);
+    const int chunk = (lane & 7) ^ (((row >> 1) & 1) << 2);
+    const char *src = (const char *)src_tile + row * 128 + chunk * 16;
+    __builtin_amdgcn_global_load_lds((glb_void *)src, (lds_void *)(lds_tile + (16 * w + 8 * i) * 128), 16, 0, 0);
   }
 }
 
-__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(const uint16_t *__restrict__ Q,
-                                                        const uint16_t *__restrict__ K,
-                                                        const uint16_t *__restrict__ V,
-                                                        const uint16_t *__restrict__ dO,
-                                                        const float *__restrict__ LSE,
-                                                        const float *__restrict__ delta, uint16_t *__restrict__ dQ,
-                                                        int B, int T, int H, int KV, int W, float scale) {
-  __shared__ __attribute__((aligned(1024))) char buf0[2 * kTileBytes];  // K | V, double buffer
-  __shared__ __attribute__((aligned(1024))) char buf1[2 * kTileBytes];
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t *__restrict__ K,
+                                                        const uint16_t *__restrict__ dsband,
+                                                        uint16_t *__restrict__ dQ, int B, int T, int H, int KV,
+                                                        int W, float scale, int nqt, int nbw) {
+  // double buffer: [K tile | dS^T tile of query tile 2 qblk | of query tile 2 qblk + 1]
+  __shared__ __attribute__((aligned(1024))) char buf0[kTileBytes + 2 * 8192];
+  __shared__ __attribute__((aligned(1024))) char buf1[kTileBytes + 2 * 8192];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -292,59 +285,83 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(const uint16_t *__restri
   const int qw0 = q0 + 32 * wave;
   const int q_lane = qw0 + (lane & 31);
   const int hh = lane >> 5;
-  const float c = scale * kLog2e;
 
-  const long long q_stride = (long long)H * kD;
   const long long kv_stride = (long long)KV * kD;
   const uint16_t *Kb = K + (long long)b * T * kv_stride + (long long)kvh * kD;
-  const uint16_t *Vb = V + (long long)b * T * kv_stride + (long long)kvh * kD;
   const TileLoader tl = make_tile_loader(kv_stride, tid);
+  const uint16_t *dsh = dsband + (long long)bh * nqt * nbw * (kTileN * kTileN);
 
   const int q_last_blk = min(q0 + kBlockM - 1, T - 1);
-  const int k_lo = W < 0 ? 0 : max(0, q0 - W);
-  const int t0 = k_lo / kTileN;
+  const int t0 = (W < 0 ? 0 : max(0, q0 - W)) / kTileN;
   const int t1 = q_last_blk / kTileN;
-
-  tile_load_lds(buf0, Kb, tl, t0 * kTileN, T);
-  tile_load_lds(buf0 + kTileBytes, Vb, tl, t0 * kTileN, T);
-
-  const bool valid = q_lane < T;
-  bf16x8 qreg[8], doreg[8];
-  {
-    const int qr = min(q_lane, T - 1);
-    const long long off = ((long long)b * T + qr) * q_stride + (long long)h * kD + 8 * hh;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      qreg[s] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(Q + off + 16 * s));
-      doreg[s] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(dO + off + 16 * s));
-    }
-  }
-  const long long ri = ((long long)b * H + h) * T + min(q_lane, T - 1);
-  const float lse2 = valid ? LSE[ri] * kLog2e : INFINITY;  // rows past T get P = 0
-  const float del = valid ? delta[ri] : 0.f;
-  const TileLane L = make_tile_lane(lane);
   const int qw_last = min(qw0 + 31, T - 1);
   const bool wave_active = qw0 < T;
+  const int tw0 = max(t0, (W < 0 ? 0 : max(0, qw0 - W)) / kTileN);
+  const int tw1 = wave_active ? qw_last / kTileN : t0 - 1;
 
-  DqState st;
+  // copies for key tile t: K, and the dS^T tiles of the block's two query tiles
+  // that see tile t
+  auto load = [&](char *buf, int t) {
+    tile_load_lds(buf, Kb, tl, t * kTileN, T);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) st.dqacc[i] = f32x16{};
+    for (int sub = 0; sub < 2; ++sub) {
+      const int qt = 2 * qblk + sub;
+      const int j = t - ds_kt_lo(qt, W);
+      if (qt < nqt && j >= 0 && t <= qt)
+        ds_tile_load(buf + kTileBytes + sub * 8192, dsh + ((long long)qt * nbw + j) * (kTileN * kTileN), tid);
+    }
+  };
 
+  const TileLane L = make_tile_lane(lane);
+  // per-lane offsets of the dS^T operand (query column 32 (wave & 1) + l%32, keys
+  // {16 c + x + k, 16 c + x + 8 + k}, x = 4 (l/32) + ((l%16) >> 2)); + 2048 B per c
+  int soff[2];
+  {
+    const int g = lane >> 4, r = lane & 15;
+    const int x = 4 * (g >> 1) + (r >> 2);
+    const int qc = 32 * (wave & 1) + ((g & 1) << 4) + 4 * (r & 3);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) soff[half] = ds_swz(x + 8 * half, qc >> 3) + (qc & 7) * 2;
+  }
+  const int ssub = (wave >> 1) * 8192;
+
+  f32x16 dqacc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dqacc[i] = f32x16{};
+
+  load(buf0, t0);
   lds_loads_done_barrier();
 
   auto step = [&](const char *cur, char *nxt, int t) {
-    if (t < t1) {
-      tile_load_lds(nxt, Kb, tl, (t + 1) * kTileN, T);
-      tile_load_lds(nxt + kTileBytes, Vb, tl, (t + 1) * kTileN, T);
-    }
-    const int k0 = t * kTileN;
-    const bool skip = !wave_active || k0 > qw_last || (W >= 0 && qw0 - (k0 + kTileN - 1) > W);
-    if (!skip) {
+    if (t < t1) load(nxt, t + 1);
+    if (t >= tw0 && t <= tw1) {
+      const int k0 = t * kTileN;
       const bool need_mask = !(k0 + kTileN - 1 <= qw0 && (W < 0 || qw_last - k0 <= W));
-      if (need_mask)
-        dq_tile<true>(st, cur, cur + kTileBytes, L, qreg, doreg, k0, q_lane, W, c, lse2, del, hh);
-      else
-        dq_tile<false>(st, cur, cur + kTileBytes, L, qreg, doreg, k0, q_lane, W, c, lse2, del, hh);
+      const char *st = cur + kTileBytes + ssub;
+#pragma unroll
+      for (int cs = 0; cs < 4; ++cs) {
+        const u32x2 lo = __builtin_bit_cast(u32x2, lds_read_tr16(st + soff[0] + cs * 16 * 128));
+        const u32x2 hi = __builtin_bit_cast(u32x2, lds_read_tr16(st + soff[1] + cs * 16 * 128));
+        u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
+        if (need_mask) {
+          // operand element e holds key k0 + 16 cs + 4 hh + (e & 3) + 8 (e >> 2)
+#pragma unroll
+          for (int e2 = 0; e2 < 4; ++e2) {
+            uint32_t keep = 0u;
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+              const int e = 2 * e2 + half;
+              const int key = k0 + 16 * cs + 4 * hh + (e & 3) + 8 * (e >> 2);
+              const bool vis = key <= q_lane && (W < 0 || q_lane - key <= W);
+              keep |= vis ? (0xffffu << (16 * half)) : 0u;
+            }
+            w[e2] &= keep;
+          }
+        }
+        const bf16x8 dsb = __builtin_bit_cast(bf16x8, w);
+#pragma unroll
+        for (int db = 0; db < 4; ++db) dqacc[db] = mfma32(col_operand(cur, L, db, cs), dsb, dqacc[db]);
+      }
     }
     lds_loads_done_barrier();
   };
@@ -354,25 +371,35 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(const uint16_t *__restri
     step(buf1, buf0, t + 1);
   }
 
-  if (!wave_active || !valid) return;
-  uint16_t *dqp = dQ + ((long long)b * T + q_lane) * q_stride + (long long)h * kD;
+  if (!wave_active || q_lane >= T) return;
+  uint16_t *dqp = dQ + ((long long)b * T + q_lane) * ((long long)H * kD) + (long long)h * kD;
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int d = 32 * db + 8 * i + 4 * hh;
       u32x2 w;
-      w[0] = pack_bf16x2(st.dqacc[db][4 * i + 0] * scale, st.dqacc[db][4 * i + 1] * scale);
-      w[1] = pack_bf16x2(st.dqacc[db][4 * i + 2] * scale, st.dqacc[db][4 * i + 3] * scale);
+      w[0] = pack_bf16x2(dqacc[db][4 * i + 0] * scale, dqacc[db][4 * i + 1] * scale);
+      w[1] = pack_bf16x2(dqacc[db][4 * i + 2] * scale, dqacc[db][4 * i + 3] * scale);
       *(u32x2 *)(dqp + d) = w;
     }
 }
 
 }  // namespace
 
+size_t bwd_workspace_bytes(int B, int T, int H, int W, bool bf16) {
+  const size_t delta = ((size_t)B * H * T * sizeof(float) + 255) & ~(size_t)255;
+  if (!bf16) return delta;
+  const DsBand band = ds_band(T, W);
+  return delta + (size_t)B * H * band.nqt * band.nbw * (kTileN * kTileN) * 2;
+}
+
 hipError_t launch_bwd_bf16(const void *q, const void *k, const void *v, const void *o, const float *lse,
-                           const void *dout, void *dq, void *dk, void *dv, float *delta, const AttnShape &sh,
+                           const void *dout, void *dq, void *dk, void *dv, void *workspace, const AttnShape &sh,
                            int stages, hipStream_t s) {
+  float *delta = (float *)workspace;
+  uint16_t *dsband = (uint16_t *)((char *)workspace + (((size_t)sh.B * sh.H * sh.T * sizeof(float) + 255) & ~(size_t)255));
+  const DsBand band = ds_band(sh.T, sh.window);
   const long long rows = (long long)sh.B * sh.T * sh.H;
   const long long dblocks = (rows + 15) / 16;
   const long long nkb = (sh.T + kBlockN - 1) / kBlockN;
@@ -382,15 +409,14 @@ hipError_t launch_bwd_bf16(const void *q, const void *k, const void *v, const vo
   if (dblocks > 0x7fffffffLL || kvblocks > 0x7fffffffLL || qblocks > 0x7fffffffLL) return hipErrorInvalidValue;
   if (stages & kBwdDelta)
     hipLaunchKernelGGL(bwd_delta_kernel, dim3((unsigned)dblocks), dim3(256), 0, s, (const uint16_t *)o,
-                     (const uint16_t *)dout, delta, sh.B, sh.T, sh.H);
+                       (const uint16_t *)dout, delta, sh.B, sh.T, sh.H);
   if (stages & kBwdDkDv)
     hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)kvblocks), dim3(256), 0, s, (const uint16_t *)q,
-                     (const uint16_t *)k, (const uint16_t *)v, (const uint16_t *)dout, lse, delta, (uint16_t *)dk,
-                     (uint16_t *)dv, sh.B, sh.T, sh.H, sh.KV, sh.window, sh.scale);
+                       (const uint16_t *)k, (const uint16_t *)v, (const uint16_t *)dout, lse, delta, (uint16_t *)dk,
+                       (uint16_t *)dv, dsband, sh.B, sh.T, sh.H, sh.KV, sh.window, sh.scale, band.nqt, band.nbw);
   if (stages & kBwdDq)
-    hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)qblocks), dim3(256), 0, s, (const uint16_t *)q,
-                     (const uint16_t *)k, (const uint16_t *)v, (const uint16_t *)dout, lse, delta, (uint16_t *)dq,
-                     sh.B, sh.T, sh.H, sh.KV, sh.window, sh.scale);
+    hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)qblocks), dim3(256), 0, s, (const uint16_t *)k, dsband,
+                       (uint16_t *)dq, sh.B, sh.T, sh.H, sh.KV, sh.window, sh.scale, band.nqt, band.nbw);
   return hipGetLastError();
 }
 

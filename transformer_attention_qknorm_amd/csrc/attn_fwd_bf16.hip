@@ -10,15 +10,19 @@
 // Work decomposition: one workgroup (4 waves) per (b, h, 128-row query block),
 // heaviest (latest) query blocks first; wave w owns query rows 32w..32w+31 of the
 // block and keeps them in registers.  Key/value tiles of 64 rows are copied
-// global -> LDS directly (no register staging), double-buffered, so the copy of
-// tile t+1 overlaps the math on tile t.  Each wave computes S^T = K Q^T (keys as
-// MFMA rows, queries as columns) so that every lane holds one query's scores: the
-// row max and row sum are lane-local plus one exchange with lane l^32, and the
-// probabilities feed O^T += V^T P^T directly as the MFMA B operand (V^T comes
-// from LDS with transposing reads).  All LDS read addresses are per-lane
-// constants computed once.  Tiles entirely outside a wave's window are skipped;
-// masks are applied only on tiles that straddle the causal diagonal or the
-// window edge.
+// global -> LDS directly (no register staging).  Each wave computes S^T = K Q^T
+// (keys as MFMA rows, queries as columns) so that every lane holds one query's
+// scores: the row max and row sum are lane-local plus one exchange with lane
+// l^32, and the probabilities feed O^T += V^T P^T directly as the MFMA B operand
+// (V^T comes from LDS with transposing reads).
+//
+// Software pipeline: in step t a wave issues the S^T MFMAs of tile t+1 and, in
+// the same instruction stream, the softmax of tile t (independent work, so the
+// vector ALU and the matrix cores run together), then O += P V for tile t.  K
+// therefore runs one tile ahead of V: step t reads K(t+1) and V(t) while
+// K(t+2) and V(t+1) are being copied into the other halves of two LDS rings.
+// Tiles entirely outside a wave's window are skipped; masks are applied only on
+// tiles that straddle the causal diagonal or the window edge.
 #include "attn_tiles.hpp"
 #include "internal.hpp"
 
@@ -27,7 +31,6 @@ namespace ncattn {
 namespace {
 
 constexpr int kBlockM = 128;
-constexpr int kBufBytes = 2 * kTileBytes;  // K tile + V tile
 constexpr float kRescaleThreshold = 8.0f;  // log2 units: rescale O only when the max grows by > 2^8
 
 struct FwdState {
@@ -36,20 +39,22 @@ struct FwdState {
   float l_run;  // this lane's partial row sum (its 32 of every 64 keys)
 };
 
-// One 64-key tile: S^T, online softmax, O^T += V^T P^T.
-template <bool kMask>
-__device__ __forceinline__ void fwd_tile(FwdState &st, const char *ks, const char *vs, const TileLane &L,
-                                         const bf16x8 (&qreg)[8], int k0, int q_lane, int W, float c, int hh) {
-  f32x16 sacc[2];
+__device__ __forceinline__ void s_tile(f32x16 (&sacc)[2], const char *ks, const TileLane &L,
+                                       const bf16x8 (&qreg)[8]) {
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     f32x16 acc = f32x16{};
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
-      acc = mfma32(row_operand(ks, L, s, kb), qreg[s], acc);
+    for (int s = 0; s < 8; ++s) acc = mfma32(row_operand(ks, L, s, kb), qreg[s], acc);
     sacc[kb] = acc;
   }
-  if constexpr (kMask) {
+}
+
+// Online softmax of one tile, part 1: mask, tile max and (rarely) the lazy
+// rescale of O.  Returns the exponent offset -m_run * c for part 2.
+__device__ __forceinline__ float softmax_max(FwdState &st, f32x16 (&sacc)[2], bool need_mask, int k0, int q_lane,
+                                             int W, float c, int hh) {
+  if (need_mask) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -80,20 +85,27 @@ __device__ __forceinline__ void fwd_tile(FwdState &st, const char *ks, const cha
       st.m_run = m_new;
     }
   }
-  const float mc = (st.m_run == -INFINITY) ? 0.f : st.m_run * c;
+  return (st.m_run == -INFINITY) ? 0.f : -st.m_run * c;
+}
+
+// Part 2: probabilities (in place) and the row-sum update; straight-line code.
+__device__ __forceinline__ void softmax_exp(FwdState &st, f32x16 (&sacc)[2], float nmc, float c) {
   float ls = 0.f;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const float p = fast_exp2(__builtin_fmaf(sacc[kb][e], c, -mc));
+      const float p = fast_exp2(__builtin_fmaf(sacc[kb][e], c, nmc));
       sacc[kb][e] = p;
       ls += p;
     }
   st.l_run += ls;
+}
+
+__device__ __forceinline__ void pv_tile(FwdState &st, const f32x16 (&pacc)[2], const char *vs, const TileLane &L) {
 #pragma unroll
   for (int cs = 0; cs < 4; ++cs) {
-    const bf16x8 pb = acc_to_operand(sacc[cs >> 1], cs & 1);
+    const bf16x8 pb = acc_to_operand(pacc[cs >> 1], cs & 1);
 #pragma unroll
     for (int db = 0; db < 4; ++db) st.oacc[db] = mfma32(col_operand(vs, L, db, cs), pb, st.oacc[db]);
   }
@@ -104,11 +116,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const uint16_t *_
                                                                const uint16_t *__restrict__ V,
                                                                uint16_t *__restrict__ O, float *__restrict__ LSE,
                                                                int B, int T, int H, int KV, int W, float scale) {
-  // Two separate LDS objects for the double buffer, so that the compiler can tell
-  // the direct-to-LDS copy into one from the reads of the other and does not
-  // wait for the copy before reading.
-  __shared__ __attribute__((aligned(1024))) char buf0[kBufBytes];  // K | V
-  __shared__ __attribute__((aligned(1024))) char buf1[kBufBytes];
+  // Two-slot rings for K and V, each slot its own LDS object so the compiler can
+  // tell a copy into one slot from reads of the other.
+  __shared__ __attribute__((aligned(1024))) char kb0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char kb1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char vb0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char vb1[kTileBytes];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -131,13 +144,23 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const uint16_t *_
   const uint16_t *Vb = V + (long long)b * T * kv_stride + (long long)kvh * kD;
   const TileLoader tl = make_tile_loader(kv_stride, tid);
 
+  // tiles of the block, and the contiguous range of them this wave needs
   const int q_last_blk = min(q0 + kBlockM - 1, T - 1);
-  const int k_lo = W < 0 ? 0 : max(0, q0 - W);
-  const int t0 = k_lo / kTileN;
+  const int t0 = (W < 0 ? 0 : max(0, q0 - W)) / kTileN;
   const int t1 = q_last_blk / kTileN;
+  const int qw_last = min(qw0 + 31, T - 1);
+  const bool wave_active = qw0 < T;
+  const int tw0 = max(t0, (W < 0 ? 0 : max(0, qw0 - W)) / kTileN);
+  const int tw1 = wave_active ? qw_last / kTileN : t0 - 1;  // empty range if inactive
+  auto in_range = [&](int t) { return t >= tw0 && t <= tw1; };
+  auto masked = [&](int t) {
+    const int k0 = t * kTileN;
+    return !(k0 + kTileN - 1 <= qw0 && (W < 0 || qw_last - k0 <= W));
+  };
 
-  tile_load_lds(buf0, Kb, tl, t0 * kTileN, T);
-  tile_load_lds(buf0 + kTileBytes, Vb, tl, t0 * kTileN, T);
+  tile_load_lds(kb0, Kb, tl, t0 * kTileN, T);
+  tile_load_lds(vb0, Vb, tl, t0 * kTileN, T);
+  if (t0 + 1 <= t1) tile_load_lds(kb1, Kb, tl, (t0 + 1) * kTileN, T);
 
   // Q^T operand in registers: lane holds q row q_lane, d = 16 s + 8 hh + [0, 8).
   bf16x8 qreg[8];
@@ -148,8 +171,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const uint16_t *_
     for (int s = 0; s < 8; ++s) qreg[s] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qp + 16 * s));
   }
   const TileLane L = make_tile_lane(lane);
-  const int qw_last = min(qw0 + 31, T - 1);
-  const bool wave_active = qw0 < T;
 
   FwdState st;
 #pragma unroll
@@ -158,28 +179,38 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const uint16_t *_
   st.l_run = 0.f;
 
   lds_loads_done_barrier();
+  f32x16 scur[2], snext[2];
+  if (in_range(t0)) s_tile(scur, kb0, L, qreg);
+  __syncthreads();  // every wave is done with K(t0) before its slot is refilled
 
-  // One tile of work on `cur` while the next tile is copied into `nxt`.
-  auto step = [&](const char *cur, char *nxt, int t) {
-    if (t < t1) {
-      tile_load_lds(nxt, Kb, tl, (t + 1) * kTileN, T);
-      tile_load_lds(nxt + kTileBytes, Vb, tl, (t + 1) * kTileN, T);
-    }
-    const int k0 = t * kTileN;
-    const bool skip = !wave_active || k0 > qw_last || (W >= 0 && qw0 - (k0 + kTileN - 1) > W);
-    if (!skip) {
-      const bool need_mask = !(k0 + kTileN - 1 <= qw0 && (W < 0 || qw_last - k0 <= W));
-      if (need_mask)
-        fwd_tile<true>(st, cur, cur + kTileBytes, L, qreg, k0, q_lane, W, c, hh);
-      else
-        fwd_tile<false>(st, cur, cur + kTileBytes, L, qreg, k0, q_lane, W, c, hh);
+  // Step t: S of tile t+1 from kcur, softmax + PV of tile t from vcur; copies of
+  // K(t+2) into kfill and V(t+1) into vfill run meanwhile.
+  auto step = [&](const char *kcur, char *kfill, const char *vcur, char *vfill, int t) {
+    if (t + 2 <= t1) tile_load_lds(kfill, Kb, tl, (t + 2) * kTileN, T);
+    if (t + 1 <= t1) tile_load_lds(vfill, Vb, tl, (t + 1) * kTileN, T);
+    const bool cur = in_range(t), next = in_range(t + 1);
+    if (cur && next) {
+      // steady state: one straight-line block holding the S MFMAs of tile t+1,
+      // the exponentials of tile t and the PV MFMAs of tile t
+      const float nmc = softmax_max(st, scur, masked(t), t * kTileN, q_lane, W, c, hh);
+      s_tile(snext, kcur, L, qreg);
+      softmax_exp(st, scur, nmc, c);
+      pv_tile(st, scur, vcur, L);
+      scur[0] = snext[0];
+      scur[1] = snext[1];
+    } else if (cur) {
+      const float nmc = softmax_max(st, scur, masked(t), t * kTileN, q_lane, W, c, hh);
+      softmax_exp(st, scur, nmc, c);
+      pv_tile(st, scur, vcur, L);
+    } else if (next) {
+      s_tile(scur, kcur, L, qreg);
     }
     lds_loads_done_barrier();
   };
   for (int t = t0; t <= t1; t += 2) {
-    step(buf0, buf1, t);
+    step(kb1, kb0, vb0, vb1, t);
     if (t + 1 > t1) break;
-    step(buf1, buf0, t + 1);
+    step(kb0, kb1, vb1, vb0, t + 1);
   }
 
   if (!wave_active) return;

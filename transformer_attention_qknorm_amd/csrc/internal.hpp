@@ -23,12 +23,33 @@ hipError_t launch_qknorm_rope(void *q, void *k, int B, int T, int H, int KV, int
 // Backward stages (bit mask): D_i = dO.O, then dK/dV, then dQ.
 constexpr int kBwdDelta = 1, kBwdDkDv = 2, kBwdDq = 4, kBwdAll = 7;
 
+// The bf16 backward hands dS = P (dP - D) from the dK/dV stage to the dQ stage
+// through the workspace, as bf16 64 x 64 tiles stored transposed ([key][query],
+// row-major), one per (b, head, query tile, key tile) inside the window band:
+// query tile qt keeps key tiles kt_lo(qt) .. qt, slot j = kt - kt_lo(qt).
+struct DsBand {
+  int nqt;  // query tiles of 64 rows
+  int nbw;  // key-tile slots per query tile
+};
+inline DsBand ds_band(int T, int W) {
+  const int nt = (T + 63) / 64;
+  const int nbw = W < 0 ? nt : (W + 63) / 64 + 1;
+  return DsBand{nt, nbw < nt ? nbw : nt};
+}
+__host__ __device__ inline int ds_kt_lo(int qt, int W) {
+  if (W < 0) return 0;
+  const int x = 64 * qt - W;
+  return x > 0 ? x / 64 : 0;
+}
+// workspace: D [B][H][T] fp32 (padded to 256 B), then (bf16 only) the dS band
+size_t bwd_workspace_bytes(int B, int T, int H, int W, bool bf16);
+
 // bf16, head_dim 128, MFMA kernels.
 hipError_t launch_fwd_bf16(const void *q, const void *k, const void *v, void *o, float *lse,
                            const AttnShape &sh, hipStream_t s);
 hipError_t launch_bwd_bf16(const void *q, const void *k, const void *v, const void *o,
                            const float *lse, const void *dout, void *dq, void *dk, void *dv,
-                           float *delta, const AttnShape &sh, int stages, hipStream_t s);
+                           void *workspace, const AttnShape &sh, int stages, hipStream_t s);
 
 // fp32 reference-precision kernels (head_dim 64 or 128).
 hipError_t launch_fwd_f32(const float *q, const float *k, const float *v, float *o, float *lse,

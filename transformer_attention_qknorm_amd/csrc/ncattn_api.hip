@@ -7,7 +7,7 @@
 
 #include <new>
 
-#include "../../include/ncattn.h"
+#include "ncattn.h"
 #include "internal.hpp"
 
 namespace {
@@ -132,12 +132,12 @@ int ncattn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
   return hip_status(e, fn);
 }
 
-size_t ncattn_bwd_workspace_bytes(int B, int T, int n_head, int n_kv_head, int head_dim, int dtype) {
+size_t ncattn_bwd_workspace_bytes(int B, int T, int n_head, int n_kv_head, int head_dim, int window_left,
+                                  int dtype) {
   (void)n_kv_head;
   (void)head_dim;
-  (void)dtype;
-  if (B <= 0 || T <= 0 || n_head <= 0) return 0;
-  return (size_t)B * n_head * T * sizeof(float);
+  if (B <= 0 || T <= 0 || n_head <= 0 || window_left < -1) return 0;
+  return ncattn::bwd_workspace_bytes(B, T, n_head, window_left, dtype == NCATTN_BF16);
 }
 
 }  // extern "C"
@@ -168,7 +168,7 @@ int bwd_common(const char *fn, int stages, const void *q, const void *k, const v
     for (const void *y : ins)
       if (x == y) return fail(NCATTN_EINVAL, "%s: gradients must not alias an input", fn);
   if (dq == dk || dq == dv || dk == dv) return fail(NCATTN_EINVAL, "%s: dq, dk, dv must be distinct", fn);
-  size_t need = ncattn_bwd_workspace_bytes(B, T, n_head, n_kv_head, head_dim, dtype);
+  size_t need = ncattn_bwd_workspace_bytes(B, T, n_head, n_kv_head, head_dim, window_left, dtype);
   if (workspace == nullptr || workspace_bytes < need)
     return fail(NCATTN_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
                 workspace == nullptr ? (size_t)0 : workspace_bytes);
@@ -176,7 +176,7 @@ int bwd_common(const char *fn, int stages, const void *q, const void *k, const v
   ncattn::AttnShape sh{B, T, n_head, n_kv_head, head_dim, window_left, resolve_scale(softmax_scale, head_dim)};
   hipError_t e =
       dtype == NCATTN_BF16
-          ? ncattn::launch_bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, (float *)workspace, sh, stages,
+          ? ncattn::launch_bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, workspace, sh, stages,
                                     (hipStream_t)stream)
           : ncattn::launch_bwd_f32((const float *)q, (const float *)k, (const float *)v, (const float *)o, lse,
                                    (const float *)dout, (float *)dq, (float *)dk, (float *)dv, (float *)workspace, sh,
