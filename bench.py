@@ -112,6 +112,9 @@ def main():
     ap.add_argument("--decode-iters", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after timing, copy a buffer of this many MiB device-to-device 3 times: a kernel of "
+                         "known traffic for calibrating rocprofv3's FETCH_SIZE/WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU only (the attention path needs no collective); "
@@ -260,6 +263,15 @@ def main():
         "decode": decode,
         "detail": detail,
     }
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg)
     print(json.dumps(out), flush=True)
