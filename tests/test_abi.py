@@ -82,12 +82,13 @@ def test_qknorm_rope_validation(L):
 
 
 def test_bwd_validation_and_workspace(L):
-    # fp32: the per-row D only (padded to 256 B); bf16 adds the dS band of 64 x 64
-    # bf16 tiles: ceil(T/64) query tiles x min(ceil(T/64), ceil(W/64) + 1) key tiles
+    # fp32: the per-row D only (padded to 256 B); bf16 adds LSE * log2(e) (same size)
+    # and the dS band of 64 x 64 bf16 tiles: ceil(T/64) query tiles x
+    # min(ceil(T/64), ceil(W/64) + 1) key tiles
     assert L.ncattn_bwd_workspace_bytes(2, 100, 4, 2, 128, -1, 1) == 3328
-    assert L.ncattn_bwd_workspace_bytes(2, 100, 4, 2, 128, -1, 0) == 3328 + 2 * 4 * 2 * 2 * 8192
-    assert L.ncattn_bwd_workspace_bytes(1, 2048, 1, 1, 128, 1024, 0) == 8192 + 32 * 17 * 8192
-    assert L.ncattn_bwd_workspace_bytes(1, 2048, 1, 1, 128, 0, 0) == 8192 + 32 * 1 * 8192
+    assert L.ncattn_bwd_workspace_bytes(2, 100, 4, 2, 128, -1, 0) == 2 * 3328 + 2 * 4 * 2 * 2 * 8192
+    assert L.ncattn_bwd_workspace_bytes(1, 2048, 1, 1, 128, 1024, 0) == 2 * 8192 + 32 * 17 * 8192
+    assert L.ncattn_bwd_workspace_bytes(1, 2048, 1, 1, 128, 0, 0) == 2 * 8192 + 32 * 1 * 8192
     assert L.ncattn_bwd_workspace_bytes(1, 2048, 1, 1, 128, -2, 0) == 0
     need = L.ncattn_bwd_workspace_bytes(2, 100, 4, 2, 128, -1, 0)
     args = [P, P + 16, P + 32, P + 48, P + 64, P + 80, P + 96, P + 112, P + 128, 2, 100, 4, 2, 128, -1, 0, 0.0, 0]

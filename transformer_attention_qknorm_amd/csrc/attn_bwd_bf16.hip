@@ -30,9 +30,11 @@ constexpr int kBlockM = 128;  // query rows per dq workgroup
 constexpr int kBlockN = 128;  // keys per dkdv workgroup
 
 // ---------------------------------------------------------------- D_i = dO . O
+// (also stores LSE_i * log2(e), the exponent offset of P in base 2, next to D)
 __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t *__restrict__ O,
-                                                        const uint16_t *__restrict__ dO, float *__restrict__ delta,
-                                                        int B, int T, int H) {
+                                                        const uint16_t *__restrict__ dO,
+                                                        const float *__restrict__ LSE, float *__restrict__ delta,
+                                                        float *__restrict__ lse2, int B, int T, int H) {
   // 16 lanes per (token, head) row, 16 rows per block
   const long long row = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
   const int part = threadIdx.x & 15;
@@ -51,26 +53,35 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t *__restri
     const int h = (int)(row % H);
     const int b = (int)(tok / T);
     const int t = (int)(tok % T);
-    delta[((long long)b * H + h) * T + t] = s;
+    const long long ri = ((long long)b * H + h) * T + t;
+    delta[ri] = s;
+    lse2[ri] = LSE[ri] * kLog2e;
   }
 }
 
 // ---------------------------------------------------------------- dK, dV
 constexpr int kQBuf = 2 * kTileBytes + 2 * kTileN * 4;  // Q tile, dO tile, lse2[64], delta[64]
 
-// One 32-query block (rows 32 qb.. of the staged tile) against this wave's 32 keys.
-// dS of the block also goes to `ds_tile` (the [key][query] bf16 64 x 64 tile of
-// this query tile and key tile; this wave's keys are rows kofs..kofs+31).
-__device__ __forceinline__ void dkdv_block(bool need_mask, f32x16 (&dkacc)[4], f32x16 (&dvacc)[4], const char *qs,
-                                           const char *dos, const float *lse2, const float *dl, const TileLane &L,
-                                           const bf16x8 (&kreg)[8], const bf16x8 (&vreg)[8], int qb, int qtile0,
-                                           int key_lane, int T, int W, float c, int hh, uint16_t *ds_row) {
-  f32x16 sacc = f32x16{}, dpacc = f32x16{};
+// S = Q K^T and dP = dO V^T for one 32-query block (rows 32 qb.. of the staged
+// tile) against this wave's 32 keys (queries as rows, the wave's keys as columns).
+__device__ __forceinline__ void dkdv_sdp(f32x16 &sacc, f32x16 &dpacc, const char *qs, const char *dos,
+                                         const TileLane &L, const bf16x8 (&kreg)[8], const bf16x8 (&vreg)[8],
+                                         int qb) {
+  sacc = f32x16{};
+  dpacc = f32x16{};
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
     sacc = mfma32(row_operand(qs, L, s, qb), kreg[s], sacc);
     dpacc = mfma32(row_operand(dos, L, s, qb), vreg[s], dpacc);
   }
+}
+
+// P = exp2(S c - LSE log2 e) and dS = P (dP - D) in place; dS also goes to the
+// workspace row `ds_row` ([key][query] tile row of this lane's key).
+__device__ __forceinline__ void dkdv_p_ds(f32x16 &sacc, f32x16 &dpacc, const float *lse2, const float *dl,
+                                          bool need_mask, int qb, int qtile0, int key_lane, int T, int W, float c,
+                                          int hh, uint16_t *ds_row) {
+  uint32_t packed[8];
   // rows of this lane's accumulator elements: 32 qb + 8 i + 4 hh + j
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -89,17 +100,38 @@ __device__ __forceinline__ void dkdv_block(bool need_mask, f32x16 (&dkacc)[4], f
       sacc[e] = p;
       dpacc[e] = p * (dpacc[e] - d4[j]);
     }
-    // dS^T row of this lane's key, query columns r0 .. r0+3
-    u32x2 w;
-    w[0] = pack_bf16x2(dpacc[4 * i + 0], dpacc[4 * i + 1]);
-    w[1] = pack_bf16x2(dpacc[4 * i + 2], dpacc[4 * i + 3]);
-    *(u32x2 *)(ds_row + r0) = w;
+    packed[2 * i] = pack_bf16x2(dpacc[4 * i + 0], dpacc[4 * i + 1]);
+    packed[2 * i + 1] = pack_bf16x2(dpacc[4 * i + 2], dpacc[4 * i + 3]);
   }
-  // dV^T += dO^T P and dK^T += Q^T dS, contraction over the 32 query rows.
+  // The two half-waves hold interleaved groups of 4 queries of the same key
+  // (h = 0: 0-3, 8-11, 16-19, 24-27; h = 1: 4-7, ...).  Swap half of them across
+  // lane l ^ 32 so that each lane owns 16 consecutive queries, then store 32 B.
+  uint32_t send[4], recv[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) send[k] = hh ? packed[k] : packed[4 + k];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) recv[k] = (uint32_t)__shfl_xor((int)send[k], 32, 64);
+  u32x4 lo, hi;
+  if (hh == 0) {
+    lo = u32x4{packed[0], packed[1], recv[0], recv[1]};
+    hi = u32x4{packed[2], packed[3], recv[2], recv[3]};
+  } else {
+    lo = u32x4{recv[0], recv[1], packed[4], packed[5]};
+    hi = u32x4{recv[2], recv[3], packed[6], packed[7]};
+  }
+  u32x4 *dst = (u32x4 *)(ds_row + 32 * qb + 16 * hh);
+  dst[0] = lo;
+  dst[1] = hi;
+}
+
+// dV^T += dO^T P and dK^T += Q^T dS, contraction over the 32 query rows of block qb.
+__device__ __forceinline__ void dkdv_acc(f32x16 (&dkacc)[4], f32x16 (&dvacc)[4], const f32x16 &pacc,
+                                         const f32x16 &dsacc, const char *qs, const char *dos, const TileLane &L,
+                                         int qb) {
 #pragma unroll
   for (int c2 = 0; c2 < 2; ++c2) {
-    const bf16x8 pb = acc_to_operand(sacc, c2);
-    const bf16x8 dsb = acc_to_operand(dpacc, c2);
+    const bf16x8 pb = acc_to_operand(pacc, c2);
+    const bf16x8 dsb = acc_to_operand(dsacc, c2);
     const int cs = 2 * qb + c2;
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
@@ -113,7 +145,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__rest
                                                           const uint16_t *__restrict__ K,
                                                           const uint16_t *__restrict__ V,
                                                           const uint16_t *__restrict__ dO,
-                                                          const float *__restrict__ LSE,
+                                                          const float *__restrict__ lse2g,
                                                           const float *__restrict__ delta, uint16_t *__restrict__ dK,
                                                           uint16_t *__restrict__ dV, uint16_t *__restrict__ dsband,
                                                           int B, int T, int H, int KV, int W, float scale, int nqt,
@@ -159,7 +191,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__rest
     tile_load_lds(base + kTileBytes, dO + hoff, tl, qt * kTileN, T);
     if (tid < 128) {  // waves 0, 1: 64 lse rows and 64 delta rows, 4 bytes per lane
       const int qi = min(qt * kTileN + lane, T - 1);
-      const float *src = (tid < 64 ? LSE : delta) + ((long long)b * H + h) * T + qi;
+      const float *src = (tid < 64 ? lse2g : delta) + ((long long)b * H + h) * T + qi;
       typedef __attribute__((address_space(3))) void lds_void;
       typedef __attribute__((address_space(1))) const void glb_void;
       __builtin_amdgcn_global_load_lds((glb_void *)src, (lds_void *)(base + 2 * kTileBytes + (tid >> 6) * kTileN * 4),
@@ -195,26 +227,42 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__rest
   auto step = [&](char *cur, char *nxt, int it) {
     const char *qs = cur;
     const char *dos = cur + kTileBytes;
-    float *lse2 = (float *)(cur + 2 * kTileBytes);
+    const float *lse2 = (const float *)(cur + 2 * kTileBytes);
     const float *dl = lse2 + kTileN;
     if (it + 1 < n_iter) stage(it + 1, nxt);
     const int qtile0 = (qt0 + it / G) * kTileN;
-    // the staged lse is natural-log; scale it to log2 units in place once per tile
-    if (tid < kTileN) lse2[tid] *= kLog2e;
-    __syncthreads();
     const bool skip = !wave_active || qtile0 + kTileN - 1 < kw0 || (W >= 0 && qtile0 - kw_last > W);
     if (!skip) {
-#pragma unroll 1
+      const int qt = qtile0 / kTileN;
+      const int h = kvh * G + it % G;
+      const long long tile = (((long long)b * H + h) * nqt + qt) * nbw + (kt - ds_kt_lo(qt, W));
+      uint16_t *ds_row = dsband + tile * (kTileN * kTileN) + (kofs + (lane & 31)) * kTileN;
+      bool act[2], msk[2];
+#pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         const int qr0 = qtile0 + 32 * qb;
-        if (qr0 + 31 < kw0 || (W >= 0 && qr0 - kw_last > W)) continue;
-        const bool need_mask = !(qr0 >= kw_last && (W < 0 || qr0 + 31 - kw0 <= W) && qr0 + 31 < T);
-        const int qt = qtile0 / kTileN;
-        const int h = kvh * G + it % G;
-        const long long tile = (((long long)b * H + h) * nqt + qt) * nbw + (kt - ds_kt_lo(qt, W));
-        uint16_t *ds_row = dsband + tile * (kTileN * kTileN) + (kofs + (lane & 31)) * kTileN;
-        dkdv_block(need_mask, dkacc, dvacc, qs, dos, lse2, dl, L, kreg, vreg, qb, qtile0, key_lane, T, W, c, hh,
-                   ds_row);
+        act[qb] = !(qr0 + 31 < kw0 || (W >= 0 && qr0 - kw_last > W));
+        msk[qb] = !(qr0 >= kw_last && (W < 0 || qr0 + 31 - kw0 <= W) && qr0 + 31 < T);
+      }
+      if (act[0] && act[1] && !msk[0] && !msk[1]) {
+        // steady state, one straight-line block: the S/dP MFMAs of the second
+        // query block can run under the exponentials of the first
+        f32x16 s0, p0, s1, p1;
+        dkdv_sdp(s0, p0, qs, dos, L, kreg, vreg, 0);
+        dkdv_sdp(s1, p1, qs, dos, L, kreg, vreg, 1);
+        dkdv_p_ds(s0, p0, lse2, dl, false, 0, qtile0, key_lane, T, W, c, hh, ds_row);
+        dkdv_acc(dkacc, dvacc, s0, p0, qs, dos, L, 0);
+        dkdv_p_ds(s1, p1, lse2, dl, false, 1, qtile0, key_lane, T, W, c, hh, ds_row);
+        dkdv_acc(dkacc, dvacc, s1, p1, qs, dos, L, 1);
+      } else {
+#pragma unroll 1
+        for (int qb = 0; qb < 2; ++qb) {
+          if (!act[qb]) continue;
+          f32x16 s0, p0;
+          dkdv_sdp(s0, p0, qs, dos, L, kreg, vreg, qb);
+          dkdv_p_ds(s0, p0, lse2, dl, msk[qb], qb, qtile0, key_lane, T, W, c, hh, ds_row);
+          dkdv_acc(dkacc, dvacc, s0, p0, qs, dos, L, qb);
+        }
       }
     }
     lds_loads_done_barrier();
@@ -388,17 +436,19 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t *__restri
 }  // namespace
 
 size_t bwd_workspace_bytes(int B, int T, int H, int W, bool bf16) {
-  const size_t delta = ((size_t)B * H * T * sizeof(float) + 255) & ~(size_t)255;
-  if (!bf16) return delta;
+  const size_t rows = ((size_t)B * H * T * sizeof(float) + 255) & ~(size_t)255;
+  if (!bf16) return rows;
   const DsBand band = ds_band(T, W);
-  return delta + (size_t)B * H * band.nqt * band.nbw * (kTileN * kTileN) * 2;
+  return 2 * rows + (size_t)B * H * band.nqt * band.nbw * (kTileN * kTileN) * 2;
 }
 
 hipError_t launch_bwd_bf16(const void *q, const void *k, const void *v, const void *o, const float *lse,
                            const void *dout, void *dq, void *dk, void *dv, void *workspace, const AttnShape &sh,
                            int stages, hipStream_t s) {
+  const size_t row_bytes = ((size_t)sh.B * sh.H * sh.T * sizeof(float) + 255) & ~(size_t)255;
   float *delta = (float *)workspace;
-  uint16_t *dsband = (uint16_t *)((char *)workspace + (((size_t)sh.B * sh.H * sh.T * sizeof(float) + 255) & ~(size_t)255));
+  float *lse2 = (float *)((char *)workspace + row_bytes);
+  uint16_t *dsband = (uint16_t *)((char *)workspace + 2 * row_bytes);
   const DsBand band = ds_band(sh.T, sh.window);
   const long long rows = (long long)sh.B * sh.T * sh.H;
   const long long dblocks = (rows + 15) / 16;
@@ -409,10 +459,10 @@ hipError_t launch_bwd_bf16(const void *q, const void *k, const void *v, const vo
   if (dblocks > 0x7fffffffLL || kvblocks > 0x7fffffffLL || qblocks > 0x7fffffffLL) return hipErrorInvalidValue;
   if (stages & kBwdDelta)
     hipLaunchKernelGGL(bwd_delta_kernel, dim3((unsigned)dblocks), dim3(256), 0, s, (const uint16_t *)o,
-                       (const uint16_t *)dout, delta, sh.B, sh.T, sh.H);
+                       (const uint16_t *)dout, lse, delta, lse2, sh.B, sh.T, sh.H);
   if (stages & kBwdDkDv)
     hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)kvblocks), dim3(256), 0, s, (const uint16_t *)q,
-                       (const uint16_t *)k, (const uint16_t *)v, (const uint16_t *)dout, lse, delta, (uint16_t *)dk,
+                       (const uint16_t *)k, (const uint16_t *)v, (const uint16_t *)dout, lse2, delta, (uint16_t *)dk,
                        (uint16_t *)dv, dsband, sh.B, sh.T, sh.H, sh.KV, sh.window, sh.scale, band.nqt, band.nbw);
   if (stages & kBwdDq)
     hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)qblocks), dim3(256), 0, s, (const uint16_t *)k, dsband,

@@ -41,7 +41,8 @@ __host__ __device__ inline int ds_kt_lo(int qt, int W) {
   const int x = 64 * qt - W;
   return x > 0 ? x / 64 : 0;
 }
-// workspace: D [B][H][T] fp32 (padded to 256 B), then (bf16 only) the dS band
+// workspace: D [B][H][T] fp32 (padded to 256 B); bf16 adds LSE * log2(e) (same size) and
+// the dS band
 size_t bwd_workspace_bytes(int B, int T, int H, int W, bool bf16);
 
 // bf16, head_dim 128, MFMA kernels.
