@@ -67,12 +67,21 @@ constexpr int kQBuf = 2 * kTileBytes + 2 * kTileN * 4;  // Q tile, dO tile, lse2
 __device__ __forceinline__ void dkdv_sdp(f32x16 &sacc, f32x16 &dpacc, const char *qs, const char *dos,
                                          const TileLane &L, const bf16x8 (&kreg)[8], const bf16x8 (&vreg)[8],
                                          int qb) {
+  // all 16 operands are read from LDS before the first MFMA (the scheduler would
+  // otherwise wait for each read just before its MFMA and expose its latency)
+  bf16x8 qa[8], da[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    qa[s] = row_operand(qs, L, s, qb);
+    da[s] = row_operand(dos, L, s, qb);
+  }
+  __builtin_amdgcn_sched_barrier(0);
   sacc = f32x16{};
   dpacc = f32x16{};
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
-    sacc = mfma32(row_operand(qs, L, s, qb), kreg[s], sacc);
-    dpacc = mfma32(row_operand(dos, L, s, qb), vreg[s], dpacc);
+    sacc = mfma32(qa[s], kreg[s], sacc);
+    dpacc = mfma32(da[s], vreg[s], dpacc);
   }
 }
 
@@ -125,18 +134,26 @@ __device__ __forceinline__ void dkdv_p_ds(f32x16 &sacc, f32x16 &dpacc, const flo
 }
 
 // dV^T += dO^T P and dK^T += Q^T dS, contraction over the 32 query rows of block qb.
+// The transposed operands are read in two batches of 8 ahead of their MFMAs.
 __device__ __forceinline__ void dkdv_acc(f32x16 (&dkacc)[4], f32x16 (&dvacc)[4], const f32x16 &pacc,
                                          const f32x16 &dsacc, const char *qs, const char *dos, const TileLane &L,
                                          int qb) {
 #pragma unroll
   for (int c2 = 0; c2 < 2; ++c2) {
-    const bf16x8 pb = acc_to_operand(pacc, c2);
-    const bf16x8 dsb = acc_to_operand(dsacc, c2);
     const int cs = 2 * qb + c2;
+    bf16x8 dop[4], qop[4];
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
-      dvacc[db] = mfma32(col_operand(dos, L, db, cs), pb, dvacc[db]);
-      dkacc[db] = mfma32(col_operand(qs, L, db, cs), dsb, dkacc[db]);
+      dop[db] = col_operand(dos, L, db, cs);
+      qop[db] = col_operand(qs, L, db, cs);
+    }
+    const bf16x8 pb = acc_to_operand(pacc, c2);
+    const bf16x8 dsb = acc_to_operand(dsacc, c2);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      dvacc[db] = mfma32(dop[db], pb, dvacc[db]);
+      dkacc[db] = mfma32(qop[db], dsb, dkacc[db]);
     }
   }
 }
@@ -386,13 +403,21 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t *__restri
       const int k0 = t * kTileN;
       const bool need_mask = !(k0 + kTileN - 1 <= qw0 && (W < 0 || qw_last - k0 <= W));
       const char *st = cur + kTileBytes + ssub;
+      // every operand of the tile is read from LDS before the first MFMA
+      u32x4 dsw[4];
+      bf16x8 kop[4][4];
 #pragma unroll
       for (int cs = 0; cs < 4; ++cs) {
         const u32x2 lo = __builtin_bit_cast(u32x2, lds_read_tr16(st + soff[0] + cs * 16 * 128));
         const u32x2 hi = __builtin_bit_cast(u32x2, lds_read_tr16(st + soff[1] + cs * 16 * 128));
-        u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
-        if (need_mask) {
-          // operand element e holds key k0 + 16 cs + 4 hh + (e & 3) + 8 (e >> 2)
+        dsw[cs] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+        for (int db = 0; db < 4; ++db) kop[cs][db] = col_operand(cur, L, db, cs);
+      }
+      if (need_mask) {
+        // operand element e holds key k0 + 16 cs + 4 hh + (e & 3) + 8 (e >> 2)
+#pragma unroll
+        for (int cs = 0; cs < 4; ++cs)
 #pragma unroll
           for (int e2 = 0; e2 < 4; ++e2) {
             uint32_t keep = 0u;
@@ -403,12 +428,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t *__restri
               const bool vis = key <= q_lane && (W < 0 || q_lane - key <= W);
               keep |= vis ? (0xffffu << (16 * half)) : 0u;
             }
-            w[e2] &= keep;
+            dsw[cs][e2] &= keep;
           }
-        }
-        const bf16x8 dsb = __builtin_bit_cast(bf16x8, w);
+      }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int db = 0; db < 4; ++db) dqacc[db] = mfma32(col_operand(cur, L, db, cs), dsb, dqacc[db]);
+      for (int cs = 0; cs < 4; ++cs) {
+        const bf16x8 dsb = __builtin_bit_cast(bf16x8, dsw[cs]);
+#pragma unroll
+        for (int db = 0; db < 4; ++db) dqacc[db] = mfma32(kop[cs][db], dsb, dqacc[db]);
       }
     }
     lds_loads_done_barrier();

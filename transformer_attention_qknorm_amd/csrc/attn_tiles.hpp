@@ -26,12 +26,12 @@ __device__ __forceinline__ int swz(int row, int chunk) {
 
 __device__ __forceinline__ int swz_f(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
 
-// Direct global -> LDS copy of a 64 x 128 bf16 tile (16 KB) by the 4 waves of a
-// 256-thread block, bypassing registers (global_load_lds_dwordx4: lane l of an
-// instruction writes 16 bytes at the wave-uniform LDS base + 16 l).  Instruction i
-// of wave w fills tile rows 16 i + 4 w + [0, 4); lane l of it covers row
-// 16 i + 4 w + l/16 at LDS chunk position l%16, so it fetches global chunk
-// (l%16) ^ f(row) of that row.  Rows at or past `nrows` are fetched from row
+// Direct global -> LDS copy of a 64 x 128 bf16 tile (16 KB) by the NW waves of a
+// block, bypassing registers (global_load_lds_dwordx4: lane l of an instruction
+// writes 16 bytes at the wave-uniform LDS base + 16 l).  Instruction i of wave w
+// fills tile rows 4 (NW i + w) + [0, 4); lane l of it covers row 4 (NW i + w) +
+// l/16 at LDS chunk position l%16, so it fetches global chunk (l%16) ^ f(row) of
+// that row (f depends on the row's low 4 bits only, a lane constant).  Rows at or past `nrows` are fetched from row
 // nrows - 1 instead: finite data that every caller masks out or multiplies by 0.
 struct TileLoader {
   long long lane_off;  // byte offset of this lane's chunk within a row + its row-in-group * stride
@@ -49,17 +49,18 @@ __device__ __forceinline__ TileLoader make_tile_loader(long long row_stride_elem
   return t;
 }
 
+template <int NW = 4>
 __device__ __forceinline__ void tile_load_lds(char *lds_tile, const uint16_t *base, const TileLoader &t, int row0,
                                               int nrows) {
   const int w = threadIdx.x >> 6;
   typedef __attribute__((address_space(3))) void lds_void;
   typedef __attribute__((address_space(1))) const void glb_void;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = min(row0 + 16 * i + t.lane_row, nrows - 1);
+  for (int i = 0; i < 16 / NW; ++i) {
+    const int row = min(row0 + 4 * NW * i + t.lane_row, nrows - 1);
     const char *src = (const char *)base + (long long)row * t.stride + t.lane_off;
-    __builtin_amdgcn_global_load_lds((glb_void *)src, (lds_void *)(lds_tile + (16 * i + 4 * w) * kRowBytes), 16, 0,
-                                     0);
+    __builtin_amdgcn_global_load_lds((glb_void *)src, (lds_void *)(lds_tile + (4 * NW * i + 4 * w) * kRowBytes), 16,
+                                     0, 0);
   }
 }
 
