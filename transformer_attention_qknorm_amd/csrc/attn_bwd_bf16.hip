@@ -191,7 +191,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__rest
 
   const long long q_stride = (long long)H * kD;
   const long long kv_stride = (long long)KV * kD;
-  const TileLoader tl = make_tile_loader(q_stride, tid);
+  const int voff = tile_lane_voff((int)(q_stride * 2), tid);
 
   // Query tiles that can see any key of the block, times the G heads of the group.
   const int k_last_blk = min(k0 + kBlockN - 1, T - 1);
@@ -204,15 +204,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__rest
     const int qt = qt0 + it / G;
     const int h = kvh * G + it % G;
     const long long hoff = (long long)b * T * q_stride + (long long)h * kD;
-    tile_load_lds(base, Q + hoff, tl, qt * kTileN, T);
-    tile_load_lds(base + kTileBytes, dO + hoff, tl, qt * kTileN, T);
-    if (tid < 128) {  // waves 0, 1: 64 lse rows and 64 delta rows, 4 bytes per lane
-      const int qi = min(qt * kTileN + lane, T - 1);
-      const float *src = (tid < 64 ? lse2g : delta) + ((long long)b * H + h) * T + qi;
-      typedef __attribute__((address_space(3))) void lds_void;
-      typedef __attribute__((address_space(1))) const void glb_void;
-      __builtin_amdgcn_global_load_lds((glb_void *)src, (lds_void *)(base + 2 * kTileBytes + (tid >> 6) * kTileN * 4),
-                                       4, 0, 0);
+    tile_load_lds(base, make_tile_src(Q + hoff, q_stride, T), voff, qt * kTileN);
+    tile_load_lds(base + kTileBytes, make_tile_src(dO + hoff, q_stride, T), voff, qt * kTileN);
+    if (wave < 2) {  // waves 0, 1: 64 lse rows and 64 delta rows, 4 bytes per lane (zeros past T)
+      const float *row = (wave == 0 ? lse2g : delta) + ((long long)b * H + h) * T;
+      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void *)row, (short)0, T * 4, 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(base + 2 * kTileBytes + wave * kTileN * 4), 4,
+                                               lane * 4, qt * kTileN * 4, 0, 0);
     }
   };
 
@@ -353,7 +351,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t *__restri
 
   const long long kv_stride = (long long)KV * kD;
   const uint16_t *Kb = K + (long long)b * T * kv_stride + (long long)kvh * kD;
-  const TileLoader tl = make_tile_loader(kv_stride, tid);
+  const TileSrc ksrc = make_tile_src(Kb, kv_stride, T);
+  const int voff = tile_lane_voff(ksrc.stride, tid);
   const uint16_t *dsh = dsband + (long long)bh * nqt * nbw * (kTileN * kTileN);
 
   const int q_last_blk = min(q0 + kBlockM - 1, T - 1);
@@ -367,7 +366,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t *__restri
   // copies for key tile t: K, and the dS^T tiles of the block's two query tiles
   // that see tile t
   auto load = [&](char *buf, int t) {
-    tile_load_lds(buf, Kb, tl, t * kTileN, T);
+    tile_load_lds(buf, ksrc, voff, t * kTileN);
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       const int qt = 2 * qblk + sub;

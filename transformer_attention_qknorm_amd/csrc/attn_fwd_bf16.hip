@@ -61,7 +61,8 @@ __device__ __forceinline__ float softmax_max(FwdState &st, f32x16 (&sacc)[2], bo
       for (int e = 0; e < 16; ++e) {
         const int key = k0 + 32 * kb + 8 * (e >> 2) + 4 * hh + (e & 3);
         const bool vis = key <= q_lane && (W < 0 || q_lane - key <= W);
-        if (!vis) sacc[kb][e] = -INFINITY;
+        const float x = sacc[kb][e];
+        sacc[kb][e] = vis ? x : -INFINITY;
       }
   }
   float mt = sacc[0][0];
@@ -142,7 +143,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const uint16_t *_
   const long long kv_stride = (long long)KV * kD;
   const uint16_t *Kb = K + (long long)b * T * kv_stride + (long long)kvh * kD;
   const uint16_t *Vb = V + (long long)b * T * kv_stride + (long long)kvh * kD;
-  const TileLoader tl = make_tile_loader(kv_stride, tid);
+  const TileSrc ksrc = make_tile_src(Kb, kv_stride, T);
+  const TileSrc vsrc = make_tile_src(Vb, kv_stride, T);
+  const int voff = tile_lane_voff(ksrc.stride, tid);
 
   // tiles of the block, and the contiguous range of them this wave needs
   const int q_last_blk = min(q0 + kBlockM - 1, T - 1);
@@ -158,9 +161,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const uint16_t *_
     return !(k0 + kTileN - 1 <= qw0 && (W < 0 || qw_last - k0 <= W));
   };
 
-  tile_load_lds(kb0, Kb, tl, t0 * kTileN, T);
-  tile_load_lds(vb0, Vb, tl, t0 * kTileN, T);
-  if (t0 + 1 <= t1) tile_load_lds(kb1, Kb, tl, (t0 + 1) * kTileN, T);
+  tile_load_lds(kb0, ksrc, voff, t0 * kTileN);
+  tile_load_lds(vb0, vsrc, voff, t0 * kTileN);
+  if (t0 + 1 <= t1) tile_load_lds(kb1, ksrc, voff, (t0 + 1) * kTileN);
 
   // Q^T operand in registers: lane holds q row q_lane, d = 16 s + 8 hh + [0, 8).
   bf16x8 qreg[8];
@@ -186,8 +189,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const uint16_t *_
   // Step t: S of tile t+1 from kcur, softmax + PV of tile t from vcur; copies of
   // K(t+2) into kfill and V(t+1) into vfill run meanwhile.
   auto step = [&](const char *kcur, char *kfill, const char *vcur, char *vfill, int t) {
-    if (t + 2 <= t1) tile_load_lds(kfill, Kb, tl, (t + 2) * kTileN, T);
-    if (t + 1 <= t1) tile_load_lds(vfill, Vb, tl, (t + 1) * kTileN, T);
+    if (t + 2 <= t1) tile_load_lds(kfill, ksrc, voff, (t + 2) * kTileN);
+    if (t + 1 <= t1) tile_load_lds(vfill, vsrc, voff, (t + 1) * kTileN);
     const bool cur = in_range(t), next = in_range(t + 1);
     if (cur && next) {
       // steady state: one straight-line block holding the S MFMAs of tile t+1,

@@ -27,41 +27,45 @@ __device__ __forceinline__ int swz(int row, int chunk) {
 __device__ __forceinline__ int swz_f(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
 
 // Direct global -> LDS copy of a 64 x 128 bf16 tile (16 KB) by the NW waves of a
-// block, bypassing registers (global_load_lds_dwordx4: lane l of an instruction
-// writes 16 bytes at the wave-uniform LDS base + 16 l).  Instruction i of wave w
-// fills tile rows 4 (NW i + w) + [0, 4); lane l of it covers row 4 (NW i + w) +
-// l/16 at LDS chunk position l%16, so it fetches global chunk (l%16) ^ f(row) of
-// that row (f depends on the row's low 4 bits only, a lane constant).  Rows at or past `nrows` are fetched from row
-// nrows - 1 instead: finite data that every caller masks out or multiplies by 0.
-struct TileLoader {
-  long long lane_off;  // byte offset of this lane's chunk within a row + its row-in-group * stride
-  int lane_row;        // 4 w + l / 16
-  long long stride;    // row stride in bytes
+// block, bypassing registers (buffer_load_dwordx4 ... lds: lane l of an
+// instruction writes 16 bytes at the wave-uniform LDS base + 16 l).  Instruction
+// i of wave w fills tile rows 4 (NW i + w) + [0, 4); lane l of it covers row
+// 4 (NW i + w) + l/16 at LDS chunk position l%16, so it fetches global chunk
+// (l%16) ^ f(row) of that row (f depends on the row's low 4 bits only, a lane
+// constant).  The source is a buffer resource over the `nrows` rows of one
+// (batch, head) slice: the lane's part of the address is a constant VGPR and the
+// tile's row offset a scalar, so a copy costs no vector ALU work, and rows at or
+// past `nrows` fall outside the resource and arrive as zeros (finite data that
+// every caller masks out or multiplies by 0).
+typedef __attribute__((address_space(3))) void lds_void;
+
+struct TileSrc {
+  __amdgpu_buffer_rsrc_t rsrc;
+  int stride;  // row stride in bytes
 };
 
-__device__ __forceinline__ TileLoader make_tile_loader(long long row_stride_elems, int tid) {
-  TileLoader t;
+// rows [0, nrows) of a row-major slice starting at `base`, `row_stride_elems` bf16 apart
+__device__ __forceinline__ TileSrc make_tile_src(const uint16_t *base, long long row_stride_elems, int nrows) {
+  TileSrc s;
+  s.stride = (int)(row_stride_elems * 2);
+  s.rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, nrows * s.stride, 0x00020000);
+  return s;
+}
+
+// lane constant: byte offset of this lane's 16-byte piece for instruction 0
+__device__ __forceinline__ int tile_lane_voff(int row_stride_bytes, int tid) {
   const int lane = tid & 63, w = tid >> 6;
-  t.lane_row = 4 * w + (lane >> 4);
-  const int chunk = (lane & 15) ^ swz_f(t.lane_row);
-  t.stride = row_stride_elems * 2;
-  t.lane_off = (long long)chunk * 16;
-  return t;
+  const int lane_row = 4 * w + (lane >> 4);
+  return lane_row * row_stride_bytes + (((lane & 15) ^ swz_f(lane_row)) << 4);
 }
 
 template <int NW = 4>
-__device__ __forceinline__ void tile_load_lds(char *lds_tile, const uint16_t *base, const TileLoader &t, int row0,
-                                              int nrows) {
-  const int w = threadIdx.x >> 6;
-  typedef __attribute__((address_space(3))) void lds_void;
-  typedef __attribute__((address_space(1))) const void glb_void;
+__device__ __forceinline__ void tile_load_lds(char *lds_tile, const TileSrc &src, int voff, int row0) {
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
-  for (int i = 0; i < 16 / NW; ++i) {
-    const int row = min(row0 + 4 * NW * i + t.lane_row, nrows - 1);
-    const char *src = (const char *)base + (long long)row * t.stride + t.lane_off;
-    __builtin_amdgcn_global_load_lds((glb_void *)src, (lds_void *)(lds_tile + (4 * NW * i + 4 * w) * kRowBytes), 16,
-                                     0, 0);
-  }
+  for (int i = 0; i < 16 / NW; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.rsrc, (lds_void *)(lds_tile + (4 * NW * i + 4 * w) * kRowBytes), 16,
+                                             voff, (row0 + 4 * NW * i) * src.stride, 0, 0);
 }
 
 // Wait for this thread's direct-to-LDS loads, then a block barrier.

@@ -51,9 +51,13 @@ int check_dtype(const char *fn, int dtype) {
   return NCATTN_OK;
 }
 
-int check_attn_support(const char *fn, int dtype, int D) {
+int check_attn_support(const char *fn, int dtype, int T, int H, int D) {
   if (dtype == NCATTN_BF16 && D != 128)
     return fail(NCATTN_EUNSUPPORTED, "%s: bf16 attention supports head_dim 128 only (got %d)", fn, D);
+  // the bf16 kernels address one (batch, head) slice of q/k/v/dO through 32-bit
+  // byte offsets: (T + 64) rows of the token stride must stay below 2^31
+  if (dtype == NCATTN_BF16 && ((double)T + 64.0) * H * D * 2.0 >= 2147483648.0)
+    return fail(NCATTN_EUNSUPPORTED, "%s: seq_len x n_head too large for the bf16 kernels (T=%d n_head=%d)", fn, T, H);
   if (dtype == NCATTN_F32 && D != 64 && D != 128)
     return fail(NCATTN_EUNSUPPORTED, "%s: fp32 attention supports head_dim 64 or 128 (got %d)", fn, D);
   return NCATTN_OK;
@@ -121,7 +125,7 @@ int ncattn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
   NC_TRY(check_heads(fn, B, T, n_head, n_kv_head, head_dim));
   NC_TRY(check_dtype(fn, dtype));
   NC_TRY(check_window(fn, window_left, window_right));
-  NC_TRY(check_attn_support(fn, dtype, head_dim));
+  NC_TRY(check_attn_support(fn, dtype, T, n_head, head_dim));
   if (!isfinite(softmax_scale)) return fail(NCATTN_EINVAL, "%s: softmax_scale must be finite", fn);
   if (o == q || o == k || o == v) return fail(NCATTN_EINVAL, "%s: o must not alias an input", fn);
   ncattn::AttnShape sh{B, T, n_head, n_kv_head, head_dim, window_left, resolve_scale(softmax_scale, head_dim)};
@@ -160,7 +164,7 @@ int bwd_common(const char *fn, int stages, const void *q, const void *k, const v
   NC_TRY(check_heads(fn, B, T, n_head, n_kv_head, head_dim));
   NC_TRY(check_dtype(fn, dtype));
   NC_TRY(check_window(fn, window_left, window_right));
-  NC_TRY(check_attn_support(fn, dtype, head_dim));
+  NC_TRY(check_attn_support(fn, dtype, T, n_head, head_dim));
   if (!isfinite(softmax_scale)) return fail(NCATTN_EINVAL, "%s: softmax_scale must be finite", fn);
   const void *ins[] = {q, k, v, o, lse, dout};
   void *outs[] = {dq, dk, dv};
