@@ -91,7 +91,8 @@ int ncattn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
 
 /*
  * Bytes of workspace ncattn_bwd needs for this shape and window: the per-row
- * fp32 D_i = sum_d dO_i O_i and, for bf16, the bf16 dS = P (dP - D) tiles of the
+ * fp32 D_i = sum_d dO_i O_i (for bf16 stored negated, next to LSE_i log2 e) and,
+ * for bf16, the bf16 dS = P (dP - D) tiles of the
  * window band that the dk/dv stage hands to the dq stage (64 x 64 tiles, about
  * 2 bytes per visible (query, key) pair and head).  0 for invalid sizes.
  */

@@ -13,6 +13,7 @@ import torch
 
 import oracle
 import transformer_attention_qknorm_amd as nc
+from conftest import tol_check
 from parity_util import LSE_TOL, TOL, check, check_lse, f64
 from workloads import attn_inputs, decode_inputs
 
@@ -112,6 +113,44 @@ def test_fwd_bwd_closed_forms_on_gpu():
     assert float(dq.abs().max()) <= 1e-5 and float(dk.abs().max()) <= 1e-5
     ref = f64(do).reshape(2, 300, 2, 2, 128).sum(axis=3)
     check(dv, ref, "bf16", "dv(W=0)")
+
+
+def test_fwd_bwd_scores_far_above_first_tile():
+    """Rows whose first key tile scores about -44 and whose later keys score about
+    +44 (natural log units): the probabilities against the first tile's reference
+    would overflow fp32, so the forward must take its exact-maximum second pass.
+    Checked against the oracle like any other case, backward included.  (q is
+    100 u, k is +-5 u plus unit noise, for a random unit vector u: a large common
+    part in k would make the bf16 rounding of dS dominate dQ, which the exact
+    cancellation sum_j dS_ij = 0 leaves small.)"""
+    B, T, H, KV, D = 1, 300, 2, 2, 128
+    rng = np.random.default_rng(77)
+    u = rng.standard_normal(D)
+    u /= np.linalg.norm(u)
+    sign = np.where(np.arange(T) < 100, -1.0, 1.0)[None, :, None, None]
+    q = 100.0 * u + 0.5 * rng.standard_normal((B, T, H, D))
+    k = sign * 5.0 * u + rng.standard_normal((B, T, KV, D))
+    v = rng.standard_normal((B, T, KV, D))
+    do = rng.standard_normal((B, T, H, D))
+    q, k, v, do = (torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16) for x in (q, k, v, do))
+    for W in (-1, 150):
+        say(f"large score growth W={W}")
+        ro, rlse = oracle.attn_fwd(f64(q), f64(k), f64(v), W)
+        rdq, rdk, rdv = oracle.attn_bwd(f64(q), f64(k), f64(v), f64(do), W)
+        assert float(rlse.max() - rlse.min()) > 60.0  # the construction does what it says
+        qd, kd, vd, dod = to_dev(q, k, v, do)
+        o, lse = nc.fwd(qd, kd, vd, window=(W, 0))
+        torch.cuda.synchronize()
+        check(o, ro, "bf16", "o")
+        check_lse(lse, rlse, "bf16", "lse")
+        dq, dk, dv = nc.bwd(qd, kd, vd, o, lse, dod, window=(W, 0))
+        torch.cuda.synchronize()
+        # The gradients here reach ~100 (q is 100 u), so the absolute bound,
+        # stated for unit-scale data, is applied to the gradients divided by their
+        # largest reference magnitude (rounded up to a power of 2); the relative Frobenius bound is unchanged.
+        for name, got, ref in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
+            m = 2.0 ** max(0, math.ceil(math.log2(float(np.abs(ref).max()))))  # exact binary scaling
+            tol_check(f64(got) / m, ref / m, what=name, out_bf16=True, **TOL["bf16"])
 
 
 def test_determinism():

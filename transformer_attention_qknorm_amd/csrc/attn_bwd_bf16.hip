@@ -30,7 +30,8 @@ constexpr int kBlockM = 128;  // query rows per dq workgroup
 constexpr int kBlockN = 128;  // keys per dkdv workgroup
 
 // ---------------------------------------------------------------- D_i = dO . O
-// (also stores LSE_i * log2(e), the exponent offset of P in base 2, next to D)
+// Stores -D_i (the initial value of the dP - D accumulators of the dK/dV stage)
+// and LSE_i * log2(e), the exponent offset of P in base 2.
 __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t *__restrict__ O,
                                                         const uint16_t *__restrict__ dO,
                                                         const float *__restrict__ LSE, float *__restrict__ delta,
@@ -54,7 +55,7 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t *__restri
     const int b = (int)(tok / T);
     const int t = (int)(tok % T);
     const long long ri = ((long long)b * H + h) * T + t;
-    delta[ri] = s;
+    delta[ri] = -s;
     lse2[ri] = LSE[ri] * kLog2e;
   }
 }
@@ -62,22 +63,26 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t *__restri
 // ---------------------------------------------------------------- dK, dV
 constexpr int kQBuf = 2 * kTileBytes + 2 * kTileN * 4;  // Q tile, dO tile, lse2[64], delta[64]
 
-// S = Q K^T and dP = dO V^T for one 32-query block (rows 32 qb.. of the staged
-// tile) against this wave's 32 keys (queries as rows, the wave's keys as columns).
+// S = Q K^T and dP - D = dO V^T - D for one 32-query block (rows 32 qb.. of the
+// staged tile) against this wave's 32 keys (queries as rows, the wave's keys as
+// columns).  The dP accumulator starts at -D of its query rows (staged next to
+// the tile), so it ends holding dP - D.
 __device__ __forceinline__ void dkdv_sdp(f32x16 &sacc, f32x16 &dpacc, const char *qs, const char *dos,
-                                         const TileLane &L, const bf16x8 (&kreg)[8], const bf16x8 (&vreg)[8],
-                                         int qb) {
-  // all 16 operands are read from LDS before the first MFMA (the scheduler would
-  // otherwise wait for each read just before its MFMA and expose its latency)
+                                         const float *ndl, const TileLane &L, const bf16x8 (&kreg)[8],
+                                         const bf16x8 (&vreg)[8], int qb, int hh) {
   bf16x8 qa[8], da[8];
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
     qa[s] = row_operand(qs, L, s, qb);
     da[s] = row_operand(dos, L, s, qb);
   }
-  __builtin_amdgcn_sched_barrier(0);
   sacc = f32x16{};
-  dpacc = f32x16{};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f32x4 d4 = *(const f32x4 *)(ndl + 32 * qb + 8 * i + 4 * hh);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dpacc[4 * i + j] = d4[j];
+  }
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
     sacc = mfma32(qa[s], kreg[s], sacc);
@@ -85,76 +90,84 @@ __device__ __forceinline__ void dkdv_sdp(f32x16 &sacc, f32x16 &dpacc, const char
   }
 }
 
-// P = exp2(S c - LSE log2 e) and dS = P (dP - D) in place; dS also goes to the
-// workspace row `ds_row` ([key][query] tile row of this lane's key).
-__device__ __forceinline__ void dkdv_p_ds(f32x16 &sacc, f32x16 &dpacc, const float *lse2, const float *dl,
-                                          bool need_mask, int qb, int qtile0, int key_lane, int T, int W, float c,
-                                          int hh, uint16_t *ds_row) {
-  uint32_t packed[8];
+// P = exp2(S c - LSE log2 e) and dS = P (dP - D) as bf16 MFMA operands (pk, dk:
+// element pairs of accumulator rows 8 i + 4 hh + j, the layout acc_to_operand
+// gives), and dS rearranged for the workspace: `out` holds this lane's 16
+// consecutive queries of its key's [key][query] tile row, starting at query
+// 32 qb + 16 hh (see ds_store).
+__device__ __forceinline__ void dkdv_p_ds(const f32x16 &sacc, const f32x16 &dmd, const float *lse2, bool need_mask,
+                                          int qb, int qtile0, int key_lane, int T, int W, float c, int hh,
+                                          uint32_t (&pk)[8], uint32_t (&dk)[8], u32x4 (&out)[2]) {
   // rows of this lane's accumulator elements: 32 qb + 8 i + 4 hh + j
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r0 = 32 * qb + 8 * i + 4 * hh;
     const f32x4 l4 = *(const f32x4 *)(lse2 + r0);
-    const f32x4 d4 = *(const f32x4 *)(dl + r0);
+    float p[4], ds[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int e = 4 * i + j;
-      float p = fast_exp2(__builtin_fmaf(sacc[e], c, -l4[j]));
+      p[j] = fast_exp2(__builtin_fmaf(sacc[e], c, -l4[j]));
       if (need_mask) {
         const int qi = qtile0 + r0 + j;
         const bool vis = qi < T && key_lane <= qi && (W < 0 || qi - key_lane <= W);
-        if (!vis) p = 0.f;
+        if (!vis) p[j] = 0.f;
       }
-      sacc[e] = p;
-      dpacc[e] = p * (dpacc[e] - d4[j]);
+      ds[j] = p[j] * dmd[e];
     }
-    packed[2 * i] = pack_bf16x2(dpacc[4 * i + 0], dpacc[4 * i + 1]);
-    packed[2 * i + 1] = pack_bf16x2(dpacc[4 * i + 2], dpacc[4 * i + 3]);
+    pk[2 * i] = pack_bf16x2(p[0], p[1]);
+    pk[2 * i + 1] = pack_bf16x2(p[2], p[3]);
+    dk[2 * i] = pack_bf16x2(ds[0], ds[1]);
+    dk[2 * i + 1] = pack_bf16x2(ds[2], ds[3]);
   }
   // The two half-waves hold interleaved groups of 4 queries of the same key
-  // (h = 0: 0-3, 8-11, 16-19, 24-27; h = 1: 4-7, ...).  Swap half of them across
-  // lane l ^ 32 so that each lane owns 16 consecutive queries, then store 32 B.
-  uint32_t send[4], recv[4];
+  // (h = 0: 0-3, 8-11, 16-19, 24-27; h = 1: 4-7, ...).  v_permlane32_swap of
+  // (dk[k], dk[4 + k]) hands lane l < 32 its partner's dk[k] in the second value
+  // and lane l >= 32 its partner's dk[4 + k] in the first, so that every lane then
+  // owns 16 consecutive queries (32 B).
+  uint32_t x[4], y[4];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) send[k] = hh ? packed[k] : packed[4 + k];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) recv[k] = (uint32_t)__shfl_xor((int)send[k], 32, 64);
-  u32x4 lo, hi;
-  if (hh == 0) {
-    lo = u32x4{packed[0], packed[1], recv[0], recv[1]};
-    hi = u32x4{packed[2], packed[3], recv[2], recv[3]};
-  } else {
-    lo = u32x4{recv[0], recv[1], packed[4], packed[5]};
-    hi = u32x4{recv[2], recv[3], packed[6], packed[7]};
+  for (int k = 0; k < 4; ++k) {
+    const auto r = __builtin_amdgcn_permlane32_swap(dk[k], dk[4 + k], false, false);
+    x[k] = r[0];
+    y[k] = r[1];
   }
+  out[0] = u32x4{x[0], x[1], y[0], y[1]};
+  out[1] = u32x4{x[2], x[3], y[2], y[3]};
+}
+
+// Writes a lane's 32 dS bytes (from dkdv_p_ds) into its workspace tile row.
+__device__ __forceinline__ void ds_store(uint16_t *ds_row, const u32x4 (&out)[2], int qb, int hh) {
   u32x4 *dst = (u32x4 *)(ds_row + 32 * qb + 16 * hh);
-  dst[0] = lo;
-  dst[1] = hi;
+  dst[0] = out[0];
+  dst[1] = out[1];
 }
 
 // dV^T += dO^T P and dK^T += Q^T dS, contraction over the 32 query rows of block qb.
-// The transposed operands are read in two batches of 8 ahead of their MFMAs.
-__device__ __forceinline__ void dkdv_acc(f32x16 (&dkacc)[4], f32x16 (&dvacc)[4], const f32x16 &pacc,
-                                         const f32x16 &dsacc, const char *qs, const char *dos, const TileLane &L,
+__device__ __forceinline__ void dkdv_acc(f32x16 (&dkacc)[4], f32x16 (&dvacc)[4], const uint32_t (&pk)[8],
+                                         const uint32_t (&dk)[8], const char *qs, const char *dos, const TileLane &L,
                                          int qb) {
 #pragma unroll
   for (int c2 = 0; c2 < 2; ++c2) {
     const int cs = 2 * qb + c2;
-    bf16x8 dop[4], qop[4];
+    const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pk[4 * c2], pk[4 * c2 + 1], pk[4 * c2 + 2], pk[4 * c2 + 3]});
+    const bf16x8 dsb = __builtin_bit_cast(bf16x8, u32x4{dk[4 * c2], dk[4 * c2 + 1], dk[4 * c2 + 2], dk[4 * c2 + 3]});
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
-      dop[db] = col_operand(dos, L, db, cs);
-      qop[db] = col_operand(qs, L, db, cs);
+      dvacc[db] = mfma32(col_operand(dos, L, db, cs), pb, dvacc[db]);
+      dkacc[db] = mfma32(col_operand(qs, L, db, cs), dsb, dkacc[db]);
     }
-    const bf16x8 pb = acc_to_operand(pacc, c2);
-    const bf16x8 dsb = acc_to_operand(dsacc, c2);
-    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Interleave the next n MFMAs of the scheduling region with the vector ALU work
+// (k VALU instructions after each), so the matrix cores and the VALU run together.
+template <int N, int K>
+__device__ __forceinline__ void interleave_mfma_valu() {
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      dvacc[db] = mfma32(dop[db], pb, dvacc[db]);
-      dkacc[db] = mfma32(qop[db], dsb, dkacc[db]);
-    }
+  for (int i = 0; i < N; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, K, 0);  // VALU
   }
 }
 
@@ -243,7 +256,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__rest
     const char *qs = cur;
     const char *dos = cur + kTileBytes;
     const float *lse2 = (const float *)(cur + 2 * kTileBytes);
-    const float *dl = lse2 + kTileN;
+    const float *ndl = lse2 + kTileN;
     if (it + 1 < n_iter) stage(it + 1, nxt);
     const int qtile0 = (qt0 + it / G) * kTileN;
     const bool skip = !wave_active || qtile0 + kTileN - 1 < kw0 || (W >= 0 && qtile0 - kw_last > W);
@@ -260,23 +273,36 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__rest
         msk[qb] = !(qr0 >= kw_last && (W < 0 || qr0 + 31 - kw0 <= W) && qr0 + 31 < T);
       }
       if (act[0] && act[1] && !msk[0] && !msk[1]) {
-        // steady state, one straight-line block: the S/dP MFMAs of the second
-        // query block can run under the exponentials of the first
+        // steady state, one straight-line block: the S/dP MFMAs of query block 1
+        // run under the P/dS arithmetic of block 0, and the dV/dK MFMAs of block
+        // 0 under that of block 1
         f32x16 s0, p0, s1, p1;
-        dkdv_sdp(s0, p0, qs, dos, L, kreg, vreg, 0);
-        dkdv_sdp(s1, p1, qs, dos, L, kreg, vreg, 1);
-        dkdv_p_ds(s0, p0, lse2, dl, false, 0, qtile0, key_lane, T, W, c, hh, ds_row);
-        dkdv_acc(dkacc, dvacc, s0, p0, qs, dos, L, 0);
-        dkdv_p_ds(s1, p1, lse2, dl, false, 1, qtile0, key_lane, T, W, c, hh, ds_row);
-        dkdv_acc(dkacc, dvacc, s1, p1, qs, dos, L, 1);
+        uint32_t pk0[8], dk0[8], pk1[8], dk1[8];
+        u32x4 out0[2], out1[2];
+        dkdv_sdp(s0, p0, qs, dos, ndl, L, kreg, vreg, 0, hh);
+        __builtin_amdgcn_sched_barrier(0);
+        dkdv_sdp(s1, p1, qs, dos, ndl, L, kreg, vreg, 1, hh);
+        dkdv_p_ds(s0, p0, lse2, false, 0, qtile0, key_lane, T, W, c, hh, pk0, dk0, out0);
+        ds_store(ds_row, out0, 0, hh);
+        interleave_mfma_valu<16, 5>();
+        __builtin_amdgcn_sched_barrier(0);
+        dkdv_acc(dkacc, dvacc, pk0, dk0, qs, dos, L, 0);
+        dkdv_p_ds(s1, p1, lse2, false, 1, qtile0, key_lane, T, W, c, hh, pk1, dk1, out1);
+        ds_store(ds_row, out1, 1, hh);
+        interleave_mfma_valu<16, 5>();
+        __builtin_amdgcn_sched_barrier(0);
+        dkdv_acc(dkacc, dvacc, pk1, dk1, qs, dos, L, 1);
       } else {
 #pragma unroll 1
         for (int qb = 0; qb < 2; ++qb) {
           if (!act[qb]) continue;
           f32x16 s0, p0;
-          dkdv_sdp(s0, p0, qs, dos, L, kreg, vreg, qb);
-          dkdv_p_ds(s0, p0, lse2, dl, msk[qb], qb, qtile0, key_lane, T, W, c, hh, ds_row);
-          dkdv_acc(dkacc, dvacc, s0, p0, qs, dos, L, qb);
+          uint32_t pk0[8], dk0[8];
+          dkdv_sdp(s0, p0, qs, dos, ndl, L, kreg, vreg, qb, hh);
+          u32x4 out[2];
+          dkdv_p_ds(s0, p0, lse2, msk[qb], qb, qtile0, key_lane, T, W, c, hh, pk0, dk0, out);
+          ds_store(ds_row, out, qb, hh);
+          dkdv_acc(dkacc, dvacc, pk0, dk0, qs, dos, L, qb);
         }
       }
     }
@@ -287,7 +313,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__rest
     if (it + 1 >= n_iter) break;
     step(buf1, buf0, it + 1);
   }
-
   if (!wave_active || key_lane >= T) return;
   const long long off = ((long long)b * T + key_lane) * kv_stride + (long long)kvh * kD;
 #pragma unroll

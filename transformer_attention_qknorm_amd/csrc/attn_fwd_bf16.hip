@@ -23,6 +23,13 @@
 // K(t+2) and V(t+1) are being copied into the other halves of two LDS rings.
 // Tiles entirely outside a wave's window are skipped; masks are applied only on
 // tiles that straddle the causal diagonal or the window edge.
+//
+// Exponent reference: a row's offset is the max of its first tile with a visible
+// key and stays fixed, so O is never rescaled and no tile max is needed after the
+// first.  That is exact as long as no probability exceeds 2^64 (the sums stay far
+// inside fp32); a tile whose row sum does exceed it sends the workgroup through a
+// second pass that computes the exact row maxima first and repeats the loop with
+// them.
 #include "attn_tiles.hpp"
 #include "internal.hpp"
 
@@ -31,11 +38,11 @@ namespace ncattn {
 namespace {
 
 constexpr int kBlockM = 128;
-constexpr float kRescaleThreshold = 8.0f;  // log2 units: rescale O only when the max grows by > 2^8
+constexpr float kSumLimit = 18446744073709551616.0f;  // 2^64
 
 struct FwdState {
   f32x16 oacc[4];
-  float m_run;  // running reference max of raw scores (both half-waves agree)
+  float m_ref;  // exponent reference of the raw scores (both half-waves agree; -inf: none yet)
   float l_run;  // this lane's partial row sum (its 32 of every 64 keys)
 };
 
@@ -50,47 +57,43 @@ __device__ __forceinline__ void s_tile(f32x16 (&sacc)[2], const char *ks, const 
   }
 }
 
-// Online softmax of one tile, part 1: mask, tile max and (rarely) the lazy
-// rescale of O.  Returns the exponent offset -m_run * c for part 2.
-__device__ __forceinline__ float softmax_max(FwdState &st, f32x16 (&sacc)[2], bool need_mask, int k0, int q_lane,
-                                             int W, float c, int hh) {
-  if (need_mask) {
+// Masks a tile that straddles the causal diagonal or the window edge.  Element e
+// of sacc[kb] is key k0 + 32 kb + 8 (e >> 2) + 4 hh + (e & 3) of query q_lane.
+__device__ __forceinline__ void mask_tile(f32x16 (&sacc)[2], int k0, int q_lane, int W, int hh) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+  for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int key = k0 + 32 * kb + 8 * (e >> 2) + 4 * hh + (e & 3);
-        const bool vis = key <= q_lane && (W < 0 || q_lane - key <= W);
-        const float x = sacc[kb][e];
-        sacc[kb][e] = vis ? x : -INFINITY;
-      }
-  }
+    for (int e = 0; e < 16; ++e) {
+      const int key = k0 + 32 * kb + 8 * (e >> 2) + 4 * hh + (e & 3);
+      const bool vis = key <= q_lane && (W < 0 || q_lane - key <= W);
+      const float x = sacc[kb][e];
+      sacc[kb][e] = vis ? x : -INFINITY;
+    }
+}
+
+// Row max of a tile, agreed by the lane pair (l, l^32).
+__device__ __forceinline__ float tile_max(const f32x16 (&sacc)[2]) {
   float mt = sacc[0][0];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int e = 0; e < 16; ++e) mt = fmaxf(mt, sacc[kb][e]);
-  mt = fmaxf(mt, shfl_xor(mt, 32));
-  // Lazy rescale: move the reference max only when it grows by more than
-  // 2^kRescaleThreshold in probability terms (exact either way: the same
-  // reference scales O and l).
-  if (__any(mt > st.m_run + kRescaleThreshold / c)) {
-    const float m_new = fmaxf(st.m_run, mt);
-    if (m_new != st.m_run) {
-      const float alpha = (st.m_run == -INFINITY) ? 0.f : fast_exp2((st.m_run - m_new) * c);
-      st.l_run *= alpha;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) st.oacc[i][e] *= alpha;
-      st.m_run = m_new;
-    }
-  }
-  return (st.m_run == -INFINITY) ? 0.f : -st.m_run * c;
+  return fmaxf(mt, shfl_xor(mt, 32));
 }
 
-// Part 2: probabilities (in place) and the row-sum update; straight-line code.
-__device__ __forceinline__ void softmax_exp(FwdState &st, f32x16 (&sacc)[2], float nmc, float c) {
+// Gives rows without a reference yet (their O and l are still zero) the max of
+// this tile.
+__device__ __forceinline__ void init_ref(FwdState &st, const f32x16 (&sacc)[2]) {
+  if (__any(st.m_ref == -INFINITY)) {
+    const float mt = tile_max(sacc);
+    if (st.m_ref == -INFINITY) st.m_ref = mt;
+  }
+}
+
+// Probabilities (in place) and the row-sum update; a row sum above 2^64 (or
+// infinite) raises `overflow`.
+__device__ __forceinline__ void softmax_exp(FwdState &st, f32x16 (&sacc)[2], float c, bool &overflow) {
+  const float nmc = (st.m_ref == -INFINITY) ? 0.f : -st.m_ref * c;
   float ls = 0.f;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
@@ -100,6 +103,7 @@ __device__ __forceinline__ void softmax_exp(FwdState &st, f32x16 (&sacc)[2], flo
       sacc[kb][e] = p;
       ls += p;
     }
+  overflow |= ls > kSumLimit;
   st.l_run += ls;
 }
 
@@ -123,6 +127,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const uint16_t *_
   __shared__ __attribute__((aligned(1024))) char kb1[kTileBytes];
   __shared__ __attribute__((aligned(1024))) char vb0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) char vb1[kTileBytes];
+  __shared__ int overflow_flag;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -176,44 +181,75 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const uint16_t *_
   const TileLane L = make_tile_lane(lane);
 
   FwdState st;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) st.oacc[i] = f32x16{};
-  st.m_run = -INFINITY;
-  st.l_run = 0.f;
+  float m_init = -INFINITY;
+  if (tid == 0) overflow_flag = 0;
 
-  lds_loads_done_barrier();
-  f32x16 scur[2], snext[2];
-  if (in_range(t0)) s_tile(scur, kb0, L, qreg);
-  __syncthreads();  // every wave is done with K(t0) before its slot is refilled
-
-  // Step t: S of tile t+1 from kcur, softmax + PV of tile t from vcur; copies of
-  // K(t+2) into kfill and V(t+1) into vfill run meanwhile.
-  auto step = [&](const char *kcur, char *kfill, const char *vcur, char *vfill, int t) {
-    if (t + 2 <= t1) tile_load_lds(kfill, ksrc, voff, (t + 2) * kTileN);
-    if (t + 1 <= t1) tile_load_lds(vfill, vsrc, voff, (t + 1) * kTileN);
-    const bool cur = in_range(t), next = in_range(t + 1);
-    if (cur && next) {
-      // steady state: one straight-line block holding the S MFMAs of tile t+1,
-      // the exponentials of tile t and the PV MFMAs of tile t
-      const float nmc = softmax_max(st, scur, masked(t), t * kTileN, q_lane, W, c, hh);
-      s_tile(snext, kcur, L, qreg);
-      softmax_exp(st, scur, nmc, c);
-      pv_tile(st, scur, vcur, L);
-      scur[0] = snext[0];
-      scur[1] = snext[1];
-    } else if (cur) {
-      const float nmc = softmax_max(st, scur, masked(t), t * kTileN, q_lane, W, c, hh);
-      softmax_exp(st, scur, nmc, c);
-      pv_tile(st, scur, vcur, L);
-    } else if (next) {
-      s_tile(scur, kcur, L, qreg);
+#pragma unroll 1
+  for (int pass = 0; pass < 2; ++pass) {
+    if (pass == 1) {
+      // Rare: a probability exceeded 2^64 against its row's reference.  Compute
+      // the exact row maxima over the wave's tiles, then repeat the loop.
+      if (!overflow_flag) break;
+#pragma unroll 1
+      for (int t = t0; t <= t1; ++t) {
+        tile_load_lds(kb0, ksrc, voff, t * kTileN);
+        lds_loads_done_barrier();
+        if (in_range(t)) {
+          f32x16 sx[2];
+          s_tile(sx, kb0, L, qreg);
+          mask_tile(sx, t * kTileN, q_lane, W, hh);
+          m_init = fmaxf(m_init, tile_max(sx));
+        }
+        __syncthreads();
+      }
+      tile_load_lds(kb0, ksrc, voff, t0 * kTileN);
+      tile_load_lds(vb0, vsrc, voff, t0 * kTileN);
+      if (t0 + 1 <= t1) tile_load_lds(kb1, ksrc, voff, (t0 + 1) * kTileN);
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) st.oacc[i] = f32x16{};
+    st.m_ref = m_init;
+    st.l_run = 0.f;
+    bool overflow = false;
+
     lds_loads_done_barrier();
-  };
-  for (int t = t0; t <= t1; t += 2) {
-    step(kb1, kb0, vb0, vb1, t);
-    if (t + 1 > t1) break;
-    step(kb0, kb1, vb1, vb0, t + 1);
+    f32x16 scur[2], snext[2];
+    if (in_range(t0)) s_tile(scur, kb0, L, qreg);
+    __syncthreads();  // every wave is done with K(t0) before its slot is refilled
+
+    // Step t: S of tile t+1 from kcur, softmax + PV of tile t from vcur; copies of
+    // K(t+2) into kfill and V(t+1) into vfill run meanwhile.
+    auto step = [&](const char *kcur, char *kfill, const char *vcur, char *vfill, int t) {
+      if (t + 2 <= t1) tile_load_lds(kfill, ksrc, voff, (t + 2) * kTileN);
+      if (t + 1 <= t1) tile_load_lds(vfill, vsrc, voff, (t + 1) * kTileN);
+      const bool cur = in_range(t), next = in_range(t + 1);
+      if (cur) {
+        if (masked(t)) mask_tile(scur, t * kTileN, q_lane, W, hh);
+        init_ref(st, scur);
+      }
+      if (cur && next) {
+        // steady state: one straight-line block holding the S MFMAs of tile t+1,
+        // the exponentials of tile t and the PV MFMAs of tile t
+        s_tile(snext, kcur, L, qreg);
+        softmax_exp(st, scur, c, overflow);
+        pv_tile(st, scur, vcur, L);
+        scur[0] = snext[0];
+        scur[1] = snext[1];
+      } else if (cur) {
+        softmax_exp(st, scur, c, overflow);
+        pv_tile(st, scur, vcur, L);
+      } else if (next) {
+        s_tile(scur, kcur, L, qreg);
+      }
+      lds_loads_done_barrier();
+    };
+    for (int t = t0; t <= t1; t += 2) {
+      step(kb1, kb0, vb0, vb1, t);
+      if (t + 1 > t1) break;
+      step(kb0, kb1, vb1, vb0, t + 1);
+    }
+    if (__any(overflow) && lane == 0) overflow_flag = 1;
+    __syncthreads();
   }
 
   if (!wave_active) return;
@@ -231,7 +267,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const uint16_t *_
         w[1] = pack_bf16x2(st.oacc[db][4 * i + 2] * inv_l, st.oacc[db][4 * i + 3] * inv_l);
         *(u32x2 *)(op + d) = w;
       }
-    if (hh == 0) LSE[((long long)b * H + h) * T + q_lane] = st.m_run * scale + logf(l_tot);
+    if (hh == 0) LSE[((long long)b * H + h) * T + q_lane] = st.m_ref * scale + logf(l_tot);
   }
 }
 
