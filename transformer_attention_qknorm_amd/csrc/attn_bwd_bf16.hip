@@ -34,29 +34,48 @@ constexpr int kBlockN = 128;  // keys per dkdv workgroup
 // and LSE_i * log2(e), the exponent offset of P in base 2.
 __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t *__restrict__ O,
                                                         const uint16_t *__restrict__ dO,
-                                                        const float *__restrict__ LSE, float *__restrict__ delta,
+                                                        const float *__restrict__ LSE, float *__restrict__ ndelta,
                                                         float *__restrict__ lse2, int B, int T, int H) {
-  // 16 lanes per (token, head) row, 16 rows per block
-  const long long row = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int part = threadIdx.x & 15;
+  // 8 lanes per (token, head) row, 32 bytes of O and of dO each; a wave covers 8
+  // rows per pass and issues the loads of two passes before reducing.
   const long long nrows = (long long)B * T * H;
-  float s = 0.f;
-  if (row < nrows) {
-    const u32x4 a = *(const u32x4 *)(O + row * kD + part * 8);
-    const u32x4 g = *(const u32x4 *)(dO + row * kD + part * 8);
+  const int part = threadIdx.x & 7;
+  const long long row_base = ((long long)blockIdx.x * 256 + (threadIdx.x & ~7)) / 8 * 2;  // 64 rows per block
+  float s[2];
+  u32x4 a[2][2], g[2][2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s += lo_bf16(a[i]) * lo_bf16(g[i]) + hi_bf16(a[i]) * hi_bf16(g[i]);
+  for (int p = 0; p < 2; ++p) {
+    const long long row = row_base + p;
+    const long long r = row < nrows ? row : nrows - 1;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      a[p][c] = *(const u32x4 *)(O + r * kD + part * 16 + 8 * c);
+      g[p][c] = *(const u32x4 *)(dO + r * kD + part * 16 + 8 * c);
+    }
   }
 #pragma unroll
-  for (int m = 1; m < 16; m <<= 1) s += shfl_xor(s, m);
-  if (row < nrows && part == 0) {
-    const long long tok = row / H;
-    const int h = (int)(row % H);
-    const int b = (int)(tok / T);
-    const int t = (int)(tok % T);
-    const long long ri = ((long long)b * H + h) * T + t;
-    delta[ri] = -s;
-    lse2[ri] = LSE[ri] * kLog2e;
+  for (int p = 0; p < 2; ++p) {
+    float acc = 0.f;
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        acc += lo_bf16(a[p][c][i]) * lo_bf16(g[p][c][i]) + hi_bf16(a[p][c][i]) * hi_bf16(g[p][c][i]);
+#pragma unroll
+    for (int m = 1; m < 8; m <<= 1) acc += shfl_xor(acc, m);
+    s[p] = acc;
+  }
+  if (part < 2) {
+    const long long row = row_base + part;
+    if (row < nrows) {
+      const long long tok = row / H;
+      const int h = (int)(row % H);
+      const int b = (int)(tok / T);
+      const int t = (int)(tok % T);
+      const long long ri = ((long long)b * H + h) * T + t;
+      ndelta[ri] = -(part == 0 ? s[0] : s[1]);
+      lse2[ri] = LSE[ri] * kLog2e;
+    }
   }
 }
 
@@ -503,7 +522,7 @@ hipError_t launch_bwd_bf16(const void *q, const void *k, const void *v, const vo
   uint16_t *dsband = (uint16_t *)((char *)workspace + 2 * row_bytes);
   const DsBand band = ds_band(sh.T, sh.window);
   const long long rows = (long long)sh.B * sh.T * sh.H;
-  const long long dblocks = (rows + 15) / 16;
+  const long long dblocks = (rows + 63) / 64;
   const long long nkb = (sh.T + kBlockN - 1) / kBlockN;
   const long long nqb = (sh.T + kBlockM - 1) / kBlockM;
   const long long kvblocks = nkb * sh.B * sh.KV;

@@ -46,14 +46,21 @@ struct FwdState {
   float l_run;  // this lane's partial row sum (its 32 of every 64 keys)
 };
 
+// The K operands are read from LDS four MFMAs ahead of their use (the reads are
+// fenced in place, so their latency hides under the MFMAs in between).
 __device__ __forceinline__ void s_tile(f32x16 (&sacc)[2], const char *ks, const TileLane &L,
                                        const bf16x8 (&qreg)[8]) {
+  constexpr int kAhead = 4;
+  bf16x8 kop[16];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    f32x16 acc = f32x16{};
+  for (int i = 0; i < kAhead; ++i) kop[i] = row_operand(ks, L, i >> 1, i & 1);
+  sacc[0] = f32x16{};
+  sacc[1] = f32x16{};
 #pragma unroll
-    for (int s = 0; s < 8; ++s) acc = mfma32(row_operand(ks, L, s, kb), qreg[s], acc);
-    sacc[kb] = acc;
+  for (int i = 0; i < 16; ++i) {  // i = 2 s + kb
+    if (i + kAhead < 16) kop[i + kAhead] = row_operand(ks, L, (i + kAhead) >> 1, (i + kAhead) & 1);
+    sacc[i & 1] = mfma32(kop[i], qreg[i >> 1], sacc[i & 1]);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
