@@ -22,6 +22,9 @@ from .attention import (  # noqa: F401
     rope_angles,
     apply_rope,
     qknorm_rope,
+    rope_inverse,
+    rms_norm_bwd,
+    qknorm_rope_bwd,
     visible_mask,
     n_visible_pairs,
     attn_fwd,

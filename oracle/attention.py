@@ -107,6 +107,48 @@ def qknorm_rope(q, k, pos_offset=None, base=100000.0, eps=1e-6, gain=1.0):
     return qn, kn
 
 
+def rope_inverse(y, pos, base):
+    """The transpose of apply_rope's rotation (its inverse): every pair
+    (y_j, y_{j+D/2}) rotated by -theta(pos, j).  This is how a gradient flows
+    back through RoPE."""
+    y = np.asarray(y, dtype=np.float64)
+    D = y.shape[-1]
+    half = D // 2
+    theta = rope_angles(pos, D, base)[:, :, None, :]
+    c, s = np.cos(theta), np.sin(theta)
+    a, b = y[..., :half], y[..., half:]
+    return np.concatenate([a * c + b * s, -a * s + b * c], axis=-1)
+
+
+def rms_norm_bwd(x, dn, eps=1e-6, gain=1.0):
+    """Gradient of rms_norm at x, given dn = dL/dn for n = g x / r with
+    r = sqrt(mean(x^2) + eps):  dL/dx = (g / r) (dn - x sum(dn x) / (D r^2)),
+    the derivative of n_i with respect to x_k being g (delta_ik / r - x_i x_k / (D r^3))."""
+    x = np.asarray(x, dtype=np.float64)
+    dn = np.asarray(dn, dtype=np.float64)
+    D = x.shape[-1]
+    r2 = np.mean(x * x, axis=-1, keepdims=True) + eps
+    r = np.sqrt(r2)
+    dot = np.sum(dn * x, axis=-1, keepdims=True)
+    return gain / r * (dn - x * dot / (D * r2))
+
+
+def qknorm_rope_bwd(q, k, dq_out, dk_out, pos_offset=None, base=100000.0, eps=1e-6, gain=1.0):
+    """Gradient of qknorm_rope with respect to its inputs q and k, given the
+    gradients dq_out, dk_out of its outputs: back through RoPE (rope_inverse),
+    then through the RMSNorm (rms_norm_bwd), the chain rule in the forward's
+    reverse order ("nanochat (Python)" catalog, Backward pass: autograd of the
+    forward; the forward is section 3 of the nanochat Admin & Developer Guide)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    B, T = q.shape[0], q.shape[1]
+    off = np.zeros(B) if pos_offset is None else np.asarray(pos_offset, dtype=np.float64)
+    pos = off[:, None] + np.arange(T, dtype=np.float64)[None, :]
+    dq = rms_norm_bwd(q, rope_inverse(dq_out, pos, base), eps, gain)
+    dk = rms_norm_bwd(k, rope_inverse(dk_out, pos, base), eps, gain)
+    return dq, dk
+
+
 # --------------------------------------------------------------------------
 # Attention forward / backward
 # ("nanoGPT Administrator & Developer Guide" section 8 CausalSelfAttention;

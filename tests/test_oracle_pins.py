@@ -271,6 +271,88 @@ def test_decode_equals_sdpa_last_row(W):
         np.testing.assert_allclose(o[:, 0], np.repeat(vn[:, 0], H // KV, axis=1), atol=1e-15)
 
 
+# ----------------------------------------------------------------- QK-norm + RoPE backward
+
+def _qkr_loss(q, k, dyq, dyk, off, base, eps, gain):
+    yq, yk = oracle.qknorm_rope(q, k, off, base, eps, gain)
+    return float(np.sum(yq * dyq) + np.sum(yk * dyk))
+
+
+def _fd_grad(x, loss, h=1e-6):
+    num = np.zeros_like(x)
+    for idx in np.ndindex(x.shape):
+        old = x[idx]
+        x[idx] = old + h
+        lp = loss()
+        x[idx] = old - h
+        lm = loss()
+        x[idx] = old
+        num[idx] = (lp - lm) / (2 * h)
+    return num
+
+
+@pytest.mark.parametrize("D,gain,eps", [(8, 1.0, 1e-6), (16, math.sqrt(1.2), 1e-2)])
+def test_qknorm_rope_bwd_matches_finite_differences(D, gain, eps):
+    """Central differences of the forward (not the backward's formulas) pin the gradient."""
+    B, T, H, KV, base = 2, 3, 2, 1, 10000.0
+    q, k = rand(B, T, H, D), rand(B, T, KV, D)
+    dyq, dyk = rand(B, T, H, D), rand(B, T, KV, D)
+    off = np.array([5, 1000])
+    gq, gk = oracle.qknorm_rope_bwd(q, k, dyq, dyk, off, base, eps, gain)
+    loss = lambda: _qkr_loss(q, k, dyq, dyk, off, base, eps, gain)  # noqa: E731
+    np.testing.assert_allclose(gq, _fd_grad(q, loss), atol=1e-8, rtol=1e-6)
+    np.testing.assert_allclose(gk, _fd_grad(k, loss), atol=1e-8, rtol=1e-6)
+
+
+def test_qknorm_rope_bwd_matches_torch_autograd():
+    """torch autograd through torch's rms_norm and a complex-multiplication RoPE."""
+    B, T, H, D, base, eps, gain = 2, 5, 3, 16, 100000.0, 1e-6, 1.3
+    x, dy = rand(B, T, H, D), rand(B, T, H, D)
+    off = np.array([0, 77])
+    xt = torch.from_numpy(x.copy()).requires_grad_(True)
+    n = gain * F.rms_norm(xt, (D,), eps=eps)
+    pos = torch.from_numpy(off[:, None] + np.arange(T)[None, :]).double()
+    j = torch.arange(D // 2, dtype=torch.float64)
+    ang = pos[..., None, None] * base ** (-2.0 * j / D)
+    z = torch.complex(n[..., : D // 2], n[..., D // 2:]) * torch.exp(1j * ang)
+    y = torch.cat([z.real, z.imag], dim=-1)
+    (y * torch.from_numpy(dy)).sum().backward()
+    gq, _ = oracle.qknorm_rope_bwd(x, x[:, :, :1], dy, dy[:, :, :1], off, base, eps, gain)
+    np.testing.assert_allclose(gq, xt.grad.numpy(), atol=1e-12, rtol=1e-10)
+
+
+def test_qknorm_rope_bwd_invariants():
+    B, T, H, D = 1, 4, 2, 32
+    x, dy = rand(B, T, H, D), rand(B, T, H, D)
+    pos = np.arange(T, dtype=np.float64)[None, :] + 3.0
+    # RoPE's backward undoes its rotation
+    np.testing.assert_allclose(oracle.rope_inverse(oracle.apply_rope(x, pos, 10000.0), pos, 10000.0), x,
+                               atol=1e-13)
+    # with eps = 0 the norm is invariant to scaling x, so the gradient is orthogonal to x
+    g = oracle.rms_norm_bwd(x, dy, eps=0.0, gain=1.0)
+    np.testing.assert_allclose(np.sum(g * x, axis=-1), 0.0, atol=1e-12)
+    # and scaling x by c scales the gradient by 1/c
+    np.testing.assert_allclose(oracle.rms_norm_bwd(3.0 * x, dy, eps=0.0), g / 3.0, atol=1e-13)
+
+
+def test_qknorm_rope_bwd_planted_mistakes():
+    """A backward rotating by +theta, or one without the norm's projection term,
+    fails the finite-difference pin."""
+    import oracle.attention as A
+    B, T, H, D, base, eps = 1, 3, 1, 8, 10000.0, 1e-6
+    x, dy = rand(B, T, H, D), rand(B, T, H, D)
+    off = np.array([40])
+    pos = off[:, None] + np.arange(T, dtype=np.float64)[None, :]
+    num = _fd_grad(x, lambda: _qkr_loss(x, x[:, :, :1] * 0 + 1, dy, dy[:, :, :1] * 0, off, base, eps, 1.0))
+    good = A.rms_norm_bwd(x, A.rope_inverse(dy, pos, base), eps)
+    np.testing.assert_allclose(good, num, atol=1e-8, rtol=1e-6)
+    wrong_sign = A.rms_norm_bwd(x, A.apply_rope(dy, pos, base), eps)
+    assert not np.allclose(wrong_sign, num, atol=1e-6)
+    r = np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    no_projection = A.rope_inverse(dy, pos, base) / r
+    assert not np.allclose(no_projection, num, atol=1e-6)
+
+
 # ----------------------------------------------------------------- planted mistakes
 
 def test_planted_mistakes_are_caught(monkeypatch):
