@@ -220,6 +220,23 @@ def main():
         "algorithmic_gflop_per_step": round(flops_step / 1e9, 2),
     }
 
+    # Backward of QK-norm + RoPE (not part of the step's attention FLOPs): read the
+    # forward's inputs and the output gradients, write the input gradients.
+    Lq = layers[0]
+    for _ in range(3):
+        nc.qknorm_rope_bwd_(Lq["dq"], Lq["dk"], Lq["q"], Lq["k"], None, rope_base=cfg.rope_base, eps=1e-6)
+    torch.cuda.synchronize()
+    qb_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+    for a, b in qb_ev:
+        a.record(stream)
+        nc.qknorm_rope_bwd_(Lq["dq"], Lq["dk"], Lq["q"], Lq["k"], None, rope_base=cfg.rope_base, eps=1e-6)
+        b.record(stream)
+    torch.cuda.synchronize()
+    qb_us = sum(a.elapsed_time(b) for a, b in qb_ev) * 1e3 / len(qb_ev)
+    qb_gbps = 3 * (qk_bytes // 2) / (qb_us * 1e-6) / 1e9
+    detail["qknorm_rope_bwd"] = {"us": round(qb_us, 2), "GBps": round(qb_gbps, 1),
+                                 "frac_hbm": round(qb_gbps / PEAK_HBM_GBPS, 4), "algorithmic_bytes": 3 * (qk_bytes // 2)}
+
     decode = None
     if not args.no_decode:
         c = DECODE

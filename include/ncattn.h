@@ -77,6 +77,23 @@ int ncattn_qknorm_rope(void *q, void *k, int B, int T, int n_head, int n_kv_head
                        int dtype, void *stream);
 
 /*
+ * Backward of ncattn_qknorm_rope ("nanochat (Python)" catalog, Backward pass:
+ * autograd of the forward; the forward is section 3 of the nanochat Admin &
+ * Developer Guide).  With n = g x / r, r = sqrt(mean_d(x_d^2) + eps), y = R(pos) n:
+ *     dn = R(pos)^T dy                 (each pair rotated by -a)
+ *     dx = (g / r) (dn - x sum_d(dn_d x_d) / (D r^2))
+ *   dq [B][T][n_head][head_dim], dk [B][T][n_kv_head][head_dim]: on entry the
+ *     gradients dy of the forward's outputs, on return the gradients dx of its
+ *     inputs (in place, dtype).
+ *   q, k: the forward's inputs (before normalisation), read only; they must not
+ *     overlap dq / dk.
+ *   Other arguments, arithmetic, validation and status codes as ncattn_qknorm_rope.
+ */
+int ncattn_qknorm_rope_bwd(void *dq, void *dk, const void *q, const void *k, int B, int T, int n_head,
+                           int n_kv_head, int head_dim, const int32_t *pos_offset, float rope_base,
+                           float eps, float qk_gain, int dtype, void *stream);
+
+/*
  * Attention forward ("nanoGPT Administrator & Developer Guide" section 8;
  * "nanochat Admin & Developer Guide" sections 3 and 6).
  *   q [B][T][n_head][D], k, v [B][T][n_kv_head][D]          (dtype)

@@ -35,7 +35,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert {"ncattn_qknorm_rope", "ncattn_fwd", "ncattn_bwd", "ncattn_decode"} <= set(names)
+    assert {"ncattn_qknorm_rope", "ncattn_qknorm_rope_bwd", "ncattn_fwd", "ncattn_bwd", "ncattn_decode"} <= set(names)
     for n in names:
         assert hasattr(L, n), f"libncattn.so does not export {n}"
     # and the shared object's dynamic symbol table agrees
@@ -48,6 +48,25 @@ def test_exports_every_declared_symbol(L):
 def test_version_and_empty_error(L):
     assert L.ncattn_version().decode().startswith("ncattn")
     assert isinstance(L.ncattn_last_error(), bytes)
+
+
+def test_qknorm_rope_bwd_validation(L):
+    f = L.ncattn_qknorm_rope_bwd
+    args = dict(dq=P, dk=P + 16, q=P + 32, k=P + 48)
+    def call(dq=P, dk=P + 16, q=P + 32, k=P + 48, D=128, base=1e5, eps=1e-6, gain=1.0, dt=0, pos=None):
+        return f(dq, dk, q, k, 1, 4, 2, 2, D, pos, base, eps, gain, dt, None)
+    assert call(dq=None) == EINVAL
+    assert call(k=None) == EINVAL
+    assert call(dq=P + 32) == EINVAL          # dq aliases q
+    assert call(dk=P + 48) == EINVAL          # dk aliases k
+    assert call(dk=P) == EINVAL               # dq == dk
+    assert call(q=MIS) == EINVAL
+    assert call(D=96) == EUNSUP
+    assert call(base=1.0) == EINVAL
+    assert call(eps=-1.0) == EINVAL
+    assert call(pos=P + 2) == EINVAL
+    assert call(dt=5) == EINVAL
+    assert "ncattn_qknorm_rope_bwd" in L.ncattn_last_error().decode()
 
 
 def fwd(L, q=P, k=P, v=P, o=P + 16, lse=P + 32, B=1, T=64, H=2, KV=2, D=128, wl=-1, wr=0, scale=0.0, dt=0):

@@ -52,6 +52,30 @@ def test_qknorm_rope(dtype, B, T, H, KV, D, base, gain, offset):
     assert torch.equal(vd, v_before)
 
 
+@pytest.mark.parametrize("dtype,B,T,H,KV,D,base,gain,offset", [
+    ("f32", 1, 64, 2, 2, 64, 10000.0, 1.0, False),
+    ("f32", 2, 37, 4, 2, 128, 100000.0, math.sqrt(1.2), True),
+    ("bf16", 3, 130, 6, 6, 128, 100000.0, 1.0, False),
+    ("bf16", 64, 1, 10, 10, 128, 100000.0, 1.0, True),
+    ("bf16", 2, 50, 12, 4, 64, 10000.0, math.sqrt(1.2), True),
+])
+def test_qknorm_rope_bwd(dtype, B, T, H, KV, D, base, gain, offset):
+    say(f"qknorm_rope_bwd {dtype} B={B} T={T} H={H} KV={KV} D={D}")
+    q, k, _, _ = attn_inputs(B, T, H, KV, D, dtype, seed=21)
+    gq, gk, _, _ = attn_inputs(B, T, H, KV, D, dtype, seed=22)
+    pos = torch.from_numpy(np.random.default_rng(4).integers(0, 8192, size=B).astype(np.int32)) if offset else None
+    ref_q, ref_k = oracle.qknorm_rope_bwd(f64(q), f64(k), f64(gq), f64(gk), None if pos is None else pos.numpy(),
+                                          base, 1e-6, gain)
+    qd, kd, gqd, gkd = to_dev(q, k, gq, gk)
+    q_before, k_before = qd.clone(), kd.clone()
+    nc.qknorm_rope_bwd_(gqd, gkd, qd, kd, None if pos is None else pos.to(DEV), rope_base=base, eps=1e-6,
+                        qk_gain=gain)
+    torch.cuda.synchronize()
+    check(gqd, ref_q, dtype, "dq_in")
+    check(gkd, ref_k, dtype, "dk_in")
+    assert torch.equal(qd, q_before) and torch.equal(kd, k_before)
+
+
 # ------------------------------------------------------------------ forward / backward
 
 FWD_CASES = [

@@ -50,6 +50,7 @@ def lib():
     L = ctypes.CDLL(LIB_PATH)
     vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     L.ncattn_qknorm_rope.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, f32, f32, f32, i32, vp]
+    L.ncattn_qknorm_rope_bwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, f32, f32, f32, i32, vp]
     L.ncattn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp]
     L.ncattn_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
     L.ncattn_bwd_workspace_bytes.restype = sz
@@ -63,7 +64,7 @@ def lib():
     L.ncattn_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp, sz, vp]
     L.ncattn_last_error.restype = ctypes.c_char_p
     L.ncattn_version.restype = ctypes.c_char_p
-    for fn in ("ncattn_qknorm_rope", "ncattn_fwd", "ncattn_bwd", "ncattn_decode"):
+    for fn in ("ncattn_qknorm_rope", "ncattn_qknorm_rope_bwd", "ncattn_fwd", "ncattn_bwd", "ncattn_decode"):
         getattr(L, fn).restype = i32
     _lib = L
     return L
@@ -130,6 +131,29 @@ def qknorm_rope_(q, k, pos_offset=None, rope_base=100000.0, eps=1e-6, qk_gain=1.
                                       float(rope_base), float(eps), float(qk_gain), _dtype_code(q), _stream(dev))
     _check("ncattn_qknorm_rope", rc)
     return q, k
+
+
+def qknorm_rope_bwd_(dq, dk, q, k, pos_offset=None, rope_base=100000.0, eps=1e-6, qk_gain=1.0):
+    """Backward of qknorm_rope_, in place: dq, dk hold the gradients of its outputs
+    on entry and those of its inputs on return; q, k are its inputs (before
+    normalisation, untouched).  Returns (dq, dk)."""
+    dev = _dev(dq, dk, q, k)
+    if q.dim() != 4 or k.dim() != 4 or dq.shape != q.shape or dk.shape != k.shape \
+            or len({dq.dtype, dk.dtype, q.dtype, k.dtype}) != 1:
+        raise ValueError("ncattn.qknorm_rope_bwd_: dq, dk must match q, k (4-D, one dtype)")
+    B, T, H, D = q.shape
+    if k.shape[0] != B or k.shape[1] != T or k.shape[3] != D:
+        raise ValueError("ncattn.qknorm_rope_bwd_: k must be [B][T][n_kv_head][D] matching q")
+    if pos_offset is not None:
+        _dev(pos_offset)
+        if pos_offset.dtype != torch.int32 or pos_offset.numel() != B:
+            raise ValueError("ncattn.qknorm_rope_bwd_: pos_offset must be int32 [B]")
+    with torch.cuda.device(dev):
+        rc = lib().ncattn_qknorm_rope_bwd(_ptr(dq), _ptr(dk), _ptr(q), _ptr(k), B, T, H, k.shape[2], D,
+                                          _ptr(pos_offset), float(rope_base), float(eps), float(qk_gain),
+                                          _dtype_code(q), _stream(dev))
+    _check("ncattn_qknorm_rope_bwd", rc)
+    return dq, dk
 
 
 def fwd(q, k, v, window=(-1, 0), softmax_scale=None, out=None):

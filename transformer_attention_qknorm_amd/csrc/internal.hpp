@@ -20,6 +20,11 @@ hipError_t launch_qknorm_rope(void *q, void *k, int B, int T, int H, int KV, int
                               const int32_t *pos_offset, const double *inv_freq_host, float eps,
                               float gain, bool bf16, hipStream_t s);
 
+// Its backward: dq/dk hold dy on entry and dx on return; q/k are the forward's inputs.
+hipError_t launch_qknorm_rope_bwd(void *dq, void *dk, const void *q, const void *k, int B, int T, int H, int KV,
+                                  int D, const int32_t *pos_offset, const double *inv_freq_host, float eps,
+                                  float gain, bool bf16, hipStream_t s);
+
 // Backward stages (bit mask): D_i = dO.O, then dK/dV, then dQ.
 constexpr int kBwdDelta = 1, kBwdDkDv = 2, kBwdDq = 4, kBwdAll = 7;
 

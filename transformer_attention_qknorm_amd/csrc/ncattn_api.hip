@@ -91,12 +91,10 @@ const char *ncattn_last_error(void) { return g_err; }
 
 const char *ncattn_version(void) { return "ncattn 0.1.0 (gfx950)"; }
 
-int ncattn_qknorm_rope(void *q, void *k, int B, int T, int n_head, int n_kv_head, int head_dim,
-                       const int32_t *pos_offset, float rope_base, float eps, float qk_gain, int dtype,
-                       void *stream) {
-  const char *fn = "ncattn_qknorm_rope";
-  NC_PTR(q, fn);
-  NC_PTR(k, fn);
+// Checks shared by the QK-norm + RoPE calls; fills inv_freq[j] = base^(-2j/D).
+static int check_qknorm(const char *fn, int B, int T, int n_head, int n_kv_head, int head_dim,
+                        const int32_t *pos_offset, float rope_base, float eps, float qk_gain, int dtype,
+                        double *inv_freq) {
   NC_TRY(check_heads(fn, B, T, n_head, n_kv_head, head_dim));
   NC_TRY(check_dtype(fn, dtype));
   if (head_dim != 64 && head_dim != 128)
@@ -106,10 +104,41 @@ int ncattn_qknorm_rope(void *q, void *k, int B, int T, int n_head, int n_kv_head
   if (!(rope_base > 1.0f) || !isfinite(rope_base)) return fail(NCATTN_EINVAL, "%s: rope_base must be > 1", fn);
   if (!(eps >= 0.0f) || !isfinite(eps)) return fail(NCATTN_EINVAL, "%s: eps must be >= 0", fn);
   if (!isfinite(qk_gain)) return fail(NCATTN_EINVAL, "%s: qk_gain must be finite", fn);
-  double inv_freq[64];
   for (int j = 0; j < head_dim / 2; ++j) inv_freq[j] = pow((double)rope_base, -2.0 * j / head_dim);
+  return NCATTN_OK;
+}
+
+int ncattn_qknorm_rope(void *q, void *k, int B, int T, int n_head, int n_kv_head, int head_dim,
+                       const int32_t *pos_offset, float rope_base, float eps, float qk_gain, int dtype,
+                       void *stream) {
+  const char *fn = "ncattn_qknorm_rope";
+  NC_PTR(q, fn);
+  NC_PTR(k, fn);
+  double inv_freq[64];
+  NC_TRY(check_qknorm(fn, B, T, n_head, n_kv_head, head_dim, pos_offset, rope_base, eps, qk_gain, dtype,
+                      inv_freq));
   return hip_status(ncattn::launch_qknorm_rope(q, k, B, T, n_head, n_kv_head, head_dim, pos_offset, inv_freq, eps,
                                                qk_gain, dtype == NCATTN_BF16, (hipStream_t)stream),
+                    fn);
+}
+
+int ncattn_qknorm_rope_bwd(void *dq, void *dk, const void *q, const void *k, int B, int T, int n_head,
+                           int n_kv_head, int head_dim, const int32_t *pos_offset, float rope_base, float eps,
+                           float qk_gain, int dtype, void *stream) {
+  const char *fn = "ncattn_qknorm_rope_bwd";
+  NC_PTR(dq, fn);
+  NC_PTR(dk, fn);
+  NC_PTR(q, fn);
+  NC_PTR(k, fn);
+  double inv_freq[64];
+  NC_TRY(check_qknorm(fn, B, T, n_head, n_kv_head, head_dim, pos_offset, rope_base, eps, qk_gain, dtype,
+                      inv_freq));
+  if (dq == q || dq == k || dk == q || dk == k)
+    return fail(NCATTN_EINVAL, "%s: dq / dk must not alias the forward's inputs", fn);
+  if (dq == dk) return fail(NCATTN_EINVAL, "%s: dq and dk must differ", fn);
+  return hip_status(ncattn::launch_qknorm_rope_bwd(dq, dk, q, k, B, T, n_head, n_kv_head, head_dim, pos_offset,
+                                                   inv_freq, eps, qk_gain, dtype == NCATTN_BF16,
+                                                   (hipStream_t)stream),
                     fn);
 }
 
