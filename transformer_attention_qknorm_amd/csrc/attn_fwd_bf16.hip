@@ -66,16 +66,31 @@ __device__ __forceinline__ void s_tile(f32x16 (&sacc)[2], const char *ks, const 
 
 // Masks a tile that straddles the causal diagonal or the window edge.  Element e
 // of sacc[kb] is key k0 + 32 kb + 8 (e >> 2) + 4 hh + (e & 3) of query q_lane.
+// With d0 = k0 + 4 hh - q_lane, element (kb, e) has key - query = d0 + off(kb, e)
+// for a compile-time off, so each condition is one compare of d0 (or of
+// d0 + W) against a constant.
 __device__ __forceinline__ void mask_tile(f32x16 (&sacc)[2], int k0, int q_lane, int W, int hh) {
+  const int d0 = k0 + 4 * hh - q_lane;
+  if (W < 0) {
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int key = k0 + 32 * kb + 8 * (e >> 2) + 4 * hh + (e & 3);
-      const bool vis = key <= q_lane && (W < 0 || q_lane - key <= W);
-      const float x = sacc[kb][e];
-      sacc[kb][e] = vis ? x : -INFINITY;
-    }
+      for (int e = 0; e < 16; ++e) {
+        const int off = 32 * kb + 8 * (e >> 2) + (e & 3);
+        const float x = sacc[kb][e];
+        sacc[kb][e] = d0 <= -off ? x : -INFINITY;  // key <= query
+      }
+  } else {
+    const int d0w = d0 + W;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int off = 32 * kb + 8 * (e >> 2) + (e & 3);
+        const float x = sacc[kb][e];
+        sacc[kb][e] = (d0 <= -off && d0w >= -off) ? x : -INFINITY;  // and query - key <= W
+      }
+  }
 }
 
 // Row max of a tile, agreed by the lane pair (l, l^32).
