@@ -11,8 +11,9 @@
 // the H query rows and KV key rows, D/8 lanes per row.  A lane owns the four
 // pair indices j in [4r, 4r+4) of its row slot r and their partners j + D/2,
 // so the rotation is lane-local and cos/sin are computed once per token per
-// lane and reused for all H + KV rows.  The angle is formed and reduced to
-// [-pi, pi] in fp64 (positions reach ~10^4 radians), then sin/cos in fp32.
+// lane and reused for all H + KV rows.  The angle is formed in turns and
+// reduced to [-1/2, 1/2] in fp64 (positions reach ~10^4 radians), then sin/cos
+// by the hardware (v_sin_f32 / v_cos_f32) in fp32.
 //
 // The backward (same layout) takes the forward's inputs x and the gradients dy
 // of its outputs and writes dx over dy: dn = R^T dy (pairs rotated by -theta),
@@ -24,93 +25,8 @@
 namespace ncattn {
 
 struct InvFreq {
-  double v[64];
+  double v[64];  // base^(-2j/D) / (2 pi): turns of the rotation per position
 };
-
-template <int D, bool BF16>
-__global__ __launch_bounds__(256) void qknorm_rope_kernel(void *__restrict__ qp, void *__restrict__ kp, int B, int T,
-                                                          int H, int KV, const int32_t *__restrict__ pos_offset,
-                                                          InvFreq inv_freq, float eps, float gain) {
-  constexpr int R = D / 8;          // lanes per row
-  constexpr int ROWS = 64 / R;      // rows per wave pass
-  constexpr int HALF = D / 2;
-  const int lane = threadIdx.x & 63;
-  const int slot = lane / R;        // row slot within the pass
-  const int r = lane % R;           // which 4-pair group of the row
-  const int j0 = 4 * r;
-  double w[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) w[i] = inv_freq.v[j0 + i];
-
-  const long long ntok = (long long)B * T;
-  const long long wave = ((long long)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
-  const long long nwaves = ((long long)gridDim.x * blockDim.x) >> 6;
-  const int nrows = H + KV;
-  const double two_pi = 6.283185307179586;
-
-  for (long long tok = wave; tok < ntok; tok += nwaves) {
-    const int b = (int)(tok / T);
-    const int t = (int)(tok % T);
-    const double pos = (double)((pos_offset ? pos_offset[b] : 0) + t);
-    float c[4], s[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      double th = pos * w[i];
-      th -= two_pi * rint(th / two_pi);
-      float tf = (float)th;
-      s[i] = sinf(tf);
-      c[i] = cosf(tf);
-    }
-    for (int row0 = 0; row0 < nrows; row0 += ROWS) {
-      const int row = row0 + slot;
-      if (row >= nrows) break;
-      const bool isq = row < H;
-      const long long base = isq ? ((long long)tok * H + row) * D : ((long long)tok * KV + (row - H)) * D;
-      float a[4], bb[4];
-      if constexpr (BF16) {
-        uint16_t *x = (uint16_t *)(isq ? qp : kp) + base;
-        u32x2 va = *(const u32x2 *)(x + j0);
-        u32x2 vb = *(const u32x2 *)(x + HALF + j0);
-        a[0] = lo_bf16(va[0]); a[1] = hi_bf16(va[0]); a[2] = lo_bf16(va[1]); a[3] = hi_bf16(va[1]);
-        bb[0] = lo_bf16(vb[0]); bb[1] = hi_bf16(vb[0]); bb[2] = lo_bf16(vb[1]); bb[3] = hi_bf16(vb[1]);
-      } else {
-        float *x = (float *)(isq ? qp : kp) + base;
-        f32x4 va = *(const f32x4 *)(x + j0);
-        f32x4 vb = *(const f32x4 *)(x + HALF + j0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) { a[i] = va[i]; bb[i] = vb[i]; }
-      }
-      float ss = 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ss += a[i] * a[i] + bb[i] * bb[i];
-#pragma unroll
-      for (int m = 1; m < R; m <<= 1) ss += shfl_xor(ss, m);
-      const float inv = gain / sqrtf(ss / (float)D + eps);
-      float ya[4], yb[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float xa = a[i] * inv, xb = bb[i] * inv;
-        ya[i] = xa * c[i] - xb * s[i];
-        yb[i] = xa * s[i] + xb * c[i];
-      }
-      if constexpr (BF16) {
-        uint16_t *x = (uint16_t *)(isq ? qp : kp) + base;
-        u32x2 oa, ob;
-        oa[0] = pack_bf16x2(ya[0], ya[1]); oa[1] = pack_bf16x2(ya[2], ya[3]);
-        ob[0] = pack_bf16x2(yb[0], yb[1]); ob[1] = pack_bf16x2(yb[2], yb[3]);
-        *(u32x2 *)(x + j0) = oa;
-        *(u32x2 *)(x + HALF + j0) = ob;
-      } else {
-        float *x = (float *)(isq ? qp : kp) + base;
-        f32x4 oa, ob;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) { oa[i] = ya[i]; ob[i] = yb[i]; }
-        *(f32x4 *)(x + j0) = oa;
-        *(f32x4 *)(x + HALF + j0) = ob;
-      }
-    }
-  }
-}
 
 // Loads the lane's 4 pairs (x_j, x_{j+D/2}), j = j0..j0+3, of a row as fp32.
 template <int D, bool BF16>
@@ -151,14 +67,101 @@ __device__ __forceinline__ void store_pairs(void *base, long long off, int j0, c
   }
 }
 
+// cos / sin of the lane's 4 angles: pos * w[i] turns, reduced to [-1/2, 1/2] in
+// fp64 (positions reach ~10^4 radians), then the hardware sin / cos of a turn
+// fraction (v_sin_f32 / v_cos_f32 take their argument in turns).
+__device__ __forceinline__ void rope_cos_sin(double pos, const double (&w)[4], float (&c)[4], float (&s)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    double turns = pos * w[i];
+    turns -= rint(turns);
+    const float tf = (float)turns;
+    s[i] = __builtin_amdgcn_sinf(tf);
+    c[i] = __builtin_amdgcn_cosf(tf);
+  }
+}
+
+// Sum over the R lanes of a row (R = 8 or 16: aligned groups within a DPP row),
+// every lane of the group receiving it: quad permutes, then half-row and row
+// mirrors.
+template <int R>
+__device__ __forceinline__ float row_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, true));   // quad [1,0,3,2]
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, true));   // quad [2,3,0,1]
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, true));  // row_half_mirror
+  if constexpr (R == 16)
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, true));  // row_mirror
+  return x;
+}
+
+// The rows of a token are walked in groups of kPasses passes of ROWS rows; every
+// load of a group is issued before its first row is reduced, so that a wave keeps
+// several passes of q/k in flight.  Rows past the last one re-read it and are not
+// written.
+constexpr int kPasses = 4;
+
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void qknorm_rope_kernel(void *__restrict__ qp, void *__restrict__ kp, int B, int T,
+                                                          int H, int KV, const int32_t *__restrict__ pos_offset,
+                                                          InvFreq inv_freq, float eps, float gain) {
+  constexpr int R = D / 8;          // lanes per row
+  constexpr int ROWS = 64 / R;      // rows per wave pass
+  const int lane = threadIdx.x & 63;
+  const int slot = lane / R;        // row slot within the pass
+  const int r = lane % R;           // which 4-pair group of the row
+  const int j0 = 4 * r;
+  double w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = inv_freq.v[j0 + i];
+
+  const long long ntok = (long long)B * T;
+  const long long wave = ((long long)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const long long nwaves = ((long long)gridDim.x * blockDim.x) >> 6;
+  const int nrows = H + KV;
+
+  for (long long tok = wave; tok < ntok; tok += nwaves) {
+    const int b = (int)(tok / T);
+    const int t = (int)(tok % T);
+    float c[4], s[4];
+    rope_cos_sin((double)((pos_offset ? pos_offset[b] : 0) + t), w, c, s);
+    for (int row0 = 0; row0 < nrows; row0 += ROWS * kPasses) {
+      float a[kPasses][4], bb[kPasses][4];
+      long long off[kPasses];
+#pragma unroll
+      for (int p = 0; p < kPasses; ++p) {
+        const int row = min(row0 + p * ROWS + slot, nrows - 1);
+        off[p] = row < H ? ((long long)tok * H + row) * D : ((long long)tok * KV + (row - H)) * D;
+        load_pairs<D, BF16>(row < H ? qp : kp, off[p], j0, a[p], bb[p]);
+      }
+#pragma unroll
+      for (int p = 0; p < kPasses; ++p) {
+        const int row = row0 + p * ROWS + slot;
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ss += a[p][i] * a[p][i] + bb[p][i] * bb[p][i];
+        ss = row_sum<R>(ss);
+        const float inv = gain / sqrtf(ss / (float)D + eps);
+        float ya[4], yb[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float xa = a[p][i] * inv, xb = bb[p][i] * inv;
+          ya[i] = xa * c[i] - xb * s[i];
+          yb[i] = xa * s[i] + xb * c[i];
+        }
+        if (row < nrows) store_pairs<D, BF16>(row < H ? qp : kp, off[p], j0, ya, yb);
+      }
+    }
+  }
+}
+
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void qknorm_rope_bwd_kernel(void *__restrict__ dqp, void *__restrict__ dkp,
                                                               const void *__restrict__ qp,
                                                               const void *__restrict__ kp, int B, int T, int H,
                                                               int KV, const int32_t *__restrict__ pos_offset,
                                                               InvFreq inv_freq, float eps, float gain) {
-  constexpr int R = D / 8;          // lanes per row
-  constexpr int ROWS = 64 / R;      // rows per wave pass
+  constexpr int R = D / 8;
+  constexpr int ROWS = 64 / R;
   const int lane = threadIdx.x & 63;
   const int slot = lane / R;
   const int r = lane % R;
@@ -171,53 +174,47 @@ __global__ __launch_bounds__(256) void qknorm_rope_bwd_kernel(void *__restrict__
   const long long wave = ((long long)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
   const long long nwaves = ((long long)gridDim.x * blockDim.x) >> 6;
   const int nrows = H + KV;
-  const double two_pi = 6.283185307179586;
 
   for (long long tok = wave; tok < ntok; tok += nwaves) {
     const int b = (int)(tok / T);
     const int t = (int)(tok % T);
-    const double pos = (double)((pos_offset ? pos_offset[b] : 0) + t);
     float c[4], s[4];
+    rope_cos_sin((double)((pos_offset ? pos_offset[b] : 0) + t), w, c, s);
+    for (int row0 = 0; row0 < nrows; row0 += ROWS * kPasses) {
+      float xa[kPasses][4], xb[kPasses][4], ga[kPasses][4], gb[kPasses][4];
+      long long off[kPasses];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      double th = pos * w[i];
-      th -= two_pi * rint(th / two_pi);
-      const float tf = (float)th;
-      s[i] = sinf(tf);
-      c[i] = cosf(tf);
-    }
-    for (int row0 = 0; row0 < nrows; row0 += ROWS) {
-      const int row = row0 + slot;
-      if (row >= nrows) break;
-      const bool isq = row < H;
-      const long long off = isq ? ((long long)tok * H + row) * D : ((long long)tok * KV + (row - H)) * D;
-      float xa[4], xb[4], ga[4], gb[4];
-      load_pairs<D, BF16>(isq ? qp : kp, off, j0, xa, xb);
-      load_pairs<D, BF16>(isq ? dqp : dkp, off, j0, ga, gb);
-      float na[4], nb[4];
-      float ss = 0.f, dot = 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        na[i] = ga[i] * c[i] + gb[i] * s[i];   // rotation by -theta
-        nb[i] = gb[i] * c[i] - ga[i] * s[i];
-        ss += xa[i] * xa[i] + xb[i] * xb[i];
-        dot += na[i] * xa[i] + nb[i] * xb[i];
+      for (int p = 0; p < kPasses; ++p) {
+        const int row = min(row0 + p * ROWS + slot, nrows - 1);
+        off[p] = row < H ? ((long long)tok * H + row) * D : ((long long)tok * KV + (row - H)) * D;
+        load_pairs<D, BF16>(row < H ? qp : kp, off[p], j0, xa[p], xb[p]);
+        load_pairs<D, BF16>(row < H ? dqp : dkp, off[p], j0, ga[p], gb[p]);
       }
 #pragma unroll
-      for (int m = 1; m < R; m <<= 1) {
-        ss += shfl_xor(ss, m);
-        dot += shfl_xor(dot, m);
-      }
-      const float r2 = ss / (float)D + eps;
-      const float g_r = gain / sqrtf(r2);
-      const float coef = dot / ((float)D * r2);
-      float da[4], db[4];
+      for (int p = 0; p < kPasses; ++p) {
+        const int row = row0 + p * ROWS + slot;
+        float na[4], nb[4];
+        float ss = 0.f, dot = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        da[i] = g_r * (na[i] - xa[i] * coef);
-        db[i] = g_r * (nb[i] - xb[i] * coef);
+        for (int i = 0; i < 4; ++i) {
+          na[i] = ga[p][i] * c[i] + gb[p][i] * s[i];  // rotation by -theta
+          nb[i] = gb[p][i] * c[i] - ga[p][i] * s[i];
+          ss += xa[p][i] * xa[p][i] + xb[p][i] * xb[p][i];
+          dot += na[i] * xa[p][i] + nb[i] * xb[p][i];
+        }
+        ss = row_sum<R>(ss);
+        dot = row_sum<R>(dot);
+        const float r2 = ss / (float)D + eps;
+        const float g_r = gain / sqrtf(r2);
+        const float coef = dot / ((float)D * r2);
+        float da[4], db[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          da[i] = g_r * (na[i] - xa[p][i] * coef);
+          db[i] = g_r * (nb[i] - xb[p][i] * coef);
+        }
+        if (row < nrows) store_pairs<D, BF16>(row < H ? dqp : dkp, off[p], j0, da, db);
       }
-      store_pairs<D, BF16>(isq ? dqp : dkp, off, j0, da, db);
     }
   }
 }
@@ -226,7 +223,7 @@ hipError_t launch_qknorm_rope_bwd(void *dq, void *dk, const void *q, const void 
                                   int D, const int32_t *pos_offset, const double *inv_freq_host, float eps,
                                   float gain, bool bf16, hipStream_t s) {
   InvFreq f;
-  for (int j = 0; j < 64; ++j) f.v[j] = j < D / 2 ? inv_freq_host[j] : 0.0;
+  for (int j = 0; j < 64; ++j) f.v[j] = j < D / 2 ? inv_freq_host[j] / 6.283185307179586 : 0.0;
   const long long ntok = (long long)B * T;
   long long blocks = (ntok + 3) / 4;
   if (blocks > 4096) blocks = 4096;
@@ -244,7 +241,7 @@ hipError_t launch_qknorm_rope_bwd(void *dq, void *dk, const void *q, const void 
 hipError_t launch_qknorm_rope(void *q, void *k, int B, int T, int H, int KV, int D, const int32_t *pos_offset,
                               const double *inv_freq_host, float eps, float gain, bool bf16, hipStream_t s) {
   InvFreq f;
-  for (int j = 0; j < 64; ++j) f.v[j] = j < D / 2 ? inv_freq_host[j] : 0.0;
+  for (int j = 0; j < 64; ++j) f.v[j] = j < D / 2 ? inv_freq_host[j] / 6.283185307179586 : 0.0;
   const long long ntok = (long long)B * T;
   // 4 waves per block; enough blocks to fill 256 CUs several times, each wave
   // then walks several tokens so its per-lane setup is amortised.
