@@ -30,6 +30,7 @@ from .attention import (  # noqa: F401
     attn_fwd,
     attn_bwd,
     decode,
+    prefill,
     window_sizes,
     attn_flops,
     decode_bytes,

@@ -287,6 +287,47 @@ def decode(q, k_new, v_new, k_cache, v_cache, cache_seqlens, window_left=-1, sof
     return o, lse, kc, vc
 
 
+def prefill(q, k_new, v_new, k_cache, v_cache, cache_seqlens, window_left=-1, softmax_scale=None):
+    """Chunked prefill against the KV cache (multi-token decode).
+
+    For each sequence b with s = cache_seqlens[b]: write the chunk's keys and
+    values k_new[b, i], v_new[b, i] into cache slots s + i, then attend query
+    q[b, i] (position s + i) over keys [max(0, s + i - W), s + i] of the updated
+    cache ("nanochat Admin & Developer Guide", section 6: chunked inference
+    against the cache through the fallback path; section 7: the cache updated in
+    place at each sequence's position).  q [B][Tn][H][D], k_new/v_new
+    [B][Tn][KV][D], caches [B][T_max][KV][D].  Returns (o [B][Tn][H][D],
+    lse [B][H][Tn], k_cache', v_cache') with the caches as updated copies.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k_new = np.asarray(k_new, dtype=np.float64)
+    v_new = np.asarray(v_new, dtype=np.float64)
+    kc = np.array(k_cache, dtype=np.float64, copy=True)
+    vc = np.array(v_cache, dtype=np.float64, copy=True)
+    B, Tn, H, D = q.shape
+    KV = k_new.shape[2]
+    G = H // KV
+    scale = _scale(D, softmax_scale)
+    o = np.empty((B, Tn, H, D))
+    lse = np.empty((B, H, Tn))
+    for b in range(B):
+        s_b = int(cache_seqlens[b])
+        kc[b, s_b:s_b + Tn] = k_new[b]
+        vc[b, s_b:s_b + Tn] = v_new[b]
+        for i in range(Tn):
+            p = s_b + i
+            lo = 0 if window_left < 0 else max(0, p - window_left)
+            for h in range(H):
+                kh = h // G
+                sc = scale * (kc[b, lo:p + 1, kh, :] @ q[b, i, h, :])
+                m = sc.max()
+                e = np.exp(sc - m)
+                z = e.sum()
+                o[b, i, h, :] = (e / z) @ vc[b, lo:p + 1, kh, :]
+                lse[b, h, i] = m + np.log(z)
+    return o, lse, kc, vc
+
+
 # --------------------------------------------------------------------------
 # Window schedule and work accounting
 # --------------------------------------------------------------------------

@@ -353,6 +353,47 @@ def test_qknorm_rope_bwd_planted_mistakes():
     assert not np.allclose(no_projection, num, atol=1e-6)
 
 
+# ----------------------------------------------------------------- chunked prefill
+
+@pytest.mark.parametrize("W", [-1, 0, 3, 9])
+def test_prefill_equals_rows_of_full_forward(W):
+    """Prefill of a chunk after s cached tokens = rows s.. of the forward over the
+    whole sequence (the forward itself pinned to torch SDPA above)."""
+    B, H, KV, D, Tn, T_max = 3, 4, 2, 8, 5, 24
+    lens = [0, 7, 19]
+    full_q, full_k, full_v = rand(B, T_max, H, D), rand(B, T_max, KV, D), rand(B, T_max, KV, D)
+    q = np.stack([full_q[b, lens[b]:lens[b] + Tn] for b in range(B)])
+    kn = np.stack([full_k[b, lens[b]:lens[b] + Tn] for b in range(B)])
+    vn = np.stack([full_v[b, lens[b]:lens[b] + Tn] for b in range(B)])
+    kc = np.full((B, T_max, KV, D), np.nan)
+    vc = np.full((B, T_max, KV, D), np.nan)
+    for b in range(B):
+        kc[b, :lens[b]] = full_k[b, :lens[b]]
+        vc[b, :lens[b]] = full_v[b, :lens[b]]
+    o, lse, kc2, vc2 = oracle.prefill(q, kn, vn, kc, vc, np.array(lens), W)
+    for b in range(B):
+        T = lens[b] + Tn
+        ref = sdpa_ref(full_q[b:b + 1, :T], full_k[b:b + 1, :T], full_v[b:b + 1, :T], W)[0, lens[b]:]
+        np.testing.assert_allclose(o[b], ref, atol=1e-12)
+        _, rl = oracle.attn_fwd(full_q[b:b + 1, :T], full_k[b:b + 1, :T], full_v[b:b + 1, :T], W)
+        np.testing.assert_allclose(lse[b], rl[0][:, lens[b]:], atol=1e-12)
+        np.testing.assert_array_equal(kc2[b, lens[b]:lens[b] + Tn], kn[b])
+        assert np.all(np.isnan(kc2[b, lens[b] + Tn:]))
+
+
+def test_prefill_of_one_token_is_decode():
+    B, H, KV, D, T_max = 2, 4, 1, 8, 12
+    q, kn, vn = rand(B, 1, H, D), rand(B, 1, KV, D), rand(B, 1, KV, D)
+    kc, vc = rand(B, T_max, KV, D), rand(B, T_max, KV, D)
+    lens = np.array([3, 11])
+    for W in (-1, 2):
+        o1, l1, k1, v1 = oracle.prefill(q, kn, vn, kc, vc, lens, W)
+        o2, l2, k2, v2 = oracle.decode(q, kn, vn, kc, vc, lens, W)
+        np.testing.assert_allclose(o1, o2, atol=1e-14)
+        np.testing.assert_allclose(l1[:, :, 0], l2, atol=1e-14)
+        np.testing.assert_array_equal(k1, k2)
+
+
 # ----------------------------------------------------------------- planted mistakes
 
 def test_planted_mistakes_are_caught(monkeypatch):
