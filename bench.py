@@ -237,6 +237,34 @@ def main():
     detail["qknorm_rope_bwd"] = {"us": round(qb_us, 2), "GBps": round(qb_gbps, 1),
                                  "frac_hbm": round(qb_gbps / PEAK_HBM_GBPS, 4), "algorithmic_bytes": 3 * (qk_bytes // 2)}
 
+    prefill = None
+    if not args.no_decode:
+        from workloads import PREFILL, prefill_inputs
+        c = PREFILL
+        qp, knp, vnp, kcp, vcp, lensp = (x.to(dev) for x in prefill_inputs(
+            c.B, c.Tn, c.H, c.KV, c.D, c.min_len, c.max_len, c.T_max, seed=c.seed, poison=False))
+        op = torch.empty_like(qp)
+        lens_h = lensp.cpu().tolist()
+        prefill = {}
+        for W in c.windows:
+            for _ in range(3):
+                nc.prefill(qp, knp, vnp, kcp, vcp, lensp, window=W, out=op)
+            torch.cuda.synchronize()
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+            for a, b_ in evs:
+                a.record(stream)
+                nc.prefill(qp, knp, vnp, kcp, vcp, lensp, window=W, out=op)
+                b_.record(stream)
+            torch.cuda.synchronize()
+            us = sum(a.elapsed_time(b_) for a, b_ in evs) * 1e3 / len(evs)
+            pairs = sum(min(s_ + i + 1, W + 1) if W >= 0 else s_ + i + 1 for s_ in lens_h for i in range(c.Tn))
+            flops = 4 * c.D * pairs * c.H
+            tf = flops / (us * 1e-6) / 1e12
+            prefill["L" if W < 0 else "S"] = {"window": W, "us": round(us, 2), "tflops": round(tf, 1),
+                                              "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                                              "workload": c.name}
+        del qp, knp, vnp, kcp, vcp
+
     decode = None
     if not args.no_decode:
         c = DECODE
@@ -278,6 +306,7 @@ def main():
                    "head_dim": D, "windows": list(cfg.windows), "parallelism": "single GPU"},
         "roofline": roof,
         "decode": decode,
+        "prefill": prefill,
         "detail": detail,
     }
     if args.copy_probe_mib > 0:

@@ -183,6 +183,27 @@ int ncattn_decode(const void *q, const void *k_new, const void *v_new,
                   int window_left, float softmax_scale, int dtype,
                   void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Chunked prefill against a KV cache (multi-token decode; "nanochat Admin &
+ * Developer Guide", section 6: chunked inference against the cache; section 7:
+ * the cache updated in place).  For every sequence b with s = cache_seqlens[b]:
+ *   1. k_new[b, i], v_new[b, i] are written into cache rows s + i (in place);
+ *   2. o[b, i] = softmax(scale * q[b, i] . K[j]) V[j] over
+ *      j in [max(0, s + i - W), s + i] (all of [0, s + i] when window_left < 0).
+ *   q [B][Tn][n_head][D], k_new, v_new [B][Tn][n_kv_head][D],
+ *   k_cache, v_cache [B][T_max][n_kv_head][D] (bf16), cache_seqlens device
+ *   int32 [B] (NOT advanced: the caller owns the position),
+ *   o [B][Tn][n_head][D] bf16, lse [B][n_head][Tn] fp32 or NULL.
+ *   Precondition 0 <= cache_seqlens[b] <= T_max - Tn (not checkable on the host
+ *   without a sync): a sequence that breaks it is skipped, its cache is left
+ *   untouched and its rows of o (and lse) are NaN.
+ *   Supported: bf16, head_dim 128; no workspace.
+ */
+int ncattn_prefill(const void *q, const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                   const int32_t *cache_seqlens, void *o, float *lse, int B, int Tn, int T_max,
+                   int n_head, int n_kv_head, int head_dim, int window_left, float softmax_scale,
+                   int dtype, void *stream);
+
 /* Thread-local description of the last non-OK return on this thread ("" if none). */
 const char *ncattn_last_error(void);
 

@@ -144,6 +144,24 @@ def test_decode_validation_and_workspace(L):
     assert L.ncattn_decode(*bad, 0, P + 256, ws, None) == EUNSUP
 
 
+def test_prefill_validation(L):
+    f = L.ncattn_prefill
+    def call(q=P, kn=P + 16, vn=P + 32, kc=P + 48, vc=P + 64, lens=P + 80, o=P + 96, lse=None, Tn=8, T_max=64,
+             D=128, W=-1, dt=0):
+        return f(q, kn, vn, kc, vc, lens, o, lse, 2, Tn, T_max, 2, 2, D, W, 0.0, dt, None)
+    assert call(q=None) == EINVAL
+    assert call(lens=None) == EINVAL
+    assert call(lens=P + 82) == EINVAL
+    assert call(lse=P + 2) == EINVAL
+    assert call(Tn=0) == EINVAL
+    assert call(Tn=65) == EINVAL
+    assert call(W=-3) == EINVAL
+    assert call(kc=P + 64) == EINVAL          # k_cache == v_cache
+    assert call(o=P) == EINVAL                # o aliases q
+    assert call(dt=1) == EUNSUP
+    assert call(D=64) == EUNSUP
+
+
 def test_window_sizes_binding_golden():
     g = json.load(open(os.path.join(ROOT, "tests", "golden", "window_schedule.json")))
     for c in g["cases"]:

@@ -15,7 +15,7 @@ import oracle
 import transformer_attention_qknorm_amd as nc
 from conftest import tol_check
 from parity_util import LSE_TOL, TOL, check, check_lse, f64
-from workloads import attn_inputs, decode_inputs
+from workloads import attn_inputs, decode_inputs, prefill_inputs
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -264,3 +264,68 @@ def test_decode_deterministic():
         o2 = nc.decode(q, kn, vn, kc, vc, lens, window=W)
         torch.cuda.synchronize()
         assert torch.equal(o1, o2)
+
+
+# ------------------------------------------------------------------ chunked prefill
+
+PREFILL_CASES = [
+    # B, Tn, H, KV, min_len, max_len, T_max, W
+    (3, 1, 4, 2, 0, 100, 160, -1),
+    (3, 7, 4, 2, 0, 100, 160, -1),
+    (2, 64, 2, 2, 0, 200, 300, 50),
+    (2, 130, 6, 2, 60, 300, 512, -1),
+    (2, 200, 2, 1, 0, 0, 256, 0),
+    (2, 65, 4, 4, 500, 700, 800, 128),
+    (1, 257, 2, 2, 1, 1, 258, 1000),
+]
+
+
+@pytest.mark.parametrize("case", PREFILL_CASES, ids=[_ids(c) for c in PREFILL_CASES])
+def test_prefill(case):
+    B, Tn, H, KV, lo, hi, T_max, W = case
+    say(f"prefill {case}")
+    q, kn, vn, kc, vc, lens = prefill_inputs(B, Tn, H, KV, 128, lo, hi, T_max, seed=31 + Tn)
+    ro, rlse, rkc, rvc = oracle.prefill(f64(q), f64(kn), f64(vn), f64(kc), f64(vc), lens.numpy(), W)
+    qd, knd, vnd, kcd, vcd, lensd = to_dev(q, kn, vn, kc, vc, lens)
+    o, lse = nc.prefill(qd, knd, vnd, kcd, vcd, lensd, window=W, return_lse=True)
+    torch.cuda.synchronize()
+    check(o, ro, "bf16", "o")
+    check_lse(lse, rlse, "bf16", "lse")
+    # the chunk lands in the cache bit for bit; every other slot keeps its bits (NaN poison included)
+    for b in range(B):
+        s_ = int(lens[b])
+        assert torch.equal(kcd[b, s_:s_ + Tn].cpu().view(torch.int16), kn[b].view(torch.int16))
+        assert torch.equal(vcd[b, s_:s_ + Tn].cpu().view(torch.int16), vn[b].view(torch.int16))
+        keep = torch.ones(T_max, dtype=torch.bool)
+        keep[s_:s_ + Tn] = False
+        assert torch.equal(kcd[b, keep].cpu().view(torch.int16), kc[b, keep].view(torch.int16))
+        assert torch.equal(vcd[b, keep].cpu().view(torch.int16), vc[b, keep].view(torch.int16))
+
+
+def test_prefill_from_empty_cache_is_the_forward():
+    """With empty caches, prefill of a whole sequence runs the forward kernel on the
+    same rows: the outputs are bitwise those of ncattn_fwd."""
+    B, T, H, KV, D = 2, 300, 4, 2, 128
+    q, k, v, _ = to_dev(*attn_inputs(B, T, H, KV, D, "bf16", seed=41))
+    for W in (-1, 77):
+        o_f, lse_f = nc.fwd(q, k, v, window=(W, 0))
+        kc = torch.zeros(B, T + 20, KV, D, dtype=torch.bfloat16, device=DEV)
+        vc = torch.zeros_like(kc)
+        lens = torch.zeros(B, dtype=torch.int32, device=DEV)
+        o_p, lse_p = nc.prefill(q, k, v, kc, vc, lens, window=W, return_lse=True)
+        torch.cuda.synchronize()
+        assert torch.equal(o_p, o_f) and torch.equal(lse_p, lse_f)
+
+
+def test_prefill_invalid_lengths_give_nan_and_leave_cache():
+    B, Tn, H, KV, T_max = 3, 10, 2, 2, 64
+    q, kn, vn, kc, vc, lens = prefill_inputs(B, Tn, H, KV, 128, 0, 20, T_max, seed=8, poison=False)
+    lens = torch.tensor([5, T_max - Tn + 1, -1], dtype=torch.int32)
+    qd, knd, vnd, kcd, vcd, lensd = to_dev(q, kn, vn, kc, vc, lens)
+    o, lse = nc.prefill(qd, knd, vnd, kcd, vcd, lensd, window=-1, return_lse=True)
+    torch.cuda.synchronize()
+    ro, rlse, _, _ = oracle.prefill(f64(q[:1]), f64(kn[:1]), f64(vn[:1]), f64(kc[:1]), f64(vc[:1]), [5], -1)
+    check(o[:1], ro, "bf16", "o valid row")
+    assert torch.isnan(o[1:].float()).all() and torch.isnan(lse[1:]).all()
+    for b in (1, 2):
+        assert torch.equal(kcd[b].cpu(), kc[b]) and torch.equal(vcd[b].cpu(), vc[b])

@@ -62,9 +62,11 @@ def lib():
     L.ncattn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     L.ncattn_decode_workspace_bytes.restype = sz
     L.ncattn_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp, sz, vp]
+    L.ncattn_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp]
     L.ncattn_last_error.restype = ctypes.c_char_p
     L.ncattn_version.restype = ctypes.c_char_p
-    for fn in ("ncattn_qknorm_rope", "ncattn_qknorm_rope_bwd", "ncattn_fwd", "ncattn_bwd", "ncattn_decode"):
+    for fn in ("ncattn_qknorm_rope", "ncattn_qknorm_rope_bwd", "ncattn_fwd", "ncattn_bwd", "ncattn_decode",
+               "ncattn_prefill"):
         getattr(L, fn).restype = i32
     _lib = L
     return L
@@ -264,6 +266,38 @@ def decode(q, k_new, v_new, k_cache, v_cache, cache_seqlens, window=-1, softmax_
                              _ptr(o), _ptr(lse), B, T_max, H, KV, D, wl, _scale(softmax_scale), dt, _ptr(ws),
                              ws.numel(), _stream(dev))
     _check("ncattn_decode", rc)
+    return (o, lse) if return_lse else o
+
+
+def prefill(q, k_new, v_new, k_cache, v_cache, cache_seqlens, window=-1, softmax_scale=None, return_lse=False,
+            out=None):
+    """Chunked prefill: writes the chunk k_new/v_new [B][Tn][KV][D] into cache rows
+    cache_seqlens[b].. in place, then attends q [B][Tn][H][D] (positions
+    cache_seqlens[b] + i) over the cache.  caches [B][T_max][KV][D] (bf16),
+    cache_seqlens int32 [B] (not advanced).  Returns o [B][Tn][H][D] (and lse
+    [B][H][Tn])."""
+    dev = _dev(q, k_new, v_new, k_cache, v_cache, cache_seqlens)
+    B, Tn, H, D = q.shape
+    T_max, KV = k_cache.shape[1], k_cache.shape[2]
+    if k_new.shape != (B, Tn, KV, D) or v_new.shape != (B, Tn, KV, D) or k_cache.shape != v_cache.shape \
+            or k_cache.shape[0] != B or k_cache.shape[3] != D:
+        raise ValueError("ncattn.prefill: inconsistent shapes")
+    if cache_seqlens.dtype != torch.int32 or cache_seqlens.numel() != B:
+        raise ValueError("ncattn.prefill: cache_seqlens must be int32 [B]")
+    wl = window if isinstance(window, int) else _window(window)[0]
+    if out is None:
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, Tn), dtype=torch.float32, device=dev) if return_lse else None
+    else:
+        o, lse = out if isinstance(out, tuple) else (out, None)
+        _dev(o)
+        if o.shape != q.shape or o.dtype != q.dtype:
+            raise ValueError("ncattn.prefill: out must be like q")
+    with torch.cuda.device(dev):
+        rc = lib().ncattn_prefill(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                                  _ptr(cache_seqlens), _ptr(o), _ptr(lse), B, Tn, T_max, H, KV, D, wl,
+                                  _scale(softmax_scale), _dtype_code(q), _stream(dev))
+    _check("ncattn_prefill", rc)
     return (o, lse) if return_lse else o
 
 

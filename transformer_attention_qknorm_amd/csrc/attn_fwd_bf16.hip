@@ -142,7 +142,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const uint16_t *_
                                                                const uint16_t *__restrict__ K,
                                                                const uint16_t *__restrict__ V,
                                                                uint16_t *__restrict__ O, float *__restrict__ LSE,
-                                                               int B, int T, int H, int KV, int W, float scale) {
+                                                               const int32_t *__restrict__ q_pos0, int B, int Tq,
+                                                               int Tk, int H, int KV, int W, float scale) {
   // Two-slot rings for K and V, each slot its own LDS object so the compiler can
   // tell a copy into one slot from reads of the other.
   __shared__ __attribute__((aligned(1024))) char kb0[kTileBytes];
@@ -153,50 +154,66 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const uint16_t *_
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int nqb = (T + kBlockM - 1) / kBlockM;
+  const int nqb = (Tq + kBlockM - 1) / kBlockM;
   const int BH = B * H;
   const int qblk = nqb - 1 - (int)(blockIdx.x / BH);
   const int bh = (int)(blockIdx.x % BH);
   const int b = bh / H;
   const int h = bh % H;
   const int kvh = h / (H / KV);
-  const int q0 = qblk * kBlockM;
+  const int q0 = qblk * kBlockM;  // query rows of the block (index into Q / O)
   const int qw0 = q0 + 32 * wave;
-  const int q_lane = qw0 + (lane & 31);
   const int hh = lane >> 5;
   const float c = scale * kLog2e;
-
   const long long q_stride = (long long)H * kD;
   const long long kv_stride = (long long)KV * kD;
-  const uint16_t *Kb = K + (long long)b * T * kv_stride + (long long)kvh * kD;
-  const uint16_t *Vb = V + (long long)b * T * kv_stride + (long long)kvh * kD;
-  const TileSrc ksrc = make_tile_src(Kb, kv_stride, T);
-  const TileSrc vsrc = make_tile_src(Vb, kv_stride, T);
+
+  // Query row r sits at position s0 + r of a sequence whose keys are rows
+  // [0, s0 + Tq) of K / V (s0 = 0 for a whole sequence; the cache length before a
+  // chunk for a prefill, which must leave the chunk inside the Tk rows).
+  const int s0 = q_pos0 ? q_pos0[b] : 0;
+  if (s0 < 0 || s0 > Tk - Tq) {
+    // invalid cache length: this block's rows of o and lse are NaN
+    const int qr = qw0 + (lane & 31);
+    if (qr < Tq) {
+      uint16_t *op = O + ((long long)b * Tq + qr) * q_stride + (long long)h * kD;
+      for (int d = 4 * hh; d < kD; d += 8) *(u32x2 *)(op + d) = u32x2{0x7fc07fc0u, 0x7fc07fc0u};
+      if (hh == 0 && LSE) LSE[((long long)b * H + h) * Tq + qr] = __builtin_nanf("");
+    }
+    return;
+  }
+  const int nkeys = s0 + Tq;
+  const int q_lane = s0 + qw0 + (lane & 31);  // position of this lane's query
+  const int pw0 = s0 + qw0;                   // position of the wave's first query
+  const uint16_t *Kb = K + (long long)b * Tk * kv_stride + (long long)kvh * kD;
+  const uint16_t *Vb = V + (long long)b * Tk * kv_stride + (long long)kvh * kD;
+  const TileSrc ksrc = make_tile_src(Kb, kv_stride, nkeys);
+  const TileSrc vsrc = make_tile_src(Vb, kv_stride, nkeys);
   const int voff = tile_lane_voff(ksrc.stride, tid);
 
-  // tiles of the block, and the contiguous range of them this wave needs
-  const int q_last_blk = min(q0 + kBlockM - 1, T - 1);
-  const int t0 = (W < 0 ? 0 : max(0, q0 - W)) / kTileN;
-  const int t1 = q_last_blk / kTileN;
-  const int qw_last = min(qw0 + 31, T - 1);
-  const bool wave_active = qw0 < T;
-  const int tw0 = max(t0, (W < 0 ? 0 : max(0, qw0 - W)) / kTileN);
-  const int tw1 = wave_active ? qw_last / kTileN : t0 - 1;  // empty range if inactive
+  // key tiles of the block, and the contiguous range of them this wave needs
+  const int p_last_blk = s0 + min(q0 + kBlockM - 1, Tq - 1);
+  const int t0 = (W < 0 ? 0 : max(0, s0 + q0 - W)) / kTileN;
+  const int t1 = p_last_blk / kTileN;
+  const int pw_last = s0 + min(qw0 + 31, Tq - 1);
+  const bool wave_active = qw0 < Tq;
+  const int tw0 = max(t0, (W < 0 ? 0 : max(0, pw0 - W)) / kTileN);
+  const int tw1 = wave_active ? pw_last / kTileN : t0 - 1;  // empty range if inactive
   auto in_range = [&](int t) { return t >= tw0 && t <= tw1; };
   auto masked = [&](int t) {
     const int k0 = t * kTileN;
-    return !(k0 + kTileN - 1 <= qw0 && (W < 0 || qw_last - k0 <= W));
+    return !(k0 + kTileN - 1 <= pw0 && (W < 0 || pw_last - k0 <= W));
   };
 
   tile_load_lds(kb0, ksrc, voff, t0 * kTileN);
   tile_load_lds(vb0, vsrc, voff, t0 * kTileN);
   if (t0 + 1 <= t1) tile_load_lds(kb1, ksrc, voff, (t0 + 1) * kTileN);
 
-  // Q^T operand in registers: lane holds q row q_lane, d = 16 s + 8 hh + [0, 8).
+  // Q^T operand in registers: lane holds the query of row qw0 + l%32, d = 16 s + 8 hh + [0, 8).
   bf16x8 qreg[8];
   {
-    const int qr = min(q_lane, T - 1);
-    const uint16_t *qp = Q + ((long long)b * T + qr) * q_stride + (long long)h * kD + 8 * hh;
+    const int qr = min(qw0 + (lane & 31), Tq - 1);
+    const uint16_t *qp = Q + ((long long)b * Tq + qr) * q_stride + (long long)h * kD + 8 * hh;
 #pragma unroll
     for (int s = 0; s < 8; ++s) qreg[s] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qp + 16 * s));
   }
@@ -277,8 +294,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const uint16_t *_
   if (!wave_active) return;
   const float l_tot = st.l_run + shfl_xor(st.l_run, 32);
   const float inv_l = 1.f / l_tot;
-  if (q_lane < T) {
-    uint16_t *op = O + ((long long)b * T + q_lane) * q_stride + (long long)h * kD;
+  const int qr = qw0 + (lane & 31);
+  if (qr < Tq) {
+    uint16_t *op = O + ((long long)b * Tq + qr) * q_stride + (long long)h * kD;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -289,21 +307,26 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const uint16_t *_
         w[1] = pack_bf16x2(st.oacc[db][4 * i + 2] * inv_l, st.oacc[db][4 * i + 3] * inv_l);
         *(u32x2 *)(op + d) = w;
       }
-    if (hh == 0) LSE[((long long)b * H + h) * T + q_lane] = st.m_ref * scale + logf(l_tot);
+    if (hh == 0 && LSE) LSE[((long long)b * H + h) * Tq + qr] = st.m_ref * scale + logf(l_tot);
   }
 }
 
 }  // namespace
 
-hipError_t launch_fwd_bf16(const void *q, const void *k, const void *v, void *o, float *lse, const AttnShape &sh,
-                           hipStream_t s) {
-  const int nqb = (sh.T + kBlockM - 1) / kBlockM;
-  const long long blocks = (long long)nqb * sh.B * sh.H;
+hipError_t launch_fwd_bf16_rows(const void *q, const void *k, const void *v, void *o, float *lse,
+                                const int32_t *q_pos0, int B, int Tq, int Tk, int H, int KV, int W, float scale,
+                                hipStream_t s) {
+  const int nqb = (Tq + kBlockM - 1) / kBlockM;
+  const long long blocks = (long long)nqb * B * H;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL(attn_fwd_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (const uint16_t *)q,
-                     (const uint16_t *)k, (const uint16_t *)v, (uint16_t *)o, lse, sh.B, sh.T, sh.H, sh.KV, sh.window,
-                     sh.scale);
+                     (const uint16_t *)k, (const uint16_t *)v, (uint16_t *)o, lse, q_pos0, B, Tq, Tk, H, KV, W, scale);
   return hipGetLastError();
+}
+
+hipError_t launch_fwd_bf16(const void *q, const void *k, const void *v, void *o, float *lse, const AttnShape &sh,
+                           hipStream_t s) {
+  return launch_fwd_bf16_rows(q, k, v, o, lse, nullptr, sh.B, sh.T, sh.T, sh.H, sh.KV, sh.window, sh.scale, s);
 }
 
 }  // namespace ncattn

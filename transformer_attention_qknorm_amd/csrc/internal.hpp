@@ -53,6 +53,13 @@ size_t bwd_workspace_bytes(int B, int T, int H, int W, bool bf16);
 // bf16, head_dim 128, MFMA kernels.
 hipError_t launch_fwd_bf16(const void *q, const void *k, const void *v, void *o, float *lse,
                            const AttnShape &sh, hipStream_t s);
+// The same forward for Tq query rows per sequence at positions q_pos0[b] + r
+// (q_pos0 device int32 [B], NULL for 0) over key rows [0, q_pos0[b] + Tq) of K/V
+// arrays with Tk rows per sequence; lse may be NULL.  Sequences whose offset
+// leaves the queries outside [0, Tk) get NaN rows.
+hipError_t launch_fwd_bf16_rows(const void *q, const void *k, const void *v, void *o, float *lse,
+                                const int32_t *q_pos0, int B, int Tq, int Tk, int H, int KV, int W, float scale,
+                                hipStream_t s);
 hipError_t launch_bwd_bf16(const void *q, const void *k, const void *v, const void *o,
                            const float *lse, const void *dout, void *dq, void *dk, void *dv,
                            void *workspace, const AttnShape &sh, int stages, hipStream_t s);
@@ -70,5 +77,11 @@ hipError_t launch_decode_bf16(const void *q, const void *k_new, const void *v_ne
                               void *v_cache, const int32_t *seqlens, void *o, float *lse, int B,
                               int T_max, int H, int KV, int D, int window, float scale,
                               void *workspace, hipStream_t s);
+
+// Chunked prefill, bf16, head_dim 128: append k_new/v_new [B][Tn][KV][D] at
+// cache rows seqlens[b].., then the forward of q [B][Tn][H][D] over the cache.
+hipError_t launch_prefill_bf16(const void *q, const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                               const int32_t *seqlens, void *o, float *lse, int B, int Tn, int T_max, int H,
+                               int KV, int window, float scale, hipStream_t s);
 
 }  // namespace ncattn

@@ -172,7 +172,6 @@ size_t ncattn_bwd_workspace_bytes(int B, int T, int n_head, int n_kv_head, int h
   if (B <= 0 || T <= 0 || n_head <= 0 || window_left < -1) return 0;
   return ncattn::bwd_workspace_bytes(B, T, n_head, window_left, dtype == NCATTN_BF16);
 }
-
 }  // extern "C"
 
 namespace {
@@ -272,6 +271,35 @@ int ncattn_decode(const void *q, const void *k_new, const void *v_new, void *k_c
   hipError_t e = ncattn::launch_decode_bf16(q, k_new, v_new, k_cache, v_cache, cache_seqlens, o, lse, B, T_max,
                                             n_head, n_kv_head, head_dim, window_left,
                                             resolve_scale(softmax_scale, head_dim), workspace, (hipStream_t)stream);
+  return hip_status(e, fn);
+}
+
+int ncattn_prefill(const void *q, const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                   const int32_t *cache_seqlens, void *o, float *lse, int B, int Tn, int T_max, int n_head,
+                   int n_kv_head, int head_dim, int window_left, float softmax_scale, int dtype, void *stream) {
+  const char *fn = "ncattn_prefill";
+  NC_PTR(q, fn);
+  NC_PTR(k_new, fn);
+  NC_PTR(v_new, fn);
+  NC_PTR(k_cache, fn);
+  NC_PTR(v_cache, fn);
+  NC_PTR(o, fn);
+  if (cache_seqlens == nullptr) return fail(NCATTN_EINVAL, "%s: cache_seqlens is NULL", fn);
+  if ((uintptr_t)cache_seqlens & 3u) return fail(NCATTN_EINVAL, "%s: cache_seqlens is not 4-byte aligned", fn);
+  if (lse != nullptr && ((uintptr_t)lse & 3u)) return fail(NCATTN_EINVAL, "%s: lse is not 4-byte aligned", fn);
+  NC_TRY(check_heads(fn, B, T_max, n_head, n_kv_head, head_dim));
+  if (Tn <= 0 || Tn > T_max) return fail(NCATTN_EINVAL, "%s: need 0 < Tn <= T_max (Tn=%d T_max=%d)", fn, Tn, T_max);
+  NC_TRY(check_dtype(fn, dtype));
+  if (window_left < -1) return fail(NCATTN_EINVAL, "%s: window_left must be >= -1 (got %d)", fn, window_left);
+  if (dtype != NCATTN_BF16) return fail(NCATTN_EUNSUPPORTED, "%s: prefill supports bf16 only", fn);
+  NC_TRY(check_attn_support(fn, dtype, T_max, n_head, head_dim));
+  if (!isfinite(softmax_scale)) return fail(NCATTN_EINVAL, "%s: softmax_scale must be finite", fn);
+  if (k_cache == v_cache) return fail(NCATTN_EINVAL, "%s: k_cache and v_cache must differ", fn);
+  if (o == q || o == k_cache || o == v_cache || o == k_new || o == v_new)
+    return fail(NCATTN_EINVAL, "%s: o must not alias an input", fn);
+  hipError_t e = ncattn::launch_prefill_bf16(q, k_new, v_new, k_cache, v_cache, cache_seqlens, o, lse, B, Tn, T_max,
+                                             n_head, n_kv_head, window_left, resolve_scale(softmax_scale, head_dim),
+                                             (hipStream_t)stream);
   return hip_status(e, fn);
 }
 

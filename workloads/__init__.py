@@ -56,6 +56,22 @@ class DecodeConfig:
     dtype: str = "bf16"
 
 
+@dataclass(frozen=True)
+class PrefillConfig:
+    name: str
+    B: int
+    Tn: int          # tokens of the chunk appended to every sequence
+    H: int
+    KV: int
+    D: int
+    min_len: int     # cached tokens before the chunk, U[min_len, max_len]
+    max_len: int
+    T_max: int
+    windows: tuple = (-1, 1024)
+    seed: int = 6
+    dtype: str = "bf16"
+
+
 # The five workloads: a tiny fp32 case, two nanochat-shaped layers (d12: model
 # dim 768, 6 heads; d20: 1280, 10 heads; head_dim 128, T = 2048, SSSL windows),
 # a grouped-query case at T = 4096 and an engine decode batch.
@@ -70,6 +86,11 @@ GQA = AttnConfig("gqa_b16_t4096_h12_kv4_d128_bf16", B=16, T=4096, H=12, KV=4, D=
                  pre_normed=True, seed=4)
 DECODE = DecodeConfig("decode_b64_h10_d128_bf16", B=64, H=10, KV=10, D=128,
                       min_len=256, max_len=8192, T_max=8320)
+
+# Chunked prefill (the engine path beyond single-token decode): 16 sequences with
+# 0..3584 cached tokens each receive a 512-token chunk.
+PREFILL = PrefillConfig("prefill_b16_tn512_h10_d128_bf16", B=16, Tn=512, H=10, KV=10, D=128,
+                        min_len=0, max_len=3584, T_max=4096)
 
 ATTN_CONFIGS = {c.name: c for c in (TINY, D12, D20, GQA)}
 
@@ -112,6 +133,27 @@ def decode_inputs(B, H, KV, D, min_len, max_len, T_max, seed=5, poison=True, dty
     q = rng.standard_normal((B, 1, H, D), dtype=np.float32)
     kn = rng.standard_normal((B, 1, KV, D), dtype=np.float32)
     vn = rng.standard_normal((B, 1, KV, D), dtype=np.float32)
+    out = [_to_dtype(x, dtype) for x in (q, kn, vn, kc, vc)]
+    return (*out, torch.from_numpy(lens))
+
+
+def prefill_inputs(B, Tn, H, KV, D, min_len, max_len, T_max, seed=6, poison=True, dtype="bf16"):
+    """Prefill batch: lengths L_b ~ U[min_len, max_len] (inclusive), caches
+    [B][T_max][KV][D] with slots < L_b ~ N(0, 1) and slots >= L_b NaN (poison) or
+    N(0, 1), then q [B][Tn][H][D], k_new, v_new [B][Tn][KV][D]; cache_seqlens =
+    L_b.  Returns CPU torch tensors (lengths int32)."""
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(min_len, max_len + 1, size=B).astype(np.int32)
+    assert int(lens.max()) + Tn <= T_max
+    kc = rng.standard_normal((B, T_max, KV, D), dtype=np.float32)
+    vc = rng.standard_normal((B, T_max, KV, D), dtype=np.float32)
+    if poison:
+        dead = np.arange(T_max)[None, :] >= lens[:, None]
+        kc[dead] = np.nan
+        vc[dead] = np.nan
+    q = rng.standard_normal((B, Tn, H, D), dtype=np.float32)
+    kn = rng.standard_normal((B, Tn, KV, D), dtype=np.float32)
+    vn = rng.standard_normal((B, Tn, KV, D), dtype=np.float32)
     out = [_to_dtype(x, dtype) for x in (q, kn, vn, kc, vc)]
     return (*out, torch.from_numpy(lens))
 
