@@ -17,7 +17,8 @@
 // writes it into the cache; no other chunk touches slot s, and slots past s are
 // never read (they may hold anything, NaN included).
 // decode_combine: one workgroup per (b, h) merges the chunk partials
-// (max, sum, unnormalised output) into o and lse.
+// (max, sum, unnormalised output) into o and lse: the maximum over the chunks in
+// parallel, then the weighted sums with eight chunks' loads in flight.
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -151,6 +152,7 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(const float *__rest
                                                              const int32_t *__restrict__ seqlens,
                                                              uint16_t *__restrict__ O, float *__restrict__ LSE,
                                                              int B, int T_max, int H, int W, int C_max) {
+  __shared__ float wmax[2];
   const int bh = blockIdx.x;
   const int b = bh / H;
   const int d = threadIdx.x;
@@ -163,10 +165,33 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(const float *__rest
   const int lo = W < 0 ? 0 : max(0, s - W);
   const int nc = (s - lo + 1 + kCH - 1) / kCH;
   const long long base = (long long)bh * C_max;
+  // max of the chunk maxima: threads stride over the chunks, then the two waves reduce
   float M = -INFINITY;
-  for (int ci = 0; ci < nc; ++ci) M = fmaxf(M, ws_m[base + ci]);
+  for (int ci = d; ci < nc; ci += kDD) M = fmaxf(M, ws_m[base + ci]);
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) M = fmaxf(M, shfl_xor(M, m));
+  if ((d & 63) == 0) wmax[d >> 6] = M;
+  __syncthreads();
+  M = fmaxf(wmax[0], wmax[1]);
+  // weighted sums, eight chunks' loads in flight per step
   float L = 0.f, o = 0.f;
-  for (int ci = 0; ci < nc; ++ci) {
+  int ci = 0;
+  for (; ci + 8 <= nc; ci += 8) {
+    float mm[8], ll[8], oo[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      mm[u] = ws_m[base + ci + u];
+      ll[u] = ws_l[base + ci + u];
+      oo[u] = ws_o[(base + ci + u) * kDD + d];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float a = fast_exp2(mm[u] - M);
+      L = __builtin_fmaf(ll[u], a, L);
+      o = __builtin_fmaf(oo[u], a, o);
+    }
+  }
+  for (; ci < nc; ++ci) {
     const float a = fast_exp2(ws_m[base + ci] - M);
     L = __builtin_fmaf(ws_l[base + ci], a, L);
     o = __builtin_fmaf(ws_o[(base + ci) * kDD + d], a, o);
