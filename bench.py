@@ -265,6 +265,31 @@ def main():
                                               "workload": c.name}
         del qp, knp, vnp, kcp, vcp
 
+    replicate = None
+    if not args.no_decode:
+        # prefill once, clone for the samples: a 2048-token batch-1 prompt cache
+        # copied into the 64 rows of the engine decode cache
+        from workloads import replicate_inputs
+        c, s_len = DECODE, 2048
+        ksr, vsr, kdr, vdr, slr = (x.to(dev) for x in replicate_inputs(c.B, s_len, c.T_max, c.KV, c.D, s_len, seed=9))
+        dlr = torch.empty(c.B, dtype=torch.int32, device=dev)
+        for _ in range(3):
+            nc.cache_replicate(ksr, vsr, slr, kdr, vdr, dlr)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+        for a, b_ in evs:
+            a.record(stream)
+            nc.cache_replicate(ksr, vsr, slr, kdr, vdr, dlr)
+            b_.record(stream)
+        torch.cuda.synchronize()
+        us = sum(a.elapsed_time(b_) for a, b_ in evs) * 1e3 / len(evs)
+        part = 2 * s_len * c.KV * c.D * 2            # K and V of the prompt
+        nbytes = part * (1 + c.B)                    # read once, written to every row
+        gbps = nbytes / (us * 1e-6) / 1e9
+        replicate = {"rows": c.B, "prompt_len": s_len, "us": round(us, 2), "GBps": round(gbps, 1),
+                     "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4), "algorithmic_bytes": nbytes}
+        del ksr, vsr, kdr, vdr
+
     decode = None
     if not args.no_decode:
         c = DECODE
@@ -307,6 +332,7 @@ def main():
         "roofline": roof,
         "decode": decode,
         "prefill": prefill,
+        "cache_replicate": replicate,
         "detail": detail,
     }
     if args.copy_probe_mib > 0:

@@ -204,6 +204,26 @@ int ncattn_prefill(const void *q, const void *k_new, const void *v_new, void *k_
                    int n_head, int n_kv_head, int head_dim, int window_left, float softmax_scale,
                    int dtype, void *stream);
 
+/*
+ * Replication of a batch-1 prefill cache into a batch-N decode cache ("nanochat
+ * Admin & Developer Guide", section 7, KV cache and generation flow: the prompt is
+ * prefilled once at batch 1 and its cache copied into every row of the cache the
+ * samples then decode from).  With s = src_seqlen[0] (device int32):
+ *   k_dst[n, t] = k_src[0, t] and v_dst[n, t] = v_src[0, t] for n < N, t < s;
+ *   dst_seqlens[n] = s for n < N.
+ *   k_src, v_src [1][T_src][n_kv_head][D]; k_dst, v_dst [N][T_max][n_kv_head][D],
+ *   same dtype (bf16 or fp32), 16-byte aligned, a row of n_kv_head * D elements a
+ *   multiple of 16 bytes; dst_seqlens device int32 [N].  Destination rows t >= s
+ *   are left untouched.  Requires T_src <= T_max.
+ *   Precondition 0 <= s <= T_src (a device value, not checkable on the host
+ *   without a sync): otherwise nothing is copied and every dst_seqlens[n] is set
+ *   to -1, which ncattn_decode treats as an invalid row (NaN output).
+ *   No workspace; the sources are only read.
+ */
+int ncattn_cache_replicate(const void *k_src, const void *v_src, const int32_t *src_seqlen, void *k_dst,
+                           void *v_dst, int32_t *dst_seqlens, int N, int T_src, int T_max, int n_kv_head,
+                           int head_dim, int dtype, void *stream);
+
 /* Thread-local description of the last non-OK return on this thread ("" if none). */
 const char *ncattn_last_error(void);
 

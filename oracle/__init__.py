@@ -31,6 +31,7 @@ from .attention import (  # noqa: F401
     attn_bwd,
     decode,
     prefill,
+    cache_replicate,
     window_sizes,
     attn_flops,
     decode_bytes,

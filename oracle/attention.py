@@ -328,6 +328,32 @@ def prefill(q, k_new, v_new, k_cache, v_cache, cache_seqlens, window_left=-1, so
     return o, lse, kc, vc
 
 
+def cache_replicate(k_src, v_src, src_seqlen, k_dst, v_dst):
+    """Replication of a batch-1 prefill cache into a batch-N decode cache.
+
+    With s = src_seqlen: rows [0, s) of the single source sequence are copied
+    into rows [0, s) of every destination sequence, and every destination length
+    becomes s ("nanochat Admin & Developer Guide", section 7, "KV cache": the
+    prompt is prefilled once at batch 1, then its cache is copied into each row
+    of the cache the samples decode from).  k_src, v_src [1][T_src][KV][D],
+    k_dst, v_dst [N][T_max][KV][D]; destination rows t >= s keep their contents.
+    A length outside [0, T_src] (an invalid source) copies nothing and marks
+    every destination length -1.  The copy keeps the arrays' own dtype: it moves
+    values, it computes none.  Returns (k_dst', v_dst', dst_seqlens int32 [N]).
+    """
+    kd = np.array(k_dst, copy=True)
+    vd = np.array(v_dst, copy=True)
+    N = kd.shape[0]
+    T_src = np.shape(k_src)[1]
+    s = int(src_seqlen)
+    if not 0 <= s <= T_src:
+        return kd, vd, np.full(N, -1, dtype=np.int32)
+    for n in range(N):
+        kd[n, :s] = k_src[0, :s]
+        vd[n, :s] = v_src[0, :s]
+    return kd, vd, np.full(N, s, dtype=np.int32)
+
+
 # --------------------------------------------------------------------------
 # Window schedule and work accounting
 # --------------------------------------------------------------------------

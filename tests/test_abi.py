@@ -175,3 +175,20 @@ def test_binding_fails_loudly_without_gpu_tensors():
     x = torch.zeros(1, 4, 2, 128, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         nc.fwd(x, x, x)
+
+
+def test_cache_replicate_validation(L):
+    f = L.ncattn_cache_replicate
+    def call(ks=P, vs=P + 16, sl=P + 32, kd=P + 48, vd=P + 64, dl=P + 80, N=4, T_src=16, T_max=32, KV=2, D=128, dt=0):
+        return f(ks, vs, sl, kd, vd, dl, N, T_src, T_max, KV, D, dt, None)
+    assert call(ks=None) == EINVAL
+    assert call(dl=None) == EINVAL
+    assert call(sl=P + 34) == EINVAL          # misaligned length pointer
+    assert call(N=0) == EINVAL
+    assert call(T_src=0) == EINVAL
+    assert call(T_max=15) == EINVAL           # T_src > T_max
+    assert call(KV=1, D=4) == EINVAL          # a row of 8 bytes is not a multiple of 16
+    assert call(kd=P + 8) == EINVAL           # misaligned cache pointer
+    assert call(vd=P + 48) == EINVAL          # k_dst == v_dst
+    assert call(kd=P) == EINVAL               # destination aliases a source
+    assert call(dt=7) == EINVAL

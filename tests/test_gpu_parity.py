@@ -15,7 +15,7 @@ import oracle
 import transformer_attention_qknorm_amd as nc
 from conftest import tol_check
 from parity_util import LSE_TOL, TOL, check, check_lse, f64
-from workloads import attn_inputs, decode_inputs, prefill_inputs
+from workloads import attn_inputs, decode_inputs, prefill_inputs, replicate_inputs
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -329,3 +329,73 @@ def test_prefill_invalid_lengths_give_nan_and_leave_cache():
     assert torch.isnan(o[1:].float()).all() and torch.isnan(lse[1:]).all()
     for b in (1, 2):
         assert torch.equal(kcd[b].cpu(), kc[b]) and torch.equal(vcd[b].cpu(), vc[b])
+
+
+# ------------------------------------------------------------ cache replication
+
+def _bits_equal(a, b):
+    """Bitwise equality of two CPU tensors of one dtype (NaN payloads included)."""
+    if a.dtype == torch.bfloat16:
+        return torch.equal(a.view(torch.int16), b.view(torch.int16))
+    return torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+REPLICATE_CASES = [
+    # N, T_src, T_max, KV, D, dtype, prompt length
+    (3, 37, 64, 3, 64, "f32", 29),
+    (5, 16, 16, 2, 8, "bf16", 16),         # the whole source, T_src == T_max, 32-byte rows
+    (4, 20, 40, 2, 128, "bf16", 0),        # empty prompt: nothing copied
+    (64, 1024, 1536, 10, 128, "bf16", 777),  # the Engine decode batch and heads
+    (2, 9, 9, 1, 4, "f32", 1),             # 16-byte rows, a single prompt row
+]
+
+
+@pytest.mark.parametrize("N,T_src,T_max,KV,D,dtype,s", REPLICATE_CASES)
+def test_cache_replicate(N, T_src, T_max, KV, D, dtype, s):
+    say(f"cache_replicate N={N} T_src={T_src} T_max={T_max} KV={KV} D={D} {dtype} s={s}")
+    ks, vs, kd, vd, sl = replicate_inputs(N, T_src, T_max, KV, D, s, seed=9 + N, dtype=dtype)
+    ksd, vsd, kdd, vdd, sld = to_dev(ks, vs, kd, vd, sl)
+    dl = torch.full((N,), 12345, dtype=torch.int32, device=DEV)
+    nc.cache_replicate(ksd, vsd, sld, kdd, vdd, dl)
+    torch.cuda.synchronize()
+    # the oracle moves the values in their own dtype's float32 image (exact for bf16)
+    rk, rv, rl = oracle.cache_replicate(ks.float().numpy(), vs.float().numpy(), s, kd.float().numpy(),
+                                        vd.float().numpy())
+    assert dl.cpu().tolist() == rl.tolist()
+    exp_k = torch.from_numpy(rk).to(kd.dtype)
+    exp_v = torch.from_numpy(rv).to(vd.dtype)
+    assert _bits_equal(kdd.cpu(), exp_k) and _bits_equal(vdd.cpu(), exp_v)
+    assert _bits_equal(ksd.cpu(), ks) and _bits_equal(vsd.cpu(), vs)   # sources only read
+
+
+@pytest.mark.parametrize("bad", [-1, 21, -2 ** 31])
+def test_cache_replicate_invalid_length_copies_nothing(bad):
+    N, T_src, T_max, KV, D = 3, 20, 32, 2, 128
+    ks, vs, kd, vd, _ = replicate_inputs(N, T_src, T_max, KV, D, bad, seed=31)
+    ksd, vsd, kdd, vdd = to_dev(ks, vs, kd, vd)
+    sld = torch.tensor([bad], dtype=torch.int32, device=DEV)
+    dl = torch.zeros(N, dtype=torch.int32, device=DEV)
+    nc.cache_replicate(ksd, vsd, sld, kdd, vdd, dl)
+    torch.cuda.synchronize()
+    assert dl.cpu().tolist() == [-1] * N
+    assert _bits_equal(kdd.cpu(), kd) and _bits_equal(vdd.cpu(), vd)
+
+
+def test_cache_replicate_then_decode():
+    """Prefill once, replicate, decode every sample: each row's decode matches the
+    oracle decode over the replicated cache (the Engine's prefill-then-sample flow)."""
+    N, T_src, T_max, H, KV, D, s = 8, 300, 512, 4, 2, 128, 250
+    ks, vs, kd, vd, sl = replicate_inputs(N, T_src, T_max, KV, D, s, seed=33)
+    ksd, vsd, kdd, vdd, sld = to_dev(ks, vs, kd, vd, sl)
+    dl = torch.empty(N, dtype=torch.int32, device=DEV)
+    nc.cache_replicate(ksd, vsd, sld, kdd, vdd, dl)
+    q, kn, vn, _, _, _ = decode_inputs(N, H, KV, D, 1, 2, 4, seed=34, poison=False)
+    qd, knd, vnd = to_dev(q, kn, vn)
+    rk, rv, rl = oracle.cache_replicate(f64(ks), f64(vs), s, f64(kd), f64(vd))
+    for W in (-1, 100):
+        kc, vc = kdd.clone(), vdd.clone()
+        o, lse = nc.decode(qd, knd, vnd, kc, vc, dl, window=W, return_lse=True)
+        torch.cuda.synchronize()
+        ro, rlse, _, _ = oracle.decode(f64(q), f64(kn), f64(vn), rk, rv, rl, W)
+        check(o, ro, "bf16", f"decode after replicate W={W}")
+        check_lse(lse, rlse, "bf16", f"decode lse after replicate W={W}")

@@ -394,6 +394,42 @@ def test_prefill_of_one_token_is_decode():
         np.testing.assert_array_equal(k1, k2)
 
 
+def test_cache_replicate_then_decode_equals_decode_on_the_prefilled_cache():
+    """Decoding from every replicated row reproduces decoding from the batch-1
+    cache it was copied from (the point of prefilling once and cloning), and the
+    rows past the prompt keep their old contents."""
+    KV, D, T_src, T_max, N, H = 2, 8, 9, 14, 3, 4
+    s = 6
+    k_src, v_src = rand(1, T_src, KV, D), rand(1, T_src, KV, D)
+    k_dst = np.full((N, T_max, KV, D), 7.25)
+    v_dst = np.full((N, T_max, KV, D), -3.5)
+    kd, vd, lens = oracle.cache_replicate(k_src, v_src, s, k_dst, v_dst)
+    assert lens.dtype == np.int32 and list(lens) == [s] * N
+    assert np.all(kd[:, s:] == 7.25) and np.all(vd[:, s:] == -3.5)
+    # a batch-1 decode cache of the source's own size holds the prompt rows at [0, s)
+    for n in range(N):
+        q, kn, vn = rand(1, 1, H, D), rand(1, 1, KV, D), rand(1, 1, KV, D)
+        for W in (-1, 3):
+            o_rep, lse_rep, _, _ = oracle.decode(q, kn, vn, kd[n:n + 1], vd[n:n + 1], [s], W)
+            o_src, lse_src, _, _ = oracle.decode(q, kn, vn, k_src, v_src, [s], W)
+            assert np.array_equal(o_rep, o_src) and np.array_equal(lse_rep, lse_src)
+
+
+def test_cache_replicate_lengths_at_the_edges():
+    KV, D, T_src, T_max, N = 1, 4, 5, 8, 2
+    k_src, v_src = rand(1, T_src, KV, D), rand(1, T_src, KV, D)
+    k_dst, v_dst = rand(N, T_max, KV, D), rand(N, T_max, KV, D)
+    kd, vd, lens = oracle.cache_replicate(k_src, v_src, 0, k_dst, v_dst)   # empty prompt: nothing copied
+    assert list(lens) == [0, 0] and np.array_equal(kd, k_dst) and np.array_equal(vd, v_dst)
+    kd, vd, lens = oracle.cache_replicate(k_src, v_src, T_src, k_dst, v_dst)   # whole source
+    assert list(lens) == [T_src] * N
+    assert all(np.array_equal(kd[n, :T_src], k_src[0]) for n in range(N))
+    assert np.array_equal(kd[:, T_src:], k_dst[:, T_src:])
+    for bad in (-1, T_src + 1):   # invalid source length: untouched, lengths -1
+        kd, vd, lens = oracle.cache_replicate(k_src, v_src, bad, k_dst, v_dst)
+        assert list(lens) == [-1, -1] and np.array_equal(kd, k_dst) and np.array_equal(vd, v_dst)
+
+
 # ----------------------------------------------------------------- planted mistakes
 
 def test_planted_mistakes_are_caught(monkeypatch):

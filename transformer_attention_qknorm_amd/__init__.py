@@ -23,7 +23,8 @@ import os
 
 import torch
 
-__all__ = ["qknorm_rope_", "fwd", "bwd", "decode", "window_sizes", "lib", "NcattnError", "LIB_PATH",
+__all__ = ["qknorm_rope_", "qknorm_rope_bwd_", "fwd", "bwd", "decode", "prefill", "cache_replicate",
+           "window_sizes", "lib", "NcattnError", "LIB_PATH",
            "BF16", "F32", "STATUS", "bwd_workspace", "decode_workspace", "BWD_STAGES"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libncattn.so")
@@ -63,10 +64,11 @@ def lib():
     L.ncattn_decode_workspace_bytes.restype = sz
     L.ncattn_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp, sz, vp]
     L.ncattn_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp]
+    L.ncattn_cache_replicate.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
     L.ncattn_last_error.restype = ctypes.c_char_p
     L.ncattn_version.restype = ctypes.c_char_p
     for fn in ("ncattn_qknorm_rope", "ncattn_qknorm_rope_bwd", "ncattn_fwd", "ncattn_bwd", "ncattn_decode",
-               "ncattn_prefill"):
+               "ncattn_prefill", "ncattn_cache_replicate"):
         getattr(L, fn).restype = i32
     _lib = L
     return L
@@ -299,6 +301,32 @@ def prefill(q, k_new, v_new, k_cache, v_cache, cache_seqlens, window=-1, softmax
                                   _scale(softmax_scale), _dtype_code(q), _stream(dev))
     _check("ncattn_prefill", rc)
     return (o, lse) if return_lse else o
+
+
+def cache_replicate(k_src, v_src, src_seqlen, k_dst, v_dst, dst_seqlens):
+    """Copies the first src_seqlen[0] rows of a batch-1 cache k_src, v_src
+    [1][T_src][KV][D] into every row of k_dst, v_dst [N][T_max][KV][D] and sets
+    dst_seqlens [N] (int32) to that length, in place ("nanochat Admin & Developer
+    Guide", section 7: prefill once, then copy the cache to the samples).  A
+    length outside [0, T_src] copies nothing and sets dst_seqlens to -1."""
+    dev = _dev(k_src, v_src, src_seqlen, k_dst, v_dst, dst_seqlens)
+    if k_src.dim() != 4 or k_src.shape[0] != 1 or v_src.shape != k_src.shape:
+        raise ValueError("ncattn.cache_replicate: sources must be [1][T_src][KV][D]")
+    _, T_src, KV, D = k_src.shape
+    if k_dst.dim() != 4 or v_dst.shape != k_dst.shape or k_dst.shape[2:] != (KV, D):
+        raise ValueError("ncattn.cache_replicate: destinations must be [N][T_max][KV][D] like the sources")
+    if k_dst.dtype != k_src.dtype or v_dst.dtype != k_src.dtype or v_src.dtype != k_src.dtype:
+        raise ValueError("ncattn.cache_replicate: sources and destinations must share a dtype")
+    N, T_max = k_dst.shape[0], k_dst.shape[1]
+    if src_seqlen.dtype != torch.int32 or src_seqlen.numel() != 1:
+        raise ValueError("ncattn.cache_replicate: src_seqlen must be int32 [1]")
+    if dst_seqlens.dtype != torch.int32 or dst_seqlens.numel() != N:
+        raise ValueError("ncattn.cache_replicate: dst_seqlens must be int32 [N]")
+    with torch.cuda.device(dev):
+        rc = lib().ncattn_cache_replicate(_ptr(k_src), _ptr(v_src), _ptr(src_seqlen), _ptr(k_dst), _ptr(v_dst),
+                                          _ptr(dst_seqlens), N, T_src, T_max, KV, D, _dtype_code(k_src),
+                                          _stream(dev))
+    _check("ncattn_cache_replicate", rc)
 
 
 def window_sizes(pattern, n_layer, short_window, long_window=-1):

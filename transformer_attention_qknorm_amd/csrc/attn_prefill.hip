@@ -12,6 +12,10 @@
 // sequence's query offset from seqlens and bounds its key rows by s + Tn.  A
 // sequence with s outside [0, T_max - Tn] is left untouched in the cache and gets
 // NaN rows in o and lse (it cannot be checked on the host without a sync).
+//
+// Also the replication of a batch-1 prefill cache into a batch-N decode cache
+// (same guide, section 7: the prompt is prefilled once, then its cache is copied
+// into every row the samples decode from).
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -44,7 +48,47 @@ __global__ __launch_bounds__(256) void prefill_append_kernel(const uint16_t *__r
   }
 }
 
+// Copies the first s = *src_seqlen rows of a batch-1 cache into each of the N rows
+// of a batch-N cache and sets the N lengths to s; a length outside [0, T_src]
+// copies nothing and marks the rows -1.  Each lane reads a 16-byte piece of K and
+// of V once and stores it N times.
+__global__ __launch_bounds__(256) void cache_replicate_kernel(const u32x4 *__restrict__ k_src,
+                                                              const u32x4 *__restrict__ v_src,
+                                                              const int32_t *__restrict__ src_seqlen,
+                                                              u32x4 *__restrict__ k_dst, u32x4 *__restrict__ v_dst,
+                                                              int32_t *__restrict__ dst_seqlens, int N, int T_src,
+                                                              int T_max, int row_pieces) {
+  const int s = *src_seqlen;
+  const bool valid = s >= 0 && s <= T_src;
+  if (blockIdx.x == 0)
+    for (int n = threadIdx.x; n < N; n += blockDim.x) dst_seqlens[n] = valid ? s : -1;
+  if (!valid) return;
+  const long long pieces = (long long)s * row_pieces;  // the source prefix is contiguous
+  const long long dst_seq = (long long)T_max * row_pieces;
+  for (long long p = (long long)blockIdx.x * blockDim.x + threadIdx.x; p < pieces;
+       p += (long long)gridDim.x * blockDim.x) {
+    const u32x4 kk = k_src[p];
+    const u32x4 vv = v_src[p];
+    for (int n = 0; n < N; ++n) {
+      k_dst[n * dst_seq + p] = kk;
+      v_dst[n * dst_seq + p] = vv;
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_cache_replicate(const void *k_src, const void *v_src, const int32_t *src_seqlen, void *k_dst,
+                                  void *v_dst, int32_t *dst_seqlens, int N, int T_src, int T_max, int row_pieces,
+                                  hipStream_t s) {
+  long long blocks = ((long long)T_src * row_pieces + 255) / 256;
+  if (blocks < 1) blocks = 1;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(cache_replicate_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (const u32x4 *)k_src,
+                     (const u32x4 *)v_src, src_seqlen, (u32x4 *)k_dst, (u32x4 *)v_dst, dst_seqlens, N, T_src, T_max,
+                     row_pieces);
+  return hipGetLastError();
+}
 
 hipError_t launch_prefill_bf16(const void *q, const void *k_new, const void *v_new, void *k_cache, void *v_cache,
                                const int32_t *seqlens, void *o, float *lse, int B, int Tn, int T_max, int H,

@@ -80,6 +80,9 @@ hipError_t launch_decode_bf16(const void *q, const void *k_new, const void *v_ne
 
 // Chunked prefill, bf16, head_dim 128: append k_new/v_new [B][Tn][KV][D] at
 // cache rows seqlens[b].., then the forward of q [B][Tn][H][D] over the cache.
+hipError_t launch_cache_replicate(const void *k_src, const void *v_src, const int32_t *src_seqlen, void *k_dst,
+                                  void *v_dst, int32_t *dst_seqlens, int N, int T_src, int T_max, int row_pieces,
+                                  hipStream_t s);
 hipError_t launch_prefill_bf16(const void *q, const void *k_new, const void *v_new, void *k_cache, void *v_cache,
                                const int32_t *seqlens, void *o, float *lse, int B, int Tn, int T_max, int H,
                                int KV, int window, float scale, hipStream_t s);

@@ -303,4 +303,33 @@ int ncattn_prefill(const void *q, const void *k_new, const void *v_new, void *k_
   return hip_status(e, fn);
 }
 
+int ncattn_cache_replicate(const void *k_src, const void *v_src, const int32_t *src_seqlen, void *k_dst,
+                           void *v_dst, int32_t *dst_seqlens, int N, int T_src, int T_max, int n_kv_head,
+                           int head_dim, int dtype, void *stream) {
+  const char *fn = "ncattn_cache_replicate";
+  NC_PTR(k_src, fn);
+  NC_PTR(v_src, fn);
+  NC_PTR(k_dst, fn);
+  NC_PTR(v_dst, fn);
+  if (src_seqlen == nullptr || dst_seqlens == nullptr) return fail(NCATTN_EINVAL, "%s: a length pointer is NULL", fn);
+  if (((uintptr_t)src_seqlen & 3u) || ((uintptr_t)dst_seqlens & 3u))
+    return fail(NCATTN_EINVAL, "%s: length pointers must be 4-byte aligned", fn);
+  NC_TRY(check_dtype(fn, dtype));
+  if (N < 1 || T_src < 1 || n_kv_head < 1 || head_dim < 1)
+    return fail(NCATTN_EINVAL, "%s: need N, T_src, n_kv_head, head_dim >= 1 (N=%d T_src=%d n_kv_head=%d head_dim=%d)",
+                fn, N, T_src, n_kv_head, head_dim);
+  if (T_max < T_src) return fail(NCATTN_EINVAL, "%s: need T_src <= T_max (T_src=%d T_max=%d)", fn, T_src, T_max);
+  const long long row_bytes = (long long)n_kv_head * head_dim * (dtype == NCATTN_BF16 ? 2 : 4);
+  if (row_bytes % 16) return fail(NCATTN_EINVAL, "%s: a cache row (n_kv_head * head_dim elements) must be a multiple of 16 bytes", fn);
+  if (row_bytes / 16 > 0x7fffffffLL || (long long)N * T_max * row_bytes / 16 > (1LL << 60))
+    return fail(NCATTN_EINVAL, "%s: sizes too large", fn);
+  if ((((uintptr_t)k_src | (uintptr_t)v_src | (uintptr_t)k_dst | (uintptr_t)v_dst) & 15u))
+    return fail(NCATTN_EINVAL, "%s: cache pointers must be 16-byte aligned", fn);
+  if (k_dst == v_dst || k_dst == k_src || k_dst == v_src || v_dst == k_src || v_dst == v_src)
+    return fail(NCATTN_EINVAL, "%s: the destination caches must be distinct from each other and from the sources", fn);
+  hipError_t e = ncattn::launch_cache_replicate(k_src, v_src, src_seqlen, k_dst, v_dst, dst_seqlens, N, T_src, T_max,
+                                                (int)(row_bytes / 16), (hipStream_t)stream);
+  return hip_status(e, fn);
+}
+
 }  // extern "C"

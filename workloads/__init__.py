@@ -137,6 +137,23 @@ def decode_inputs(B, H, KV, D, min_len, max_len, T_max, seed=5, poison=True, dty
     return (*out, torch.from_numpy(lens))
 
 
+def replicate_inputs(N, T_src, T_max, KV, D, prompt_len, seed=9, dtype="bf16"):
+    """Batch-1 prefill cache k_src, v_src [1][T_src][KV][D] ~ N(0, 1) with rows
+    >= prompt_len NaN (they must not be copied), destination caches k_dst, v_dst
+    [N][T_max][KV][D] ~ N(0, 1) (their rows >= prompt_len must survive), and the
+    source length as int32 [1].  CPU torch tensors of the I/O dtype."""
+    rng = np.random.default_rng(seed)
+    ks = rng.standard_normal((1, T_src, KV, D), dtype=np.float32)
+    vs = rng.standard_normal((1, T_src, KV, D), dtype=np.float32)
+    if 0 <= prompt_len <= T_src:
+        ks[:, prompt_len:] = np.nan
+        vs[:, prompt_len:] = np.nan
+    kd = rng.standard_normal((N, T_max, KV, D), dtype=np.float32)
+    vd = rng.standard_normal((N, T_max, KV, D), dtype=np.float32)
+    out = [_to_dtype(x, dtype) for x in (ks, vs, kd, vd)]
+    return (*out, torch.tensor([prompt_len], dtype=torch.int32))
+
+
 def prefill_inputs(B, Tn, H, KV, D, min_len, max_len, T_max, seed=6, poison=True, dtype="bf16"):
     """Prefill batch: lengths L_b ~ U[min_len, max_len] (inclusive), caches
     [B][T_max][KV][D] with slots < L_b ~ N(0, 1) and slots >= L_b NaN (poison) or
