@@ -24,6 +24,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -236,6 +237,23 @@ def main():
     qb_gbps = 3 * (qk_bytes // 2) / (qb_us * 1e-6) / 1e9
     detail["qknorm_rope_bwd"] = {"us": round(qb_us, 2), "GBps": round(qb_gbps, 1),
                                  "frac_hbm": round(qb_gbps / PEAK_HBM_GBPS, 4), "algorithmic_bytes": 3 * (qk_bytes // 2)}
+
+    # The same forward kernel with the pages' logit gain split between q and k
+    # (g = sqrt(1.2) on each); the step above uses plain weightless RMSNorm (g = 1).
+    gq, gk = Lq["q"].clone(), Lq["k"].clone()
+    for _ in range(3):
+        nc.qknorm_rope_(gq, gk, None, rope_base=cfg.rope_base, eps=1e-6, qk_gain=math.sqrt(1.2))
+    torch.cuda.synchronize()
+    qg_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+    for a, b in qg_ev:
+        a.record(stream)
+        nc.qknorm_rope_(gq, gk, None, rope_base=cfg.rope_base, eps=1e-6, qk_gain=math.sqrt(1.2))
+        b.record(stream)
+    torch.cuda.synchronize()
+    qg_us = sum(a.elapsed_time(b) for a, b in qg_ev) * 1e3 / len(qg_ev)
+    detail["qknorm_rope_gain_sqrt1p2"] = {"us": round(qg_us, 2), "GBps": round(qk_bytes / (qg_us * 1e-6) / 1e9, 1),
+                                          "qk_gain": round(math.sqrt(1.2), 6)}
+    del gq, gk
 
     prefill = None
     if not args.no_decode:
