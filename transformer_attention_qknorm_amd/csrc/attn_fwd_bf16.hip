@@ -16,11 +16,13 @@
 // l^32, and the probabilities feed O^T += V^T P^T directly as the MFMA B operand
 // (V^T comes from LDS with transposing reads).
 //
-// Software pipeline: in step t a wave issues the S^T MFMAs of tile t+1 and, in
-// the same instruction stream, the softmax of tile t (independent work, so the
-// vector ALU and the matrix cores run together), then O += P V for tile t.  K
-// therefore runs one tile ahead of V: step t reads K(t+1) and V(t) while
-// K(t+2) and V(t+1) are being copied into the other halves of two LDS rings.
+// Software pipeline: in step t a wave issues the S^T MFMAs of tile t+1 (their K
+// operands read four MFMAs ahead), then the softmax of tile t, then O += P V for
+// tile t; two workgroups share a CU, so a SIMD runs two such waves.  K therefore
+// runs one tile ahead of V: step t reads K(t+1) and V(t) while K(t+2) and V(t+1)
+// are being copied into the other halves of two LDS rings.  (Placing the
+// softmax's exponentials between the S MFMAs of the same wave was measured too:
+// no faster on this chip.)
 // Tiles entirely outside a wave's window are skipped; masks are applied only on
 // tiles that straddle the causal diagonal or the window edge.
 //
@@ -268,7 +270,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const uint16_t *_
       }
       if (cur && next) {
         // steady state: one straight-line block holding the S MFMAs of tile t+1,
-        // the exponentials of tile t and the PV MFMAs of tile t
+        // then the exponentials and the PV MFMAs of tile t
         s_tile(snext, kcur, L, qreg);
         softmax_exp(st, scur, c, overflow);
         pv_tile(st, scur, vcur, L);
