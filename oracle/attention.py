@@ -27,7 +27,7 @@ online softmax, fusion or reordering.  Sources (page title, section):
 * "nanochat (Python)" feature catalog, entry AI / Model & kernels / Backward
   pass: the backward is autograd of the forward, i.e. its exact gradient.
 
-Readings where the pages are silent (each also listed in the design doc):
+Readings where the pages are silent:
 * RMSNorm eps is an argument (default 1e-6); the norm is per head over head_dim.
 * The 1.2 gain is read as a total logit gain, g = sqrt(1.2) on each of q and k;
   ``gain`` is an argument and the workloads use g = 1 (plain weightless RMSNorm).
