@@ -13,7 +13,10 @@ same run at the full-causal and 1024 windows and reported under "decode".
 Prints ONE JSON line.  ``value`` = unmasked attention FLOPs of a step (fwd 4*D
 and bwd 8*D per visible (query, key) pair and head) / wall time of the step
 (QK-norm included in the time).  ``roofline`` is for the kernel with the largest
-share of the step, timed with HIP events on the stream it runs on; ``traffic``
+share of the step, timed with HIP events on the stream it runs on inside the
+timed region (step s brackets that kernel of layer s mod 4; the per-kernel
+figures under "detail" come from an untimed pass with events around every
+kernel, since each event is a GPU packet of its own between kernels); ``traffic``
 comes from the committed rocprofv3 counter summary in profiles/ when it was
 taken on the current kernel source, else null.  ``cpu_baseline`` times the CPU
 oracle on a bounded sample of the same workload.
@@ -110,6 +113,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--profile-steps", type=int, default=5,
+                    help="untimed steps with an event around every kernel, for the per-kernel breakdown")
     ap.add_argument("--decode-iters", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
@@ -144,10 +149,13 @@ def main():
     stream = torch.cuda.current_stream(dev)
 
     def step(ev=None):
+        # ev: {(layer, i): Event}; event i of a layer is recorded before kernel i of
+        # `names` (i = len(names): after the last), only where ev has an entry
         for li, L in enumerate(layers):
             def rec(i):
-                if ev is not None:
-                    ev[li][i].record(stream)
+                e = None if ev is None else ev.get((li, i))
+                if e is not None:
+                    e.record(stream)
             rec(0)
             nc.qknorm_rope_(L["q"], L["k"], None, rope_base=cfg.rope_base, eps=1e-6)
             rec(1)
@@ -158,10 +166,37 @@ def main():
                        out=(L["dq"], L["dk"], L["dv"]), workspace=ws, stage=st)
                 rec(3 + si)
 
+    nl = len(layers)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in layers] for _ in range(args.steps)]
+
+    # Per-kernel breakdown (the "detail" figures): an untimed pass with an event
+    # before and after every kernel.  Each event is a packet of its own between
+    # kernels (a few us of GPU time), so the timed region below records events
+    # around the dominant kernel only.
+    prof_steps = max(1, args.profile_steps)
+    pev = [{(li, i): torch.cuda.Event(enable_timing=True) for li in range(nl) for i in range(len(names) + 1)}
+           for _ in range(prof_steps)]
+    for s in range(prof_steps):
+        step(pev[s])
+    torch.cuda.synchronize()
+    dur = {n: [0.0] * nl for n in names}  # ms per launch, per layer
+    for s in range(prof_steps):
+        for li in range(nl):
+            for i, n in enumerate(names):
+                dur[n][li] += pev[s][(li, i)].elapsed_time(pev[s][(li, i + 1)]) / prof_steps
+    totals = {n: sum(dur[n]) for n in names}
+    dominant = max(totals, key=totals.get)
+    kd = names.index(dominant)
+
+    # Timed region: step s brackets the dominant kernel of layer s mod 4 with HIP
+    # events (every layer when there are fewer steps than layers), so the launches
+    # of every layer type are sampled equally.
+    def timed_events(s):
+        lis = range(nl) if args.steps < nl else (s % nl,)
+        return {(li, i): torch.cuda.Event(enable_timing=True) for li in lis for i in (kd, kd + 1)}
+    events = [timed_events(s) for s in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
@@ -169,38 +204,36 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
+    samples = [[] for _ in range(nl)]  # dominant-kernel durations (ms), per layer
+    for ev in events:
+        for li in range(nl):
+            if (li, kd) in ev:
+                samples[li].append(ev[(li, kd)].elapsed_time(ev[(li, kd + 1)]))
+    dom_ms = [sum(x) / len(x) for x in samples]  # average launch per layer, over the timed region
 
-    # per-kernel durations (ms), per layer, averaged over steps
-    dur = {n: [0.0] * len(layers) for n in names}
-    for s in range(args.steps):
-        for li in range(len(layers)):
-            e = events[s][li]
-            for i, n in enumerate(names):
-                dur[n][li] += e[i].elapsed_time(e[i + 1]) / args.steps
     pairs = [visible_pairs(T, L["W"]) * B * H for L in layers]
     f_fwd = [4 * D * p for p in pairs]
     f_bwd = [8 * D * p for p in pairs]
     flops_step = sum(f_fwd) + sum(f_bwd)
     value = flops_step / (ms_per_step * 1e-3) / 1e12
     t_attn = sum(sum(dur[n]) for n in names[1:])
-    totals = {n: sum(dur[n]) for n in names}
-    dominant = max(totals, key=totals.get)
     # algorithmic work attributed per kernel: fwd 4D/pair; dkdv computes dV, dP, dK
     # (6D/pair); dq computes dQ (2D/pair); the S/dP recomputations are not counted
     share = {"fwd": 4, "bwd_dkdv": 6, "bwd_dq": 2}
     if dominant in share:
         work = sum(share[dominant] * D * p for p in pairs)
-        achieved = work / (totals[dominant] * 1e-3) / 1e12
+        achieved = work / (sum(dom_ms) * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "kernel": dominant}
     else:
         nbytes = (B * T * (H + KV) * D * 2 * 2) if dominant == "qknorm_rope" else (B * T * H * D * 2 * 2 + B * H * T * 4)
-        achieved = nbytes * len(layers) / (totals[dominant] * 1e-3) / 1e9
+        achieved = nbytes * len(layers) / (sum(dom_ms) * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBPS, 4), "kernel": dominant}
     tr = measured_traffic(dominant)
     roof["traffic"] = None if tr is None else tr
-    roof["avg_launch_us"] = round(totals[dominant] * 1e3 / len(layers), 2)
+    roof["avg_launch_us"] = round(sum(dom_ms) * 1e3 / nl, 2)
+    roof["launches_timed"] = sum(len(x) for x in samples)
 
     per_layer = []
     for li, L in enumerate(layers):
@@ -219,6 +252,7 @@ def main():
         "kernel_ms_per_step": {n: round(totals[n], 4) for n in names},
         "layers": per_layer,
         "algorithmic_gflop_per_step": round(flops_step / 1e9, 2),
+        "per_kernel_from": f"untimed pass of {prof_steps} steps with events around every kernel",
     }
 
     # Backward of QK-norm + RoPE (not part of the step's attention FLOPs): read the
