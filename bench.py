@@ -8,7 +8,8 @@ One step = the training-side hot path of a nanochat d12-shaped model's attention
 forward, attention backward.  Inputs are seeded synthetic N(0, 1) tensors
 already resident in HBM, one distinct set per layer.  The engine-decode row (64
 sequences, cache lengths U[256, 8192], 10 heads, head_dim 128) is timed in the
-same run at the full-causal and 1024 windows and reported under "decode".
+same run at the full-causal and 1024 windows and reported under "decode"; the
+d20 and GQA workloads' forward and backward per layer type under "configs".
 
 Prints ONE JSON line.  ``value`` = unmasked attention FLOPs of a step (fwd 4*D
 and bwd 8*D per visible (query, key) pair and head) / wall time of the step
@@ -108,6 +109,51 @@ def cpu_baseline(cfg, budget_s=12.0):
                       f"window 1024 and full causal, fwd+bwd in float64 numpy; {t_used:.1f} s of CPU work"}
 
 
+def time_config(nc, torch, cfg, dev, stream, iters=10):
+    """Forward and backward of each layer type (short window, full causal) of a
+    workload, timed with HIP events over `iters` calls each: the per-layer-type
+    TFLOP/s and the SSSL-weighted total.  Reported under "configs"; not part of
+    the step above."""
+    from workloads import config_inputs
+    q, k, v, do = (x.to(dev) for x in config_inputs(cfg))
+    o = torch.empty_like(q)
+    lse = torch.empty(cfg.B, cfg.H, cfg.T, dtype=torch.float32, device=dev)
+    grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    layers = {}
+    for W in sorted(set(cfg.windows), reverse=True):
+        ws = nc.bwd_workspace(q, k, (W, 0))
+        for _ in range(2):
+            nc.fwd(q, k, v, window=(W, 0), out=(o, lse))
+            nc.bwd(q, k, v, o, lse, do, window=(W, 0), out=grads, workspace=ws)
+        torch.cuda.synchronize()
+        evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(iters)]
+        for a, b, c in evs:
+            a.record(stream)
+            nc.fwd(q, k, v, window=(W, 0), out=(o, lse))
+            b.record(stream)
+            nc.bwd(q, k, v, o, lse, do, window=(W, 0), out=grads, workspace=ws)
+            c.record(stream)
+        torch.cuda.synchronize()
+        tf = sum(a.elapsed_time(b) for a, b, _ in evs) / iters * 1e-3
+        tb = sum(b.elapsed_time(c) for _, b, c in evs) / iters * 1e-3
+        pairs = visible_pairs(cfg.T, W) * cfg.B * cfg.H
+        ff, fb = 4 * cfg.D * pairs, 8 * cfg.D * pairs
+        layers["L" if W < 0 else "S"] = {
+            "window": W, "fwd_us": round(tf * 1e6, 1), "bwd_us": round(tb * 1e6, 1),
+            "fwd_tflops": round(ff / tf / 1e12, 1), "bwd_tflops": round(fb / tb / 1e12, 1),
+            "fwd_bwd_tflops": round((ff + fb) / (tf + tb) / 1e12, 1),
+            "frac_bf16_peak": round((ff + fb) / (tf + tb) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "_f": ff + fb, "_t": tf + tb}
+        del ws
+    n = {key: sum(1 for W in cfg.windows if (W < 0) == (key == "L")) for key in layers}
+    tot_f = sum(n[key] * layers[key].pop("_f") for key in layers)
+    tot_t = sum(n[key] * layers[key].pop("_t") for key in layers)
+    del q, k, v, do, o, lse, grads
+    torch.cuda.empty_cache()
+    return {"workload": cfg.name, "layers": layers, "sssl_fwd_bwd_tflops": round(tot_f / tot_t / 1e12, 1),
+            "sssl_frac_bf16_peak": round(tot_f / tot_t / 1e12 / PEAK_BF16_TFLOPS, 4), "timed_calls": iters}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -118,6 +164,8 @@ def main():
     ap.add_argument("--decode-iters", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-layer-type fwd/bwd timings of the d20 and GQA workloads")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, copy a buffer of this many MiB device-to-device 3 times: a kernel of "
                          "known traffic for calibrating rocprofv3's FETCH_SIZE/WRITE_SIZE counters")
@@ -375,6 +423,11 @@ def main():
                                              "algorithmic_bytes": nbytes}
         del sets
 
+    configs = None
+    if not args.no_configs:
+        from workloads import D20, GQA
+        configs = {c.name: time_config(nc, torch, c, dev, stream) for c in (D20, GQA)}
+
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
@@ -385,6 +438,7 @@ def main():
         "decode": decode,
         "prefill": prefill,
         "cache_replicate": replicate,
+        "configs": configs,
         "detail": detail,
     }
     if args.copy_probe_mib > 0:
