@@ -95,6 +95,8 @@ FWD_CASES = [
     ("bf16", 1, 129, 3, 1, 128, 20),
     ("bf16", 3, 520, 2, 2, 128, -1),
     ("bf16", 1, 777, 6, 2, 128, 256),
+    ("bf16", 1, 300, 8, 1, 128, -1),   # eight query heads on one kv head: dK/dV sum over the group
+    ("bf16", 2, 333, 8, 1, 128, 100),
     ("f32", 1, 64, 2, 2, 64, -1),
     ("f32", 2, 100, 4, 2, 64, 17),
     ("f32", 1, 150, 2, 1, 128, -1),
