@@ -8,7 +8,9 @@
 //   o[b, h] = softmax_j(scale q[b, h] . k_j) v_j over j in [max(0, s - W), s].
 //
 // Split-KV: the visible keys of each (b, kv head) are cut into chunks of 128.
-// decode_split: one workgroup per (b, kv head, chunk); 16 groups of 16 lanes,
+// decode_split: one workgroup per (b, chunk, kv head), the kv heads of a chunk
+// on consecutive blocks so that the KV x 256 contiguous bytes of each cached key
+// are read at about the same time; 16 groups of 16 lanes,
 // each group owning 8 keys (16 B per lane per K or V row, so every load
 // instruction covers four whole 256-byte rows).  All K and V loads of the chunk
 // are issued up front; scores are reduced over the 16 lanes with DPP, the softmax
@@ -45,10 +47,12 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   const int tid = threadIdx.x;
   const int grp = tid >> 4;
   const int p16 = tid & 15;
-  const int chunk = (int)(blockIdx.x % C_max);
-  const int bk = (int)(blockIdx.x / C_max);
-  const int b = bk / KV;
-  const int kvh = bk % KV;
+  // the KV heads of one (sequence, chunk) are consecutive blocks: they read the
+  // same keys' rows (KV x 256 contiguous bytes per key) at about the same time
+  const int kvh = (int)(blockIdx.x % KV);
+  const int rest = (int)(blockIdx.x / KV);
+  const int chunk = rest % C_max;
+  const int b = rest / C_max;
   const int G = H / KV;
   const int s = seqlens[b];
   if (s < 0 || s >= T_max) return;
