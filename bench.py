@@ -110,6 +110,73 @@ def cpu_baseline(cfg, budget_s=12.0):
                       f"numpy; {t_used:.1f} s of CPU work"}
 
 
+class ClockSampler:
+    """Samples the GPU's current graphics clock (MHz) through amdsmi on a
+    background thread, every `period` seconds, while a `with` block runs (the
+    mean of the per-XCD clocks of the GPU metrics table where the driver reports
+    them, else the graphics clock).  The driver refreshes that table about once a
+    second, so a block must run well over a second to show the clock under load.
+    When no sample could be taken, summary() says why."""
+
+    def __init__(self, period=0.02):
+        import threading
+        self.period, self.samples, self.error = period, [], None
+        self._stop = threading.Event()
+        self._thread = None
+        self._read = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            if len(handles) != 1:
+                raise RuntimeError(f"{len(handles)} GPUs visible to amdsmi, expected one")
+            h = handles[0]
+
+            def read():
+                try:
+                    m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+                    xs = [x for x in (m.get("current_gfxclks") or []) if isinstance(x, (int, float)) and x > 0]
+                    if xs:
+                        return sum(xs) / len(xs)
+                except Exception:  # pragma: no cover - depends on the driver
+                    pass
+                return float(amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.SYS)["clk"])
+            read()
+            self._read = read
+        except Exception as e:  # pragma: no cover - depends on the machine
+            self.error = f"{type(e).__name__}: {e}"
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                self.samples.append(self._read())
+            except Exception as e:  # pragma: no cover
+                self.error = f"{type(e).__name__}: {e}"
+                return
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        import threading
+        if self._read is not None:
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread is not None:
+            self._thread.join()
+        return False
+
+    def summary(self, skip_s=1.0):
+        """Median, min and max of the samples after the first `skip_s` seconds."""
+        xs = sorted(self.samples[int(skip_s / self.period):])
+        if not xs:
+            return {"error": self.error or "no samples"}
+        return {"median_mhz": round(xs[len(xs) // 2]), "min_mhz": round(xs[0]), "max_mhz": round(xs[-1]),
+                "samples": len(xs)}
+
+
 def time_config(nc, torch, cfg, dev, stream, iters=10):
     """Forward and backward of each layer type (short window, full causal) of a
     workload, timed with HIP events over `iters` calls each: the per-layer-type
@@ -303,6 +370,24 @@ def main():
         "algorithmic_gflop_per_step": round(flops_step / 1e9, 2),
         "per_kernel_from": f"untimed pass of {prof_steps} steps with events around every kernel",
     }
+
+    # Graphics clock while the dominant kernel runs back to back for 2 s (full
+    # causal layer), after the timed region: amdsmi's table lags about a second.
+    Ll = layers[-1]
+    launch = {"qknorm_rope": lambda: nc.qknorm_rope_(Ll["q"], Ll["k"], None, rope_base=cfg.rope_base, eps=1e-6),
+              "fwd": lambda: nc.fwd(Ll["q"], Ll["k"], Ll["v"], window=(Ll["W"], 0), out=(Ll["o"], Ll["lse"]))}
+    for st, n in (("preprocess", "bwd_delta"), ("dkdv", "bwd_dkdv"), ("dq", "bwd_dq")):
+        launch[n] = (lambda st=st: nc.bwd(Ll["q"], Ll["k"], Ll["v"], Ll["o"], Ll["lse"], Ll["do"], window=(Ll["W"], 0),
+                                          out=(Ll["dq"], Ll["dk"], Ll["dv"]), workspace=ws, stage=st))
+    clock = ClockSampler()
+    with clock:
+        t_end = time.perf_counter() + 2.0
+        while time.perf_counter() < t_end:
+            for _ in range(10):
+                launch[dominant]()
+            torch.cuda.synchronize()
+    detail["gpu_clock_mhz"] = dict(clock.summary(skip_s=1.2), under=f"{dominant} back to back, full-causal layer",
+                                   source="amdsmi, every 20 ms, samples of the last 0.8 s")
 
     # Backward of QK-norm + RoPE (not part of the step's attention FLOPs): read the
     # forward's inputs and the output gradients, write the input gradients.
