@@ -232,6 +232,8 @@ def main():
     ap.add_argument("--decode-iters", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the 2 s graphics-clock measurement under the dominant kernel")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the per-layer-type fwd/bwd timings of the d20 and GQA workloads")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -379,15 +381,16 @@ def main():
     for st, n in (("preprocess", "bwd_delta"), ("dkdv", "bwd_dkdv"), ("dq", "bwd_dq")):
         launch[n] = (lambda st=st: nc.bwd(Ll["q"], Ll["k"], Ll["v"], Ll["o"], Ll["lse"], Ll["do"], window=(Ll["W"], 0),
                                           out=(Ll["dq"], Ll["dk"], Ll["dv"]), workspace=ws, stage=st))
-    clock = ClockSampler()
-    with clock:
-        t_end = time.perf_counter() + 2.0
-        while time.perf_counter() < t_end:
-            for _ in range(10):
-                launch[dominant]()
-            torch.cuda.synchronize()
-    detail["gpu_clock_mhz"] = dict(clock.summary(skip_s=1.2), under=f"{dominant} back to back, full-causal layer",
-                                   source="amdsmi, every 20 ms, samples of the last 0.8 s")
+    if not args.no_clock:
+        clock = ClockSampler()
+        with clock:
+            t_end = time.perf_counter() + 2.0
+            while time.perf_counter() < t_end:
+                for _ in range(10):
+                    launch[dominant]()
+                torch.cuda.synchronize()
+        detail["gpu_clock_mhz"] = dict(clock.summary(skip_s=1.2), under=f"{dominant} back to back, full-causal layer",
+                                       source="amdsmi, every 20 ms, samples of the last 0.8 s")
 
     # Backward of QK-norm + RoPE (not part of the step's attention FLOPs): read the
     # forward's inputs and the output gradients, write the input gradients.
