@@ -1,7 +1,8 @@
 """Turn two rocprofv3 counter runs of bench.py into per-launch HBM traffic.
 
     rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir_f> -o run -- \\
-        python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-decode --copy-probe-mib 1024
+        python3 bench.py --steps 3 --warmup 1 --profile-steps 1 --no-cpu-baseline --no-decode \\
+        --no-configs --no-clock --copy-probe-mib 1024
     rocprofv3 --pmc WRITE_SIZE ... (same command, another directory)
     python bench_traffic.py <dir_f>/run_counter_collection.csv <dir_w>/run_counter_collection.csv \\
         --copy-mib 1024 --json profiles/traffic.json --md profiles/traffic_d12_bench.md
