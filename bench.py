@@ -113,8 +113,8 @@ def cpu_baseline(cfg, budget_s=12.0):
 class ClockSampler:
     """Samples the GPU's current graphics clock (MHz) through amdsmi on a
     background thread, every `period` seconds, while a `with` block runs (the
-    mean of the per-XCD clocks of the GPU metrics table where the driver reports
-    them, else the graphics clock).  The driver refreshes that table about once a
+    mean of the per-XCD clocks of the GPU metrics table where the amdgpu driver
+    reports them, else the graphics clock).  amdgpu refreshes that table about once a
     second, so a block must run well over a second to show the clock under load.
     When no sample could be taken, summary() says why."""
 
@@ -138,7 +138,7 @@ class ClockSampler:
                     xs = [x for x in (m.get("current_gfxclks") or []) if isinstance(x, (int, float)) and x > 0]
                     if xs:
                         return sum(xs) / len(xs)
-                except Exception:  # pragma: no cover - depends on the driver
+                except Exception:  # pragma: no cover - depends on the amdgpu version
                     pass
                 return float(amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.SYS)["clk"])
             read()
@@ -241,7 +241,7 @@ def main():
                          "known traffic for calibrating rocprofv3's FETCH_SIZE/WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build measures one GPU only (the attention path needs no collective); "
+        print("bench.py: measures one GPU only (the attention path needs no collective); "
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
