@@ -127,6 +127,27 @@ def test_fwd_bwd(case):
     check(dv, rdv, dtype, "dv")
 
 
+def _random_cases(n, seed=2024):
+    """Seeded random shapes (bf16, head_dim 128): ragged T in [1, 400], group sizes
+    1-4, windows unbounded or drawn up to T + 50 (so some exceed T)."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        B, T = int(rng.integers(1, 4)), int(rng.integers(1, 401))
+        KV, G = int(rng.integers(1, 4)), int(rng.integers(1, 5))
+        W = -1 if rng.random() < 0.4 else int(rng.integers(0, T + 51))
+        cases.append(("bf16", B, T, KV * G, KV, 128, W))
+    return cases
+
+
+RANDOM_CASES = _random_cases(12)
+
+
+@pytest.mark.parametrize("case", RANDOM_CASES, ids=[_ids(c) for c in RANDOM_CASES])
+def test_fwd_bwd_random_shapes(case):
+    test_fwd_bwd(case)
+
+
 def test_fwd_bwd_closed_forms_on_gpu():
     """W = 0 gives O = v, dQ = dK = 0, dV = sum of the group's dO (exact up to rounding)."""
     q, k, v, do = to_dev(*attn_inputs(2, 300, 4, 2, 128, "bf16", seed=9))
