@@ -243,6 +243,43 @@ def test_decode_small(W):
         assert torch.equal(x, y)
 
 
+def _random_decode_cases(n, seed=2026):
+    """Seeded random decode shapes: 1-8 sequences, cached lengths anywhere in
+    [0, T_max - 1], group sizes 1-4, random windows."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        B, KV, G = int(rng.integers(1, 9)), int(rng.integers(1, 4)), int(rng.integers(1, 5))
+        Tm = int(rng.integers(2, 600))
+        W = -1 if rng.random() < 0.4 else int(rng.integers(0, Tm + 51))
+        cases.append((B, KV * G, KV, Tm, W))
+    return cases
+
+
+RANDOM_DECODE_CASES = _random_decode_cases(8)
+
+
+@pytest.mark.parametrize("case", RANDOM_DECODE_CASES, ids=[_ids(c) for c in RANDOM_DECODE_CASES])
+def test_decode_random_shapes(case):
+    B, H, KV, Tm, W = case
+    say(f"decode {case}")
+    q, kn, vn, kc, vc, lens = decode_inputs(B, H, KV, 128, 0, Tm - 1, Tm, seed=40 + Tm, poison=True)
+    ro, rlse, _, _ = oracle.decode(f64(q), f64(kn), f64(vn), f64(kc), f64(vc), lens.numpy(), W)
+    qd, knd, vnd, kcd, vcd, ld = to_dev(q, kn, vn, kc, vc, lens)
+    o, lse = nc.decode(qd, knd, vnd, kcd, vcd, ld, window=W, return_lse=True)
+    torch.cuda.synchronize()
+    check(o, ro, "bf16", "o")
+    check_lse(lse, rlse, "bf16", "lse")
+    kc_after, vc_after = kcd.cpu(), vcd.cpu()
+    mask = torch.ones(B, Tm, dtype=torch.bool)
+    for b in range(B):
+        s_ = int(lens[b])
+        assert torch.equal(kc_after[b, s_], kn[b, 0]) and torch.equal(vc_after[b, s_], vn[b, 0])
+        mask[b, s_] = False
+    for a, b_ in ((kc_after, kc), (vc_after, vc)):
+        assert torch.equal(a[mask].view(torch.int16), b_[mask].view(torch.int16))
+
+
 def test_decode_matches_fwd_row():
     """Decode at position s equals row s of the forward over the prefix (the
     incremental computation equals the full one)."""
@@ -323,6 +360,30 @@ def test_prefill(case):
         keep[s_:s_ + Tn] = False
         assert torch.equal(kcd[b, keep].cpu().view(torch.int16), kc[b, keep].view(torch.int16))
         assert torch.equal(vcd[b, keep].cpu().view(torch.int16), vc[b, keep].view(torch.int16))
+
+
+def _random_prefill_cases(n, seed=2025):
+    """Seeded random chunked-prefill shapes: chunks of 1-150 tokens onto cached
+    lengths anywhere in [0, T_max - Tn], group sizes 1-4, random windows."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        B, Tn = int(rng.integers(1, 4)), int(rng.integers(1, 151))
+        KV, G = int(rng.integers(1, 4)), int(rng.integers(1, 5))
+        T_max = int(rng.integers(Tn + 1, 700))
+        hi = int(rng.integers(0, T_max - Tn + 1))
+        lo = int(rng.integers(0, hi + 1))
+        W = -1 if rng.random() < 0.4 else int(rng.integers(0, T_max + 51))
+        cases.append((B, Tn, KV * G, KV, lo, hi, T_max, W))
+    return cases
+
+
+RANDOM_PREFILL_CASES = _random_prefill_cases(8)
+
+
+@pytest.mark.parametrize("case", RANDOM_PREFILL_CASES, ids=[_ids(c) for c in RANDOM_PREFILL_CASES])
+def test_prefill_random_shapes(case):
+    test_prefill(case)
 
 
 def test_prefill_from_empty_cache_is_the_forward():
