@@ -143,6 +143,23 @@ def _random_cases(n, seed=2024):
 RANDOM_CASES = _random_cases(12)
 
 
+def _random_f32_cases(n, seed=2027):
+    """Seeded random shapes for the fp32 kernels: head_dim 64 or 128, T in
+    [1, 260], group sizes 1-3, random windows."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        B, T = int(rng.integers(1, 3)), int(rng.integers(1, 261))
+        KV, G = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+        D = 64 if rng.random() < 0.5 else 128
+        W = -1 if rng.random() < 0.4 else int(rng.integers(0, T + 51))
+        cases.append(("f32", B, T, KV * G, KV, D, W))
+    return cases
+
+
+RANDOM_CASES += _random_f32_cases(6)
+
+
 @pytest.mark.parametrize("case", RANDOM_CASES, ids=[_ids(c) for c in RANDOM_CASES])
 def test_fwd_bwd_random_shapes(case):
     test_fwd_bwd(case)
