@@ -107,6 +107,26 @@ int ncattn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
                int window_left, int window_right, float softmax_scale, int dtype, void *stream);
 
 /*
+ * QK-norm + RoPE fused into the attention forward ("nanochat Admin & Developer
+ * Guide", section 3: q and k are RMS-normalised and rotated before attention;
+ * sections 3 and 6 for the attention).  Exactly ncattn_qknorm_rope(q, k, ...)
+ * followed by ncattn_fwd(q, k, v, ...) with the same arguments: q and k are
+ * normalised and rotated IN PLACE (the backward needs them), then o and lse are
+ * computed from them.  For bf16 the query rows are normalised and rotated in the
+ * forward's prologue (each row once, by the workgroup that attends from it) and k
+ * by a separate pass, which saves the separate read and write of q; for fp32 the
+ * two calls run one after the other.
+ *   q [B][T][n_head][D], k [B][T][n_kv_head][D]: raw on entry, normalised and
+ *   rotated on return; v, o, lse as ncattn_fwd; pos_offset, rope_base, eps and
+ *   qk_gain as ncattn_qknorm_rope; window and scale as ncattn_fwd.  o and v must
+ *   not alias q, k or each other.  Validation and status codes as the two calls.
+ */
+int ncattn_fwd_qknorm_rope(void *q, void *k, const void *v, void *o, float *lse, int B, int T, int n_head,
+                           int n_kv_head, int head_dim, const int32_t *pos_offset, float rope_base, float eps,
+                           float qk_gain, int window_left, int window_right, float softmax_scale, int dtype,
+                           void *stream);
+
+/*
  * Bytes of workspace ncattn_bwd needs for this shape and window: the per-row
  * fp32 D_i = sum_d dO_i O_i (for bf16 stored negated, next to LSE_i log2 e) and,
  * for bf16, the bf16 dS = P (dP - D) tiles of the

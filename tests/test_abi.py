@@ -90,6 +90,27 @@ def test_fwd_validation(L):
     assert fwd(L, scale=float("nan")) == EINVAL
 
 
+def test_fwd_qknorm_rope_validation(L):
+    f = L.ncattn_fwd_qknorm_rope
+    def call(q=P, k=P + 16, v=P + 32, o=P + 48, lse=P + 64, B=1, T=4, H=2, KV=2, D=128, pos=None, base=1e5,
+             eps=1e-6, gain=1.0, wl=-1, wr=0, scale=0.0, dt=0):
+        return f(q, k, v, o, lse, B, T, H, KV, D, pos, base, eps, gain, wl, wr, scale, dt, None)
+    assert call(q=None) == EINVAL
+    assert call(lse=MIS) == EINVAL
+    assert call(k=P) == EINVAL                # q and k must be distinct
+    assert call(o=P + 16) == EINVAL           # o aliases k
+    assert call(v=P) == EINVAL                # v aliases q
+    assert call(H=6, KV=4) == EINVAL
+    assert call(base=0.5) == EINVAL
+    assert call(eps=-1.0) == EINVAL
+    assert call(pos=P + 2) == EINVAL          # pos_offset misaligned
+    assert call(wl=-2) == EINVAL
+    assert call(wr=1) == EINVAL
+    assert call(D=64) == EUNSUP               # bf16 MFMA path is head_dim 128
+    assert call(D=96, dt=1) == EUNSUP
+    assert call(scale=float("inf")) == EINVAL
+
+
 def test_qknorm_rope_validation(L):
     f = L.ncattn_qknorm_rope
     assert f(None, P, 1, 4, 2, 2, 128, None, 1e5, 1e-6, 1.0, 0, None) == EINVAL

@@ -14,7 +14,7 @@ import torch
 import oracle
 import transformer_attention_qknorm_amd as nc
 from conftest import tol_check
-from parity_util import LSE_TOL, TOL, check, check_lse, f64
+from parity_util import LSE_TOL, TOL, check, check_lse, f64, lse_tol_after_bf16_inputs
 from workloads import attn_inputs, decode_inputs, prefill_inputs, replicate_inputs
 
 pytestmark = pytest.mark.gpu
@@ -74,6 +74,47 @@ def test_qknorm_rope_bwd(dtype, B, T, H, KV, D, base, gain, offset):
     check(gqd, ref_q, dtype, "dq_in")
     check(gkd, ref_k, dtype, "dk_in")
     assert torch.equal(qd, q_before) and torch.equal(kd, k_before)
+
+
+FUSED_CASES = [
+    # dtype, B, T, H, KV, D, W, base, gain, pos_offset
+    ("bf16", 2, 200, 4, 2, 128, -1, 100000.0, 1.0, False),
+    ("bf16", 2, 333, 8, 1, 128, 100, 100000.0, math.sqrt(1.2), True),
+    ("bf16", 1, 1, 2, 1, 128, -1, 100000.0, 1.0, True),
+    ("bf16", 3, 130, 6, 6, 128, 64, 10000.0, 1.0, True),
+    ("bf16", 1, 777, 6, 2, 128, 256, 100000.0, math.sqrt(1.2), False),
+    ("f32", 2, 100, 4, 2, 64, 17, 10000.0, math.sqrt(1.2), True),
+    ("f32", 1, 150, 3, 3, 128, -1, 100000.0, 1.0, False),
+]
+
+
+@pytest.mark.parametrize("case", FUSED_CASES, ids=lambda c: "-".join(str(x)[:6] for x in c))
+def test_fwd_qknorm_rope(case):
+    """The fused call: q and k normalised and rotated in place, then the forward
+    on them; checked against the oracle's QK-norm + RoPE followed by its forward."""
+    dtype, B, T, H, KV, D, W, base, gain, offset = case
+    say(f"fwd_qknorm_rope {case}")
+    q, k, v, _ = attn_inputs(B, T, H, KV, D, dtype, seed=300 + T)
+    pos = torch.from_numpy(np.random.default_rng(5).integers(0, 8192, size=B).astype(np.int32)) if offset else None
+    xq, xk = oracle.qknorm_rope(f64(q), f64(k), None if pos is None else pos.numpy(), base, 1e-6, gain)
+    ro, rlse = oracle.attn_fwd(xq, xk, f64(v), W)
+    qd, kd, vd = to_dev(q, k, v)
+    v_before = vd.clone()
+    o, lse = nc.fwd_qknorm_rope_(qd, kd, vd, None if pos is None else pos.to(DEV), rope_base=base, eps=1e-6,
+                                 qk_gain=gain, window=(W, 0))
+    torch.cuda.synchronize()
+    check(qd, xq, dtype, "q'")
+    check(kd, xk, dtype, "k'")
+    check(o, ro, dtype, "o")
+    check_lse(lse, rlse, dtype, "lse", tol=lse_tol_after_bf16_inputs(D, gain) if dtype == "bf16" else None)
+    assert torch.equal(vd, v_before)
+    # the same result as the two calls it fuses
+    q2, k2 = to_dev(q, k)
+    nc.qknorm_rope_(q2, k2, None if pos is None else pos.to(DEV), rope_base=base, eps=1e-6, qk_gain=gain)
+    o2, lse2 = nc.fwd(q2, k2, vd, window=(W, 0))
+    torch.cuda.synchronize()
+    assert torch.equal(kd, k2), "k' differs from the unfused call"
+    check(o, f64(o2), dtype, "o vs unfused")
 
 
 # ------------------------------------------------------------------ forward / backward

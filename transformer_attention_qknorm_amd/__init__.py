@@ -23,7 +23,8 @@ import os
 
 import torch
 
-__all__ = ["qknorm_rope_", "qknorm_rope_bwd_", "fwd", "bwd", "decode", "prefill", "cache_replicate",
+__all__ = ["qknorm_rope_", "qknorm_rope_bwd_", "fwd", "fwd_qknorm_rope_", "bwd", "decode", "prefill",
+           "cache_replicate",
            "window_sizes", "lib", "NcattnError", "LIB_PATH",
            "BF16", "F32", "STATUS", "bwd_workspace", "decode_workspace", "BWD_STAGES"]
 
@@ -53,6 +54,8 @@ def lib():
     L.ncattn_qknorm_rope.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, f32, f32, f32, i32, vp]
     L.ncattn_qknorm_rope_bwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, f32, f32, f32, i32, vp]
     L.ncattn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp]
+    L.ncattn_fwd_qknorm_rope.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, f32, f32, f32, i32, i32,
+                                         f32, i32, vp]
     L.ncattn_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
     L.ncattn_bwd_workspace_bytes.restype = sz
     L.ncattn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32,
@@ -67,7 +70,8 @@ def lib():
     L.ncattn_cache_replicate.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
     L.ncattn_last_error.restype = ctypes.c_char_p
     L.ncattn_version.restype = ctypes.c_char_p
-    for fn in ("ncattn_qknorm_rope", "ncattn_qknorm_rope_bwd", "ncattn_fwd", "ncattn_bwd", "ncattn_decode",
+    for fn in ("ncattn_qknorm_rope", "ncattn_qknorm_rope_bwd", "ncattn_fwd", "ncattn_fwd_qknorm_rope", "ncattn_bwd",
+               "ncattn_decode",
                "ncattn_prefill", "ncattn_cache_replicate"):
         getattr(L, fn).restype = i32
     _lib = L
@@ -181,6 +185,37 @@ def fwd(q, k, v, window=(-1, 0), softmax_scale=None, out=None):
         rc = lib().ncattn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, T, H, k.shape[2], D, wl, wr,
                               _scale(softmax_scale), _dtype_code(q), _stream(dev))
     _check("ncattn_fwd", rc)
+    return o, lse
+
+
+def fwd_qknorm_rope_(q, k, v, pos_offset=None, rope_base=100000.0, eps=1e-6, qk_gain=1.0, window=(-1, 0),
+                     softmax_scale=None, out=None):
+    """QK-norm + RoPE of q and k, in place, fused with the attention forward:
+    the same as qknorm_rope_(q, k, ...) then fwd(q, k, v, ...).  Returns (o, lse)."""
+    dev = _dev(q, k, v)
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or len({q.dtype, k.dtype, v.dtype}) != 1:
+        raise ValueError("ncattn.fwd_qknorm_rope_: q, k, v must be 4-D of one dtype, k and v alike")
+    B, T, H, D = q.shape
+    if k.shape[0] != B or k.shape[1] != T or k.shape[3] != D:
+        raise ValueError("ncattn.fwd_qknorm_rope_: k, v must be [B][T][n_kv_head][D] matching q")
+    if pos_offset is not None:
+        _dev(pos_offset)
+        if pos_offset.dtype != torch.int32 or pos_offset.numel() != B:
+            raise ValueError("ncattn.fwd_qknorm_rope_: pos_offset must be int32 [B]")
+    wl, wr = _window(window)
+    if out is None:
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    else:
+        o, lse = out
+        _dev(o, lse)
+        if o.shape != q.shape or o.dtype != q.dtype or lse.shape != (B, H, T) or lse.dtype != torch.float32:
+            raise ValueError("ncattn.fwd_qknorm_rope_: out must be (o like q, lse fp32 [B][H][T])")
+    with torch.cuda.device(dev):
+        rc = lib().ncattn_fwd_qknorm_rope(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, T, H, k.shape[2], D,
+                                          _ptr(pos_offset), float(rope_base), float(eps), float(qk_gain), wl, wr,
+                                          _scale(softmax_scale), _dtype_code(q), _stream(dev))
+    _check("ncattn_fwd_qknorm_rope", rc)
     return o, lse
 
 

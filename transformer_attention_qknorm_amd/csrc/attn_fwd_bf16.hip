@@ -140,12 +140,26 @@ __device__ __forceinline__ void pv_tile(FwdState &st, const f32x16 (&pacc)[2], c
   }
 }
 
+// QK-norm + RoPE of the query rows, for the fused forward: rotation turns per
+// position of pair j (base^(-2j/D) / 2 pi), epsilon, gain, position offsets.
+struct QkNormRope {
+  double turns[64];
+  float eps, gain;
+  const int32_t *pos_offset;  // device [B] or NULL
+};
+
+// FUSE: the query rows arrive raw; the prologue normalises and rotates them in
+// registers ("nanochat Admin & Developer Guide", section 3: weightless RMSNorm of
+// q, then rotary embedding) and writes them back through Qw (the same array as Q,
+// each row touched by the one lane pair that owns it).
+template <bool FUSE>
 __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const uint16_t *__restrict__ Q,
                                                                const uint16_t *__restrict__ K,
                                                                const uint16_t *__restrict__ V,
                                                                uint16_t *__restrict__ O, float *__restrict__ LSE,
                                                                const int32_t *__restrict__ q_pos0, int B, int Tq,
-                                                               int Tk, int H, int KV, int W, float scale) {
+                                                               int Tk, int H, int KV, int W, float scale,
+                                                               uint16_t *Qw, QkNormRope qn) {
   // Two-slot rings for K and V, each slot its own LDS object so the compiler can
   // tell a copy into one slot from reads of the other.
   __shared__ __attribute__((aligned(1024))) char kb0[kTileBytes];
@@ -213,11 +227,62 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const uint16_t *_
 
   // Q^T operand in registers: lane holds the query of row qw0 + l%32, d = 16 s + 8 hh + [0, 8).
   bf16x8 qreg[8];
-  {
+  if constexpr (!FUSE) {
     const int qr = min(qw0 + (lane & 31), Tq - 1);
     const uint16_t *qp = Q + ((long long)b * Tq + qr) * q_stride + (long long)h * kD + 8 * hh;
 #pragma unroll
     for (int s = 0; s < 8; ++s) qreg[s] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qp + 16 * s));
+  } else {
+    // The row's 128 elements are split between lanes l and l ^ 32 (64 each); the
+    // rotation pairs d and d + 64 are steps s and s + 4 of the same lane.
+    const int qrow = qw0 + (lane & 31);
+    const int qr = min(qrow, Tq - 1);
+    uint16_t *qp = Qw + ((long long)b * Tq + qr) * q_stride + (long long)h * kD + 8 * hh;
+    u32x4 raw[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) raw[s] = *(const u32x4 *)(qp + 16 * s);
+    float ss = 0.f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ss += lo_bf16(raw[s][i]) * lo_bf16(raw[s][i]) + hi_bf16(raw[s][i]) * hi_bf16(raw[s][i]);
+    ss += shfl_xor(ss, 32);
+    const float inv = qn.gain / sqrtf(ss / (float)kD + qn.eps);
+    const double pos = (double)((qn.pos_offset ? qn.pos_offset[b] : 0) + qr);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      u32x4 ya, yb;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float ra[2], rb[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int j0 = 16 * s + 2 * i + e;  // pair index for hh = 0; hh = 1 adds 8
+          // both candidates as uniform (scalar) loads, then a per-lane select: a
+          // per-lane index into the argument block would become a vector load
+          double f_lo = qn.turns[j0], f_hi = qn.turns[j0 + 8];
+          asm("" : "+s"(f_lo), "+s"(f_hi));
+          double turns = pos * (hh ? f_hi : f_lo);
+          turns -= rint(turns);
+          const float tf = (float)turns;
+          const float sn = __builtin_amdgcn_sinf(tf), cs = __builtin_amdgcn_cosf(tf);
+          const float a = (e ? hi_bf16(raw[s][i]) : lo_bf16(raw[s][i])) * inv;
+          const float bb = (e ? hi_bf16(raw[s + 4][i]) : lo_bf16(raw[s + 4][i])) * inv;
+          ra[e] = a * cs - bb * sn;
+          rb[e] = a * sn + bb * cs;
+        }
+        ya[i] = pack_bf16x2(ra[0], ra[1]);
+        yb[i] = pack_bf16x2(rb[0], rb[1]);
+      }
+      raw[s] = ya;
+      raw[s + 4] = yb;
+    }
+    if (qrow < Tq) {
+#pragma unroll
+      for (int s = 0; s < 8; ++s) *(u32x4 *)(qp + 16 * s) = raw[s];
+    }
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qreg[s] = __builtin_bit_cast(bf16x8, raw[s]);
   }
   const TileLane L = make_tile_lane(lane);
 
@@ -321,8 +386,27 @@ hipError_t launch_fwd_bf16_rows(const void *q, const void *k, const void *v, voi
   const int nqb = (Tq + kBlockM - 1) / kBlockM;
   const long long blocks = (long long)nqb * B * H;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(attn_fwd_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (const uint16_t *)q,
-                     (const uint16_t *)k, (const uint16_t *)v, (uint16_t *)o, lse, q_pos0, B, Tq, Tk, H, KV, W, scale);
+  QkNormRope none{};
+  hipLaunchKernelGGL(attn_fwd_bf16_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s, (const uint16_t *)q,
+                     (const uint16_t *)k, (const uint16_t *)v, (uint16_t *)o, lse, q_pos0, B, Tq, Tk, H, KV, W, scale,
+                     nullptr, none);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_bf16_qknorm_rope(void *q, const void *k, const void *v, void *o, float *lse,
+                                       const AttnShape &sh, const int32_t *pos_offset,
+                                       const double *inv_freq_host, float eps, float gain, hipStream_t s) {
+  const int nqb = (sh.T + kBlockM - 1) / kBlockM;
+  const long long blocks = (long long)nqb * sh.B * sh.H;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  QkNormRope qn;
+  for (int j = 0; j < 64; ++j) qn.turns[j] = inv_freq_host[j] / 6.283185307179586;
+  qn.eps = eps;
+  qn.gain = gain;
+  qn.pos_offset = pos_offset;
+  hipLaunchKernelGGL(attn_fwd_bf16_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s, (const uint16_t *)q,
+                     (const uint16_t *)k, (const uint16_t *)v, (uint16_t *)o, lse, nullptr, sh.B, sh.T, sh.T, sh.H,
+                     sh.KV, sh.window, sh.scale, (uint16_t *)q, qn);
   return hipGetLastError();
 }
 

@@ -53,6 +53,13 @@ size_t bwd_workspace_bytes(int B, int T, int H, int W, bool bf16);
 // bf16, head_dim 128, MFMA kernels.
 hipError_t launch_fwd_bf16(const void *q, const void *k, const void *v, void *o, float *lse,
                            const AttnShape &sh, hipStream_t s);
+// The same forward with QK-norm + RoPE of q done in its prologue: each query row
+// is normalised and rotated in registers and written back into q, which the
+// attention then uses; k must already be normalised.  inv_freq_host[j] =
+// base^(-2j/D) in fp64.
+hipError_t launch_fwd_bf16_qknorm_rope(void *q, const void *k, const void *v, void *o, float *lse,
+                                       const AttnShape &sh, const int32_t *pos_offset,
+                                       const double *inv_freq_host, float eps, float gain, hipStream_t s);
 // The same forward for Tq query rows per sequence at positions q_pos0[b] + r
 // (q_pos0 device int32 [B], NULL for 0) over key rows [0, q_pos0[b] + Tq) of K/V
 // arrays with Tk rows per sequence; lse may be NULL.  Sequences whose offset

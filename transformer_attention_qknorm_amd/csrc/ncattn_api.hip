@@ -165,6 +165,42 @@ int ncattn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
   return hip_status(e, fn);
 }
 
+int ncattn_fwd_qknorm_rope(void *q, void *k, const void *v, void *o, float *lse, int B, int T, int n_head,
+                           int n_kv_head, int head_dim, const int32_t *pos_offset, float rope_base, float eps,
+                           float qk_gain, int window_left, int window_right, float softmax_scale, int dtype,
+                           void *stream) {
+  const char *fn = "ncattn_fwd_qknorm_rope";
+  NC_PTR(q, fn);
+  NC_PTR(k, fn);
+  NC_PTR(v, fn);
+  NC_PTR(o, fn);
+  NC_PTR(lse, fn);
+  double inv_freq[64];
+  NC_TRY(check_qknorm(fn, B, T, n_head, n_kv_head, head_dim, pos_offset, rope_base, eps, qk_gain, dtype,
+                      inv_freq));
+  NC_TRY(check_window(fn, window_left, window_right));
+  NC_TRY(check_attn_support(fn, dtype, T, n_head, head_dim));
+  if (!isfinite(softmax_scale)) return fail(NCATTN_EINVAL, "%s: softmax_scale must be finite", fn);
+  if (q == k) return fail(NCATTN_EINVAL, "%s: q and k must be distinct", fn);
+  if (o == q || o == k || o == v || v == q || v == k)
+    return fail(NCATTN_EINVAL, "%s: o and v must not alias q, k or each other", fn);
+  ncattn::AttnShape sh{B, T, n_head, n_kv_head, head_dim, window_left, resolve_scale(softmax_scale, head_dim)};
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if (dtype == NCATTN_BF16) {
+    // k alone (no query rows), then the forward that normalises q in its prologue
+    e = ncattn::launch_qknorm_rope(k, k, B, T, 0, n_kv_head, head_dim, pos_offset, inv_freq, eps, qk_gain, true, s);
+    if (e == hipSuccess)
+      e = ncattn::launch_fwd_bf16_qknorm_rope(q, k, v, o, lse, sh, pos_offset, inv_freq, eps, qk_gain, s);
+  } else {
+    e = ncattn::launch_qknorm_rope(q, k, B, T, n_head, n_kv_head, head_dim, pos_offset, inv_freq, eps, qk_gain,
+                                   false, s);
+    if (e == hipSuccess)
+      e = ncattn::launch_fwd_f32((const float *)q, (const float *)k, (const float *)v, (float *)o, lse, sh, s);
+  }
+  return hip_status(e, fn);
+}
+
 size_t ncattn_bwd_workspace_bytes(int B, int T, int n_head, int n_kv_head, int head_dim, int window_left,
                                   int dtype) {
   (void)n_kv_head;
