@@ -426,6 +426,40 @@ def main():
                                           "qk_gain": round(math.sqrt(1.2), 6)}
     del gq, gk
 
+    # QK-norm + RoPE fused into the forward (q normalised and rotated in the
+    # forward's prologue, k by the standalone kernel) against the two calls it
+    # replaces, for each window of the layer pattern; the fused forward is not
+    # part of the step above.
+    fq, fk = Lq["q"].clone(), Lq["k"].clone()
+    fo, flse = torch.empty_like(fq), torch.empty_like(Lq["lse"])
+    fused = {}
+    for W in sorted(set(cfg.windows)):
+        def two_calls():
+            nc.qknorm_rope_(fq, fk, None, rope_base=cfg.rope_base, eps=1e-6)
+            nc.fwd(fq, fk, Lq["v"], window=(W, 0), out=(fo, flse))
+
+        def one_call():
+            nc.fwd_qknorm_rope_(fq, fk, Lq["v"], None, rope_base=cfg.rope_base, eps=1e-6, window=(W, 0),
+                                out=(fo, flse))
+        us = {}
+        for name, fn in (("two_calls", two_calls), ("fused", one_call)):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(20):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us[name] = e0.elapsed_time(e1) * 1e3 / 20
+        fl = 4 * D * visible_pairs(T, W) * B * H
+        fused["full" if W < 0 else f"w{W}"] = {
+            "two_calls_us": round(us["two_calls"], 2), "fused_us": round(us["fused"], 2),
+            "fused_fwd_TFLOPs": round(fl / (us["fused"] * 1e-6) / 1e12, 1)}
+    detail["fwd_qknorm_rope"] = fused
+    del fq, fk, fo, flse
+
     prefill = None
     if not args.no_decode:
         from workloads import PREFILL, prefill_inputs
