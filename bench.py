@@ -235,7 +235,8 @@ def main():
     ap.add_argument("--no-clock", action="store_true",
                     help="skip the 2 s graphics-clock measurement under the dominant kernel")
     ap.add_argument("--no-configs", action="store_true",
-                    help="skip the per-layer-type fwd/bwd timings of the d20 and GQA workloads")
+                    help="skip the per-layer-type fwd/bwd timings of the d20 and GQA workloads and the "
+                         "fused QK-norm + RoPE forward comparison")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, copy a buffer of this many MiB device-to-device 3 times: a kernel of "
                          "known traffic for calibrating rocprofv3's FETCH_SIZE/WRITE_SIZE counters")
@@ -433,7 +434,7 @@ def main():
     fq, fk = Lq["q"].clone(), Lq["k"].clone()
     fo, flse = torch.empty_like(fq), torch.empty_like(Lq["lse"])
     fused = {}
-    for W in sorted(set(cfg.windows)):
+    for W in ([] if args.no_configs else sorted(set(cfg.windows))):
         def two_calls():
             nc.qknorm_rope_(fq, fk, None, rope_base=cfg.rope_base, eps=1e-6)
             nc.fwd(fq, fk, Lq["v"], window=(W, 0), out=(fo, flse))
@@ -457,7 +458,8 @@ def main():
         fused["full" if W < 0 else f"w{W}"] = {
             "two_calls_us": round(us["two_calls"], 2), "fused_us": round(us["fused"], 2),
             "fused_fwd_TFLOPs": round(fl / (us["fused"] * 1e-6) / 1e12, 1)}
-    detail["fwd_qknorm_rope"] = fused
+    if fused:
+        detail["fwd_qknorm_rope"] = fused
     del fq, fk, fo, flse
 
     prefill = None
