@@ -168,6 +168,32 @@ def test_fwd_bwd(case):
     check(dv, rdv, dtype, "dv")
 
 
+def test_long_sequence_window_sampled():
+    """T = 32768 (256 query tiles, 512 key tiles), window 1024, on sampled rows.
+    With inputs taken as post-norm the windowed attention is translation
+    invariant, so the oracle runs on the slice [c - 2W, c + W + 128): query rows
+    [c, c + 128) see their whole windows inside it (o, lse, dq), and every query
+    that sees keys [c, c + 128) lies inside it with its whole window (dk, dv)."""
+    B, T, H, KV, D, W, R = 1, 32768, 2, 1, 128, 1024, 128
+    q, k, v, do = attn_inputs(B, T, H, KV, D, "bf16", seed=77)
+    qd, kd, vd, dod = to_dev(q, k, v, do)
+    o, lse = nc.fwd(qd, kd, vd, window=(W, 0))
+    dq, dk, dv = nc.bwd(qd, kd, vd, o, lse, dod, window=(W, 0))
+    torch.cuda.synchronize()
+    for c in (T // 2 + 37, T - R):
+        say(f"long sequence: rows [{c}, {c + R})")
+        a, e = c - 2 * W, min(T, c + W + R)
+        sq, sk, sv, sdo = (f64(t[:, a:e]) for t in (q, k, v, do))
+        ro, rlse = oracle.attn_fwd(sq, sk, sv, W)
+        rdq, rdk, rdv = oracle.attn_bwd(sq, sk, sv, sdo, W)
+        r = slice(c - a, c - a + R)
+        check(o[:, c:c + R], ro[:, r], "bf16", "o")
+        check_lse(lse[:, :, c:c + R], rlse[:, :, r], "bf16", "lse")
+        check(dq[:, c:c + R], rdq[:, r], "bf16", "dq")
+        check(dk[:, c:c + R], rdk[:, r], "bf16", "dk")
+        check(dv[:, c:c + R], rdv[:, r], "bf16", "dv")
+
+
 def _random_cases(n, seed=2024):
     """Seeded random shapes (bf16, head_dim 128): ragged T in [1, 400], group sizes
     1-4, windows unbounded or drawn up to T + 50 (so some exceed T)."""
