@@ -327,6 +327,30 @@ def test_decode_small(W):
         assert torch.equal(x, y)
 
 
+@pytest.mark.parametrize("W", [-1, 4096])
+def test_decode_long_cache(W):
+    """Caches of 65600 slots with up to 65535 keys in use (512 split chunks for one
+    sequence), slots past each length NaN-poisoned."""
+    say(f"decode long cache W={W}")
+    B, H, KV, D, Tm = 2, 4, 2, 128, 65600
+    q, kn, vn, kc, vc, lens = decode_inputs(B, H, KV, D, 1, 100, Tm, seed=23, poison=False)
+    lens = torch.tensor([65535, 40001], dtype=torch.int32)
+    for b in range(B):
+        kc[b, int(lens[b]):] = float("nan")
+        vc[b, int(lens[b]):] = float("nan")
+    ro, rlse, _, _ = oracle.decode(f64(q), f64(kn), f64(vn), f64(kc), f64(vc), lens.numpy(), W)
+    qd, knd, vnd, kcd, vcd, ld = to_dev(q, kn, vn, kc, vc, lens)
+    o, lse = nc.decode(qd, knd, vnd, kcd, vcd, ld, window=W, return_lse=True)
+    torch.cuda.synchronize()
+    check(o, ro, "bf16", "o")
+    check_lse(lse, rlse, "bf16", "lse")
+    kc_after, vc_after = kcd.cpu(), vcd.cpu()
+    for b in range(B):
+        s = int(lens[b])
+        assert torch.equal(kc_after[b, s], kn[b, 0]) and torch.equal(vc_after[b, s], vn[b, 0])
+        assert torch.equal(kc_after[b, :s].view(torch.int16), kc[b, :s].view(torch.int16))
+
+
 def _random_decode_cases(n, seed=2026):
     """Seeded random decode shapes: 1-8 sequences, cached lengths anywhere in
     [0, T_max - 1], group sizes 1-4, random windows."""
