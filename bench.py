@@ -1,26 +1,28 @@
 """Benchmark of the attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gqa|d12|d20] [--no-cpu-baseline]
 
-One step = the training-side hot path of a nanochat d12-shaped model's attention
-(B=8, T=2048, n_head=n_kv_head=6, head_dim=128, bf16) over its four SSSL layers
-(windows 1024, 1024, 1024, full causal): per layer QK-norm + RoPE, attention
-forward, attention backward.  Inputs are seeded synthetic N(0, 1) tensors
-already resident in HBM, one distinct set per layer.  The engine-decode row (64
-sequences, cache lengths U[256, 8192], 10 heads, head_dim 128) is timed in the
-same run at the full-causal and 1024 windows and reported under "decode"; the
-d20 and GQA workloads' forward and backward per layer type under "configs".
+One step = the training-side hot path of one attention workload over its four
+SSSL layers, per layer the attention forward and backward (plus QK-norm + RoPE
+of q and k first, for the workloads whose recipe starts from raw q, k).  The
+default workload, the largest of the five, is the grouped-query layer (B=16,
+T=4096, n_head=12, n_kv_head=4, head_dim=128, bf16, windows 2048, 2048, 2048,
+full causal; q, k, v taken as already normalised and rotated).  Inputs are
+seeded synthetic N(0, 1) tensors already resident in HBM, one distinct set per
+layer.  The d12 and d20 layers are timed per layer type under "configs"; the
+engine decode (64 sequences, cache lengths U[256, 8192], 10 heads, head_dim 128)
+at the full-causal and 1024 windows under "decode".
 
 Prints ONE JSON line.  ``value`` = unmasked attention FLOPs of a step (fwd 4*D
-and bwd 8*D per visible (query, key) pair and head) / wall time of the step
-(QK-norm included in the time).  ``roofline`` is for the kernel with the largest
-share of the step, timed with HIP events on the stream it runs on inside the
-timed region (step s brackets that kernel of layer s mod 4; the per-kernel
-figures under "detail" come from an untimed pass with events around every
-kernel, since each event is a GPU packet of its own between kernels); ``traffic``
-comes from the committed rocprofv3 counter summary in profiles/ when it was
-taken on the current kernel source, else null.  ``cpu_baseline`` times the CPU
-oracle on a bounded sample of the same workload.
+and bwd 8*D per visible (query, key) pair and head) / wall time of the step.
+``roofline`` is for the kernel with the largest share of the step, timed with
+HIP events on the stream it runs on inside the timed region (step s brackets that
+kernel of layer s mod 4; the per-kernel figures under "detail" come from an
+untimed pass with events around every kernel, since each event is a GPU packet
+of its own between kernels); ``traffic`` comes from the committed rocprofv3
+counter summary in profiles/ when it was taken on the current kernel source for
+this workload, else null.  ``cpu_baseline`` times the CPU oracle on a bounded
+sample of the same workload.
 """
 
 from __future__ import annotations
@@ -48,6 +50,15 @@ def visible_pairs(T, W):
     return (W + 1) * (W + 2) // 2 + (T - W - 1) * (W + 1)
 
 
+def decode_algorithmic_bytes(lens, H, KV, D, W, elem_bytes=2):
+    """Bytes one decode call must move: the visible cached K and V rows of every
+    sequence (the newest key comes from k_new/v_new), k_new and v_new read and
+    written into the cache, q read and o written."""
+    row = KV * D * elem_bytes
+    n_cached = sum(s - (0 if W < 0 else max(0, s - W)) for s in lens)
+    return n_cached * 2 * row + len(lens) * 4 * row + len(lens) * 2 * H * D * elem_bytes
+
+
 def kernel_source_hash(name):
     p = os.path.join(ROOT, "transformer_attention_qknorm_amd", "csrc", name)
     h = hashlib.sha256()
@@ -60,17 +71,19 @@ def kernel_source_hash(name):
 
 KERNEL_SOURCES = {"fwd": "attn_fwd_bf16.hip", "bwd_dkdv": "attn_bwd_bf16.hip", "bwd_dq": "attn_bwd_bf16.hip",
                   "bwd_delta": "attn_bwd_bf16.hip", "qknorm_rope": "qknorm_rope.hip",
-                  "decode_split": "attn_decode.hip"}
+                  "decode_split": "attn_decode.hip", "decode_combine": "attn_decode.hip"}
 
 
-def measured_traffic(kernel):
-    """HBM bytes per launch from the committed counter summary, if it matches the source."""
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from the committed counter
+    summary (profiles/traffic.json), if it was taken on the kernel's current
+    source; else None."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(p):
         return None
     try:
         d = json.load(open(p))
-        e = d["kernels"][kernel]
+        e = d["workloads"][workload]["kernels"][kernel]
         if e.get("source_hash") != kernel_source_hash(KERNEL_SOURCES[kernel]):
             return None
         return e["bytes_per_launch"]
@@ -79,8 +92,9 @@ def measured_traffic(kernel):
 
 
 def cpu_baseline(cfg, budget_s=12.0):
-    """Time the CPU oracle (fwd + bwd of one (b, head) slice at a time, S and L
-    windows alternately) on the same seeded inputs until ~budget_s has passed."""
+    """Time the CPU oracle (fwd + bwd of one (b, head) slice at a time, the short
+    and the long window alternately) on the same seeded inputs until ~budget_s
+    has passed."""
     import numpy as np
     import oracle
     from workloads import config_inputs
@@ -90,13 +104,15 @@ def cpu_baseline(cfg, budget_s=12.0):
     except Exception:  # pragma: no cover
         cores = os.cpu_count() or 1
     q, k, v, do = config_inputs(cfg)
+    G = cfg.H // cfg.KV
     f = lambda t: t.double().numpy()
     flops, t_used, slices = 0, 0.0, []
     i = 0
     while t_used < budget_s and i < 8 * cfg.B * cfg.H:
         W = cfg.windows[0] if i % 2 == 0 else -1
         b, h = (i // 2) % cfg.B, (i // 2) % cfg.H
-        sq, sk, sv, sdo = (f(x[b:b + 1, :, h:h + 1]) for x in (q, k, v, do))
+        g = h // G
+        sq, sk, sv, sdo = (f(x[b:b + 1, :, j:j + 1]) for x, j in ((q, h), (k, g), (v, g), (do, h)))
         t0 = time.perf_counter()
         oracle.attn_fwd(sq, sk, sv, W)
         oracle.attn_bwd(sq, sk, sv, sdo, W)
@@ -105,9 +121,9 @@ def cpu_baseline(cfg, budget_s=12.0):
         slices.append((b, h, W))
         i += 1
     return {"value": flops / t_used / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{len(slices)} (b, head) slices of the d12 workload (T=2048, D=128; {len(set(slices))} "
-                      f"distinct (b, head, window)), alternating window 1024 and full causal, fwd+bwd in float64 "
-                      f"numpy; {t_used:.1f} s of CPU work"}
+            "sample": f"{len(slices)} (b, head) slices of the {cfg.name} workload (T={cfg.T}, D={cfg.D}; "
+                      f"{len(set(slices))} distinct (b, head, window)), alternating window {cfg.windows[0]} and "
+                      f"full causal, fwd+bwd in float64 numpy; {t_used:.1f} s of CPU work"}
 
 
 class ClockSampler:
@@ -177,6 +193,20 @@ class ClockSampler:
                 "samples": len(xs)}
 
 
+def event_us(torch, stream, fn, iters, warm=3):
+    """Average microseconds per call of fn over `iters` calls bracketed by HIP events."""
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(iters):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / iters
+
+
 def time_config(nc, torch, cfg, dev, stream, iters=10):
     """Forward and backward of each layer type (short window, full causal) of a
     workload, timed with HIP events over `iters` calls each: the per-layer-type
@@ -211,7 +241,7 @@ def time_config(nc, torch, cfg, dev, stream, iters=10):
             "fwd_tflops": round(ff / tf / 1e12, 1), "bwd_tflops": round(fb / tb / 1e12, 1),
             "fwd_bwd_tflops": round((ff + fb) / (tf + tb) / 1e12, 1),
             "frac_bf16_peak": round((ff + fb) / (tf + tb) / 1e12 / PEAK_BF16_TFLOPS, 4),
-            "_f": ff + fb, "_t": tf + tb}
+            "workspace_bytes": int(ws.numel()), "_f": ff + fb, "_t": tf + tb}
         del ws
     n = {key: sum(1 for W in cfg.windows if (W < 0) == (key == "L")) for key in layers}
     tot_f = sum(n[key] * layers[key].pop("_f") for key in layers)
@@ -222,38 +252,55 @@ def time_config(nc, torch, cfg, dev, stream, iters=10):
             "sssl_frac_bf16_peak": round(tot_f / tot_t / 1e12 / PEAK_BF16_TFLOPS, 4), "timed_calls": iters}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--profile-steps", type=int, default=5,
-                    help="untimed steps with an event around every kernel, for the per-kernel breakdown")
-    ap.add_argument("--decode-iters", type=int, default=20)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--no-clock", action="store_true",
-                    help="skip the 2 s graphics-clock measurement under the dominant kernel")
-    ap.add_argument("--no-configs", action="store_true",
-                    help="skip the per-layer-type fwd/bwd timings of the d20 and GQA workloads and the "
-                         "fused QK-norm + RoPE forward comparison")
-    ap.add_argument("--copy-probe-mib", type=int, default=0,
-                    help="after timing, copy a buffer of this many MiB device-to-device 3 times: a kernel of "
-                         "known traffic for calibrating rocprofv3's FETCH_SIZE/WRITE_SIZE counters")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: measures one GPU only (the attention path needs no collective); "
-              "run with --gpus 1", file=sys.stderr)
-        sys.exit(2)
+def qknorm_detail(nc, torch, cfg, dev, stream):
+    """QK-norm + RoPE of a workload's q, k (GB/s), its backward, the logit-gain
+    variant, and the forward with QK-norm + RoPE fused into it against the two
+    calls it replaces, per window of the layer pattern."""
+    from workloads import config_inputs
+    q0, k0, v0, _ = config_inputs(cfg)
+    q, k, v = q0.to(dev), k0.to(dev), v0.to(dev)
+    B, T, H, KV, D = cfg.B, cfg.T, cfg.H, cfg.KV, cfg.D
+    base = cfg.rope_base
+    qk_bytes = B * T * (H + KV) * D * 2 * 2
+    out = {}
+    us = event_us(torch, stream, lambda: nc.qknorm_rope_(q, k, None, rope_base=base, eps=1e-6), 20)
+    out["qknorm_rope"] = {"us": round(us, 2), "GBps": round(qk_bytes / (us * 1e-6) / 1e9, 1),
+                          "frac_hbm": round(qk_bytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+                          "algorithmic_bytes": qk_bytes}
+    us = event_us(torch, stream, lambda: nc.qknorm_rope_(q, k, None, rope_base=base, eps=1e-6,
+                                                         qk_gain=math.sqrt(1.2)), 20)
+    out["qknorm_rope_gain_sqrt1p2"] = {"us": round(us, 2), "GBps": round(qk_bytes / (us * 1e-6) / 1e9, 1),
+                                       "qk_gain": round(math.sqrt(1.2), 6)}
+    dq, dk = torch.empty_like(q), torch.empty_like(k)
+    us = event_us(torch, stream, lambda: nc.qknorm_rope_bwd_(dq, dk, q, k, None, rope_base=base, eps=1e-6), 20)
+    nb = 3 * (qk_bytes // 2)
+    out["qknorm_rope_bwd"] = {"us": round(us, 2), "GBps": round(nb / (us * 1e-6) / 1e9, 1),
+                              "frac_hbm": round(nb / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4), "algorithmic_bytes": nb}
+    o = torch.empty_like(q)
+    lse = torch.empty(B, H, T, dtype=torch.float32, device=dev)
+    fused = {}
+    for W in sorted(set(cfg.windows)):
+        def two_calls():
+            nc.qknorm_rope_(q, k, None, rope_base=base, eps=1e-6)
+            nc.fwd(q, k, v, window=(W, 0), out=(o, lse))
 
-    import torch
-    import transformer_attention_qknorm_amd as nc
-    from workloads import D12, DECODE, config_inputs, decode_inputs
+        def one_call():
+            nc.fwd_qknorm_rope_(q, k, v, None, rope_base=base, eps=1e-6, window=(W, 0), out=(o, lse))
+        t2 = event_us(torch, stream, two_calls, 20)
+        t1 = event_us(torch, stream, one_call, 20)
+        fl = 4 * D * visible_pairs(T, W) * B * H
+        fused["full" if W < 0 else f"w{W}"] = {"two_calls_us": round(t2, 2), "fused_us": round(t1, 2),
+                                               "fused_fwd_TFLOPs": round(fl / (t1 * 1e-6) / 1e12, 1)}
+    out["fwd_qknorm_rope"] = fused
+    del q, k, v, dq, dk, o, lse
+    torch.cuda.empty_cache()
+    return out
 
-    nc.lib()  # fail loudly if the HIP library is missing
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    cfg = D12
+
+def run_step_bench(nc, torch, cfg, dev, stream, args):
+    """The timed training step of `cfg` (see the module docstring).  Returns
+    (ms_per_step, value, roofline, detail, layers, workspace, launch)."""
+    from workloads import config_inputs
     B, T, H, KV, D = cfg.B, cfg.T, cfg.H, cfg.KV, cfg.D
     q0, k0, v0, do0 = config_inputs(cfg)
     layers = []
@@ -263,27 +310,37 @@ def main():
         L["lse"] = torch.empty(B, H, T, dtype=torch.float32, device=dev)
         L["dq"], L["dk"], L["dv"] = torch.empty_like(L["q"]), torch.empty_like(L["k"]), torch.empty_like(L["v"])
         layers.append(L)
-    ws = nc.bwd_workspace(layers[0]["q"], layers[0]["k"], (-1, 0))  # the full-causal band is the largest
-    names = ["qknorm_rope", "fwd", "bwd_delta", "bwd_dkdv", "bwd_dq"]
-    stream = torch.cuda.current_stream(dev)
+    del q0, k0, v0, do0
+    # one workspace for every layer, sized for the window that needs the most
+    lib = nc.lib()
+    W_ws = max(set(cfg.windows), key=lambda W: lib.ncattn_bwd_workspace_bytes(B, T, H, KV, D, W, nc.BF16))
+    ws = nc.bwd_workspace(layers[0]["q"], layers[0]["k"], (W_ws, 0))
+    with_qk = not cfg.pre_normed
+    names = (["qknorm_rope"] if with_qk else []) + ["fwd", "bwd_delta", "bwd_dkdv", "bwd_dq"]
+
+    def kernels(L):
+        out = []
+        if with_qk:
+            out.append(lambda: nc.qknorm_rope_(L["q"], L["k"], None, rope_base=cfg.rope_base, eps=1e-6))
+        out.append(lambda: nc.fwd(L["q"], L["k"], L["v"], window=(L["W"], 0), out=(L["o"], L["lse"])))
+        for st in ("preprocess", "dkdv", "dq"):
+            out.append(lambda st=st: nc.bwd(L["q"], L["k"], L["v"], L["o"], L["lse"], L["do"], window=(L["W"], 0),
+                                            out=(L["dq"], L["dk"], L["dv"]), workspace=ws, stage=st))
+        return out
+    launch = [kernels(L) for L in layers]
 
     def step(ev=None):
         # ev: {(layer, i): Event}; event i of a layer is recorded before kernel i of
         # `names` (i = len(names): after the last), only where ev has an entry
-        for li, L in enumerate(layers):
-            def rec(i):
+        for li in range(len(layers)):
+            for i, fn in enumerate(launch[li]):
                 e = None if ev is None else ev.get((li, i))
                 if e is not None:
                     e.record(stream)
-            rec(0)
-            nc.qknorm_rope_(L["q"], L["k"], None, rope_base=cfg.rope_base, eps=1e-6)
-            rec(1)
-            nc.fwd(L["q"], L["k"], L["v"], window=(L["W"], 0), out=(L["o"], L["lse"]))
-            rec(2)
-            for si, st in enumerate(("preprocess", "dkdv", "dq")):
-                nc.bwd(L["q"], L["k"], L["v"], L["o"], L["lse"], L["do"], window=(L["W"], 0),
-                       out=(L["dq"], L["dk"], L["dv"]), workspace=ws, stage=st)
-                rec(3 + si)
+                fn()
+            e = None if ev is None else ev.get((li, len(names)))
+            if e is not None:
+                e.record(stream)
 
     nl = len(layers)
     for _ in range(args.warmup):
@@ -335,7 +392,8 @@ def main():
     f_bwd = [8 * D * p for p in pairs]
     flops_step = sum(f_fwd) + sum(f_bwd)
     value = flops_step / (ms_per_step * 1e-3) / 1e12
-    t_attn = sum(sum(dur[n]) for n in names[1:])
+    attn_names = [n for n in names if n != "qknorm_rope"]
+    t_attn = sum(totals[n] for n in attn_names)
     # algorithmic work attributed per kernel: fwd 4D/pair; dkdv computes dV, dP, dK
     # (6D/pair); dq computes dQ (2D/pair); the S/dP recomputations are not counted
     share = {"fwd": 4, "bwd_dkdv": 6, "bwd_dq": 2}
@@ -343,14 +401,15 @@ def main():
         work = sum(share[dominant] * D * p for p in pairs)
         achieved = work / (sum(dom_ms) * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "kernel": dominant}
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "kernel": dominant,
+                "work_per_unit": f"{share[dominant]}*D flops per visible (query, key) pair and head",
+                "units_per_launch": sum(pairs) // nl}
     else:
         nbytes = (B * T * (H + KV) * D * 2 * 2) if dominant == "qknorm_rope" else (B * T * H * D * 2 * 2 + B * H * T * 4)
         achieved = nbytes * len(layers) / (sum(dom_ms) * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBPS, 4), "kernel": dominant}
-    tr = measured_traffic(dominant)
-    roof["traffic"] = None if tr is None else tr
+    roof["traffic"] = measured_traffic(dominant, cfg.name)
     roof["avg_launch_us"] = round(sum(dom_ms) * 1e3 / nl, 2)
     roof["launches_timed"] = sum(len(x) for x in samples)
 
@@ -358,109 +417,84 @@ def main():
     for li, L in enumerate(layers):
         tf = dur["fwd"][li]
         tb = dur["bwd_delta"][li] + dur["bwd_dkdv"][li] + dur["bwd_dq"][li]
-        per_layer.append({"window": L["W"], "fwd_us": round(tf * 1e3, 1), "bwd_us": round(tb * 1e3, 1),
-                          "fwd_tflops": round(f_fwd[li] / (tf * 1e-3) / 1e12, 1),
-                          "bwd_tflops": round(f_bwd[li] / (tb * 1e-3) / 1e12, 1),
-                          "qknorm_rope_us": round(dur["qknorm_rope"][li] * 1e3, 1),
-                          "dkdv_us": round(dur["bwd_dkdv"][li] * 1e3, 1), "dq_us": round(dur["bwd_dq"][li] * 1e3, 1)})
-    qk_bytes = B * T * (H + KV) * D * 2 * 2
+        e = {"window": L["W"], "fwd_us": round(tf * 1e3, 1), "bwd_us": round(tb * 1e3, 1),
+             "fwd_tflops": round(f_fwd[li] / (tf * 1e-3) / 1e12, 1),
+             "bwd_tflops": round(f_bwd[li] / (tb * 1e-3) / 1e12, 1),
+             "dkdv_us": round(dur["bwd_dkdv"][li] * 1e3, 1), "dq_us": round(dur["bwd_dq"][li] * 1e3, 1),
+             "delta_us": round(dur["bwd_delta"][li] * 1e3, 1)}
+        if with_qk:
+            e["qknorm_rope_us"] = round(dur["qknorm_rope"][li] * 1e3, 1)
+        per_layer.append(e)
     detail = {
         "fwd_bwd_tflops_kernels_only": round(flops_step / (t_attn * 1e-3) / 1e12, 1),
         "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
-        "qknorm_rope_gbps": round(qk_bytes * len(layers) / (totals["qknorm_rope"] * 1e-3) / 1e9, 1),
         "kernel_ms_per_step": {n: round(totals[n], 4) for n in names},
+        "kernel_share_of_step": {n: round(totals[n] / sum(totals.values()), 4) for n in names},
         "layers": per_layer,
         "algorithmic_gflop_per_step": round(flops_step / 1e9, 2),
+        "bwd_workspace_bytes": int(ws.numel()),
         "per_kernel_from": f"untimed pass of {prof_steps} steps with events around every kernel",
     }
+    names_idx = {n: i for i, n in enumerate(names)}
+    dom_launch = launch[-1][names_idx[dominant]]
+    return ms_per_step, value, roof, detail, layers, ws, dom_launch, dominant
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gqa", choices=["gqa", "d12", "d20"],
+                    help="workload of the timed step (default: the grouped-query layer, the largest)")
+    ap.add_argument("--profile-steps", type=int, default=5,
+                    help="untimed steps with an event around every kernel, for the per-kernel breakdown")
+    ap.add_argument("--decode-iters", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the 2 s graphics-clock measurement under the dominant kernel")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-layer-type fwd/bwd timings of the other workloads and the QK-norm + RoPE "
+                         "figures (standalone, backward, gain variant, fused forward)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after timing, copy a buffer of this many MiB device-to-device 3 times: a kernel of "
+                         "known traffic for calibrating rocprofv3's FETCH_SIZE/WRITE_SIZE counters")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: measures one GPU only (the attention path needs no collective); "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import transformer_attention_qknorm_amd as nc
+    from workloads import D12, D20, DECODE, GQA, decode_inputs
+
+    nc.lib()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    cfg = {"gqa": GQA, "d12": D12, "d20": D20}[args.workload]
+    ms_per_step, value, roof, detail, layers, ws, dom_launch, dominant = run_step_bench(nc, torch, cfg, dev, stream,
+                                                                                        args)
 
     # Graphics clock while the dominant kernel runs back to back for 2 s (full
     # causal layer), after the timed region: amdsmi's table lags about a second.
-    Ll = layers[-1]
-    launch = {"qknorm_rope": lambda: nc.qknorm_rope_(Ll["q"], Ll["k"], None, rope_base=cfg.rope_base, eps=1e-6),
-              "fwd": lambda: nc.fwd(Ll["q"], Ll["k"], Ll["v"], window=(Ll["W"], 0), out=(Ll["o"], Ll["lse"]))}
-    for st, n in (("preprocess", "bwd_delta"), ("dkdv", "bwd_dkdv"), ("dq", "bwd_dq")):
-        launch[n] = (lambda st=st: nc.bwd(Ll["q"], Ll["k"], Ll["v"], Ll["o"], Ll["lse"], Ll["do"], window=(Ll["W"], 0),
-                                          out=(Ll["dq"], Ll["dk"], Ll["dv"]), workspace=ws, stage=st))
     if not args.no_clock:
         clock = ClockSampler()
         with clock:
             t_end = time.perf_counter() + 2.0
             while time.perf_counter() < t_end:
-                for _ in range(10):
-                    launch[dominant]()
+                for _ in range(5):
+                    dom_launch()
                 torch.cuda.synchronize()
         detail["gpu_clock_mhz"] = dict(clock.summary(skip_s=1.2), under=f"{dominant} back to back, full-causal layer",
                                        source="amdsmi, every 20 ms, samples of the last 0.8 s")
+    del layers, ws, dom_launch
+    torch.cuda.empty_cache()
 
-    # Backward of QK-norm + RoPE (not part of the step's attention FLOPs): read the
-    # forward's inputs and the output gradients, write the input gradients.
-    Lq = layers[0]
-    for _ in range(3):
-        nc.qknorm_rope_bwd_(Lq["dq"], Lq["dk"], Lq["q"], Lq["k"], None, rope_base=cfg.rope_base, eps=1e-6)
-    torch.cuda.synchronize()
-    qb_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
-    for a, b in qb_ev:
-        a.record(stream)
-        nc.qknorm_rope_bwd_(Lq["dq"], Lq["dk"], Lq["q"], Lq["k"], None, rope_base=cfg.rope_base, eps=1e-6)
-        b.record(stream)
-    torch.cuda.synchronize()
-    qb_us = sum(a.elapsed_time(b) for a, b in qb_ev) * 1e3 / len(qb_ev)
-    qb_gbps = 3 * (qk_bytes // 2) / (qb_us * 1e-6) / 1e9
-    detail["qknorm_rope_bwd"] = {"us": round(qb_us, 2), "GBps": round(qb_gbps, 1),
-                                 "frac_hbm": round(qb_gbps / PEAK_HBM_GBPS, 4), "algorithmic_bytes": 3 * (qk_bytes // 2)}
-
-    # The same forward kernel with the pages' logit gain split between q and k
-    # (g = sqrt(1.2) on each); the step above uses plain weightless RMSNorm (g = 1).
-    gq, gk = Lq["q"].clone(), Lq["k"].clone()
-    for _ in range(3):
-        nc.qknorm_rope_(gq, gk, None, rope_base=cfg.rope_base, eps=1e-6, qk_gain=math.sqrt(1.2))
-    torch.cuda.synchronize()
-    qg_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
-    for a, b in qg_ev:
-        a.record(stream)
-        nc.qknorm_rope_(gq, gk, None, rope_base=cfg.rope_base, eps=1e-6, qk_gain=math.sqrt(1.2))
-        b.record(stream)
-    torch.cuda.synchronize()
-    qg_us = sum(a.elapsed_time(b) for a, b in qg_ev) * 1e3 / len(qg_ev)
-    detail["qknorm_rope_gain_sqrt1p2"] = {"us": round(qg_us, 2), "GBps": round(qk_bytes / (qg_us * 1e-6) / 1e9, 1),
-                                          "qk_gain": round(math.sqrt(1.2), 6)}
-    del gq, gk
-
-    # QK-norm + RoPE fused into the forward (q normalised and rotated in the
-    # forward's prologue, k by the standalone kernel) against the two calls it
-    # replaces, for each window of the layer pattern; the fused forward is not
-    # part of the step above.
-    fq, fk = Lq["q"].clone(), Lq["k"].clone()
-    fo, flse = torch.empty_like(fq), torch.empty_like(Lq["lse"])
-    fused = {}
-    for W in ([] if args.no_configs else sorted(set(cfg.windows))):
-        def two_calls():
-            nc.qknorm_rope_(fq, fk, None, rope_base=cfg.rope_base, eps=1e-6)
-            nc.fwd(fq, fk, Lq["v"], window=(W, 0), out=(fo, flse))
-
-        def one_call():
-            nc.fwd_qknorm_rope_(fq, fk, Lq["v"], None, rope_base=cfg.rope_base, eps=1e-6, window=(W, 0),
-                                out=(fo, flse))
-        us = {}
-        for name, fn in (("two_calls", two_calls), ("fused", one_call)):
-            for _ in range(3):
-                fn()
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for _ in range(20):
-                fn()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            us[name] = e0.elapsed_time(e1) * 1e3 / 20
-        fl = 4 * D * visible_pairs(T, W) * B * H
-        fused["full" if W < 0 else f"w{W}"] = {
-            "two_calls_us": round(us["two_calls"], 2), "fused_us": round(us["fused"], 2),
-            "fused_fwd_TFLOPs": round(fl / (us["fused"] * 1e-6) / 1e12, 1)}
-    if fused:
-        detail["fwd_qknorm_rope"] = fused
-    del fq, fk, fo, flse
+    if not args.no_configs:
+        detail["qknorm_rope"] = {c.name: qknorm_detail(nc, torch, c, dev, stream) for c in (D12, D20, GQA)}
 
     prefill = None
     if not args.no_decode:
@@ -472,19 +506,9 @@ def main():
         lens_h = lensp.cpu().tolist()
         prefill = {}
         for W in c.windows:
-            for _ in range(3):
-                nc.prefill(qp, knp, vnp, kcp, vcp, lensp, window=W, out=op)
-            torch.cuda.synchronize()
-            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
-            for a, b_ in evs:
-                a.record(stream)
-                nc.prefill(qp, knp, vnp, kcp, vcp, lensp, window=W, out=op)
-                b_.record(stream)
-            torch.cuda.synchronize()
-            us = sum(a.elapsed_time(b_) for a, b_ in evs) * 1e3 / len(evs)
+            us = event_us(torch, stream, lambda: nc.prefill(qp, knp, vnp, kcp, vcp, lensp, window=W, out=op), 10)
             pairs = sum(min(s_ + i + 1, W + 1) if W >= 0 else s_ + i + 1 for s_ in lens_h for i in range(c.Tn))
-            flops = 4 * c.D * pairs * c.H
-            tf = flops / (us * 1e-6) / 1e12
+            tf = 4 * c.D * pairs * c.H / (us * 1e-6) / 1e12
             prefill["L" if W < 0 else "S"] = {"window": W, "us": round(us, 2), "tflops": round(tf, 1),
                                               "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
                                               "workload": c.name}
@@ -498,16 +522,7 @@ def main():
         c, s_len = DECODE, 2048
         ksr, vsr, kdr, vdr, slr = (x.to(dev) for x in replicate_inputs(c.B, s_len, c.T_max, c.KV, c.D, s_len, seed=9))
         dlr = torch.empty(c.B, dtype=torch.int32, device=dev)
-        for _ in range(3):
-            nc.cache_replicate(ksr, vsr, slr, kdr, vdr, dlr)
-        torch.cuda.synchronize()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
-        for a, b_ in evs:
-            a.record(stream)
-            nc.cache_replicate(ksr, vsr, slr, kdr, vdr, dlr)
-            b_.record(stream)
-        torch.cuda.synchronize()
-        us = sum(a.elapsed_time(b_) for a, b_ in evs) * 1e3 / len(evs)
+        us = event_us(torch, stream, lambda: nc.cache_replicate(ksr, vsr, slr, kdr, vdr, dlr), 10)
         part = 2 * s_len * c.KV * c.D * 2            # K and V of the prompt
         nbytes = part * (1 + c.B)                    # read once, written to every row
         gbps = nbytes / (us * 1e-6) / 1e9
@@ -539,26 +554,26 @@ def main():
                 evs[i][1].record(stream)
             torch.cuda.synchronize()
             us = sum(a.elapsed_time(b) for a, b in evs) * 1e3 / len(evs)
-            KV_row = c.KV * c.D * 2
-            n_cached = sum(s - (0 if W < 0 else max(0, s - W)) for s in lens_h)
-            nbytes = n_cached * 2 * KV_row + c.B * 4 * KV_row + c.B * 2 * c.H * c.D * 2
+            nbytes = decode_algorithmic_bytes(lens_h, c.H, c.KV, c.D, W)
             gbps = nbytes / (us * 1e-6) / 1e9
+            tr = [measured_traffic(kn, f"{c.name} W={W}") for kn in ("decode_split", "decode_combine")]
             decode["L" if W < 0 else "S"] = {"window": W, "us": round(us, 2), "GBps": round(gbps, 1),
                                              "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4),
-                                             "algorithmic_bytes": nbytes}
+                                             "algorithmic_bytes": nbytes,
+                                             "traffic": None if None in tr else sum(tr)}
         del sets
 
     configs = None
     if not args.no_configs:
-        from workloads import D20, GQA
-        configs = {c.name: time_config(nc, torch, c, dev, stream) for c in (D20, GQA)}
+        configs = {c.name: time_config(nc, torch, c, dev, stream) for c in (GQA, D12, D20) if c is not cfg}
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": cfg.name, "global_batch": B, "seq_len": T, "n_head": H, "n_kv_head": KV,
-                   "head_dim": D, "windows": list(cfg.windows), "parallelism": "single GPU"},
+        "config": {"workload": cfg.name, "global_batch": cfg.B, "seq_len": cfg.T, "n_head": cfg.H,
+                   "n_kv_head": cfg.KV, "head_dim": cfg.D, "windows": list(cfg.windows),
+                   "qknorm_rope_in_step": not cfg.pre_normed, "parallelism": "single GPU"},
         "roofline": roof,
         "decode": decode,
         "prefill": prefill,

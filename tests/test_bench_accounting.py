@@ -19,9 +19,17 @@ def test_visible_pairs_matches_oracle(T, W):
     assert bench.visible_pairs(T, W) == oracle.n_visible_pairs(T, W)
 
 
+def test_decode_bytes_match_the_oracle():
+    import numpy as np
+    r = np.random.default_rng(3)
+    for W in (-1, 0, 1, 100, 1024, 9000):
+        lens = [int(x) for x in r.integers(0, 8193, size=64)]
+        assert bench.decode_algorithmic_bytes(lens, 10, 10, 128, W) == oracle.decode_bytes(lens, 10, 10, 128, W)
+
+
 def test_traffic_lookup_requires_matching_source():
-    assert bench.measured_traffic("no_such_kernel") is None
+    assert bench.measured_traffic("no_such_kernel", "no_such_workload") is None
     h = bench.kernel_source_hash("attn_bwd_bf16.hip")
     assert h == bench.kernel_source_hash("attn_bwd_bf16.hip") and len(h) == 16
-    tr = bench.measured_traffic("bwd_dkdv")
+    tr = bench.measured_traffic("bwd_dkdv", "gqa_b16_t4096_h12_kv4_d128_bf16")
     assert tr is None or (isinstance(tr, int) and tr > 0)

@@ -14,7 +14,7 @@ import torch
 import oracle
 import transformer_attention_qknorm_amd as nc
 from conftest import tol_check
-from parity_util import LSE_TOL, TOL, check, check_lse, f64, lse_tol_after_bf16_inputs
+from parity_util import LSE_TOL, TOL, check, check_lse, f64, stored
 from workloads import attn_inputs, decode_inputs, prefill_inputs, replicate_inputs
 
 pytestmark = pytest.mark.gpu
@@ -97,7 +97,7 @@ def test_fwd_qknorm_rope(case):
     q, k, v, _ = attn_inputs(B, T, H, KV, D, dtype, seed=300 + T)
     pos = torch.from_numpy(np.random.default_rng(5).integers(0, 8192, size=B).astype(np.int32)) if offset else None
     xq, xk = oracle.qknorm_rope(f64(q), f64(k), None if pos is None else pos.numpy(), base, 1e-6, gain)
-    ro, rlse = oracle.attn_fwd(xq, xk, f64(v), W)
+    ro, rlse = oracle.attn_fwd(stored(xq, dtype), stored(xk, dtype), f64(v), W)
     qd, kd, vd = to_dev(q, k, v)
     v_before = vd.clone()
     o, lse = nc.fwd_qknorm_rope_(qd, kd, vd, None if pos is None else pos.to(DEV), rope_base=base, eps=1e-6,
@@ -106,7 +106,7 @@ def test_fwd_qknorm_rope(case):
     check(qd, xq, dtype, "q'")
     check(kd, xk, dtype, "k'")
     check(o, ro, dtype, "o")
-    check_lse(lse, rlse, dtype, "lse", tol=lse_tol_after_bf16_inputs(D, gain) if dtype == "bf16" else None)
+    check_lse(lse, rlse, dtype, "lse")
     assert torch.equal(vd, v_before)
     # the same result as the two calls it fuses
     q2, k2 = to_dev(q, k)
@@ -295,6 +295,28 @@ def test_determinism():
         assert torch.equal(o1, o2) and torch.equal(l1, l2)
         for a, b in zip(g1, g2):
             assert torch.equal(a, b)
+
+
+def test_window_reaching_every_key_is_full_causal():
+    """window_left >= T - 1 (up to INT_MAX) is the same attention as -1: bit-equal
+    results from the forward, the backward (same workspace size) and decode."""
+    q, k, v, do = to_dev(*attn_inputs(2, 333, 6, 2, 128, "bf16", seed=6))
+    o_ref, l_ref = nc.fwd(q, k, v, window=(-1, 0))
+    g_ref = nc.bwd(q, k, v, o_ref, l_ref, do, window=(-1, 0))
+    for W in (332, 333, 2 ** 31 - 64, 2 ** 31 - 1):
+        say(f"window {W}")
+        o, l = nc.fwd(q, k, v, window=(W, 0))
+        g = nc.bwd(q, k, v, o_ref, l_ref, do, window=(W, 0))
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref) and torch.equal(l, l_ref), W
+        for a, b in zip(g, g_ref):
+            assert torch.equal(a, b), W
+    qd, kn, vn, kc, vc, lens = decode_inputs(5, 4, 2, 128, 1, 290, 300, seed=22, poison=True)
+    ref = nc.decode(*to_dev(qd, kn, vn, kc.clone(), vc.clone(), lens), window=-1)
+    for W in (299, 2 ** 31 - 1):
+        o = nc.decode(*to_dev(qd, kn, vn, kc.clone(), vc.clone(), lens), window=W)
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref), W
 
 
 # ------------------------------------------------------------------ decode

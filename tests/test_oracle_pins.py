@@ -177,6 +177,100 @@ def test_pair_count_brute_force():
     assert (fwd, bwd) == (4 * 128 * 1574400 * 48, 8 * 128 * 1574400 * 48)
 
 
+def _counted_attention(q, k, v, do, W):
+    """Scalar-loop attention forward and backward that counts every multiply and
+    every add of the four contractions it performs (QK^T, PV; dV, dP, dQ, dK),
+    two per multiply-accumulate.  Softmax arithmetic is not counted (the MFU
+    convention counts matmul work only).  Returns (o, dq, dk, dv, fwd_flops,
+    bwd_flops); o and the gradients are checked against the oracle so that the
+    count belongs to a real computation of the same function."""
+    B, T, H, D = q.shape
+    KV = k.shape[2]
+    G = H // KV
+    scale = 1.0 / math.sqrt(D)
+    o = np.zeros_like(q)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    ff = fb = 0
+    for b in range(B):
+        for h in range(H):
+            g = h // G
+            for i in range(T):
+                keys = [j for j in range(i + 1) if W < 0 or i - j <= W]
+                s = {}
+                for j in keys:
+                    acc = 0.0
+                    for d in range(D):
+                        acc += q[b, i, h, d] * k[b, j, g, d]
+                        ff += 2
+                    s[j] = acc * scale
+                m = max(s.values())
+                z = sum(math.exp(x - m) for x in s.values())
+                p = {j: math.exp(s[j] - m) / z for j in keys}
+                for j in keys:
+                    for d in range(D):
+                        o[b, i, h, d] += p[j] * v[b, j, g, d]
+                        ff += 2
+                dp = {}
+                for j in keys:
+                    acc = 0.0
+                    for d in range(D):
+                        dv[b, j, g, d] += p[j] * do[b, i, h, d]
+                        acc += do[b, i, h, d] * v[b, j, g, d]
+                        fb += 4
+                    dp[j] = acc
+                delta = sum(p[j] * dp[j] for j in keys)
+                for j in keys:
+                    ds = p[j] * (dp[j] - delta)
+                    for d in range(D):
+                        dq[b, i, h, d] += ds * k[b, j, g, d] * scale
+                        dk[b, j, g, d] += ds * q[b, i, h, d] * scale
+                        fb += 4
+    return o, dq, dk, dv, ff, fb
+
+
+@pytest.mark.parametrize("B,T,H,KV,D,W", [(1, 7, 2, 2, 4, -1), (2, 9, 4, 2, 3, 2), (1, 6, 3, 1, 5, 0),
+                                          (1, 8, 2, 1, 2, 20)])
+def test_attn_flops_loop_counted(B, T, H, KV, D, W):
+    q, k, v, do = rand(B, T, H, D), rand(B, T, KV, D), rand(B, T, KV, D), rand(B, T, H, D)
+    o, dq, dk, dv, ff, fb = _counted_attention(q, k, v, do, W)
+    ro, _ = oracle.attn_fwd(q, k, v, W)
+    rdq, rdk, rdv = oracle.attn_bwd(q, k, v, do, W)
+    for a, r in ((o, ro), (dq, rdq), (dk, rdk), (dv, rdv)):
+        np.testing.assert_allclose(a, r, atol=1e-12)
+    assert oracle.attn_flops(B, T, H, D, W) == (ff, fb)
+
+
+def _decode_bytes_brute(lens, H, KV, D, W, eb):
+    """Walks each sequence's cache slots and adds the bytes decode must move for
+    every visible key: a cached key's K and V rows are read from the cache; the
+    new key (slot s) comes from k_new/v_new and is written into the cache; q is
+    read and o written once per sequence."""
+    row, qrow = KV * D * eb, H * D * eb
+    total = 0
+    for s in lens:
+        total += 2 * qrow
+        for j in range(s + 1):
+            if W >= 0 and s - j > W:
+                continue
+            total += 2 * row if j < s else 4 * row
+    return total
+
+
+def test_decode_bytes_brute_force_and_golden():
+    # hand-worked: lengths 3, 0, 10 at window 2, H=2, KV=1, D=4, bf16: visible
+    # cached rows 2 + 0 + 2 (64 B of K and V), new keys 3 x (16 B read + 16 B
+    # written), q and o 3 x 32 B
+    assert oracle.decode_bytes([3, 0, 10], 2, 1, 4, 2, 2) == 64 + 96 + 96 == 256
+    r = np.random.default_rng(7)
+    for _ in range(40):
+        B = int(r.integers(1, 6))
+        lens = [int(x) for x in r.integers(0, 300, size=B)]
+        H, KV, D = 2 * int(r.integers(1, 4)), 2, int(r.choice([4, 8, 128]))
+        W = int(r.choice([-1, 0, 1, 17, 128, 299, 1000]))
+        eb = int(r.choice([2, 4]))
+        assert oracle.decode_bytes(lens, H, KV, D, W, eb) == _decode_bytes_brute(lens, H, KV, D, W, eb)
+
+
 def test_window_schedule_golden():
     g = json.load(open(os.path.join(GOLDEN, "window_schedule.json")))
     for c in g["cases"]:
@@ -498,3 +592,15 @@ def test_planted_mistakes_are_caught(monkeypatch):
     ref = np.concatenate([z.real, z.imag], axis=-1)
     assert np.allclose(A.apply_rope(xx, pos, 10000.0), ref, atol=1e-12)
     assert not np.allclose(rope_interleaved(xx, pos, 10000.0), ref, atol=1e-6)
+
+    # 6. decode byte count with the window taken as exclusive fails the brute force
+    def decode_bytes_exclusive(lens, H_, KV_, D_, W, eb=2):
+        row = KV_ * D_ * eb
+        n = sum(s - (0 if W < 0 else max(0, s - W + 1)) for s in lens)
+        return n * 2 * row + len(lens) * 4 * row + len(lens) * 2 * H_ * D_ * eb
+    assert decode_bytes_exclusive([3, 0, 10], 2, 1, 4, 2) != _decode_bytes_brute([3, 0, 10], 2, 1, 4, 2, 2)
+
+    # 7. FLOPs counted over the dense T x T square (no window) fail the loop count
+    qq, kk, vv, dd = rand(1, 6, 2, 3), rand(1, 6, 1, 3), rand(1, 6, 1, 3), rand(1, 6, 2, 3)
+    counted = _counted_attention(qq, kk, vv, dd, 1)[4:]
+    assert (4 * 3 * 36 * 2, 8 * 3 * 36 * 2) != counted == oracle.attn_flops(1, 6, 2, 3, 1)

@@ -28,6 +28,12 @@ namespace {
 
 constexpr int kBlockM = 128;  // query rows per dq workgroup
 constexpr int kBlockN = 128;  // keys per dkdv workgroup
+#ifndef KVALU_A
+#define KVALU_A 10  // VALU instructions placed after each S/dP MFMA of the second query block
+#endif
+#ifndef KVALU_B
+#define KVALU_B 5   // VALU instructions placed after each dV/dK MFMA of the first query block
+#endif
 
 // ---------------------------------------------------------------- D_i = dO . O
 // Stores -D_i (the initial value of the dP - D accumulators of the dK/dV stage)
@@ -109,14 +115,24 @@ __device__ __forceinline__ void dkdv_sdp(f32x16 &sacc, f32x16 &dpacc, const char
   }
 }
 
-// P = exp2(S c - LSE log2 e) and dS = P (dP - D) as bf16 MFMA operands (pk, dk:
-// element pairs of accumulator rows 8 i + 4 hh + j, the layout acc_to_operand
-// gives), and dS rearranged for the workspace: `out` holds this lane's 16
-// consecutive queries of its key's [key][query] tile row, starting at query
-// 32 qb + 16 hh (see ds_store).
+// The bf16 value nearest x, and the bf16 value nearest the remainder: x is
+// carried into the dV and dK products as hi + lo, so those products see P and dS
+// to about 16 significant bits rather than bf16's 8 (only the final rounding of
+// dK and dV to bf16 remains).  Packs the pair (x0, x1) into (hi, lo) dwords.
+__device__ __forceinline__ void split_bf16x2(float x0, float x1, uint32_t &hi, uint32_t &lo) {
+  hi = pack_bf16x2(x0, x1);
+  lo = pack_bf16x2(x0 - __uint_as_float(hi << 16), x1 - __uint_as_float(hi & 0xffff0000u));
+}
+
+// P = exp2(S c - LSE log2 e) and dS = P (dP - D) as bf16 MFMA operands, each as
+// a hi + lo pair (pk/pl, dk/dl: element pairs of accumulator rows 8 i + 4 hh + j,
+// the layout acc_to_operand gives), and the rounded dS rearranged for the
+// workspace: `out` holds this lane's 16 consecutive queries of its key's
+// [key][query] tile row, starting at query 32 qb + 16 hh (see ds_store).
 __device__ __forceinline__ void dkdv_p_ds(const f32x16 &sacc, const f32x16 &dmd, const float *lse2, bool need_mask,
                                           int qb, int qtile0, int key_lane, int T, int W, float c, int hh,
-                                          uint32_t (&pk)[8], uint32_t (&dk)[8], u32x4 (&out)[2]) {
+                                          uint32_t (&pk)[8], uint32_t (&pl)[8], uint32_t (&dk)[8],
+                                          uint32_t (&dl)[8], u32x4 (&out)[2]) {
   // rows of this lane's accumulator elements: 32 qb + 8 i + 4 hh + j
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -134,10 +150,10 @@ __device__ __forceinline__ void dkdv_p_ds(const f32x16 &sacc, const f32x16 &dmd,
       }
       ds[j] = p[j] * dmd[e];
     }
-    pk[2 * i] = pack_bf16x2(p[0], p[1]);
-    pk[2 * i + 1] = pack_bf16x2(p[2], p[3]);
-    dk[2 * i] = pack_bf16x2(ds[0], ds[1]);
-    dk[2 * i + 1] = pack_bf16x2(ds[2], ds[3]);
+    split_bf16x2(p[0], p[1], pk[2 * i], pl[2 * i]);
+    split_bf16x2(p[2], p[3], pk[2 * i + 1], pl[2 * i + 1]);
+    split_bf16x2(ds[0], ds[1], dk[2 * i], dl[2 * i]);
+    split_bf16x2(ds[2], ds[3], dk[2 * i + 1], dl[2 * i + 1]);
   }
   // The two half-waves hold interleaved groups of 4 queries of the same key
   // (h = 0: 0-3, 8-11, 16-19, 24-27; h = 1: 4-7, ...).  v_permlane32_swap of
@@ -162,19 +178,26 @@ __device__ __forceinline__ void ds_store(uint16_t *ds_row, const u32x4 (&out)[2]
   dst[1] = out[1];
 }
 
-// dV^T += dO^T P and dK^T += Q^T dS, contraction over the 32 query rows of block qb.
+// dV^T += dO^T (P_hi + P_lo) and dK^T += Q^T (dS_hi + dS_lo), contraction over the
+// 32 query rows of block qb.
 __device__ __forceinline__ void dkdv_acc(f32x16 (&dkacc)[4], f32x16 (&dvacc)[4], const uint32_t (&pk)[8],
-                                         const uint32_t (&dk)[8], const char *qs, const char *dos, const TileLane &L,
-                                         int qb) {
+                                         const uint32_t (&pl)[8], const uint32_t (&dk)[8], const uint32_t (&dl)[8],
+                                         const char *qs, const char *dos, const TileLane &L, int qb) {
 #pragma unroll
   for (int c2 = 0; c2 < 2; ++c2) {
     const int cs = 2 * qb + c2;
     const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pk[4 * c2], pk[4 * c2 + 1], pk[4 * c2 + 2], pk[4 * c2 + 3]});
+    const bf16x8 pbl = __builtin_bit_cast(bf16x8, u32x4{pl[4 * c2], pl[4 * c2 + 1], pl[4 * c2 + 2], pl[4 * c2 + 3]});
     const bf16x8 dsb = __builtin_bit_cast(bf16x8, u32x4{dk[4 * c2], dk[4 * c2 + 1], dk[4 * c2 + 2], dk[4 * c2 + 3]});
+    const bf16x8 dsl = __builtin_bit_cast(bf16x8, u32x4{dl[4 * c2], dl[4 * c2 + 1], dl[4 * c2 + 2], dl[4 * c2 + 3]});
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
-      dvacc[db] = mfma32(col_operand(dos, L, db, cs), pb, dvacc[db]);
-      dkacc[db] = mfma32(col_operand(qs, L, db, cs), dsb, dkacc[db]);
+      const bf16x8 a = col_operand(dos, L, db, cs);
+      const bf16x8 qa = col_operand(qs, L, db, cs);
+      dvacc[db] = mfma32(a, pb, dvacc[db]);
+      dkacc[db] = mfma32(qa, dsb, dkacc[db]);
+      dvacc[db] = mfma32(a, pbl, dvacc[db]);
+      dkacc[db] = mfma32(qa, dsl, dkacc[db]);
     }
   }
 }
@@ -197,8 +220,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__rest
                                                           const float *__restrict__ lse2g,
                                                           const float *__restrict__ delta, uint16_t *__restrict__ dK,
                                                           uint16_t *__restrict__ dV, uint16_t *__restrict__ dsband,
-                                                          int B, int T, int H, int KV, int W, float scale, int nqt,
-                                                          int nbw) {
+                                                          int B, int T, int H, int KV, int W, float scale, int band_c,
+                                                          long long band_tiles) {
   // Two separate LDS objects for the double buffer (Q | dO | lse2 | delta each),
   // so the compiler can tell the copy into one from the reads of the other.
   __shared__ __attribute__((aligned(1024))) char buf0[kQBuf];
@@ -282,7 +305,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__rest
     if (!skip) {
       const int qt = qtile0 / kTileN;
       const int h = kvh * G + it % G;
-      const long long tile = (((long long)b * H + h) * nqt + qt) * nbw + (kt - ds_kt_lo(qt, W));
+      const long long tile = ((long long)b * H + h) * band_tiles + ds_tile(qt, kt, band_c);
       uint16_t *ds_row = dsband + tile * (kTileN * kTileN) + (kofs + (lane & 31)) * kTileN;
       bool act[2], msk[2];
 #pragma unroll
@@ -296,32 +319,32 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__rest
         // run under the P/dS arithmetic of block 0, and the dV/dK MFMAs of block
         // 0 under that of block 1
         f32x16 s0, p0, s1, p1;
-        uint32_t pk0[8], dk0[8], pk1[8], dk1[8];
+        uint32_t pk0[8], pl0[8], dk0[8], dl0[8], pk1[8], pl1[8], dk1[8], dl1[8];
         u32x4 out0[2], out1[2];
         dkdv_sdp(s0, p0, qs, dos, ndl, L, kreg, vreg, 0, hh);
         __builtin_amdgcn_sched_barrier(0);
         dkdv_sdp(s1, p1, qs, dos, ndl, L, kreg, vreg, 1, hh);
-        dkdv_p_ds(s0, p0, lse2, false, 0, qtile0, key_lane, T, W, c, hh, pk0, dk0, out0);
+        dkdv_p_ds(s0, p0, lse2, false, 0, qtile0, key_lane, T, W, c, hh, pk0, pl0, dk0, dl0, out0);
         ds_store(ds_row, out0, 0, hh);
-        interleave_mfma_valu<16, 5>();
+        interleave_mfma_valu<16, KVALU_A>();
         __builtin_amdgcn_sched_barrier(0);
-        dkdv_acc(dkacc, dvacc, pk0, dk0, qs, dos, L, 0);
-        dkdv_p_ds(s1, p1, lse2, false, 1, qtile0, key_lane, T, W, c, hh, pk1, dk1, out1);
+        dkdv_acc(dkacc, dvacc, pk0, pl0, dk0, dl0, qs, dos, L, 0);
+        dkdv_p_ds(s1, p1, lse2, false, 1, qtile0, key_lane, T, W, c, hh, pk1, pl1, dk1, dl1, out1);
         ds_store(ds_row, out1, 1, hh);
-        interleave_mfma_valu<16, 5>();
+        interleave_mfma_valu<32, KVALU_B>();
         __builtin_amdgcn_sched_barrier(0);
-        dkdv_acc(dkacc, dvacc, pk1, dk1, qs, dos, L, 1);
+        dkdv_acc(dkacc, dvacc, pk1, pl1, dk1, dl1, qs, dos, L, 1);
       } else {
 #pragma unroll 1
         for (int qb = 0; qb < 2; ++qb) {
           if (!act[qb]) continue;
           f32x16 s0, p0;
-          uint32_t pk0[8], dk0[8];
+          uint32_t pk0[8], pl0[8], dk0[8], dl0[8];
           dkdv_sdp(s0, p0, qs, dos, ndl, L, kreg, vreg, qb, hh);
           u32x4 out[2];
-          dkdv_p_ds(s0, p0, lse2, msk[qb], qb, qtile0, key_lane, T, W, c, hh, pk0, dk0, out);
+          dkdv_p_ds(s0, p0, lse2, msk[qb], qb, qtile0, key_lane, T, W, c, hh, pk0, pl0, dk0, dl0, out);
           ds_store(ds_row, out, qb, hh);
-          dkdv_acc(dkacc, dvacc, pk0, dk0, qs, dos, L, qb);
+          dkdv_acc(dkacc, dvacc, pk0, pl0, dk0, dl0, qs, dos, L, qb);
         }
       }
     }
@@ -374,7 +397,7 @@ __device__ __forceinline__ void ds_tile_load(char *lds_tile, const uint16_t *src
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t *__restrict__ K,
                                                         const uint16_t *__restrict__ dsband,
                                                         uint16_t *__restrict__ dQ, int B, int T, int H, int KV,
-                                                        int W, float scale, int nqt, int nbw) {
+                                                        int W, float scale, int nqt, int band_c, long long band_tiles) {
   // double buffer: [K tile | dS^T tile of query tile 2 qblk | of query tile 2 qblk + 1]
   __shared__ __attribute__((aligned(1024))) char buf0[kTileBytes + 2 * 8192];
   __shared__ __attribute__((aligned(1024))) char buf1[kTileBytes + 2 * 8192];
@@ -397,7 +420,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t *__restri
   const uint16_t *Kb = K + (long long)b * T * kv_stride + (long long)kvh * kD;
   const TileSrc ksrc = make_tile_src(Kb, kv_stride, T);
   const int voff = tile_lane_voff(ksrc.stride, tid);
-  const uint16_t *dsh = dsband + (long long)bh * nqt * nbw * (kTileN * kTileN);
+  const uint16_t *dsh = dsband + (long long)bh * band_tiles * (kTileN * kTileN);
 
   const int q_last_blk = min(q0 + kBlockM - 1, T - 1);
   const int t0 = (W < 0 ? 0 : max(0, q0 - W)) / kTileN;
@@ -414,9 +437,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t *__restri
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       const int qt = 2 * qblk + sub;
-      const int j = t - ds_kt_lo(qt, W);
-      if (qt < nqt && j >= 0 && t <= qt)
-        ds_tile_load(buf + kTileBytes + sub * 8192, dsh + ((long long)qt * nbw + j) * (kTileN * kTileN), tid);
+      if (qt < nqt && t >= ds_kt_lo(qt, band_c) && t <= qt)
+        ds_tile_load(buf + kTileBytes + sub * 8192, dsh + ds_tile(qt, t, band_c) * (kTileN * kTileN), tid);
     }
   };
 
@@ -510,7 +532,7 @@ size_t bwd_workspace_bytes(int B, int T, int H, int W, bool bf16) {
   const size_t rows = ((size_t)B * H * T * sizeof(float) + 255) & ~(size_t)255;
   if (!bf16) return rows;
   const DsBand band = ds_band(T, W);
-  return 2 * rows + (size_t)B * H * band.nqt * band.nbw * (kTileN * kTileN) * 2;
+  return 2 * rows + (size_t)B * H * band.tiles * (kTileN * kTileN) * 2;
 }
 
 hipError_t launch_bwd_bf16(const void *q, const void *k, const void *v, const void *o, const float *lse,
@@ -534,10 +556,10 @@ hipError_t launch_bwd_bf16(const void *q, const void *k, const void *v, const vo
   if (stages & kBwdDkDv)
     hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)kvblocks), dim3(256), 0, s, (const uint16_t *)q,
                        (const uint16_t *)k, (const uint16_t *)v, (const uint16_t *)dout, lse2, delta, (uint16_t *)dk,
-                       (uint16_t *)dv, dsband, sh.B, sh.T, sh.H, sh.KV, sh.window, sh.scale, band.nqt, band.nbw);
+                       (uint16_t *)dv, dsband, sh.B, sh.T, sh.H, sh.KV, sh.window, sh.scale, band.c, band.tiles);
   if (stages & kBwdDq)
     hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)qblocks), dim3(256), 0, s, (const uint16_t *)k, dsband,
-                       (uint16_t *)dq, sh.B, sh.T, sh.H, sh.KV, sh.window, sh.scale, band.nqt, band.nbw);
+                       (uint16_t *)dq, sh.B, sh.T, sh.H, sh.KV, sh.window, sh.scale, band.nqt, band.c, band.tiles);
   return hipGetLastError();
 }
 

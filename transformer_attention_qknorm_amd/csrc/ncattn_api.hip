@@ -69,6 +69,12 @@ int check_window(const char *fn, int wl, int wr) {
   return NCATTN_OK;
 }
 
+// A window that reaches past the first key of every row is full causal
+// attention; window_left >= span - 1 (span = the rows a query can see) is mapped
+// to -1 before any sizing or launch, so that no kernel forms i + W or W + 63 with
+// a W near INT_MAX.
+int effective_window(int wl, int span) { return (wl < 0 || wl >= span - 1) ? -1 : wl; }
+
 #define NC_TRY(expr)            \
   do {                          \
     int _rc = (expr);           \
@@ -157,6 +163,7 @@ int ncattn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
   NC_TRY(check_attn_support(fn, dtype, T, n_head, head_dim));
   if (!isfinite(softmax_scale)) return fail(NCATTN_EINVAL, "%s: softmax_scale must be finite", fn);
   if (o == q || o == k || o == v) return fail(NCATTN_EINVAL, "%s: o must not alias an input", fn);
+  window_left = effective_window(window_left, T);
   ncattn::AttnShape sh{B, T, n_head, n_kv_head, head_dim, window_left, resolve_scale(softmax_scale, head_dim)};
   hipError_t e = dtype == NCATTN_BF16
                      ? ncattn::launch_fwd_bf16(q, k, v, o, lse, sh, (hipStream_t)stream)
@@ -184,6 +191,7 @@ int ncattn_fwd_qknorm_rope(void *q, void *k, const void *v, void *o, float *lse,
   if (q == k) return fail(NCATTN_EINVAL, "%s: q and k must be distinct", fn);
   if (o == q || o == k || o == v || v == q || v == k)
     return fail(NCATTN_EINVAL, "%s: o and v must not alias q, k or each other", fn);
+  window_left = effective_window(window_left, T);
   ncattn::AttnShape sh{B, T, n_head, n_kv_head, head_dim, window_left, resolve_scale(softmax_scale, head_dim)};
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
@@ -206,7 +214,7 @@ size_t ncattn_bwd_workspace_bytes(int B, int T, int n_head, int n_kv_head, int h
   (void)n_kv_head;
   (void)head_dim;
   if (B <= 0 || T <= 0 || n_head <= 0 || window_left < -1) return 0;
-  return ncattn::bwd_workspace_bytes(B, T, n_head, window_left, dtype == NCATTN_BF16);
+  return ncattn::bwd_workspace_bytes(B, T, n_head, effective_window(window_left, T), dtype == NCATTN_BF16);
 }
 }  // extern "C"
 
@@ -241,6 +249,7 @@ int bwd_common(const char *fn, int stages, const void *q, const void *k, const v
     return fail(NCATTN_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
                 workspace == nullptr ? (size_t)0 : workspace_bytes);
   if (!aligned16(workspace)) return fail(NCATTN_EINVAL, "%s: workspace is not 16-byte aligned", fn);
+  window_left = effective_window(window_left, T);
   ncattn::AttnShape sh{B, T, n_head, n_kv_head, head_dim, window_left, resolve_scale(softmax_scale, head_dim)};
   hipError_t e =
       dtype == NCATTN_BF16
@@ -273,7 +282,7 @@ int ncattn_bwd_dq(NC_BWD_PARAMS) { return bwd_common("ncattn_bwd_dq", ncattn::kB
 
 size_t ncattn_decode_workspace_bytes(int B, int T_max, int n_head, int n_kv_head, int head_dim, int window_left) {
   if (B <= 0 || T_max <= 0 || n_head <= 0 || n_kv_head <= 0 || head_dim <= 0 || window_left < -1) return 0;
-  return ncattn::decode_workspace_bytes(B, T_max, n_head, n_kv_head, head_dim, window_left);
+  return ncattn::decode_workspace_bytes(B, T_max, n_head, n_kv_head, head_dim, effective_window(window_left, T_max));
 }
 
 int ncattn_decode(const void *q, const void *k_new, const void *v_new, void *k_cache, void *v_cache,
@@ -299,6 +308,7 @@ int ncattn_decode(const void *q, const void *k_new, const void *v_new, void *k_c
   if (k_cache == v_cache) return fail(NCATTN_EINVAL, "%s: k_cache and v_cache must differ", fn);
   if (o == q || o == k_cache || o == v_cache || o == k_new || o == v_new)
     return fail(NCATTN_EINVAL, "%s: o must not alias an input", fn);
+  window_left = effective_window(window_left, T_max);
   size_t need = ncattn::decode_workspace_bytes(B, T_max, n_head, n_kv_head, head_dim, window_left);
   if (workspace == nullptr || workspace_bytes < need)
     return fail(NCATTN_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
@@ -333,6 +343,7 @@ int ncattn_prefill(const void *q, const void *k_new, const void *v_new, void *k_
   if (k_cache == v_cache) return fail(NCATTN_EINVAL, "%s: k_cache and v_cache must differ", fn);
   if (o == q || o == k_cache || o == v_cache || o == k_new || o == v_new)
     return fail(NCATTN_EINVAL, "%s: o must not alias an input", fn);
+  window_left = effective_window(window_left, T_max);
   hipError_t e = ncattn::launch_prefill_bf16(q, k_new, v_new, k_cache, v_cache, cache_seqlens, o, lse, B, Tn, T_max,
                                              n_head, n_kv_head, window_left, resolve_scale(softmax_scale, head_dim),
                                              (hipStream_t)stream);
