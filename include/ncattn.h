@@ -34,8 +34,10 @@
  *     enqueued and ncattn_last_error() (thread-local) describes the problem.
  *     No C++ exception crosses this interface.
  *   - Outputs must not alias inputs, except where a call says it works in place.
- *   - Apart from the thread-local error string the library keeps no mutable
- *     global state; calls on different streams may run concurrently.
+ *   - Apart from the thread-local error string and the per-device scratch of
+ *     ncattn_decode_noalloc (below) the library keeps no mutable global state;
+ *     calls on different streams may run concurrently, except that
+ *     ncattn_decode_noalloc calls on one device must not overlap.
  *
  * Supported: dtype NCATTN_BF16 (fp32 accumulation, bf16 MFMA contractions) with
  * head_dim 128; dtype NCATTN_F32 (fp32 throughout) with head_dim 64 or 128.
@@ -202,6 +204,30 @@ int ncattn_decode(const void *q, const void *k_new, const void *v_new,
                   int B, int T_max, int n_head, int n_kv_head, int head_dim,
                   int window_left, float softmax_scale, int dtype,
                   void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * ncattn_decode without a workspace argument, for callers that cannot allocate
+ * device memory: code recorded under HIP graph capture, serving loops that must
+ * not call the allocator, harnesses that forbid allocation.  The split-KV partials
+ * go to a file-scope device array of NCATTN_DECODE_SCRATCH_BYTES bytes, of which
+ * every device the library runs on holds one copy until the process ends (its
+ * address is looked up once per device, on the first call with that device
+ * current).  The call allocates nothing and needs no zeroed memory.
+ *   Arguments, semantics, validation and status codes as ncattn_decode (minus
+ *   the workspace); the current device must be the one `stream` belongs to.
+ *   A shape whose partials need more than NCATTN_DECODE_SCRATCH_BYTES
+ *   (ncattn_decode_workspace_bytes() > the limit: about B * n_head *
+ *   ceil(min(T_max, window_left + 1) / 128) * 520 bytes) returns
+ *   NCATTN_EWORKSPACE and enqueues nothing.
+ *   Every call on one device shares that device's array: two calls that overlap
+ *   in time on one device (different streams, or threads) race and give wrong
+ *   results; calls in order on one stream are safe.
+ */
+#define NCATTN_DECODE_SCRATCH_BYTES (32u << 20)
+int ncattn_decode_noalloc(const void *q, const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                          const int32_t *cache_seqlens, void *o, float *lse, int B, int T_max, int n_head,
+                          int n_kv_head, int head_dim, int window_left, float softmax_scale, int dtype,
+                          void *stream);
 
 /*
  * Chunked prefill against a KV cache (multi-token decode; "nanochat Admin &

@@ -196,6 +196,26 @@ def test_decode_validation_and_workspace(L):
     assert L.ncattn_decode(*bad, 0, P + 256, ws, None) == EUNSUP
 
 
+def test_decode_noalloc_validation(L):
+    # the same checks as ncattn_decode, and shapes beyond the scratch are refused
+    # on the host, before any device call
+    args = [P, P + 16, P + 32, P + 48, P + 64, P + 80, P + 96, None, 4, 512, 2, 2, 128, -1, 0.0]
+    assert L.ncattn_decode_noalloc(*args, 1, None) == EUNSUP             # fp32 decode
+    bad = list(args)
+    bad[4] = bad[3]                                                    # k_cache == v_cache
+    assert L.ncattn_decode_noalloc(*bad, 0, None) == EINVAL
+    bad = list(args)
+    bad[0] = None
+    assert L.ncattn_decode_noalloc(*bad, 0, None) == EINVAL
+    big = list(args)
+    big[8:13] = [64, 16384, 16, 16, 128]                               # 68 MB of partials
+    assert L.ncattn_decode_workspace_bytes(64, 16384, 16, 16, 128, -1) > 32 << 20
+    assert L.ncattn_decode_noalloc(*big, 0, None) == EWS
+    assert b"scratch" in L.ncattn_last_error()
+    # the engine-decode batch (64 sequences, T_max 8320, 10 heads) fits the scratch
+    assert L.ncattn_decode_workspace_bytes(64, 8320, 10, 10, 128, -1) <= 32 << 20
+
+
 def test_prefill_validation(L):
     f = L.ncattn_prefill
     def call(q=P, kn=P + 16, vn=P + 32, kc=P + 48, vc=P + 64, lens=P + 80, o=P + 96, lse=None, Tn=8, T_max=64,

@@ -13,6 +13,8 @@ Functions (names follow the C ABI):
     bwd(q, k, v, o, lse, do, window=(-1, 0), softmax_scale=None) -> (dq, dk, dv)
     decode(q, k_new, v_new, k_cache, v_cache, cache_seqlens, window=-1,
            softmax_scale=None, return_lse=False) -> o  (or (o, lse))
+    decode_noalloc(q, k_new, v_new, k_cache, v_cache, cache_seqlens, o, lse=None,
+                   window=-1, softmax_scale=None)  (no workspace; outputs given)
     window_sizes(pattern, n_layer, short_window, long_window=-1) -> [(left, 0), ...]
 """
 
@@ -23,7 +25,7 @@ import os
 
 import torch
 
-__all__ = ["qknorm_rope_", "qknorm_rope_bwd_", "fwd", "fwd_qknorm_rope_", "bwd", "decode", "prefill",
+__all__ = ["qknorm_rope_", "qknorm_rope_bwd_", "fwd", "fwd_qknorm_rope_", "bwd", "decode", "decode_noalloc", "prefill",
            "cache_replicate",
            "window_sizes", "lib", "NcattnError", "LIB_PATH",
            "BF16", "F32", "STATUS", "bwd_workspace", "decode_workspace", "BWD_STAGES"]
@@ -66,12 +68,13 @@ def lib():
     L.ncattn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     L.ncattn_decode_workspace_bytes.restype = sz
     L.ncattn_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp, sz, vp]
+    L.ncattn_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp]
     L.ncattn_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp]
     L.ncattn_cache_replicate.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
     L.ncattn_last_error.restype = ctypes.c_char_p
     L.ncattn_version.restype = ctypes.c_char_p
     for fn in ("ncattn_qknorm_rope", "ncattn_qknorm_rope_bwd", "ncattn_fwd", "ncattn_fwd_qknorm_rope", "ncattn_bwd",
-               "ncattn_decode",
+               "ncattn_decode", "ncattn_decode_noalloc",
                "ncattn_prefill", "ncattn_cache_replicate"):
         getattr(L, fn).restype = i32
     _lib = L
@@ -304,6 +307,37 @@ def decode(q, k_new, v_new, k_cache, v_cache, cache_seqlens, window=-1, softmax_
                              ws.numel(), _stream(dev))
     _check("ncattn_decode", rc)
     return (o, lse) if return_lse else o
+
+
+DECODE_SCRATCH_BYTES = 32 << 20  # NCATTN_DECODE_SCRATCH_BYTES
+
+
+def decode_noalloc(q, k_new, v_new, k_cache, v_cache, cache_seqlens, o, lse=None, window=-1, softmax_scale=None):
+    """decode() through ncattn_decode_noalloc: no workspace, the split-KV partials
+    go to the library's per-device scratch (at most DECODE_SCRATCH_BYTES); the
+    outputs o [B][1][H][D] (and optionally lse fp32 [B][H]) are given by the
+    caller, so nothing is allocated.  Calls on one device must not overlap."""
+    dev = _dev(q, k_new, v_new, k_cache, v_cache, cache_seqlens, o)
+    B, one, H, D = q.shape
+    T_max, KV = k_cache.shape[1], k_cache.shape[2]
+    if one != 1 or k_new.shape != (B, 1, KV, D) or v_new.shape != (B, 1, KV, D) \
+            or k_cache.shape != v_cache.shape or k_cache.shape[0] != B or k_cache.shape[3] != D:
+        raise ValueError("ncattn.decode_noalloc: inconsistent shapes")
+    if cache_seqlens.dtype != torch.int32 or cache_seqlens.numel() != B:
+        raise ValueError("ncattn.decode_noalloc: cache_seqlens must be int32 [B]")
+    if o.shape != q.shape or o.dtype != q.dtype:
+        raise ValueError("ncattn.decode_noalloc: o must be like q")
+    if lse is not None:
+        _dev(lse)
+        if lse.shape != (B, H) or lse.dtype != torch.float32:
+            raise ValueError("ncattn.decode_noalloc: lse must be fp32 [B][H]")
+    wl = window if isinstance(window, int) else _window(window)[0]
+    with torch.cuda.device(dev):
+        rc = lib().ncattn_decode_noalloc(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                                         _ptr(cache_seqlens), _ptr(o), _ptr(lse), B, T_max, H, KV, D, wl,
+                                         _scale(softmax_scale), _dtype_code(q), _stream(dev))
+    _check("ncattn_decode_noalloc", rc)
+    return o
 
 
 def prefill(q, k_new, v_new, k_cache, v_cache, cache_seqlens, window=-1, softmax_scale=None, return_lse=False,

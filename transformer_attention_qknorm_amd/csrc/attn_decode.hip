@@ -21,6 +21,9 @@
 // decode_combine: one workgroup per (b, h) merges the chunk partials
 // (max, sum, unnormalised output) into o and lse: the maximum over the chunks in
 // parallel, then the weighted sums with eight chunks' loads in flight.
+#include <mutex>
+
+#include "ncattn.h"
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -205,6 +208,36 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(const float *__rest
 }
 
 }  // namespace
+
+// Split-KV partials of ncattn_decode_noalloc, for callers that cannot allocate.
+// Each device the library runs on holds its own copy for the life of the process.
+// Host code never passes the array's name to a kernel (on the host it is only a
+// stand-in for the symbol): it uses the device address decode_scratch_ptr()
+// obtains once per device.
+static __device__ __attribute__((aligned(256))) char scratch[NCATTN_DECODE_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];  // per device, filled on its first use
+}  // namespace
+
+hipError_t decode_scratch_ptr(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 size_t decode_workspace_bytes(int B, int T_max, int H, int KV, int D, int window) {
   (void)KV;

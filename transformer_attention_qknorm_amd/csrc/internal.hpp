@@ -92,6 +92,11 @@ hipError_t launch_decode_bf16(const void *q, const void *k_new, const void *v_ne
                               int T_max, int H, int KV, int D, int window, float scale,
                               void *workspace, hipStream_t s);
 
+// The address of this device's file-scope decode scratch array (looked up with
+// hipGetSymbolAddress on the first call on the current device, then cached per
+// device).  The array holds NCATTN_DECODE_SCRATCH_BYTES bytes.
+hipError_t decode_scratch_ptr(void **out);
+
 // Chunked prefill, bf16, head_dim 128: append k_new/v_new [B][Tn][KV][D] at
 // cache rows seqlens[b].., then the forward of q [B][Tn][H][D] over the cache.
 hipError_t launch_cache_replicate(const void *k_src, const void *v_src, const int32_t *src_seqlen, void *k_dst,

@@ -285,11 +285,15 @@ size_t ncattn_decode_workspace_bytes(int B, int T_max, int n_head, int n_kv_head
   return ncattn::decode_workspace_bytes(B, T_max, n_head, n_kv_head, head_dim, effective_window(window_left, T_max));
 }
 
-int ncattn_decode(const void *q, const void *k_new, const void *v_new, void *k_cache, void *v_cache,
-                  const int32_t *cache_seqlens, void *o, float *lse, int B, int T_max, int n_head, int n_kv_head,
-                  int head_dim, int window_left, float softmax_scale, int dtype, void *workspace,
-                  size_t workspace_bytes, void *stream) {
-  const char *fn = "ncattn_decode";
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the two decode calls; on success window_left holds the
+// effective window.
+int decode_check(const char *fn, const void *q, const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                 const int32_t *cache_seqlens, void *o, float *lse, int B, int T_max, int n_head, int n_kv_head,
+                 int head_dim, int &window_left, float softmax_scale, int dtype) {
   NC_PTR(q, fn);
   NC_PTR(k_new, fn);
   NC_PTR(v_new, fn);
@@ -309,6 +313,20 @@ int ncattn_decode(const void *q, const void *k_new, const void *v_new, void *k_c
   if (o == q || o == k_cache || o == v_cache || o == k_new || o == v_new)
     return fail(NCATTN_EINVAL, "%s: o must not alias an input", fn);
   window_left = effective_window(window_left, T_max);
+  return NCATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ncattn_decode(const void *q, const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                  const int32_t *cache_seqlens, void *o, float *lse, int B, int T_max, int n_head, int n_kv_head,
+                  int head_dim, int window_left, float softmax_scale, int dtype, void *workspace,
+                  size_t workspace_bytes, void *stream) {
+  const char *fn = "ncattn_decode";
+  NC_TRY(decode_check(fn, q, k_new, v_new, k_cache, v_cache, cache_seqlens, o, lse, B, T_max, n_head, n_kv_head,
+                      head_dim, window_left, softmax_scale, dtype));
   size_t need = ncattn::decode_workspace_bytes(B, T_max, n_head, n_kv_head, head_dim, window_left);
   if (workspace == nullptr || workspace_bytes < need)
     return fail(NCATTN_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
@@ -317,6 +335,28 @@ int ncattn_decode(const void *q, const void *k_new, const void *v_new, void *k_c
   hipError_t e = ncattn::launch_decode_bf16(q, k_new, v_new, k_cache, v_cache, cache_seqlens, o, lse, B, T_max,
                                             n_head, n_kv_head, head_dim, window_left,
                                             resolve_scale(softmax_scale, head_dim), workspace, (hipStream_t)stream);
+  return hip_status(e, fn);
+}
+
+int ncattn_decode_noalloc(const void *q, const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                          const int32_t *cache_seqlens, void *o, float *lse, int B, int T_max, int n_head,
+                          int n_kv_head, int head_dim, int window_left, float softmax_scale, int dtype,
+                          void *stream) {
+  const char *fn = "ncattn_decode_noalloc";
+  NC_TRY(decode_check(fn, q, k_new, v_new, k_cache, v_cache, cache_seqlens, o, lse, B, T_max, n_head, n_kv_head,
+                      head_dim, window_left, softmax_scale, dtype));
+  const size_t need = ncattn::decode_workspace_bytes(B, T_max, n_head, n_kv_head, head_dim, window_left);
+  if (need > (size_t)NCATTN_DECODE_SCRATCH_BYTES)
+    return fail(NCATTN_EWORKSPACE,
+                "%s: this shape needs %zu bytes of split-KV scratch; the library's per-device scratch holds %zu "
+                "(use ncattn_decode with a workspace)",
+                fn, need, (size_t)NCATTN_DECODE_SCRATCH_BYTES);
+  void *scratch = nullptr;
+  hipError_t e = ncattn::decode_scratch_ptr(&scratch);
+  if (e != hipSuccess) return hip_status(e, fn);
+  e = ncattn::launch_decode_bf16(q, k_new, v_new, k_cache, v_cache, cache_seqlens, o, lse, B, T_max, n_head,
+                                 n_kv_head, head_dim, window_left, resolve_scale(softmax_scale, head_dim), scratch,
+                                 (hipStream_t)stream);
   return hip_status(e, fn);
 }
 
