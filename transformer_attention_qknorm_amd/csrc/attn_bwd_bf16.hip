@@ -28,12 +28,10 @@ namespace {
 
 constexpr int kBlockM = 128;  // query rows per dq workgroup
 constexpr int kBlockN = 128;  // keys per dkdv workgroup
-#ifndef KVALU_A
-#define KVALU_A 10  // VALU instructions placed after each S/dP MFMA of the second query block
-#endif
-#ifndef KVALU_B
-#define KVALU_B 5   // VALU instructions placed after each dV/dK MFMA of the first query block
-#endif
+// VALU instructions placed after each MFMA where the P/dS arithmetic of one
+// query block runs under the MFMAs of the other (3 to 12 measured within noise)
+constexpr int kValuUnderSdP = 10;   // under the S/dP MFMAs of the second block
+constexpr int kValuUnderDkDv = 5;   // under the dV/dK MFMAs of the first block
 
 // ---------------------------------------------------------------- D_i = dO . O
 // Stores -D_i (the initial value of the dP - D accumulators of the dK/dV stage)
@@ -255,21 +253,39 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__rest
   const int nq = q_hi / kTileN - qt0 + 1;
   const int n_iter = nq * G;
 
-  auto stage = [&](int it, char *base) {
-    const int qt = qt0 + it / G;
-    const int h = kvh * G + it % G;
-    const long long hoff = (long long)b * T * q_stride + (long long)h * kD;
-    tile_load_lds(base, make_tile_src(Q + hoff, q_stride, T), voff, qt * kTileN);
-    tile_load_lds(base + kTileBytes, make_tile_src(dO + hoff, q_stride, T), voff, qt * kTileN);
+  // Step order: query tile qt (outer) x head h = kvh G + g (inner), tracked
+  // incrementally (no division by G per step); `row` is the band index of the
+  // first stored tile of query tile qt (ds_row_start).
+  struct Pos {
+    int qt, g;
+    long long row;
+  };
+  auto advance = [&](Pos p) {
+    if (++p.g == G) {
+      p.g = 0;
+      p.row += min(p.qt, band_c) + 1;
+      ++p.qt;
+    }
+    return p;
+  };
+  const long long qbase = (long long)b * T * q_stride + (long long)kvh * G * kD;  // q/dO of (b, head kvh G)
+  const long long rbase = ((long long)b * H + (long long)kvh * G) * T;         // its lse / delta row
+  uint16_t *const band_b = dsband + ((long long)b * H + (long long)kvh * G) * band_tiles * (kTileN * kTileN);
+
+  auto stage = [&](const Pos &p, char *base) {
+    const long long hoff = qbase + (long long)p.g * kD;
+    tile_load_lds(base, make_tile_src(Q + hoff, q_stride, T), voff, p.qt * kTileN);
+    tile_load_lds(base + kTileBytes, make_tile_src(dO + hoff, q_stride, T), voff, p.qt * kTileN);
     if (wave < 2) {  // waves 0, 1: 64 lse rows and 64 delta rows, 4 bytes per lane (zeros past T)
-      const float *row = (wave == 0 ? lse2g : delta) + ((long long)b * H + h) * T;
+      const float *row = (wave == 0 ? lse2g : delta) + rbase + (long long)p.g * T;
       const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void *)row, (short)0, T * 4, 0x00020000);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(base + 2 * kTileBytes + wave * kTileN * 4), 4,
-                                               lane * 4, qt * kTileN * 4, 0, 0);
+                                               lane * 4, p.qt * kTileN * 4, 0, 0);
     }
   };
 
-  stage(0, buf0);
+  Pos pos{qt0, 0, ds_row_start(qt0, band_c)};
+  stage(pos, buf0);
 
   bf16x8 kreg[8], vreg[8];
   {
@@ -299,14 +315,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__rest
     const char *dos = cur + kTileBytes;
     const float *lse2 = (const float *)(cur + 2 * kTileBytes);
     const float *ndl = lse2 + kTileN;
-    if (it + 1 < n_iter) stage(it + 1, nxt);
-    const int qtile0 = (qt0 + it / G) * kTileN;
+    const Pos p = pos;
+    pos = advance(pos);
+    if (it + 1 < n_iter) stage(pos, nxt);
+    const int qtile0 = p.qt * kTileN;
     const bool skip = !wave_active || qtile0 + kTileN - 1 < kw0 || (W >= 0 && qtile0 - kw_last > W);
     if (!skip) {
-      const int qt = qtile0 / kTileN;
-      const int h = kvh * G + it % G;
-      const long long tile = ((long long)b * H + h) * band_tiles + ds_tile(qt, kt, band_c);
-      uint16_t *ds_row = dsband + tile * (kTileN * kTileN) + (kofs + (lane & 31)) * kTileN;
+      const long long tile = (long long)p.g * band_tiles + p.row + (kt - ds_kt_lo(p.qt, band_c));
+      uint16_t *ds_row = band_b + tile * (kTileN * kTileN) + (kofs + (lane & 31)) * kTileN;
       bool act[2], msk[2];
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
@@ -326,12 +342,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__rest
         dkdv_sdp(s1, p1, qs, dos, ndl, L, kreg, vreg, 1, hh);
         dkdv_p_ds(s0, p0, lse2, false, 0, qtile0, key_lane, T, W, c, hh, pk0, pl0, dk0, dl0, out0);
         ds_store(ds_row, out0, 0, hh);
-        interleave_mfma_valu<16, KVALU_A>();
+        interleave_mfma_valu<16, kValuUnderSdP>();
         __builtin_amdgcn_sched_barrier(0);
         dkdv_acc(dkacc, dvacc, pk0, pl0, dk0, dl0, qs, dos, L, 0);
         dkdv_p_ds(s1, p1, lse2, false, 1, qtile0, key_lane, T, W, c, hh, pk1, pl1, dk1, dl1, out1);
         ds_store(ds_row, out1, 1, hh);
-        interleave_mfma_valu<32, KVALU_B>();
+        interleave_mfma_valu<32, kValuUnderDkDv>();
         __builtin_amdgcn_sched_barrier(0);
         dkdv_acc(dkacc, dvacc, pk1, pl1, dk1, dl1, qs, dos, L, 1);
       } else {
