@@ -209,18 +209,29 @@ def attn_fwd(q, k, v, window_left=-1, softmax_scale=None):
     return o, lse
 
 
-def attn_bwd(q, k, v, dout, window_left=-1, softmax_scale=None):
+def attn_bwd(q, k, v, dout, window_left=-1, softmax_scale=None, o=None):
     """Exact gradient of sum(O * dO) with respect to q, k and v.
 
     Chain rule through the forward above: dV = P^T dO, dP = dO V^T,
-    dS = P * (dP - sum_j P dP) (softmax Jacobian), dQ = scale dS K,
-    dK = scale dS^T Q.  dK and dV of a kv head are summed over the query heads
-    of its group.  Returns dq [B][T][H][D], dk/dv [B][T][KV][D].
+    dS = P * (dP - Delta), dQ = scale dS K, dK = scale dS^T Q.  dK and dV of a
+    kv head are summed over the query heads of its group.  Returns dq
+    [B][T][H][D], dk/dv [B][T][KV][D].
+
+    Delta is the softmax-Jacobian term.  With o=None it is sum_j P dP per row
+    (the exact gradient).  A backward that is handed the forward's output, as
+    the attention backward of the FA3 interface is ("nanochat Admin & Developer
+    Guide", section 6: the flash_attn calls match the Flash Attention 3 API, whose
+    backward takes the forward's out and softmax_lse), forms it as
+    Delta_i = sum_d dO_i o_i from that output instead; ``o`` [B][T][H][D] is that
+    given output (the two agree when o is the exact O).  dV does not depend on
+    Delta.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     dout = np.asarray(dout, dtype=np.float64)
+    if o is not None:
+        o = np.asarray(o, dtype=np.float64)
     B, T, H, D = q.shape
     KV = k.shape[2]
     G = H // KV
@@ -239,7 +250,11 @@ def attn_bwd(q, k, v, dout, window_left=-1, softmax_scale=None):
             do = dout[b, :, h, :]
             dv[b, :, kh, :] += p.T @ do
             dp = do @ v[b, :, kh, :].T
-            ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+            if o is None:
+                delta = (p * dp).sum(axis=1, keepdims=True)
+            else:
+                delta = (do * o[b, :, h, :]).sum(axis=1, keepdims=True)
+            ds = p * (dp - delta)
             dq[b, :, h, :] = scale * (ds @ k[b, :, kh, :])
             dk[b, :, kh, :] += scale * (ds.T @ q[b, :, h, :])
     return dq, dk, dv

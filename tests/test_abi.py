@@ -142,17 +142,17 @@ def _tiles_with_visible_pairs(T, W):
 
 def test_bwd_validation_and_workspace(L):
     # fp32: the per-row D only (padded to 256 B); bf16 adds LSE * log2(e) (same
-    # size) and one 64 x 64 bf16 dS tile (8 KiB) per (b, head, query tile, key
-    # tile) holding a visible pair, and no other
+    # size) and one 64 x 64 dS tile as bf16 hi + lo (16 KiB) per (b, head, query
+    # tile, key tile) holding a visible pair, and no other
     def rows(B, T, H):
         return (B * H * T * 4 + 255) // 256 * 256
     assert L.ncattn_bwd_workspace_bytes(2, 100, 4, 2, 128, -1, 1) == rows(2, 100, 4) == 3328
     for B, T, H, W in [(2, 100, 4, -1), (2, 100, 4, 98), (1, 2048, 1, -1), (1, 2048, 1, 1024), (1, 2048, 1, 0),
                        (1, 2048, 1, 1), (1, 2048, 1, 64), (1, 2048, 1, 65), (3, 777, 2, 256), (1, 4096, 1, 2048)]:
-        want = 2 * rows(B, T, H) + B * H * _tiles_with_visible_pairs(T, W) * 8192
+        want = 2 * rows(B, T, H) + B * H * _tiles_with_visible_pairs(T, W) * 16384
         assert L.ncattn_bwd_workspace_bytes(B, T, H, H, 128, W, 0) == want, (B, T, H, W)
     # GQA full-causal layer (B16 T4096 H12): 64 * 65 / 2 tiles per (b, head)
-    assert L.ncattn_bwd_workspace_bytes(16, 4096, 12, 4, 128, -1, 0) == 2 * 16 * 12 * 4096 * 4 + 16 * 12 * 2080 * 8192
+    assert L.ncattn_bwd_workspace_bytes(16, 4096, 12, 4, 128, -1, 0) == 2 * 16 * 12 * 4096 * 4 + 16 * 12 * 2080 * 16384
     # a window reaching every key (W >= T - 1, up to INT_MAX) is full causal, sized as such
     full = L.ncattn_bwd_workspace_bytes(2, 100, 4, 2, 128, -1, 0)
     for W in (99, 100, 5000, 2 ** 31 - 64, 2 ** 31 - 1):

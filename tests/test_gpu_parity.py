@@ -138,6 +138,9 @@ FWD_CASES = [
     ("bf16", 1, 777, 6, 2, 128, 256),
     ("bf16", 1, 300, 8, 1, 128, -1),   # eight query heads on one kv head: dK/dV sum over the group
     ("bf16", 2, 333, 8, 1, 128, 100),
+    # enough (sequence, head) row blocks that dQ runs its 256-row, 8-wave shape
+    ("bf16", 64, 300, 8, 2, 128, -1),
+    ("bf16", 64, 300, 8, 2, 128, 100),
     ("f32", 1, 64, 2, 2, 64, -1),
     ("f32", 2, 100, 4, 2, 64, 17),
     ("f32", 1, 150, 2, 1, 128, -1),
@@ -155,7 +158,8 @@ def test_fwd_bwd(case):
     say(f"fwd/bwd {case}")
     q, k, v, do = attn_inputs(B, T, H, KV, D, dtype, seed=100 + T + W)
     ro, rlse = oracle.attn_fwd(f64(q), f64(k), f64(v), W)
-    rdq, rdk, rdv = oracle.attn_bwd(f64(q), f64(k), f64(v), f64(do), W)
+    # the backward is handed the forward's output as stored (the I/O dtype)
+    rdq, rdk, rdv = oracle.attn_bwd(f64(q), f64(k), f64(v), f64(do), W, o=stored(ro, dtype))
     qd, kd, vd, dod = to_dev(q, k, v, do)
     o, lse = nc.fwd(qd, kd, vd, window=(W, 0))
     torch.cuda.synchronize()
@@ -185,7 +189,7 @@ def test_long_sequence_window_sampled():
         a, e = c - 2 * W, min(T, c + W + R)
         sq, sk, sv, sdo = (f64(t[:, a:e]) for t in (q, k, v, do))
         ro, rlse = oracle.attn_fwd(sq, sk, sv, W)
-        rdq, rdk, rdv = oracle.attn_bwd(sq, sk, sv, sdo, W)
+        rdq, rdk, rdv = oracle.attn_bwd(sq, sk, sv, sdo, W, o=stored(ro, "bf16"))
         r = slice(c - a, c - a + R)
         check(o[:, c:c + R], ro[:, r], "bf16", "o")
         check_lse(lse[:, :, c:c + R], rlse[:, :, r], "bf16", "lse")
@@ -267,7 +271,7 @@ def test_fwd_bwd_scores_far_above_first_tile():
     for W in (-1, 150):
         say(f"large score growth W={W}")
         ro, rlse = oracle.attn_fwd(f64(q), f64(k), f64(v), W)
-        rdq, rdk, rdv = oracle.attn_bwd(f64(q), f64(k), f64(v), f64(do), W)
+        rdq, rdk, rdv = oracle.attn_bwd(f64(q), f64(k), f64(v), f64(do), W, o=stored(ro, "bf16"))
         assert float(rlse.max() - rlse.min()) > 60.0  # the construction does what it says
         qd, kd, vd, dod = to_dev(q, k, v, do)
         o, lse = nc.fwd(qd, kd, vd, window=(W, 0))

@@ -37,7 +37,7 @@ def test_tiny_fp32_full_chain(gain):
     q, k, v, do = config_inputs(cfg)
     qn, kn = oracle.qknorm_rope(f64(q), f64(k), None, cfg.rope_base, 1e-6, gain)
     ro, rlse = oracle.attn_fwd(qn, kn, f64(v), -1)
-    rdq, rdk, rdv = oracle.attn_bwd(qn, kn, f64(v), f64(do), -1)
+    rdq, rdk, rdv = oracle.attn_bwd(qn, kn, f64(v), f64(do), -1, o=stored(ro, "f32"))
     qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
     nc.qknorm_rope_(qd, kd, None, rope_base=cfg.rope_base, eps=1e-6, qk_gain=gain)
     o, lse = nc.fwd(qd, kd, vd)
@@ -117,7 +117,8 @@ def test_workload_layers(cfg, W):
             # the attention reads q', k' as stored (bf16)
             xq, xk = stored(xq, "bf16"), stored(xk, "bf16")
         ro, rlse = oracle.attn_fwd(xq, xk, f64(sv), W)
-        rdq, rdk, rdv = oracle.attn_bwd(xq, xk, f64(sv), f64(sdo), W)
+        # the backward is handed the forward's output as stored (bf16)
+        rdq, rdk, rdv = oracle.attn_bwd(xq, xk, f64(sv), f64(sdo), W, o=stored(ro, "bf16"))
         check(r["o"][b:b + 1, :, hs], ro, "bf16", f"o W={W} b={b} g={g}")
         check_lse(r["lse"][b:b + 1, hs], rlse, "bf16", f"lse W={W} b={b} g={g}")
         check(r["dq"][b:b + 1, :, hs], rdq, "bf16", f"dq W={W} b={b} g={g}")

@@ -604,3 +604,40 @@ def test_planted_mistakes_are_caught(monkeypatch):
     qq, kk, vv, dd = rand(1, 6, 2, 3), rand(1, 6, 1, 3), rand(1, 6, 1, 3), rand(1, 6, 2, 3)
     counted = _counted_attention(qq, kk, vv, dd, 1)[4:]
     assert (4 * 3 * 36 * 2, 8 * 3 * 36 * 2) != counted == oracle.attn_flops(1, 6, 2, 3, 1)
+
+
+# ----------------------------------------------------------------- backward given the forward's output
+
+@pytest.mark.parametrize("W", [-1, 3])
+def test_bwd_given_output_closed_forms(W):
+    """attn_bwd(..., o=O): with the exact O it is the exact gradient; dV never
+    depends on o; and replacing O by O + E moves each row's Delta by
+    sum_d dO E, which moves dQ_i by -scale (Delta'_i - Delta_i) sum_j P_ij k_j
+    and dK_j by -scale sum_i P_ij (Delta'_i - Delta_i) q_i (closed forms of the
+    Jacobian term, computed here from torch's SDPA probabilities)."""
+    B, T, H, KV, D = 1, 11, 4, 2, 8
+    q, k, v, do = rand(B, T, H, D), rand(B, T, KV, D), rand(B, T, KV, D), rand(B, T, H, D)
+    o, _ = oracle.attn_fwd(q, k, v, W)
+    exact = oracle.attn_bwd(q, k, v, do, W)
+    given = oracle.attn_bwd(q, k, v, do, W, o=o)
+    for a, b in zip(exact, given):
+        np.testing.assert_allclose(a, b, atol=1e-12)
+    E = 1e-3 * rand(B, T, H, D)
+    dq2, dk2, dv2 = oracle.attn_bwd(q, k, v, do, W, o=o + E)
+    np.testing.assert_allclose(dv2, exact[2], atol=1e-13)
+    scale = 1 / math.sqrt(D)
+    i = torch.arange(T)[:, None]
+    j = torch.arange(T)[None, :]
+    mask = (j <= i) & ((i - j <= W) if W >= 0 else torch.ones(T, T, dtype=torch.bool))
+    G = H // KV
+    want_dq = exact[0].copy()
+    want_dk = exact[1].copy()
+    for h in range(H):
+        kh = h // G
+        s = torch.from_numpy(scale * q[0, :, h] @ k[0, :, kh].T).masked_fill(~mask, float("-inf"))
+        p = torch.softmax(s, dim=-1).numpy()
+        dd = (do[0, :, h] * E[0, :, h]).sum(-1)                  # Delta' - Delta per row
+        want_dq[0, :, h] -= scale * dd[:, None] * (p @ k[0, :, kh])
+        want_dk[0, :, kh] -= scale * (p * dd[:, None]).T @ q[0, :, h]
+    np.testing.assert_allclose(dq2, want_dq, atol=1e-12)
+    np.testing.assert_allclose(dk2, want_dk, atol=1e-12)

@@ -26,8 +26,11 @@ namespace ncattn {
 
 namespace {
 
-constexpr int kBlockM = 128;  // query rows per dq workgroup
 constexpr int kBlockN = 128;  // keys per dkdv workgroup
+// One band entry: the 64 x 64 dS^T tile as bf16 hi (first 8 KB) and the bf16
+// remainder lo (next 8 KB), so the dQ stage sees dS to ~16 significant bits.
+constexpr int kDsTile = kTileN * kTileN;  // elements of one bf16 tile
+constexpr int kDsEntry = 2 * kDsTile;     // elements of a hi + lo entry
 // VALU instructions placed after each MFMA where the P/dS arithmetic of one
 // query block runs under the MFMAs of the other (3 to 12 measured within noise)
 constexpr int kValuUnderSdP = 10;   // under the S/dP MFMAs of the second block
@@ -124,13 +127,14 @@ __device__ __forceinline__ void split_bf16x2(float x0, float x1, uint32_t &hi, u
 
 // P = exp2(S c - LSE log2 e) and dS = P (dP - D) as bf16 MFMA operands, each as
 // a hi + lo pair (pk/pl, dk/dl: element pairs of accumulator rows 8 i + 4 hh + j,
-// the layout acc_to_operand gives), and the rounded dS rearranged for the
-// workspace: `out` holds this lane's 16 consecutive queries of its key's
-// [key][query] tile row, starting at query 32 qb + 16 hh (see ds_store).
+// the layout acc_to_operand gives), and dS hi and lo rearranged for the
+// workspace: out[0..1] (hi) and out[2..3] (lo) hold this lane's 16 consecutive
+// queries of its key's [key][query] tile row, from query 32 qb + 16 hh (see
+// ds_store).
 __device__ __forceinline__ void dkdv_p_ds(const f32x16 &sacc, const f32x16 &dmd, const float *lse2, bool need_mask,
                                           int qb, int qtile0, int key_lane, int T, int W, float c, int hh,
                                           uint32_t (&pk)[8], uint32_t (&pl)[8], uint32_t (&dk)[8],
-                                          uint32_t (&dl)[8], u32x4 (&out)[2]) {
+                                          uint32_t (&dl)[8], u32x4 (&out)[4]) {
   // rows of this lane's accumulator elements: 32 qb + 8 i + 4 hh + j
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -158,22 +162,30 @@ __device__ __forceinline__ void dkdv_p_ds(const f32x16 &sacc, const f32x16 &dmd,
   // (dk[k], dk[4 + k]) hands lane l < 32 its partner's dk[k] in the second value
   // and lane l >= 32 its partner's dk[4 + k] in the first, so that every lane then
   // owns 16 consecutive queries (32 B).
-  uint32_t x[4], y[4];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const auto r = __builtin_amdgcn_permlane32_swap(dk[k], dk[4 + k], false, false);
-    x[k] = r[0];
-    y[k] = r[1];
+  for (int part = 0; part < 2; ++part) {
+    const uint32_t(&w)[8] = part ? dl : dk;
+    uint32_t x[4], y[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const auto r = __builtin_amdgcn_permlane32_swap(w[k], w[4 + k], false, false);
+      x[k] = r[0];
+      y[k] = r[1];
+    }
+    out[2 * part] = u32x4{x[0], x[1], y[0], y[1]};
+    out[2 * part + 1] = u32x4{x[2], x[3], y[2], y[3]};
   }
-  out[0] = u32x4{x[0], x[1], y[0], y[1]};
-  out[1] = u32x4{x[2], x[3], y[2], y[3]};
 }
 
-// Writes a lane's 32 dS bytes (from dkdv_p_ds) into its workspace tile row.
-__device__ __forceinline__ void ds_store(uint16_t *ds_row, const u32x4 (&out)[2], int qb, int hh) {
+// Writes a lane's 32 dS bytes, hi and lo (from dkdv_p_ds), into its workspace
+// tile row (`ds_row` in the hi tile; the lo tile follows kDsTile elements on).
+__device__ __forceinline__ void ds_store(uint16_t *ds_row, const u32x4 (&out)[4], int qb, int hh) {
   u32x4 *dst = (u32x4 *)(ds_row + 32 * qb + 16 * hh);
+  u32x4 *dst_lo = (u32x4 *)(ds_row + kDsTile + 32 * qb + 16 * hh);
   dst[0] = out[0];
   dst[1] = out[1];
+  dst_lo[0] = out[2];
+  dst_lo[1] = out[3];
 }
 
 // dV^T += dO^T (P_hi + P_lo) and dK^T += Q^T (dS_hi + dS_lo), contraction over the
@@ -270,7 +282,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__rest
   };
   const long long qbase = (long long)b * T * q_stride + (long long)kvh * G * kD;  // q/dO of (b, head kvh G)
   const long long rbase = ((long long)b * H + (long long)kvh * G) * T;         // its lse / delta row
-  uint16_t *const band_b = dsband + ((long long)b * H + (long long)kvh * G) * band_tiles * (kTileN * kTileN);
+  uint16_t *const band_b = dsband + ((long long)b * H + (long long)kvh * G) * band_tiles * kDsEntry;
 
   auto stage = [&](const Pos &p, char *base) {
     const long long hoff = qbase + (long long)p.g * kD;
@@ -322,7 +334,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__rest
     const bool skip = !wave_active || qtile0 + kTileN - 1 < kw0 || (W >= 0 && qtile0 - kw_last > W);
     if (!skip) {
       const long long tile = (long long)p.g * band_tiles + p.row + (kt - ds_kt_lo(p.qt, band_c));
-      uint16_t *ds_row = band_b + tile * (kTileN * kTileN) + (kofs + (lane & 31)) * kTileN;
+      uint16_t *ds_row = band_b + tile * kDsEntry + (kofs + (lane & 31)) * kTileN;
       bool act[2], msk[2];
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
@@ -336,7 +348,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__rest
         // 0 under that of block 1
         f32x16 s0, p0, s1, p1;
         uint32_t pk0[8], pl0[8], dk0[8], dl0[8], pk1[8], pl1[8], dk1[8], dl1[8];
-        u32x4 out0[2], out1[2];
+        u32x4 out0[4], out1[4];
         dkdv_sdp(s0, p0, qs, dos, ndl, L, kreg, vreg, 0, hh);
         __builtin_amdgcn_sched_barrier(0);
         dkdv_sdp(s1, p1, qs, dos, ndl, L, kreg, vreg, 1, hh);
@@ -357,7 +369,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__rest
           f32x16 s0, p0;
           uint32_t pk0[8], pl0[8], dk0[8], dl0[8];
           dkdv_sdp(s0, p0, qs, dos, ndl, L, kreg, vreg, qb, hh);
-          u32x4 out[2];
+          u32x4 out[4];
           dkdv_p_ds(s0, p0, lse2, msk[qb], qb, qtile0, key_lane, T, W, c, hh, pk0, pl0, dk0, dl0, out);
           ds_store(ds_row, out, qb, hh);
           dkdv_acc(dkacc, dvacc, pk0, pl0, dk0, dl0, qs, dos, L, qb);
@@ -389,45 +401,60 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__rest
 }
 
 // ---------------------------------------------------------------- dQ
-// dQ = scale dS K from the dS tiles the dK/dV stage stored: one GEMM per tile.
-// A dS^T tile ([key][query], 64 x 64 bf16, 128-byte rows) is staged with its
-// 16-byte chunks permuted per row, chunk' = chunk ^ (4 ((row >> 1) & 1)), which
-// keeps the transposing reads below free of bank conflicts.
+// dQ = scale (dS_hi + dS_lo) K from the dS tiles the dK/dV stage stored: two
+// GEMMs per tile.  The stage streams the band from HBM, so it wants many bytes in
+// flight.  Two shapes: NW = 8 waves on 256 query rows (four query tiles) with one
+// key tile ahead (two LDS stages of one K tile and four hi + lo dS^T tiles, 80 KB
+// each), and NW = 4 waves on 128 rows with two key tiles ahead (three stages of
+// 48 KB) for grids too small to give every CU two of the larger workgroups; one
+// workgroup per CU either way.  A dS^T tile ([key][query],
+// 64 x 64 bf16, 128-byte rows) is staged with its 16-byte chunks permuted per
+// row, chunk' = chunk ^ (4 ((row >> 1) & 1)), which keeps the transposing reads
+// below free of bank conflicts.
+template <int NW>
+struct DqShape {
+  static constexpr int kRows = 32 * NW;                            // query rows per workgroup
+  static constexpr int kStages = NW == 8 ? 2 : 3;                  // LDS stages (key tiles in the ring)
+  static constexpr int kStage = kTileBytes + (NW / 2) * 16384;    // K tile + one hi + lo dS^T tile per 2 waves
+  static constexpr int kCopies = 16 / NW + 8;                      // copy instructions per wave per stage
+};
 __device__ __forceinline__ int ds_swz(int row, int chunk) { return row * 128 + ((chunk ^ (((row >> 1) & 1) << 2)) << 4); }
 
-// Direct global -> LDS copy of one dS^T tile (8 KB) by the 4 waves: wave w,
-// instruction i fills rows 16 w + 8 i + [0, 8), lane l row + l/8, position l%8.
-__device__ __forceinline__ void ds_tile_load(char *lds_tile, const uint16_t *src_tile, int tid) {
-  const int lane = tid & 63, w = tid >> 6;
-  typedef __attribute__((address_space(3))) void lds_void;
-  typedef __attribute__((address_space(1))) const void glb_void;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int row = 16 * w + 8 * i + (lane >> 3);
-    const int chunk = (lane & 7) ^ (((row >> 1) & 1) << 2);
-    const char *src = (const char *)src_tile + row * 128 + chunk * 16;
-    __builtin_amdgcn_global_load_lds((glb_void *)src, (lds_void *)(lds_tile + (16 * w + 8 * i) * 128), 16, 0, 0);
-  }
+// Wait until at most n of this wave's vector memory operations (and none of its
+// LDS operations) are in flight, then a barrier that drains nothing else (a plain
+// __syncthreads also waits for every outstanding load, which would empty a
+// prefetch ring deeper than one stage).
+template <int N>
+__device__ __forceinline__ void vm_wait_barrier() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0070 | N);  // vmcnt(N) lgkmcnt(0), expcnt at its maximum
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
 }
 
-__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t *__restrict__ K,
-                                                        const uint16_t *__restrict__ dsband,
-                                                        uint16_t *__restrict__ dQ, int B, int T, int H, int KV,
-                                                        int W, float scale, int nqt, int band_c, long long band_tiles) {
-  // double buffer: [K tile | dS^T tile of query tile 2 qblk | of query tile 2 qblk + 1]
-  __shared__ __attribute__((aligned(1024))) char buf0[kTileBytes + 2 * 8192];
-  __shared__ __attribute__((aligned(1024))) char buf1[kTileBytes + 2 * 8192];
+template <int NW>
+__global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(const uint16_t *__restrict__ K,
+                                                                 const uint16_t *__restrict__ dsband,
+                                                                 uint16_t *__restrict__ dQ, int B, int T, int H,
+                                                                 int KV, int W, float scale, int nqt, int band_c,
+                                                                 long long band_tiles) {
+  using S = DqShape<NW>;
+  __shared__ __attribute__((aligned(1024))) char st0[S::kStage];
+  __shared__ __attribute__((aligned(1024))) char st1[S::kStage];
+  __shared__ __attribute__((aligned(1024))) char st2[S::kStages == 3 ? S::kStage : 16];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int nqb = (T + kBlockM - 1) / kBlockM;
+  const int nqb = (T + S::kRows - 1) / S::kRows;
   const int BH = B * H;
-  const int qblk = nqb - 1 - (int)(blockIdx.x / BH);
+  const int qblk = nqb - 1 - (int)(blockIdx.x / BH);  // heaviest (latest) row blocks first
   const int bh = (int)(blockIdx.x % BH);
   const int b = bh / H;
   const int h = bh % H;
   const int kvh = h / (H / KV);
-  const int q0 = qblk * kBlockM;
+  const int q0 = qblk * S::kRows;
   const int qw0 = q0 + 32 * wave;
   const int q_lane = qw0 + (lane & 31);
   const int hh = lane >> 5;
@@ -436,9 +463,28 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t *__restri
   const uint16_t *Kb = K + (long long)b * T * kv_stride + (long long)kvh * kD;
   const TileSrc ksrc = make_tile_src(Kb, kv_stride, T);
   const int voff = tile_lane_voff(ksrc.stride, tid);
-  const uint16_t *dsh = dsband + (long long)bh * band_tiles * (kTileN * kTileN);
+  // this wave's share of the dS^T copies: query tile qt_w = (NW / 2) qblk +
+  // (wave >> 1), rows 32 (wave & 1) + 8 i + l/8 of its tile against each key
+  // tile.  The band row of qt_w (key tiles kt_lo .. qt_w) is a buffer resource of
+  // its own; a zero-size resource for tiles that do not exist keeps the number
+  // of copy instructions per stage fixed (those copies write zeros that no wave
+  // reads).
+  const int ds_sub = wave >> 1;
+  const int qt_w = (NW / 2) * qblk + ds_sub;
+  const int kt_lo_w = ds_kt_lo(qt_w, band_c);
+  const uint16_t *ds_rowp =
+      dsband + ((long long)bh * band_tiles + (qt_w < nqt ? ds_row_start(qt_w, band_c) : 0)) * kDsEntry;
+  const __amdgpu_buffer_rsrc_t band_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)ds_rowp, (short)0, qt_w < nqt ? (qt_w - kt_lo_w + 1) * 2 * 8192 : 0, 0x00020000);
+  const __amdgpu_buffer_rsrc_t none_rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)ds_rowp, (short)0, 0, 0x00020000);
+  int ds_voff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 32 * (wave & 1) + 8 * i + (lane >> 3);
+    ds_voff[i] = row * 128 + (((lane & 7) ^ (((row >> 1) & 1) << 2)) << 4);
+  }
 
-  const int q_last_blk = min(q0 + kBlockM - 1, T - 1);
+  const int q_last_blk = min(q0 + S::kRows - 1, T - 1);
   const int t0 = (W < 0 ? 0 : max(0, q0 - W)) / kTileN;
   const int t1 = q_last_blk / kTileN;
   const int qw_last = min(qw0 + 31, T - 1);
@@ -446,16 +492,20 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t *__restri
   const int tw0 = max(t0, (W < 0 ? 0 : max(0, qw0 - W)) / kTileN);
   const int tw1 = wave_active ? qw_last / kTileN : t0 - 1;
 
-  // copies for key tile t: K, and the dS^T tiles of the block's two query tiles
-  // that see tile t
-  auto load = [&](char *buf, int t) {
-    tile_load_lds(buf, ksrc, voff, t * kTileN);
+  // copies for key tile t (every wave issues exactly S::kCopies): K, and the
+  // dS^T tile of each of the block's query tiles that sees tile t
+  auto load = [&](char *stage, int t) {
+    tile_load_lds<NW>(stage, ksrc, voff, t * kTileN);
+    const bool have = qt_w < nqt && t >= kt_lo_w && t <= qt_w;
+    const __amdgpu_buffer_rsrc_t r = have ? band_rsrc : none_rsrc;
+    const int soff = have ? (t - kt_lo_w) * 2 * 8192 : 0;
+    char *dst = stage + kTileBytes + ds_sub * 16384 + (wave & 1) * 4096;
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      const int qt = 2 * qblk + sub;
-      if (qt < nqt && t >= ds_kt_lo(qt, band_c) && t <= qt)
-        ds_tile_load(buf + kTileBytes + sub * 8192, dsh + ds_tile(qt, t, band_c) * (kTileN * kTileN), tid);
-    }
+    for (int part = 0; part < 2; ++part)  // hi, then lo 8 KB further on (in the band and in LDS)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dst + 8192 * part + 1024 * i), 16, ds_voff[i],
+                                                 soff + 8192 * part, 0, 0);
   };
 
   const TileLane L = make_tile_lane(lane);
@@ -469,29 +519,45 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t *__restri
 #pragma unroll
     for (int half = 0; half < 2; ++half) soff[half] = ds_swz(x + 8 * half, qc >> 3) + (qc & 7) * 2;
   }
-  const int ssub = (wave >> 1) * 8192;
+  const int ssub = kTileBytes + ds_sub * 16384;
 
   f32x16 dqacc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) dqacc[i] = f32x16{};
 
-  load(buf0, t0);
-  lds_loads_done_barrier();
+  load(st0, t0);
+  if (S::kStages == 3 && t0 + 1 <= t1) load(st1, t0 + 1);
 
-  auto step = [&](const char *cur, char *nxt, int t) {
-    if (t < t1) load(nxt, t + 1);
+  // Step t reads the stage holding tile t and refills the one tile t + kStages - 1
+  // goes to (it held tile t - 1, which every wave finished before the barrier).
+  auto step = [&](const char *cur, char *fill, int t) {
+    if (S::kStages == 3) {
+      // the copies of tile t are done once at most those of tile t + 1 remain
+      if (t + 1 <= t1)
+        vm_wait_barrier<S::kCopies>();
+      else
+        vm_wait_barrier<0>();
+      if (t + 2 <= t1) load(fill, t + 2);
+    } else {
+      vm_wait_barrier<0>();
+      if (t + 1 <= t1) load(fill, t + 1);
+    }
     if (t >= tw0 && t <= tw1) {
       const int k0 = t * kTileN;
       const bool need_mask = !(k0 + kTileN - 1 <= qw0 && (W < 0 || qw_last - k0 <= W));
-      const char *st = cur + kTileBytes + ssub;
-      // every operand of the tile is read from LDS before the first MFMA
-      u32x4 dsw[4];
+      const char *st = cur + ssub;
+      // every operand of the tile is read from LDS before the first MFMA; dsw[2 cs]
+      // is the hi part, dsw[2 cs + 1] the lo part
+      u32x4 dsw[8];
       bf16x8 kop[4][4];
 #pragma unroll
       for (int cs = 0; cs < 4; ++cs) {
-        const u32x2 lo = __builtin_bit_cast(u32x2, lds_read_tr16(st + soff[0] + cs * 16 * 128));
-        const u32x2 hi = __builtin_bit_cast(u32x2, lds_read_tr16(st + soff[1] + cs * 16 * 128));
-        dsw[cs] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+        for (int part = 0; part < 2; ++part) {
+          const u32x2 a = __builtin_bit_cast(u32x2, lds_read_tr16(st + 8192 * part + soff[0] + cs * 16 * 128));
+          const u32x2 c = __builtin_bit_cast(u32x2, lds_read_tr16(st + 8192 * part + soff[1] + cs * 16 * 128));
+          dsw[2 * cs + part] = u32x4{a[0], a[1], c[0], c[1]};
+        }
 #pragma unroll
         for (int db = 0; db < 4; ++db) kop[cs][db] = col_operand(cur, L, db, cs);
       }
@@ -509,23 +575,37 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t *__restri
               const bool vis = key <= q_lane && (W < 0 || q_lane - key <= W);
               keep |= vis ? (0xffffu << (16 * half)) : 0u;
             }
-            dsw[cs][e2] &= keep;
+            dsw[2 * cs][e2] &= keep;
+            dsw[2 * cs + 1][e2] &= keep;
           }
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int cs = 0; cs < 4; ++cs) {
-        const bf16x8 dsb = __builtin_bit_cast(bf16x8, dsw[cs]);
+        const bf16x8 dsh = __builtin_bit_cast(bf16x8, dsw[2 * cs]);
+        const bf16x8 dsl = __builtin_bit_cast(bf16x8, dsw[2 * cs + 1]);
 #pragma unroll
-        for (int db = 0; db < 4; ++db) dqacc[db] = mfma32(kop[cs][db], dsb, dqacc[db]);
+        for (int db = 0; db < 4; ++db) {
+          dqacc[db] = mfma32(kop[cs][db], dsh, dqacc[db]);
+          dqacc[db] = mfma32(kop[cs][db], dsl, dqacc[db]);
+        }
       }
     }
-    lds_loads_done_barrier();
   };
-  for (int t = t0; t <= t1; t += 2) {
-    step(buf0, buf1, t);
-    if (t + 1 > t1) break;
-    step(buf1, buf0, t + 1);
+  if (S::kStages == 3) {
+    for (int t = t0; t <= t1; t += 3) {
+      step(st0, st2, t);
+      if (t + 1 > t1) break;
+      step(st1, st0, t + 1);
+      if (t + 2 > t1) break;
+      step(st2, st1, t + 2);
+    }
+  } else {
+    for (int t = t0; t <= t1; t += 2) {
+      step(st0, st1, t);
+      if (t + 1 > t1) break;
+      step(st1, st0, t + 1);
+    }
   }
 
   if (!wave_active || q_lane >= T) return;
@@ -548,7 +628,7 @@ size_t bwd_workspace_bytes(int B, int T, int H, int W, bool bf16) {
   const size_t rows = ((size_t)B * H * T * sizeof(float) + 255) & ~(size_t)255;
   if (!bf16) return rows;
   const DsBand band = ds_band(T, W);
-  return 2 * rows + (size_t)B * H * band.tiles * (kTileN * kTileN) * 2;
+  return 2 * rows + (size_t)B * H * band.tiles * kDsEntry * 2;
 }
 
 hipError_t launch_bwd_bf16(const void *q, const void *k, const void *v, const void *o, const float *lse,
@@ -562,7 +642,11 @@ hipError_t launch_bwd_bf16(const void *q, const void *k, const void *v, const vo
   const long long rows = (long long)sh.B * sh.T * sh.H;
   const long long dblocks = (rows + 63) / 64;
   const long long nkb = (sh.T + kBlockN - 1) / kBlockN;
-  const long long nqb = (sh.T + kBlockM - 1) / kBlockM;
+  // the 256-row dQ shape when the grid still gives every CU two of them
+  const long long nqb8 = (sh.T + DqShape<8>::kRows - 1) / DqShape<8>::kRows;
+  const bool dq8 = nqb8 * sh.B * sh.H >= 512;
+  const long long nqb = (sh.T + (dq8 ? DqShape<8>::kRows : DqShape<4>::kRows) - 1) /
+                        (dq8 ? DqShape<8>::kRows : DqShape<4>::kRows);
   const long long kvblocks = nkb * sh.B * sh.KV;
   const long long qblocks = nqb * sh.B * sh.H;
   if (dblocks > 0x7fffffffLL || kvblocks > 0x7fffffffLL || qblocks > 0x7fffffffLL) return hipErrorInvalidValue;
@@ -573,8 +657,11 @@ hipError_t launch_bwd_bf16(const void *q, const void *k, const void *v, const vo
     hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)kvblocks), dim3(256), 0, s, (const uint16_t *)q,
                        (const uint16_t *)k, (const uint16_t *)v, (const uint16_t *)dout, lse2, delta, (uint16_t *)dk,
                        (uint16_t *)dv, dsband, sh.B, sh.T, sh.H, sh.KV, sh.window, sh.scale, band.c, band.tiles);
-  if (stages & kBwdDq)
-    hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)qblocks), dim3(256), 0, s, (const uint16_t *)k, dsband,
+  if ((stages & kBwdDq) && dq8)
+    hipLaunchKernelGGL(bwd_dq_kernel<8>, dim3((unsigned)qblocks), dim3(512), 0, s, (const uint16_t *)k, dsband,
+                       (uint16_t *)dq, sh.B, sh.T, sh.H, sh.KV, sh.window, sh.scale, band.nqt, band.c, band.tiles);
+  if ((stages & kBwdDq) && !dq8)
+    hipLaunchKernelGGL(bwd_dq_kernel<4>, dim3((unsigned)qblocks), dim3(256), 0, s, (const uint16_t *)k, dsband,
                        (uint16_t *)dq, sh.B, sh.T, sh.H, sh.KV, sh.window, sh.scale, band.nqt, band.c, band.tiles);
   return hipGetLastError();
 }

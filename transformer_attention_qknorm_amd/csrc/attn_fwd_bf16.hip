@@ -131,12 +131,21 @@ __device__ __forceinline__ void softmax_exp(FwdState &st, f32x16 (&sacc)[2], flo
   st.l_run += ls;
 }
 
+// O^T += V^T P^T with the probabilities as bf16 hi + lo (two MFMAs per block):
+// a single bf16 P leaves O off by ~2^-9 relative before its own rounding, which
+// moves the stored O by an ulp often enough to matter downstream (the backward's
+// D = dO . O) and to miss 2e-2 where |O| >= 4.
 __device__ __forceinline__ void pv_tile(FwdState &st, const f32x16 (&pacc)[2], const char *vs, const TileLane &L) {
 #pragma unroll
   for (int cs = 0; cs < 4; ++cs) {
-    const bf16x8 pb = acc_to_operand(pacc[cs >> 1], cs & 1);
+    bf16x8 pb, pl;
+    acc_to_operand_split(pacc[cs >> 1], cs & 1, pb, pl);
 #pragma unroll
-    for (int db = 0; db < 4; ++db) st.oacc[db] = mfma32(col_operand(vs, L, db, cs), pb, st.oacc[db]);
+    for (int db = 0; db < 4; ++db) {
+      const bf16x8 a = col_operand(vs, L, db, cs);
+      st.oacc[db] = mfma32(a, pb, st.oacc[db]);
+      st.oacc[db] = mfma32(a, pl, st.oacc[db]);
+    }
   }
 }
 

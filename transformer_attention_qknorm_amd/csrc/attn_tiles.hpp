@@ -117,4 +117,19 @@ __device__ __forceinline__ bf16x8 acc_to_operand(const f32x16 &acc, int c2) {
   return __builtin_bit_cast(bf16x8, w);
 }
 
+// The same operand as bf16 hi + lo: hi is each value rounded to bf16, lo the
+// remainder rounded to bf16, so hi + lo carries the fp32 value to about 16
+// significant bits (a contraction fed both loses only ~2^-16 relative).
+__device__ __forceinline__ void acc_to_operand_split(const f32x16 &acc, int c2, bf16x8 &hi, bf16x8 &lo) {
+  u32x4 h, l;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float x0 = acc[8 * c2 + 2 * i], x1 = acc[8 * c2 + 2 * i + 1];
+    h[i] = pack_bf16x2(x0, x1);
+    l[i] = pack_bf16x2(x0 - __uint_as_float(h[i] << 16), x1 - __uint_as_float(h[i] & 0xffff0000u));
+  }
+  hi = __builtin_bit_cast(bf16x8, h);
+  lo = __builtin_bit_cast(bf16x8, l);
+}
+
 }  // namespace ncattn
