@@ -129,11 +129,10 @@ int ncattn_fwd_qknorm_rope(void *q, void *k, const void *v, void *o, float *lse,
                            void *stream);
 
 /*
- * Bytes of workspace ncattn_bwd needs for this shape and window: the per-row
- * fp32 D_i = sum_d dO_i O_i (for bf16 stored negated, next to LSE_i log2 e) and,
- * for bf16, the bf16 dS = P (dP - D) tiles of the
- * window band that the dk/dv stage hands to the dq stage (64 x 64 tiles, about
- * 2 bytes per visible (query, key) pair and head).  0 for invalid sizes.
+ * Bytes of workspace ncattn_bwd needs for this shape: the per-row fp32
+ * D_i = sum_d dO_i O_i (for bf16 stored negated, next to a second row array of
+ * LSE_i log2 e), i.e. 4 (fp32) or 8 (bf16) bytes per (b, head, query row), each
+ * array padded to 256 bytes.  Linear in T for every window.  0 for invalid sizes.
  */
 size_t ncattn_bwd_workspace_bytes(int B, int T, int n_head, int n_kv_head, int head_dim, int window_left,
                                   int dtype);
@@ -145,7 +144,11 @@ size_t ncattn_bwd_workspace_bytes(int B, int T, int n_head, int n_kv_head, int h
  *   ncattn_fwd, dout [B][T][n_head][D]; outputs dq [B][T][n_head][D],
  *   dk, dv [B][T][n_kv_head][D] (dtype; fp32 accumulation).  dk and dv of a kv
  *   head are summed over the query heads of its group.  Deterministic: no
- *   atomics, the same inputs give the same bits.
+ *   atomics, the same inputs give the same bits.  Delta_i = sum_d dO_i o_i is
+ *   formed from the o passed in (the forward's output, as stored), as an FA3-style
+ *   backward does.  For bf16 the probabilities P and dS = P (dP - Delta) enter the
+ *   dV, dK and dQ products as bf16 hi + lo pairs (fp32 precision), so only the final
+ *   rounding of dq, dk, dv to bf16 is lost.
  *   workspace: device memory of at least ncattn_bwd_workspace_bytes(...) bytes,
  *   overwritten.
  */
@@ -157,11 +160,11 @@ int ncattn_bwd(const void *q, const void *k, const void *v, const void *o, const
 
 /*
  * The three stages of ncattn_bwd, callable one at a time with the same
- * arguments and checks: ncattn_bwd_preprocess writes D_i = sum_d dO_i O_i into
- * the workspace, ncattn_bwd_dkdv then writes dk and dv (and, for bf16, dS into
- * the workspace), ncattn_bwd_dq writes dq from the workspace.  Enqueuing the three
- * in this order on one stream, with one workspace, is exactly ncattn_bwd; each
- * stage needs the previous one to have completed.  Useful for timing each stage.
+ * arguments and checks: ncattn_bwd_preprocess writes D_i = sum_d dO_i O_i (and,
+ * for bf16, LSE_i log2 e) into the workspace, ncattn_bwd_dkdv then writes dk and
+ * dv, ncattn_bwd_dq writes dq; the last two only read the workspace and may run
+ * in either order.  Enqueuing the three in this order on one stream, with one
+ * workspace, is exactly ncattn_bwd.  Useful for timing each stage.
  */
 int ncattn_bwd_preprocess(const void *q, const void *k, const void *v, const void *o, const float *lse,
                           const void *dout, void *dq, void *dk, void *dv,

@@ -18,7 +18,9 @@
 //      transposing LDS reads of dO and Q.
 //   3. bwd_dq: one workgroup per (b, h, 128-row query block), like the forward:
 //      S^T = K Q^T and dP^T = V dO^T with Q, dO in registers, dQ^T += K^T dS^T.
-// Tiles with no visible pair are skipped; masks only on straddling tiles.
+// Both contraction stages recompute S and dP; P and dS enter the dV, dK and dQ
+// products as bf16 hi + lo (fp32 precision, see split_bf16x2).  Tiles with no
+// visible pair are skipped; masks only on straddling tiles.
 #include "attn_tiles.hpp"
 #include "internal.hpp"
 
@@ -27,10 +29,7 @@ namespace ncattn {
 namespace {
 
 constexpr int kBlockN = 128;  // keys per dkdv workgroup
-// One band entry: the 64 x 64 dS^T tile as bf16 hi (first 8 KB) and the bf16
-// remainder lo (next 8 KB), so the dQ stage sees dS to ~16 significant bits.
-constexpr int kDsTile = kTileN * kTileN;  // elements of one bf16 tile
-constexpr int kDsEntry = 2 * kDsTile;     // elements of a hi + lo entry
+constexpr int kDqRows = 128;  // query rows per dq workgroup
 // VALU instructions placed after each MFMA where the P/dS arithmetic of one
 // query block runs under the MFMAs of the other (3 to 12 measured within noise)
 constexpr int kValuUnderSdP = 10;   // under the S/dP MFMAs of the second block
@@ -127,14 +126,11 @@ __device__ __forceinline__ void split_bf16x2(float x0, float x1, uint32_t &hi, u
 
 // P = exp2(S c - LSE log2 e) and dS = P (dP - D) as bf16 MFMA operands, each as
 // a hi + lo pair (pk/pl, dk/dl: element pairs of accumulator rows 8 i + 4 hh + j,
-// the layout acc_to_operand gives), and dS hi and lo rearranged for the
-// workspace: out[0..1] (hi) and out[2..3] (lo) hold this lane's 16 consecutive
-// queries of its key's [key][query] tile row, from query 32 qb + 16 hh (see
-// ds_store).
+// the layout acc_to_operand gives).
 __device__ __forceinline__ void dkdv_p_ds(const f32x16 &sacc, const f32x16 &dmd, const float *lse2, bool need_mask,
                                           int qb, int qtile0, int key_lane, int T, int W, float c, int hh,
                                           uint32_t (&pk)[8], uint32_t (&pl)[8], uint32_t (&dk)[8],
-                                          uint32_t (&dl)[8], u32x4 (&out)[4]) {
+                                          uint32_t (&dl)[8]) {
   // rows of this lane's accumulator elements: 32 qb + 8 i + 4 hh + j
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -157,35 +153,6 @@ __device__ __forceinline__ void dkdv_p_ds(const f32x16 &sacc, const f32x16 &dmd,
     split_bf16x2(ds[0], ds[1], dk[2 * i], dl[2 * i]);
     split_bf16x2(ds[2], ds[3], dk[2 * i + 1], dl[2 * i + 1]);
   }
-  // The two half-waves hold interleaved groups of 4 queries of the same key
-  // (h = 0: 0-3, 8-11, 16-19, 24-27; h = 1: 4-7, ...).  v_permlane32_swap of
-  // (dk[k], dk[4 + k]) hands lane l < 32 its partner's dk[k] in the second value
-  // and lane l >= 32 its partner's dk[4 + k] in the first, so that every lane then
-  // owns 16 consecutive queries (32 B).
-#pragma unroll
-  for (int part = 0; part < 2; ++part) {
-    const uint32_t(&w)[8] = part ? dl : dk;
-    uint32_t x[4], y[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const auto r = __builtin_amdgcn_permlane32_swap(w[k], w[4 + k], false, false);
-      x[k] = r[0];
-      y[k] = r[1];
-    }
-    out[2 * part] = u32x4{x[0], x[1], y[0], y[1]};
-    out[2 * part + 1] = u32x4{x[2], x[3], y[2], y[3]};
-  }
-}
-
-// Writes a lane's 32 dS bytes, hi and lo (from dkdv_p_ds), into its workspace
-// tile row (`ds_row` in the hi tile; the lo tile follows kDsTile elements on).
-__device__ __forceinline__ void ds_store(uint16_t *ds_row, const u32x4 (&out)[4], int qb, int hh) {
-  u32x4 *dst = (u32x4 *)(ds_row + 32 * qb + 16 * hh);
-  u32x4 *dst_lo = (u32x4 *)(ds_row + kDsTile + 32 * qb + 16 * hh);
-  dst[0] = out[0];
-  dst[1] = out[1];
-  dst_lo[0] = out[2];
-  dst_lo[1] = out[3];
 }
 
 // dV^T += dO^T (P_hi + P_lo) and dK^T += Q^T (dS_hi + dS_lo), contraction over the
@@ -229,9 +196,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__rest
                                                           const uint16_t *__restrict__ dO,
                                                           const float *__restrict__ lse2g,
                                                           const float *__restrict__ delta, uint16_t *__restrict__ dK,
-                                                          uint16_t *__restrict__ dV, uint16_t *__restrict__ dsband,
-                                                          int B, int T, int H, int KV, int W, float scale, int band_c,
-                                                          long long band_tiles) {
+                                                          uint16_t *__restrict__ dV, int B, int T, int H, int KV,
+                                                          int W, float scale) {
   // Two separate LDS objects for the double buffer (Q | dO | lse2 | delta each),
   // so the compiler can tell the copy into one from the reads of the other.
   __shared__ __attribute__((aligned(1024))) char buf0[kQBuf];
@@ -250,8 +216,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__rest
   const int k0 = kblk * kBlockN;
   const int kw0 = k0 + 32 * wave;
   const int key_lane = kw0 + (lane & 31);  // the key column this lane holds
-  const int kt = kw0 / kTileN;              // key tile of this wave's keys, and their first row in it
-  const int kofs = kw0 % kTileN;
   const float c = scale * kLog2e;
 
   const long long q_stride = (long long)H * kD;
@@ -266,23 +230,19 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__rest
   const int n_iter = nq * G;
 
   // Step order: query tile qt (outer) x head h = kvh G + g (inner), tracked
-  // incrementally (no division by G per step); `row` is the band index of the
-  // first stored tile of query tile qt (ds_row_start).
+  // incrementally (no division by G per step).
   struct Pos {
     int qt, g;
-    long long row;
   };
   auto advance = [&](Pos p) {
     if (++p.g == G) {
       p.g = 0;
-      p.row += min(p.qt, band_c) + 1;
       ++p.qt;
     }
     return p;
   };
   const long long qbase = (long long)b * T * q_stride + (long long)kvh * G * kD;  // q/dO of (b, head kvh G)
   const long long rbase = ((long long)b * H + (long long)kvh * G) * T;         // its lse / delta row
-  uint16_t *const band_b = dsband + ((long long)b * H + (long long)kvh * G) * band_tiles * kDsEntry;
 
   auto stage = [&](const Pos &p, char *base) {
     const long long hoff = qbase + (long long)p.g * kD;
@@ -296,7 +256,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__rest
     }
   };
 
-  Pos pos{qt0, 0, ds_row_start(qt0, band_c)};
+  Pos pos{qt0, 0};
   stage(pos, buf0);
 
   bf16x8 kreg[8], vreg[8];
@@ -333,8 +293,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__rest
     const int qtile0 = p.qt * kTileN;
     const bool skip = !wave_active || qtile0 + kTileN - 1 < kw0 || (W >= 0 && qtile0 - kw_last > W);
     if (!skip) {
-      const long long tile = (long long)p.g * band_tiles + p.row + (kt - ds_kt_lo(p.qt, band_c));
-      uint16_t *ds_row = band_b + tile * kDsEntry + (kofs + (lane & 31)) * kTileN;
       bool act[2], msk[2];
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
@@ -348,17 +306,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__rest
         // 0 under that of block 1
         f32x16 s0, p0, s1, p1;
         uint32_t pk0[8], pl0[8], dk0[8], dl0[8], pk1[8], pl1[8], dk1[8], dl1[8];
-        u32x4 out0[4], out1[4];
         dkdv_sdp(s0, p0, qs, dos, ndl, L, kreg, vreg, 0, hh);
         __builtin_amdgcn_sched_barrier(0);
         dkdv_sdp(s1, p1, qs, dos, ndl, L, kreg, vreg, 1, hh);
-        dkdv_p_ds(s0, p0, lse2, false, 0, qtile0, key_lane, T, W, c, hh, pk0, pl0, dk0, dl0, out0);
-        ds_store(ds_row, out0, 0, hh);
+        dkdv_p_ds(s0, p0, lse2, false, 0, qtile0, key_lane, T, W, c, hh, pk0, pl0, dk0, dl0);
         interleave_mfma_valu<16, kValuUnderSdP>();
         __builtin_amdgcn_sched_barrier(0);
         dkdv_acc(dkacc, dvacc, pk0, pl0, dk0, dl0, qs, dos, L, 0);
-        dkdv_p_ds(s1, p1, lse2, false, 1, qtile0, key_lane, T, W, c, hh, pk1, pl1, dk1, dl1, out1);
-        ds_store(ds_row, out1, 1, hh);
+        dkdv_p_ds(s1, p1, lse2, false, 1, qtile0, key_lane, T, W, c, hh, pk1, pl1, dk1, dl1);
         interleave_mfma_valu<32, kValuUnderDkDv>();
         __builtin_amdgcn_sched_barrier(0);
         dkdv_acc(dkacc, dvacc, pk1, pl1, dk1, dl1, qs, dos, L, 1);
@@ -369,9 +324,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__rest
           f32x16 s0, p0;
           uint32_t pk0[8], pl0[8], dk0[8], dl0[8];
           dkdv_sdp(s0, p0, qs, dos, ndl, L, kreg, vreg, qb, hh);
-          u32x4 out[4];
-          dkdv_p_ds(s0, p0, lse2, msk[qb], qb, qtile0, key_lane, T, W, c, hh, pk0, pl0, dk0, dl0, out);
-          ds_store(ds_row, out, qb, hh);
+          dkdv_p_ds(s0, p0, lse2, msk[qb], qb, qtile0, key_lane, T, W, c, hh, pk0, pl0, dk0, dl0);
           dkdv_acc(dkacc, dvacc, pk0, pl0, dk0, dl0, qs, dos, L, qb);
         }
       }
@@ -400,91 +353,84 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__rest
     }
 }
 
-// ---------------------------------------------------------------- dQ
-// dQ = scale (dS_hi + dS_lo) K from the dS tiles the dK/dV stage stored: two
-// GEMMs per tile.  The stage streams the band from HBM, so it wants many bytes in
-// flight.  Two shapes: NW = 8 waves on 256 query rows (four query tiles) with one
-// key tile ahead (two LDS stages of one K tile and four hi + lo dS^T tiles, 80 KB
-// each), and NW = 4 waves on 128 rows with two key tiles ahead (three stages of
-// 48 KB) for grids too small to give every CU two of the larger workgroups; one
-// workgroup per CU either way.  A dS^T tile ([key][query],
-// 64 x 64 bf16, 128-byte rows) is staged with its 16-byte chunks permuted per
-// row, chunk' = chunk ^ (4 ((row >> 1) & 1)), which keeps the transposing reads
-// below free of bank conflicts.
-template <int NW>
-struct DqShape {
-  static constexpr int kRows = 32 * NW;                            // query rows per workgroup
-  static constexpr int kStages = NW == 8 ? 2 : 3;                  // LDS stages (key tiles in the ring)
-  static constexpr int kStage = kTileBytes + (NW / 2) * 16384;    // K tile + one hi + lo dS^T tile per 2 waves
-  static constexpr int kCopies = 16 / NW + 8;                      // copy instructions per wave per stage
-};
-__device__ __forceinline__ int ds_swz(int row, int chunk) { return row * 128 + ((chunk ^ (((row >> 1) & 1) << 2)) << 4); }
-
-// Wait until at most n of this wave's vector memory operations (and none of its
-// LDS operations) are in flight, then a barrier that drains nothing else (a plain
-// __syncthreads also waits for every outstanding load, which would empty a
-// prefetch ring deeper than one stage).
-template <int N>
-__device__ __forceinline__ void vm_wait_barrier() {
-  static_assert(N >= 0 && N < 16, "vmcnt field");
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0x0070 | N);  // vmcnt(N) lgkmcnt(0), expcnt at its maximum
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("" ::: "memory");
+// S^T = K Q^T (or dP^T = V dO^T) of one 64-key tile against the wave's 32
+// queries: keys as MFMA rows (two 32-key blocks), queries as columns; element e of
+// acc[kb] is key 32 kb + 8 (e >> 2) + 4 hh + (e & 3) of the lane's query.  The
+// row operands are read four MFMAs ahead of their use.
+__device__ __forceinline__ void dq_st_tile(f32x16 (&acc)[2], const char *tile, const TileLane &L,
+                                           const bf16x8 (&breg)[8]) {
+  constexpr int kAhead = 4;
+  bf16x8 op[16];
+#pragma unroll
+  for (int i = 0; i < kAhead; ++i) op[i] = row_operand(tile, L, i >> 1, i & 1);
+  acc[0] = f32x16{};
+  acc[1] = f32x16{};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {  // i = 2 s + kb
+    if (i + kAhead < 16) op[i + kAhead] = row_operand(tile, L, (i + kAhead) >> 1, (i + kAhead) & 1);
+    acc[i & 1] = mfma32(op[i], breg[i >> 1], acc[i & 1]);
+  }
 }
 
-template <int NW>
-__global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(const uint16_t *__restrict__ K,
-                                                                 const uint16_t *__restrict__ dsband,
-                                                                 uint16_t *__restrict__ dQ, int B, int T, int H,
-                                                                 int KV, int W, float scale, int nqt, int band_c,
-                                                                 long long band_tiles) {
-  using S = DqShape<NW>;
-  __shared__ __attribute__((aligned(1024))) char st0[S::kStage];
-  __shared__ __attribute__((aligned(1024))) char st1[S::kStage];
-  __shared__ __attribute__((aligned(1024))) char st2[S::kStages == 3 ? S::kStage : 16];
+// -inf on the elements of a straddling tile that are not visible: with
+// d0 = k0 + 4 hh - q_lane, element (kb, e) has key - query = d0 + off(kb, e).
+__device__ __forceinline__ void dq_mask_tile(f32x16 (&sacc)[2], int k0, int q_lane, int W, int hh) {
+  const int d0 = k0 + 4 * hh - q_lane;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int off = 32 * kb + 8 * (e >> 2) + (e & 3);
+      const bool vis = d0 <= -off && (W < 0 || d0 + W >= -off);
+      sacc[kb][e] = vis ? sacc[kb][e] : -INFINITY;
+    }
+}
+
+// ---------------------------------------------------------------- dQ
+// dQ_i = scale sum_j dS_ij k_j, with dS recomputed per tile: one workgroup per
+// (b, h, 128-row query block), laid out like the forward (wave w owns query rows
+// 32 w .. 32 w + 31; Q^T and dO^T of its rows in registers, one query per lane
+// pair).  Per 64-key tile, with K and V copied global -> LDS one tile ahead:
+//   S^T = K Q^T and dP^T = V dO^T (keys as MFMA rows, the wave's queries as
+//   columns), P = exp2(S c - LSE log2 e) (masked on straddling tiles),
+//   dS = P (dP - D), and dQ^T += K^T (dS_hi + dS_lo) straight from the
+// accumulators (K^T through transposing LDS reads).  Nothing is stored between
+// the stages, so the backward needs no O(T^2) workspace, and dS enters the dQ
+// product in fp32 precision (hi + lo).
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t *__restrict__ Q,
+                                                        const uint16_t *__restrict__ K,
+                                                        const uint16_t *__restrict__ V,
+                                                        const uint16_t *__restrict__ dO,
+                                                        const float *__restrict__ lse2g,
+                                                        const float *__restrict__ ndelta, uint16_t *__restrict__ dQ,
+                                                        int B, int T, int H, int KV, int W, float scale) {
+  __shared__ __attribute__((aligned(1024))) char kb0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char kb1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char vb0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char vb1[kTileBytes];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int nqb = (T + S::kRows - 1) / S::kRows;
+  const int nqb = (T + kDqRows - 1) / kDqRows;
   const int BH = B * H;
-  const int qblk = nqb - 1 - (int)(blockIdx.x / BH);  // heaviest (latest) row blocks first
+  const int qblk = nqb - 1 - (int)(blockIdx.x / BH);  // heaviest (latest) query blocks first
   const int bh = (int)(blockIdx.x % BH);
   const int b = bh / H;
   const int h = bh % H;
   const int kvh = h / (H / KV);
-  const int q0 = qblk * S::kRows;
+  const int q0 = qblk * kDqRows;
   const int qw0 = q0 + 32 * wave;
-  const int q_lane = qw0 + (lane & 31);
   const int hh = lane >> 5;
-
+  const int q_lane = qw0 + (lane & 31);
+  const int qr = min(q_lane, T - 1);
+  const float c = scale * kLog2e;
+  const long long q_stride = (long long)H * kD;
   const long long kv_stride = (long long)KV * kD;
-  const uint16_t *Kb = K + (long long)b * T * kv_stride + (long long)kvh * kD;
-  const TileSrc ksrc = make_tile_src(Kb, kv_stride, T);
+  const TileSrc ksrc = make_tile_src(K + (long long)b * T * kv_stride + (long long)kvh * kD, kv_stride, T);
+  const TileSrc vsrc = make_tile_src(V + (long long)b * T * kv_stride + (long long)kvh * kD, kv_stride, T);
   const int voff = tile_lane_voff(ksrc.stride, tid);
-  // this wave's share of the dS^T copies: query tile qt_w = (NW / 2) qblk +
-  // (wave >> 1), rows 32 (wave & 1) + 8 i + l/8 of its tile against each key
-  // tile.  The band row of qt_w (key tiles kt_lo .. qt_w) is a buffer resource of
-  // its own; a zero-size resource for tiles that do not exist keeps the number
-  // of copy instructions per stage fixed (those copies write zeros that no wave
-  // reads).
-  const int ds_sub = wave >> 1;
-  const int qt_w = (NW / 2) * qblk + ds_sub;
-  const int kt_lo_w = ds_kt_lo(qt_w, band_c);
-  const uint16_t *ds_rowp =
-      dsband + ((long long)bh * band_tiles + (qt_w < nqt ? ds_row_start(qt_w, band_c) : 0)) * kDsEntry;
-  const __amdgpu_buffer_rsrc_t band_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)ds_rowp, (short)0, qt_w < nqt ? (qt_w - kt_lo_w + 1) * 2 * 8192 : 0, 0x00020000);
-  const __amdgpu_buffer_rsrc_t none_rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)ds_rowp, (short)0, 0, 0x00020000);
-  int ds_voff[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = 32 * (wave & 1) + 8 * i + (lane >> 3);
-    ds_voff[i] = row * 128 + (((lane & 7) ^ (((row >> 1) & 1) << 2)) << 4);
-  }
 
-  const int q_last_blk = min(q0 + S::kRows - 1, T - 1);
+  const int q_last_blk = min(q0 + kDqRows - 1, T - 1);
   const int t0 = (W < 0 ? 0 : max(0, q0 - W)) / kTileN;
   const int t1 = q_last_blk / kTileN;
   const int qw_last = min(qw0 + 31, T - 1);
@@ -492,124 +438,72 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(const uint16_t *__re
   const int tw0 = max(t0, (W < 0 ? 0 : max(0, qw0 - W)) / kTileN);
   const int tw1 = wave_active ? qw_last / kTileN : t0 - 1;
 
-  // copies for key tile t (every wave issues exactly S::kCopies): K, and the
-  // dS^T tile of each of the block's query tiles that sees tile t
-  auto load = [&](char *stage, int t) {
-    tile_load_lds<NW>(stage, ksrc, voff, t * kTileN);
-    const bool have = qt_w < nqt && t >= kt_lo_w && t <= qt_w;
-    const __amdgpu_buffer_rsrc_t r = have ? band_rsrc : none_rsrc;
-    const int soff = have ? (t - kt_lo_w) * 2 * 8192 : 0;
-    char *dst = stage + kTileBytes + ds_sub * 16384 + (wave & 1) * 4096;
-#pragma unroll
-    for (int part = 0; part < 2; ++part)  // hi, then lo 8 KB further on (in the band and in LDS)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dst + 8192 * part + 1024 * i), 16, ds_voff[i],
-                                                 soff + 8192 * part, 0, 0);
-  };
+  tile_load_lds(kb0, ksrc, voff, t0 * kTileN);
+  tile_load_lds(vb0, vsrc, voff, t0 * kTileN);
 
-  const TileLane L = make_tile_lane(lane);
-  // per-lane offsets of the dS^T operand (query column 32 (wave & 1) + l%32, keys
-  // {16 c + x + k, 16 c + x + 8 + k}, x = 4 (l/32) + ((l%16) >> 2)); + 2048 B per c
-  int soff[2];
+  // Q^T and dO^T operands of this lane's query (d = 16 s + 8 hh + [0, 8)), its
+  // LSE log2 e and -D
+  bf16x8 qreg[8], dreg[8];
   {
-    const int g = lane >> 4, r = lane & 15;
-    const int x = 4 * (g >> 1) + (r >> 2);
-    const int qc = 32 * (wave & 1) + ((g & 1) << 4) + 4 * (r & 3);
+    const long long off = ((long long)b * T + qr) * q_stride + (long long)h * kD + 8 * hh;
 #pragma unroll
-    for (int half = 0; half < 2; ++half) soff[half] = ds_swz(x + 8 * half, qc >> 3) + (qc & 7) * 2;
+    for (int s = 0; s < 8; ++s) {
+      qreg[s] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(Q + off + 16 * s));
+      dreg[s] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(dO + off + 16 * s));
+    }
   }
-  const int ssub = kTileBytes + ds_sub * 16384;
+  const long long ri = ((long long)b * H + h) * T + qr;
+  const float lse2_q = lse2g[ri];
+  const float nd_q = ndelta[ri];
+  const TileLane L = make_tile_lane(lane);
 
   f32x16 dqacc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) dqacc[i] = f32x16{};
 
-  load(st0, t0);
-  if (S::kStages == 3 && t0 + 1 <= t1) load(st1, t0 + 1);
+  lds_loads_done_barrier();
 
-  // Step t reads the stage holding tile t and refills the one tile t + kStages - 1
-  // goes to (it held tile t - 1, which every wave finished before the barrier).
-  auto step = [&](const char *cur, char *fill, int t) {
-    if (S::kStages == 3) {
-      // the copies of tile t are done once at most those of tile t + 1 remain
-      if (t + 1 <= t1)
-        vm_wait_barrier<S::kCopies>();
-      else
-        vm_wait_barrier<0>();
-      if (t + 2 <= t1) load(fill, t + 2);
-    } else {
-      vm_wait_barrier<0>();
-      if (t + 1 <= t1) load(fill, t + 1);
+  auto step = [&](const char *ks, const char *vs, char *kfill, char *vfill, int t) {
+    if (t + 1 <= t1) {
+      tile_load_lds(kfill, ksrc, voff, (t + 1) * kTileN);
+      tile_load_lds(vfill, vsrc, voff, (t + 1) * kTileN);
     }
     if (t >= tw0 && t <= tw1) {
       const int k0 = t * kTileN;
-      const bool need_mask = !(k0 + kTileN - 1 <= qw0 && (W < 0 || qw_last - k0 <= W));
-      const char *st = cur + ssub;
-      // every operand of the tile is read from LDS before the first MFMA; dsw[2 cs]
-      // is the hi part, dsw[2 cs + 1] the lo part
-      u32x4 dsw[8];
-      bf16x8 kop[4][4];
+      f32x16 sacc[2], dpacc[2];
+      dq_st_tile(sacc, ks, L, qreg);
+      dq_st_tile(dpacc, vs, L, dreg);
+      if (!(k0 + kTileN - 1 <= qw0 && (W < 0 || qw_last - k0 <= W))) dq_mask_tile(sacc, k0, q_lane, W, hh);
+      // dS^T in place of S^T: P = exp2(S c - LSE log2 e), dS = P (dP - D)
 #pragma unroll
-      for (int cs = 0; cs < 4; ++cs) {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int part = 0; part < 2; ++part) {
-          const u32x2 a = __builtin_bit_cast(u32x2, lds_read_tr16(st + 8192 * part + soff[0] + cs * 16 * 128));
-          const u32x2 c = __builtin_bit_cast(u32x2, lds_read_tr16(st + 8192 * part + soff[1] + cs * 16 * 128));
-          dsw[2 * cs + part] = u32x4{a[0], a[1], c[0], c[1]};
+        for (int e = 0; e < 16; ++e) {
+          const float p = fast_exp2(__builtin_fmaf(sacc[kb][e], c, -lse2_q));
+          sacc[kb][e] = p * (dpacc[kb][e] + nd_q);
         }
 #pragma unroll
-        for (int db = 0; db < 4; ++db) kop[cs][db] = col_operand(cur, L, db, cs);
-      }
-      if (need_mask) {
-        // operand element e holds key k0 + 16 cs + 4 hh + (e & 3) + 8 (e >> 2)
-#pragma unroll
-        for (int cs = 0; cs < 4; ++cs)
-#pragma unroll
-          for (int e2 = 0; e2 < 4; ++e2) {
-            uint32_t keep = 0u;
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-              const int e = 2 * e2 + half;
-              const int key = k0 + 16 * cs + 4 * hh + (e & 3) + 8 * (e >> 2);
-              const bool vis = key <= q_lane && (W < 0 || q_lane - key <= W);
-              keep |= vis ? (0xffffu << (16 * half)) : 0u;
-            }
-            dsw[2 * cs][e2] &= keep;
-            dsw[2 * cs + 1][e2] &= keep;
-          }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
       for (int cs = 0; cs < 4; ++cs) {
-        const bf16x8 dsh = __builtin_bit_cast(bf16x8, dsw[2 * cs]);
-        const bf16x8 dsl = __builtin_bit_cast(bf16x8, dsw[2 * cs + 1]);
+        bf16x8 dh, dl;
+        acc_to_operand_split(sacc[cs >> 1], cs & 1, dh, dl);
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
-          dqacc[db] = mfma32(kop[cs][db], dsh, dqacc[db]);
-          dqacc[db] = mfma32(kop[cs][db], dsl, dqacc[db]);
+          const bf16x8 a = col_operand(ks, L, db, cs);
+          dqacc[db] = mfma32(a, dh, dqacc[db]);
+          dqacc[db] = mfma32(a, dl, dqacc[db]);
         }
       }
     }
+    lds_loads_done_barrier();
   };
-  if (S::kStages == 3) {
-    for (int t = t0; t <= t1; t += 3) {
-      step(st0, st2, t);
-      if (t + 1 > t1) break;
-      step(st1, st0, t + 1);
-      if (t + 2 > t1) break;
-      step(st2, st1, t + 2);
-    }
-  } else {
-    for (int t = t0; t <= t1; t += 2) {
-      step(st0, st1, t);
-      if (t + 1 > t1) break;
-      step(st1, st0, t + 1);
-    }
+  for (int t = t0; t <= t1; t += 2) {
+    step(kb0, vb0, kb1, vb1, t);
+    if (t + 1 > t1) break;
+    step(kb1, vb1, kb0, vb0, t + 1);
   }
 
   if (!wave_active || q_lane >= T) return;
-  uint16_t *dqp = dQ + ((long long)b * T + q_lane) * ((long long)H * kD) + (long long)h * kD;
+  uint16_t *dqp = dQ + ((long long)b * T + q_lane) * q_stride + (long long)h * kD;
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -625,10 +519,9 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq_kernel(const uint16_t *__re
 }  // namespace
 
 size_t bwd_workspace_bytes(int B, int T, int H, int W, bool bf16) {
+  (void)W;
   const size_t rows = ((size_t)B * H * T * sizeof(float) + 255) & ~(size_t)255;
-  if (!bf16) return rows;
-  const DsBand band = ds_band(T, W);
-  return 2 * rows + (size_t)B * H * band.tiles * kDsEntry * 2;
+  return bf16 ? 2 * rows : rows;
 }
 
 hipError_t launch_bwd_bf16(const void *q, const void *k, const void *v, const void *o, const float *lse,
@@ -637,16 +530,10 @@ hipError_t launch_bwd_bf16(const void *q, const void *k, const void *v, const vo
   const size_t row_bytes = ((size_t)sh.B * sh.H * sh.T * sizeof(float) + 255) & ~(size_t)255;
   float *delta = (float *)workspace;
   float *lse2 = (float *)((char *)workspace + row_bytes);
-  uint16_t *dsband = (uint16_t *)((char *)workspace + 2 * row_bytes);
-  const DsBand band = ds_band(sh.T, sh.window);
   const long long rows = (long long)sh.B * sh.T * sh.H;
   const long long dblocks = (rows + 63) / 64;
   const long long nkb = (sh.T + kBlockN - 1) / kBlockN;
-  // the 256-row dQ shape when the grid still gives every CU two of them
-  const long long nqb8 = (sh.T + DqShape<8>::kRows - 1) / DqShape<8>::kRows;
-  const bool dq8 = nqb8 * sh.B * sh.H >= 512;
-  const long long nqb = (sh.T + (dq8 ? DqShape<8>::kRows : DqShape<4>::kRows) - 1) /
-                        (dq8 ? DqShape<8>::kRows : DqShape<4>::kRows);
+  const long long nqb = (sh.T + kDqRows - 1) / kDqRows;
   const long long kvblocks = nkb * sh.B * sh.KV;
   const long long qblocks = nqb * sh.B * sh.H;
   if (dblocks > 0x7fffffffLL || kvblocks > 0x7fffffffLL || qblocks > 0x7fffffffLL) return hipErrorInvalidValue;
@@ -656,13 +543,11 @@ hipError_t launch_bwd_bf16(const void *q, const void *k, const void *v, const vo
   if (stages & kBwdDkDv)
     hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)kvblocks), dim3(256), 0, s, (const uint16_t *)q,
                        (const uint16_t *)k, (const uint16_t *)v, (const uint16_t *)dout, lse2, delta, (uint16_t *)dk,
-                       (uint16_t *)dv, dsband, sh.B, sh.T, sh.H, sh.KV, sh.window, sh.scale, band.c, band.tiles);
-  if ((stages & kBwdDq) && dq8)
-    hipLaunchKernelGGL(bwd_dq_kernel<8>, dim3((unsigned)qblocks), dim3(512), 0, s, (const uint16_t *)k, dsband,
-                       (uint16_t *)dq, sh.B, sh.T, sh.H, sh.KV, sh.window, sh.scale, band.nqt, band.c, band.tiles);
-  if ((stages & kBwdDq) && !dq8)
-    hipLaunchKernelGGL(bwd_dq_kernel<4>, dim3((unsigned)qblocks), dim3(256), 0, s, (const uint16_t *)k, dsband,
-                       (uint16_t *)dq, sh.B, sh.T, sh.H, sh.KV, sh.window, sh.scale, band.nqt, band.c, band.tiles);
+                       (uint16_t *)dv, sh.B, sh.T, sh.H, sh.KV, sh.window, sh.scale);
+  if (stages & kBwdDq)
+    hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)qblocks), dim3(256), 0, s, (const uint16_t *)q,
+                       (const uint16_t *)k, (const uint16_t *)v, (const uint16_t *)dout, lse2, delta, (uint16_t *)dq,
+                       sh.B, sh.T, sh.H, sh.KV, sh.window, sh.scale);
   return hipGetLastError();
 }
 

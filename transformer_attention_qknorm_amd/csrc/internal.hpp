@@ -28,33 +28,7 @@ hipError_t launch_qknorm_rope_bwd(void *dq, void *dk, const void *q, const void 
 // Backward stages (bit mask): D_i = dO.O, then dK/dV, then dQ.
 constexpr int kBwdDelta = 1, kBwdDkDv = 2, kBwdDq = 4, kBwdAll = 7;
 
-// The bf16 backward hands dS = P (dP - D) from the dK/dV stage to the dQ stage
-// through the workspace, as bf16 64 x 64 tiles stored transposed ([key][query],
-// row-major), one per (b, head, query tile qt, key tile kt) that holds a visible
-// pair and no other: query tile qt sees key tiles kt_lo(qt) .. qt, with
-// kt_lo(qt) = max(0, qt - c), c = ceil(W / 64) (c = nt, i.e. all of 0 .. qt,
-// for full causal W < 0).  Rows of tiles are packed one after the other: row qt
-// starts at sum_{q < qt} (min(q, c) + 1).
-struct DsBand {
-  int nqt;          // query tiles of 64 rows
-  int c;            // key tiles a query tile reaches below its own
-  long long tiles;  // tiles per (b, head)
-};
-__host__ __device__ inline long long ds_row_start(int qt, int c) {
-  if (qt <= c + 1) return (long long)qt * (qt + 1) / 2;
-  return (long long)(c + 1) * (c + 2) / 2 + (long long)(qt - c - 1) * (c + 1);
-}
-inline DsBand ds_band(int T, int W) {
-  const int nt = (T + 63) / 64;
-  const int c = W < 0 ? nt : W / 64 + (W % 64 != 0);  // ceil(W / 64) without overflow
-  return DsBand{nt, c, ds_row_start(nt, c)};
-}
-__host__ __device__ inline int ds_kt_lo(int qt, int c) { return qt > c ? qt - c : 0; }
-__host__ __device__ inline long long ds_tile(int qt, int kt, int c) {
-  return ds_row_start(qt, c) + (kt - ds_kt_lo(qt, c));
-}
-// workspace: D [B][H][T] fp32 (padded to 256 B); bf16 adds LSE * log2(e) (same size) and
-// the dS band
+// workspace: D [B][H][T] fp32 (padded to 256 B); bf16 adds LSE * log2(e) (same size)
 size_t bwd_workspace_bytes(int B, int T, int H, int W, bool bf16);
 
 // bf16, head_dim 128, MFMA kernels.
