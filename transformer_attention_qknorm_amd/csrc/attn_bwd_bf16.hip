@@ -207,8 +207,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__rest
   const int wave = tid >> 6;
   const int hh = lane >> 5;
   const int G = H / KV;
+  // key blocks near the start of the sequence see the most queries: launched
+  // first; within one block row the (b, kv head) pairs (B KV apart, so with B KV
+  // a multiple of 8 every block of one pair runs on the same XCD)
   const int BKV = B * KV;
-  // key blocks near the start of the sequence see the most queries: schedule them first
   const int kblk = (int)(blockIdx.x / BKV);
   const int bk = (int)(blockIdx.x % BKV);
   const int b = bk / KV;
@@ -411,13 +413,18 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t *__restri
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  // launch order as the forward's: heaviest query blocks first, the G heads of a
+  // (b, kv head) B KV blocks apart (same XCD when B KV is a multiple of 8)
   const int nqb = (T + kDqRows - 1) / kDqRows;
+  const int G = H / KV;
   const int BH = B * H;
-  const int qblk = nqb - 1 - (int)(blockIdx.x / BH);  // heaviest (latest) query blocks first
-  const int bh = (int)(blockIdx.x % BH);
-  const int b = bh / H;
-  const int h = bh % H;
-  const int kvh = h / (H / KV);
+  const int BKV = B * KV;
+  const int qblk = nqb - 1 - (int)(blockIdx.x / BH);
+  const int j = (int)(blockIdx.x % BH);
+  const int bkv = j % BKV;
+  const int b = bkv / KV;
+  const int kvh = bkv % KV;
+  const int h = kvh * G + j / BKV;
   const int q0 = qblk * kDqRows;
   const int qw0 = q0 + 32 * wave;
   const int hh = lane >> 5;

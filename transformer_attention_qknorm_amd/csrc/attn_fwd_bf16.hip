@@ -179,13 +179,21 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const uint16_t *_
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  // Launch order: query blocks heaviest (latest) first; within one block row the
+  // query head's group index g major and (b, kv head) minor, so that the G heads
+  // reading one (b, kv head)'s K/V get block indexes B KV apart: workgroups are
+  // dealt to the 8 XCDs (each with its own L2) round-robin, so with B KV a
+  // multiple of 8 they share an XCD and its L2.
   const int nqb = (Tq + kBlockM - 1) / kBlockM;
+  const int G = H / KV;
   const int BH = B * H;
+  const int BKV = B * KV;
   const int qblk = nqb - 1 - (int)(blockIdx.x / BH);
-  const int bh = (int)(blockIdx.x % BH);
-  const int b = bh / H;
-  const int h = bh % H;
-  const int kvh = h / (H / KV);
+  const int j = (int)(blockIdx.x % BH);
+  const int bkv = j % BKV;
+  const int b = bkv / KV;
+  const int kvh = bkv % KV;
+  const int h = kvh * G + j / BKV;
   const int q0 = qblk * kBlockM;  // query rows of the block (index into Q / O)
   const int qw0 = q0 + 32 * wave;
   const int hh = lane >> 5;
