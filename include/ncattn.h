@@ -40,8 +40,10 @@
  *     ncattn_decode_noalloc calls on one device must not overlap.
  *
  * Supported: dtype NCATTN_BF16 (fp32 accumulation, bf16 MFMA contractions) with
- * head_dim 128; dtype NCATTN_F32 (fp32 throughout) with head_dim 64 or 128.
- * Decode is bf16 only.  Anything else returns NCATTN_EUNSUPPORTED.
+ * head_dim 64 or 128 (nanochat's --head-dim 128, "nanochat User Guide", section
+ * 13; GPT-2's n_embd / n_head = 768 / 12 = 64, "nanoGPT Administrator & Developer
+ * Guide", sections 3 and 6); dtype NCATTN_F32 (fp32 throughout) with head_dim 64 or 128.  Decode and
+ * prefill are bf16 only.  Anything else returns NCATTN_EUNSUPPORTED.
  */
 #ifndef NCATTN_H
 #define NCATTN_H
@@ -220,7 +222,7 @@ int ncattn_decode(const void *q, const void *k_new, const void *v_new,
  *   the workspace); the current device must be the one `stream` belongs to.
  *   A shape whose partials need more than NCATTN_DECODE_SCRATCH_BYTES
  *   (ncattn_decode_workspace_bytes() > the limit: about B * n_head *
- *   ceil(min(T_max, window_left + 1) / 128) * 520 bytes) returns
+ *   ceil(min(T_max, window_left + 1) / 128) * (head_dim + 2) * 4 bytes) returns
  *   NCATTN_EWORKSPACE and enqueues nothing.
  *   Every call on one device shares that device's array: two calls that overlap
  *   in time on one device (different streams, or threads) race and give wrong
@@ -246,7 +248,7 @@ int ncattn_decode_noalloc(const void *q, const void *k_new, const void *v_new, v
  *   Precondition 0 <= cache_seqlens[b] <= T_max - Tn (not checkable on the host
  *   without a sync): a sequence that breaks it is skipped, its cache is left
  *   untouched and its rows of o (and lse) are NaN.
- *   Supported: bf16, head_dim 128; no workspace.
+ *   Supported: bf16, head_dim 64 or 128; no workspace.
  */
 int ncattn_prefill(const void *q, const void *k_new, const void *v_new, void *k_cache, void *v_cache,
                    const int32_t *cache_seqlens, void *o, float *lse, int B, int Tn, int T_max,

@@ -84,7 +84,8 @@ def test_fwd_validation(L):
     assert fwd(L, wl=-2) == EINVAL
     assert fwd(L, wr=1) == EINVAL
     assert fwd(L, dt=7) == EINVAL
-    assert fwd(L, D=64) == EUNSUP          # bf16 MFMA path is head_dim 128
+    assert fwd(L, D=96) == EUNSUP          # bf16 MFMA path is head_dim 64 or 128
+    assert fwd(L, D=256) == EUNSUP
     assert fwd(L, D=96, dt=1) == EUNSUP
     assert fwd(L, o=P) == EINVAL            # o aliases q
     assert fwd(L, scale=float("nan")) == EINVAL
@@ -106,7 +107,7 @@ def test_fwd_qknorm_rope_validation(L):
     assert call(pos=P + 2) == EINVAL          # pos_offset misaligned
     assert call(wl=-2) == EINVAL
     assert call(wr=1) == EINVAL
-    assert call(D=64) == EUNSUP               # bf16 MFMA path is head_dim 128
+    assert call(D=96) == EUNSUP               # head_dim 64 or 128
     assert call(D=96, dt=1) == EUNSUP
     assert call(scale=float("inf")) == EINVAL
 
@@ -170,7 +171,9 @@ def test_decode_validation_and_workspace(L):
     bad[4] = bad[3]                                                    # k_cache == v_cache
     assert L.ncattn_decode(*bad, 0, P + 256, ws, None) == EINVAL
     bad = list(base)
-    bad[12] = 64
+    bad[12] = 96
+    assert L.ncattn_decode(*bad, 0, P + 256, ws, None) == EUNSUP       # head_dim 64 or 128
+    bad[12] = 32
     assert L.ncattn_decode(*bad, 0, P + 256, ws, None) == EUNSUP
 
 
@@ -209,7 +212,7 @@ def test_prefill_validation(L):
     assert call(kc=P + 64) == EINVAL          # k_cache == v_cache
     assert call(o=P) == EINVAL                # o aliases q
     assert call(dt=1) == EUNSUP
-    assert call(D=64) == EUNSUP
+    assert call(D=96) == EUNSUP
 
 
 def test_window_sizes_binding_golden():

@@ -83,6 +83,8 @@ FUSED_CASES = [
     ("bf16", 1, 1, 2, 1, 128, -1, 100000.0, 1.0, True),
     ("bf16", 3, 130, 6, 6, 128, 64, 10000.0, 1.0, True),
     ("bf16", 1, 777, 6, 2, 128, 256, 100000.0, math.sqrt(1.2), False),
+    ("bf16", 2, 200, 4, 2, 64, -1, 10000.0, 1.0, True),
+    ("bf16", 1, 333, 8, 1, 64, 100, 100000.0, math.sqrt(1.2), False),
     ("f32", 2, 100, 4, 2, 64, 17, 10000.0, math.sqrt(1.2), True),
     ("f32", 1, 150, 3, 3, 128, -1, 100000.0, 1.0, False),
 ]
@@ -138,9 +140,23 @@ FWD_CASES = [
     ("bf16", 1, 777, 6, 2, 128, 256),
     ("bf16", 1, 300, 8, 1, 128, -1),   # eight query heads on one kv head: dK/dV sum over the group
     ("bf16", 2, 333, 8, 1, 128, 100),
-    # enough (sequence, head) row blocks that dQ runs its 256-row, 8-wave shape
+    # many (sequence, head) blocks per CU
     ("bf16", 64, 300, 8, 2, 128, -1),
     ("bf16", 64, 300, 8, 2, 128, 100),
+    # head_dim 64 (GPT-2's 768 / 12): the same edges
+    ("bf16", 2, 200, 4, 2, 64, -1),
+    ("bf16", 2, 200, 4, 2, 64, 0),
+    ("bf16", 2, 200, 4, 2, 64, 1),
+    ("bf16", 2, 200, 4, 2, 64, 63),
+    ("bf16", 2, 200, 4, 2, 64, 65),
+    ("bf16", 2, 200, 4, 2, 64, 128),
+    ("bf16", 2, 200, 4, 2, 64, 199),
+    ("bf16", 2, 200, 4, 2, 64, 5000),
+    ("bf16", 1, 1, 2, 1, 64, -1),
+    ("bf16", 3, 520, 2, 2, 64, -1),
+    ("bf16", 1, 777, 6, 2, 64, 256),
+    ("bf16", 1, 300, 8, 1, 64, -1),
+    ("bf16", 64, 300, 12, 12, 64, 100),
     ("f32", 1, 64, 2, 2, 64, -1),
     ("f32", 2, 100, 4, 2, 64, 17),
     ("f32", 1, 150, 2, 1, 128, -1),
@@ -198,20 +214,20 @@ def test_long_sequence_window_sampled():
         check(dv[:, c:c + R], rdv[:, r], "bf16", "dv")
 
 
-def _random_cases(n, seed=2024):
-    """Seeded random shapes (bf16, head_dim 128): ragged T in [1, 400], group sizes
-    1-4, windows unbounded or drawn up to T + 50 (so some exceed T)."""
+def _random_cases(n, seed=2024, D=128):
+    """Seeded random shapes (bf16): ragged T in [1, 400], group sizes 1-4, windows
+    unbounded or drawn up to T + 50 (so some exceed T)."""
     rng = np.random.default_rng(seed)
     cases = []
     for _ in range(n):
         B, T = int(rng.integers(1, 4)), int(rng.integers(1, 401))
         KV, G = int(rng.integers(1, 4)), int(rng.integers(1, 5))
         W = -1 if rng.random() < 0.4 else int(rng.integers(0, T + 51))
-        cases.append(("bf16", B, T, KV * G, KV, 128, W))
+        cases.append(("bf16", B, T, KV * G, KV, D, W))
     return cases
 
 
-RANDOM_CASES = _random_cases(12)
+RANDOM_CASES = _random_cases(12) + _random_cases(6, seed=2028, D=64)
 
 
 def _random_f32_cases(n, seed=2027):
@@ -236,9 +252,10 @@ def test_fwd_bwd_random_shapes(case):
     test_fwd_bwd(case)
 
 
-def test_fwd_bwd_closed_forms_on_gpu():
+@pytest.mark.parametrize("D", [128, 64])
+def test_fwd_bwd_closed_forms_on_gpu(D):
     """W = 0 gives O = v, dQ = dK = 0, dV = sum of the group's dO (exact up to rounding)."""
-    q, k, v, do = to_dev(*attn_inputs(2, 300, 4, 2, 128, "bf16", seed=9))
+    q, k, v, do = to_dev(*attn_inputs(2, 300, 4, 2, D, "bf16", seed=9))
     o, lse = nc.fwd(q, k, v, window=(0, 0))
     torch.cuda.synchronize()
     assert torch.equal(o, v.repeat_interleave(2, dim=2))
@@ -246,11 +263,12 @@ def test_fwd_bwd_closed_forms_on_gpu():
     torch.cuda.synchronize()
     # dS = P (dP - D) vanishes exactly in exact arithmetic; fp32 rounding of dP and D leaves ~1e-6
     assert float(dq.abs().max()) <= 1e-5 and float(dk.abs().max()) <= 1e-5
-    ref = f64(do).reshape(2, 300, 2, 2, 128).sum(axis=3)
+    ref = f64(do).reshape(2, 300, 2, 2, D).sum(axis=3)
     check(dv, ref, "bf16", "dv(W=0)")
 
 
-def test_fwd_bwd_scores_far_above_first_tile():
+@pytest.mark.parametrize("D", [128, 64])
+def test_fwd_bwd_scores_far_above_first_tile(D):
     """Rows whose first key tile scores about -44 and whose later keys score about
     +44 (natural log units): the probabilities against the first tile's reference
     would overflow fp32, so the forward must take its exact-maximum second pass.
@@ -258,7 +276,7 @@ def test_fwd_bwd_scores_far_above_first_tile():
     100 u, k is +-5 u plus unit noise, for a random unit vector u: a large common
     part in k would make the bf16 rounding of dS dominate dQ, which the exact
     cancellation sum_j dS_ij = 0 leaves small.)"""
-    B, T, H, KV, D = 1, 300, 2, 2, 128
+    B, T, H, KV = 1, 300, 2, 2
     rng = np.random.default_rng(77)
     u = rng.standard_normal(D)
     u /= np.linalg.norm(u)
@@ -288,8 +306,9 @@ def test_fwd_bwd_scores_far_above_first_tile():
             tol_check(f64(got) / m, ref / m, what=name, out_bf16=True, **TOL["bf16"])
 
 
-def test_determinism():
-    q, k, v, do = to_dev(*attn_inputs(2, 700, 6, 2, 128, "bf16", seed=5))
+@pytest.mark.parametrize("D", [128, 64])
+def test_determinism(D):
+    q, k, v, do = to_dev(*attn_inputs(2, 700, 6, 2, D, "bf16", seed=5))
     for W in (-1, 100):
         o1, l1 = nc.fwd(q, k, v, window=(W, 0))
         o2, l2 = nc.fwd(q, k, v, window=(W, 0))
@@ -325,10 +344,11 @@ def test_window_reaching_every_key_is_full_causal():
 
 # ------------------------------------------------------------------ decode
 
+@pytest.mark.parametrize("D", [128, 64])
 @pytest.mark.parametrize("W", [-1, 0, 1, 100, 127, 128, 129, 400])
-def test_decode_small(W):
-    say(f"decode small W={W}")
-    B, H, KV, D, Tm = 6, 4, 2, 128, 300
+def test_decode_small(W, D):
+    say(f"decode small W={W} D={D}")
+    B, H, KV, Tm = 6, 4, 2, 300
     q, kn, vn, kc, vc, lens = decode_inputs(B, H, KV, D, 1, 290, Tm, seed=21, poison=False)
     lens = torch.tensor([0, 1, 127, 128, 129, 299], dtype=torch.int32)
     # poison every slot from each sequence's length on (the oracle never reads them)
@@ -353,12 +373,12 @@ def test_decode_small(W):
         assert torch.equal(x, y)
 
 
-@pytest.mark.parametrize("W", [-1, 4096])
-def test_decode_long_cache(W):
+@pytest.mark.parametrize("W,D", [(-1, 128), (4096, 128), (-1, 64)])
+def test_decode_long_cache(W, D):
     """Caches of 65600 slots with up to 65535 keys in use (512 split chunks for one
     sequence), slots past each length NaN-poisoned."""
-    say(f"decode long cache W={W}")
-    B, H, KV, D, Tm = 2, 4, 2, 128, 65600
+    say(f"decode long cache W={W} D={D}")
+    B, H, KV, Tm = 2, 4, 2, 65600
     q, kn, vn, kc, vc, lens = decode_inputs(B, H, KV, D, 1, 100, Tm, seed=23, poison=False)
     lens = torch.tensor([65535, 40001], dtype=torch.int32)
     for b in range(B):
@@ -377,7 +397,7 @@ def test_decode_long_cache(W):
         assert torch.equal(kc_after[b, :s].view(torch.int16), kc[b, :s].view(torch.int16))
 
 
-def _random_decode_cases(n, seed=2026):
+def _random_decode_cases(n, seed=2026, D=128):
     """Seeded random decode shapes: 1-8 sequences, cached lengths anywhere in
     [0, T_max - 1], group sizes 1-4, random windows."""
     rng = np.random.default_rng(seed)
@@ -386,18 +406,18 @@ def _random_decode_cases(n, seed=2026):
         B, KV, G = int(rng.integers(1, 9)), int(rng.integers(1, 4)), int(rng.integers(1, 5))
         Tm = int(rng.integers(2, 600))
         W = -1 if rng.random() < 0.4 else int(rng.integers(0, Tm + 51))
-        cases.append((B, KV * G, KV, Tm, W))
+        cases.append((B, KV * G, KV, Tm, W, D))
     return cases
 
 
-RANDOM_DECODE_CASES = _random_decode_cases(8)
+RANDOM_DECODE_CASES = _random_decode_cases(8) + _random_decode_cases(4, seed=2029, D=64)
 
 
 @pytest.mark.parametrize("case", RANDOM_DECODE_CASES, ids=[_ids(c) for c in RANDOM_DECODE_CASES])
 def test_decode_random_shapes(case):
-    B, H, KV, Tm, W = case
+    B, H, KV, Tm, W, D = case
     say(f"decode {case}")
-    q, kn, vn, kc, vc, lens = decode_inputs(B, H, KV, 128, 0, Tm - 1, Tm, seed=40 + Tm, poison=True)
+    q, kn, vn, kc, vc, lens = decode_inputs(B, H, KV, D, 0, Tm - 1, Tm, seed=40 + Tm, poison=True)
     ro, rlse, _, _ = oracle.decode(f64(q), f64(kn), f64(vn), f64(kc), f64(vc), lens.numpy(), W)
     qd, knd, vnd, kcd, vcd, ld = to_dev(q, kn, vn, kc, vc, lens)
     o, lse = nc.decode(qd, knd, vnd, kcd, vcd, ld, window=W, return_lse=True)
@@ -414,10 +434,11 @@ def test_decode_random_shapes(case):
         assert torch.equal(a[mask].view(torch.int16), b_[mask].view(torch.int16))
 
 
-def test_decode_matches_fwd_row():
+@pytest.mark.parametrize("D", [128, 64])
+def test_decode_matches_fwd_row(D):
     """Decode at position s equals row s of the forward over the prefix (the
     incremental computation equals the full one)."""
-    B, T, H, KV, D = 3, 333, 6, 2, 128
+    B, T, H, KV = 3, 333, 6, 2
     q, k, v, _ = attn_inputs(B, T, H, KV, D, "bf16", seed=8)
     qd, kd, vd = to_dev(q, k, v)
     for W in (-1, 64):
@@ -463,7 +484,7 @@ def test_decode_deterministic():
 # ------------------------------------------------------------------ chunked prefill
 
 PREFILL_CASES = [
-    # B, Tn, H, KV, min_len, max_len, T_max, W
+    # B, Tn, H, KV, min_len, max_len, T_max, W[, D = 128]
     (3, 1, 4, 2, 0, 100, 160, -1),
     (3, 7, 4, 2, 0, 100, 160, -1),
     (2, 64, 2, 2, 0, 200, 300, 50),
@@ -471,14 +492,17 @@ PREFILL_CASES = [
     (2, 200, 2, 1, 0, 0, 256, 0),
     (2, 65, 4, 4, 500, 700, 800, 128),
     (1, 257, 2, 2, 1, 1, 258, 1000),
+    (3, 7, 4, 2, 0, 100, 160, -1, 64),
+    (2, 130, 6, 2, 60, 300, 512, 77, 64),
 ]
 
 
 @pytest.mark.parametrize("case", PREFILL_CASES, ids=[_ids(c) for c in PREFILL_CASES])
 def test_prefill(case):
-    B, Tn, H, KV, lo, hi, T_max, W = case
+    B, Tn, H, KV, lo, hi, T_max, W = case[:8]
+    D = case[8] if len(case) > 8 else 128
     say(f"prefill {case}")
-    q, kn, vn, kc, vc, lens = prefill_inputs(B, Tn, H, KV, 128, lo, hi, T_max, seed=31 + Tn)
+    q, kn, vn, kc, vc, lens = prefill_inputs(B, Tn, H, KV, D, lo, hi, T_max, seed=31 + Tn)
     ro, rlse, rkc, rvc = oracle.prefill(f64(q), f64(kn), f64(vn), f64(kc), f64(vc), lens.numpy(), W)
     qd, knd, vnd, kcd, vcd, lensd = to_dev(q, kn, vn, kc, vc, lens)
     o, lse = nc.prefill(qd, knd, vnd, kcd, vcd, lensd, window=W, return_lse=True)
@@ -520,10 +544,11 @@ def test_prefill_random_shapes(case):
     test_prefill(case)
 
 
-def test_prefill_from_empty_cache_is_the_forward():
+@pytest.mark.parametrize("D", [128, 64])
+def test_prefill_from_empty_cache_is_the_forward(D):
     """With empty caches, prefill of a whole sequence runs the forward kernel on the
     same rows: the outputs are bitwise those of ncattn_fwd."""
-    B, T, H, KV, D = 2, 300, 4, 2, 128
+    B, T, H, KV = 2, 300, 4, 2
     q, k, v, _ = to_dev(*attn_inputs(B, T, H, KV, D, "bf16", seed=41))
     for W in (-1, 77):
         o_f, lse_f = nc.fwd(q, k, v, window=(W, 0))

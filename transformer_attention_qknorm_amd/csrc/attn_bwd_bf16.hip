@@ -1,4 +1,4 @@
-// Attention backward, bf16 in/out, fp32 accumulation, head_dim 128, gfx950 MFMA.
+// Attention backward, bf16 in/out, fp32 accumulation, head_dim 64 or 128, gfx950 MFMA.
 //
 // The exact gradient of sum(O * dO) through the forward ("nanochat (Python)"
 // catalog, AI / Model & kernels / Backward pass: autograd of the forward).  With
@@ -38,32 +38,34 @@ constexpr int kValuUnderDkDv = 5;   // under the dV/dK MFMAs of the first block
 // ---------------------------------------------------------------- D_i = dO . O
 // Stores -D_i (the initial value of the dP - D accumulators of the dK/dV stage)
 // and LSE_i * log2(e), the exponent offset of P in base 2.
+template <int D>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t *__restrict__ O,
                                                         const uint16_t *__restrict__ dO,
                                                         const float *__restrict__ LSE, float *__restrict__ ndelta,
                                                         float *__restrict__ lse2, int B, int T, int H) {
-  // 8 lanes per (token, head) row, 32 bytes of O and of dO each; a wave covers 8
-  // rows per pass and issues the loads of two passes before reducing.
+  // 8 lanes per (token, head) row, D / 4 bytes of O and of dO each; a wave covers
+  // 8 rows per pass and issues the loads of two passes before reducing.
+  constexpr int kC = D / 64;  // 16-byte loads per lane and row
   const long long nrows = (long long)B * T * H;
   const int part = threadIdx.x & 7;
   const long long row_base = ((long long)blockIdx.x * 256 + (threadIdx.x & ~7)) / 8 * 2;  // 64 rows per block
   float s[2];
-  u32x4 a[2][2], g[2][2];
+  u32x4 a[2][kC], g[2][kC];
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
     const long long row = row_base + p;
     const long long r = row < nrows ? row : nrows - 1;
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      a[p][c] = *(const u32x4 *)(O + r * kD + part * 16 + 8 * c);
-      g[p][c] = *(const u32x4 *)(dO + r * kD + part * 16 + 8 * c);
+    for (int c = 0; c < kC; ++c) {
+      a[p][c] = *(const u32x4 *)(O + r * D + part * (D / 8) + 8 * c);
+      g[p][c] = *(const u32x4 *)(dO + r * D + part * (D / 8) + 8 * c);
     }
   }
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
     float acc = 0.f;
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+    for (int c = 0; c < kC; ++c)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         acc += lo_bf16(a[p][c][i]) * lo_bf16(g[p][c][i]) + hi_bf16(a[p][c][i]) * hi_bf16(g[p][c][i]);
@@ -86,18 +88,22 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t *__restri
 }
 
 // ---------------------------------------------------------------- dK, dV
-constexpr int kQBuf = 2 * kTileBytes + 2 * kTileN * 4;  // Q tile, dO tile, lse2[64], delta[64]
+template <int D>
+constexpr int kQBuf = 2 * Geom<D>::kTileBytes + 2 * kTileN * 4;  // Q tile, dO tile, lse2[64], delta[64]
 
 // S = Q K^T and dP - D = dO V^T - D for one 32-query block (rows 32 qb.. of the
 // staged tile) against this wave's 32 keys (queries as rows, the wave's keys as
 // columns).  The dP accumulator starts at -D of its query rows (staged next to
 // the tile), so it ends holding dP - D.
+template <int D>
 __device__ __forceinline__ void dkdv_sdp(f32x16 &sacc, f32x16 &dpacc, const char *qs, const char *dos,
-                                         const float *ndl, const TileLane &L, const bf16x8 (&kreg)[8],
-                                         const bf16x8 (&vreg)[8], int qb, int hh) {
-  bf16x8 qa[8], da[8];
+                                         const float *ndl, const TileLane<D> &L,
+                                         const bf16x8 (&kreg)[Geom<D>::kSteps],
+                                         const bf16x8 (&vreg)[Geom<D>::kSteps], int qb, int hh) {
+  constexpr int kSteps = Geom<D>::kSteps;
+  bf16x8 qa[kSteps], da[kSteps];
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
+  for (int s = 0; s < kSteps; ++s) {
     qa[s] = row_operand(qs, L, s, qb);
     da[s] = row_operand(dos, L, s, qb);
   }
@@ -109,7 +115,7 @@ __device__ __forceinline__ void dkdv_sdp(f32x16 &sacc, f32x16 &dpacc, const char
     for (int j = 0; j < 4; ++j) dpacc[4 * i + j] = d4[j];
   }
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
+  for (int s = 0; s < kSteps; ++s) {
     sacc = mfma32(qa[s], kreg[s], sacc);
     dpacc = mfma32(da[s], vreg[s], dpacc);
   }
@@ -157,9 +163,11 @@ __device__ __forceinline__ void dkdv_p_ds(const f32x16 &sacc, const f32x16 &dmd,
 
 // dV^T += dO^T (P_hi + P_lo) and dK^T += Q^T (dS_hi + dS_lo), contraction over the
 // 32 query rows of block qb.
-__device__ __forceinline__ void dkdv_acc(f32x16 (&dkacc)[4], f32x16 (&dvacc)[4], const uint32_t (&pk)[8],
-                                         const uint32_t (&pl)[8], const uint32_t (&dk)[8], const uint32_t (&dl)[8],
-                                         const char *qs, const char *dos, const TileLane &L, int qb) {
+template <int D>
+__device__ __forceinline__ void dkdv_acc(f32x16 (&dkacc)[Geom<D>::kDBlocks], f32x16 (&dvacc)[Geom<D>::kDBlocks],
+                                         const uint32_t (&pk)[8], const uint32_t (&pl)[8], const uint32_t (&dk)[8],
+                                         const uint32_t (&dl)[8], const char *qs, const char *dos,
+                                         const TileLane<D> &L, int qb) {
 #pragma unroll
   for (int c2 = 0; c2 < 2; ++c2) {
     const int cs = 2 * qb + c2;
@@ -168,7 +176,7 @@ __device__ __forceinline__ void dkdv_acc(f32x16 (&dkacc)[4], f32x16 (&dvacc)[4],
     const bf16x8 dsb = __builtin_bit_cast(bf16x8, u32x4{dk[4 * c2], dk[4 * c2 + 1], dk[4 * c2 + 2], dk[4 * c2 + 3]});
     const bf16x8 dsl = __builtin_bit_cast(bf16x8, u32x4{dl[4 * c2], dl[4 * c2 + 1], dl[4 * c2 + 2], dl[4 * c2 + 3]});
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
+    for (int db = 0; db < Geom<D>::kDBlocks; ++db) {
       const bf16x8 a = col_operand(dos, L, db, cs);
       const bf16x8 qa = col_operand(qs, L, db, cs);
       dvacc[db] = mfma32(a, pb, dvacc[db]);
@@ -190,6 +198,7 @@ __device__ __forceinline__ void interleave_mfma_valu() {
   }
 }
 
+template <int D>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__restrict__ Q,
                                                           const uint16_t *__restrict__ K,
                                                           const uint16_t *__restrict__ V,
@@ -200,8 +209,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__rest
                                                           int W, float scale) {
   // Two separate LDS objects for the double buffer (Q | dO | lse2 | delta each),
   // so the compiler can tell the copy into one from the reads of the other.
-  __shared__ __attribute__((aligned(1024))) char buf0[kQBuf];
-  __shared__ __attribute__((aligned(1024))) char buf1[kQBuf];
+  using Gm = Geom<D>;
+  constexpr int kSteps = Gm::kSteps;
+  constexpr int kTileBytes = Gm::kTileBytes;
+  __shared__ __attribute__((aligned(1024))) char buf0[kQBuf<D>];
+  __shared__ __attribute__((aligned(1024))) char buf1[kQBuf<D>];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -220,9 +232,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__rest
   const int key_lane = kw0 + (lane & 31);  // the key column this lane holds
   const float c = scale * kLog2e;
 
-  const long long q_stride = (long long)H * kD;
-  const long long kv_stride = (long long)KV * kD;
-  const int voff = tile_lane_voff((int)(q_stride * 2), tid);
+  const long long q_stride = (long long)H * D;
+  const long long kv_stride = (long long)KV * D;
+  const int voff = tile_lane_voff<D>((int)(q_stride * 2), tid);
 
   // Query tiles that can see any key of the block, times the G heads of the group.
   const int k_last_blk = min(k0 + kBlockN - 1, T - 1);
@@ -243,13 +255,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__rest
     }
     return p;
   };
-  const long long qbase = (long long)b * T * q_stride + (long long)kvh * G * kD;  // q/dO of (b, head kvh G)
+  const long long qbase = (long long)b * T * q_stride + (long long)kvh * G * D;  // q/dO of (b, head kvh G)
   const long long rbase = ((long long)b * H + (long long)kvh * G) * T;         // its lse / delta row
 
   auto stage = [&](const Pos &p, char *base) {
-    const long long hoff = qbase + (long long)p.g * kD;
-    tile_load_lds(base, make_tile_src(Q + hoff, q_stride, T), voff, p.qt * kTileN);
-    tile_load_lds(base + kTileBytes, make_tile_src(dO + hoff, q_stride, T), voff, p.qt * kTileN);
+    const long long hoff = qbase + (long long)p.g * D;
+    tile_load_lds<D>(base, make_tile_src(Q + hoff, q_stride, T), voff, p.qt * kTileN);
+    tile_load_lds<D>(base + kTileBytes, make_tile_src(dO + hoff, q_stride, T), voff, p.qt * kTileN);
     if (wave < 2) {  // waves 0, 1: 64 lse rows and 64 delta rows, 4 bytes per lane (zeros past T)
       const float *row = (wave == 0 ? lse2g : delta) + rbase + (long long)p.g * T;
       const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void *)row, (short)0, T * 4, 0x00020000);
@@ -261,23 +273,23 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__rest
   Pos pos{qt0, 0};
   stage(pos, buf0);
 
-  bf16x8 kreg[8], vreg[8];
+  bf16x8 kreg[kSteps], vreg[kSteps];
   {
     const int kr = min(key_lane, T - 1);
-    const long long off = ((long long)b * T + kr) * kv_stride + (long long)kvh * kD + 8 * hh;
+    const long long off = ((long long)b * T + kr) * kv_stride + (long long)kvh * D + 8 * hh;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
+    for (int s = 0; s < kSteps; ++s) {
       kreg[s] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(K + off + 16 * s));
       vreg[s] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(V + off + 16 * s));
     }
   }
-  const TileLane L = make_tile_lane(lane);
+  const TileLane<D> L = make_tile_lane<D>(lane);
   const int kw_last = min(kw0 + 31, T - 1);
   const bool wave_active = kw0 < T;
 
-  f32x16 dkacc[4], dvacc[4];
+  f32x16 dkacc[Gm::kDBlocks], dvacc[Gm::kDBlocks];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < Gm::kDBlocks; ++i) {
     dkacc[i] = f32x16{};
     dvacc[i] = f32x16{};
   }
@@ -312,11 +324,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__rest
         __builtin_amdgcn_sched_barrier(0);
         dkdv_sdp(s1, p1, qs, dos, ndl, L, kreg, vreg, 1, hh);
         dkdv_p_ds(s0, p0, lse2, false, 0, qtile0, key_lane, T, W, c, hh, pk0, pl0, dk0, dl0);
-        interleave_mfma_valu<16, kValuUnderSdP>();
+        interleave_mfma_valu<2 * kSteps, kValuUnderSdP>();
         __builtin_amdgcn_sched_barrier(0);
         dkdv_acc(dkacc, dvacc, pk0, pl0, dk0, dl0, qs, dos, L, 0);
         dkdv_p_ds(s1, p1, lse2, false, 1, qtile0, key_lane, T, W, c, hh, pk1, pl1, dk1, dl1);
-        interleave_mfma_valu<32, kValuUnderDkDv>();
+        interleave_mfma_valu<8 * Gm::kDBlocks, kValuUnderDkDv>();
         __builtin_amdgcn_sched_barrier(0);
         dkdv_acc(dkacc, dvacc, pk1, pl1, dk1, dl1, qs, dos, L, 1);
       } else {
@@ -339,9 +351,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__rest
     step(buf1, buf0, it + 1);
   }
   if (!wave_active || key_lane >= T) return;
-  const long long off = ((long long)b * T + key_lane) * kv_stride + (long long)kvh * kD;
+  const long long off = ((long long)b * T + key_lane) * kv_stride + (long long)kvh * D;
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+  for (int db = 0; db < Gm::kDBlocks; ++db)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int d = 32 * db + 8 * i + 4 * hh;
@@ -359,17 +371,19 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__rest
 // queries: keys as MFMA rows (two 32-key blocks), queries as columns; element e of
 // acc[kb] is key 32 kb + 8 (e >> 2) + 4 hh + (e & 3) of the lane's query.  The
 // row operands are read four MFMAs ahead of their use.
-__device__ __forceinline__ void dq_st_tile(f32x16 (&acc)[2], const char *tile, const TileLane &L,
-                                           const bf16x8 (&breg)[8]) {
+template <int D>
+__device__ __forceinline__ void dq_st_tile(f32x16 (&acc)[2], const char *tile, const TileLane<D> &L,
+                                           const bf16x8 (&breg)[Geom<D>::kSteps]) {
   constexpr int kAhead = 4;
-  bf16x8 op[16];
+  constexpr int kN = 2 * Geom<D>::kSteps;
+  bf16x8 op[kN];
 #pragma unroll
   for (int i = 0; i < kAhead; ++i) op[i] = row_operand(tile, L, i >> 1, i & 1);
   acc[0] = f32x16{};
   acc[1] = f32x16{};
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {  // i = 2 s + kb
-    if (i + kAhead < 16) op[i + kAhead] = row_operand(tile, L, (i + kAhead) >> 1, (i + kAhead) & 1);
+  for (int i = 0; i < kN; ++i) {  // i = 2 s + kb
+    if (i + kAhead < kN) op[i + kAhead] = row_operand(tile, L, (i + kAhead) >> 1, (i + kAhead) & 1);
     acc[i & 1] = mfma32(op[i], breg[i >> 1], acc[i & 1]);
   }
 }
@@ -399,6 +413,7 @@ __device__ __forceinline__ void dq_mask_tile(f32x16 (&sacc)[2], int k0, int q_la
 // accumulators (K^T through transposing LDS reads).  Nothing is stored between
 // the stages, so the backward needs no O(T^2) workspace, and dS enters the dQ
 // product in fp32 precision (hi + lo).
+template <int D>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t *__restrict__ Q,
                                                         const uint16_t *__restrict__ K,
                                                         const uint16_t *__restrict__ V,
@@ -406,10 +421,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t *__restri
                                                         const float *__restrict__ lse2g,
                                                         const float *__restrict__ ndelta, uint16_t *__restrict__ dQ,
                                                         int B, int T, int H, int KV, int W, float scale) {
-  __shared__ __attribute__((aligned(1024))) char kb0[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char kb1[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char vb0[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char vb1[kTileBytes];
+  using Gm = Geom<D>;
+  constexpr int kSteps = Gm::kSteps;
+  __shared__ __attribute__((aligned(1024))) char kb0[Gm::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char kb1[Gm::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char vb0[Gm::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char vb1[Gm::kTileBytes];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -431,11 +448,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t *__restri
   const int q_lane = qw0 + (lane & 31);
   const int qr = min(q_lane, T - 1);
   const float c = scale * kLog2e;
-  const long long q_stride = (long long)H * kD;
-  const long long kv_stride = (long long)KV * kD;
-  const TileSrc ksrc = make_tile_src(K + (long long)b * T * kv_stride + (long long)kvh * kD, kv_stride, T);
-  const TileSrc vsrc = make_tile_src(V + (long long)b * T * kv_stride + (long long)kvh * kD, kv_stride, T);
-  const int voff = tile_lane_voff(ksrc.stride, tid);
+  const long long q_stride = (long long)H * D;
+  const long long kv_stride = (long long)KV * D;
+  const TileSrc ksrc = make_tile_src(K + (long long)b * T * kv_stride + (long long)kvh * D, kv_stride, T);
+  const TileSrc vsrc = make_tile_src(V + (long long)b * T * kv_stride + (long long)kvh * D, kv_stride, T);
+  const int voff = tile_lane_voff<D>(ksrc.stride, tid);
 
   const int q_last_blk = min(q0 + kDqRows - 1, T - 1);
   const int t0 = (W < 0 ? 0 : max(0, q0 - W)) / kTileN;
@@ -445,16 +462,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t *__restri
   const int tw0 = max(t0, (W < 0 ? 0 : max(0, qw0 - W)) / kTileN);
   const int tw1 = wave_active ? qw_last / kTileN : t0 - 1;
 
-  tile_load_lds(kb0, ksrc, voff, t0 * kTileN);
-  tile_load_lds(vb0, vsrc, voff, t0 * kTileN);
+  tile_load_lds<D>(kb0, ksrc, voff, t0 * kTileN);
+  tile_load_lds<D>(vb0, vsrc, voff, t0 * kTileN);
 
   // Q^T and dO^T operands of this lane's query (d = 16 s + 8 hh + [0, 8)), its
   // LSE log2 e and -D
-  bf16x8 qreg[8], dreg[8];
+  bf16x8 qreg[kSteps], dreg[kSteps];
   {
-    const long long off = ((long long)b * T + qr) * q_stride + (long long)h * kD + 8 * hh;
+    const long long off = ((long long)b * T + qr) * q_stride + (long long)h * D + 8 * hh;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
+    for (int s = 0; s < kSteps; ++s) {
       qreg[s] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(Q + off + 16 * s));
       dreg[s] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(dO + off + 16 * s));
     }
@@ -462,18 +479,18 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t *__restri
   const long long ri = ((long long)b * H + h) * T + qr;
   const float lse2_q = lse2g[ri];
   const float nd_q = ndelta[ri];
-  const TileLane L = make_tile_lane(lane);
+  const TileLane<D> L = make_tile_lane<D>(lane);
 
-  f32x16 dqacc[4];
+  f32x16 dqacc[Gm::kDBlocks];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) dqacc[i] = f32x16{};
+  for (int i = 0; i < Gm::kDBlocks; ++i) dqacc[i] = f32x16{};
 
   lds_loads_done_barrier();
 
   auto step = [&](const char *ks, const char *vs, char *kfill, char *vfill, int t) {
     if (t + 1 <= t1) {
-      tile_load_lds(kfill, ksrc, voff, (t + 1) * kTileN);
-      tile_load_lds(vfill, vsrc, voff, (t + 1) * kTileN);
+      tile_load_lds<D>(kfill, ksrc, voff, (t + 1) * kTileN);
+      tile_load_lds<D>(vfill, vsrc, voff, (t + 1) * kTileN);
     }
     if (t >= tw0 && t <= tw1) {
       const int k0 = t * kTileN;
@@ -494,7 +511,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t *__restri
         bf16x8 dh, dl;
         acc_to_operand_split(sacc[cs >> 1], cs & 1, dh, dl);
 #pragma unroll
-        for (int db = 0; db < 4; ++db) {
+        for (int db = 0; db < Gm::kDBlocks; ++db) {
           const bf16x8 a = col_operand(ks, L, db, cs);
           dqacc[db] = mfma32(a, dh, dqacc[db]);
           dqacc[db] = mfma32(a, dl, dqacc[db]);
@@ -510,9 +527,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t *__restri
   }
 
   if (!wave_active || q_lane >= T) return;
-  uint16_t *dqp = dQ + ((long long)b * T + q_lane) * q_stride + (long long)h * kD;
+  uint16_t *dqp = dQ + ((long long)b * T + q_lane) * q_stride + (long long)h * D;
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+  for (int db = 0; db < Gm::kDBlocks; ++db)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int d = 32 * db + 8 * i + 4 * hh;
@@ -531,9 +548,10 @@ size_t bwd_workspace_bytes(int B, int T, int H, int W, bool bf16) {
   return bf16 ? 2 * rows : rows;
 }
 
-hipError_t launch_bwd_bf16(const void *q, const void *k, const void *v, const void *o, const float *lse,
-                           const void *dout, void *dq, void *dk, void *dv, void *workspace, const AttnShape &sh,
-                           int stages, hipStream_t s) {
+template <int D>
+hipError_t launch_bwd_kernels(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                              const void *dout, void *dq, void *dk, void *dv, void *workspace, const AttnShape &sh,
+                              int stages, hipStream_t s) {
   const size_t row_bytes = ((size_t)sh.B * sh.H * sh.T * sizeof(float) + 255) & ~(size_t)255;
   float *delta = (float *)workspace;
   float *lse2 = (float *)((char *)workspace + row_bytes);
@@ -545,17 +563,25 @@ hipError_t launch_bwd_bf16(const void *q, const void *k, const void *v, const vo
   const long long qblocks = nqb * sh.B * sh.H;
   if (dblocks > 0x7fffffffLL || kvblocks > 0x7fffffffLL || qblocks > 0x7fffffffLL) return hipErrorInvalidValue;
   if (stages & kBwdDelta)
-    hipLaunchKernelGGL(bwd_delta_kernel, dim3((unsigned)dblocks), dim3(256), 0, s, (const uint16_t *)o,
+    hipLaunchKernelGGL(bwd_delta_kernel<D>, dim3((unsigned)dblocks), dim3(256), 0, s, (const uint16_t *)o,
                        (const uint16_t *)dout, lse, delta, lse2, sh.B, sh.T, sh.H);
   if (stages & kBwdDkDv)
-    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)kvblocks), dim3(256), 0, s, (const uint16_t *)q,
+    hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)kvblocks), dim3(256), 0, s, (const uint16_t *)q,
                        (const uint16_t *)k, (const uint16_t *)v, (const uint16_t *)dout, lse2, delta, (uint16_t *)dk,
                        (uint16_t *)dv, sh.B, sh.T, sh.H, sh.KV, sh.window, sh.scale);
   if (stages & kBwdDq)
-    hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)qblocks), dim3(256), 0, s, (const uint16_t *)q,
+    hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)qblocks), dim3(256), 0, s, (const uint16_t *)q,
                        (const uint16_t *)k, (const uint16_t *)v, (const uint16_t *)dout, lse2, delta, (uint16_t *)dq,
                        sh.B, sh.T, sh.H, sh.KV, sh.window, sh.scale);
   return hipGetLastError();
+}
+
+hipError_t launch_bwd_bf16(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                           const void *dout, void *dq, void *dk, void *dv, void *workspace, const AttnShape &sh,
+                           int stages, hipStream_t s) {
+  if (sh.D == 64) return launch_bwd_kernels<64>(q, k, v, o, lse, dout, dq, dk, dv, workspace, sh, stages, s);
+  if (sh.D == 128) return launch_bwd_kernels<128>(q, k, v, o, lse, dout, dq, dk, dv, workspace, sh, stages, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace ncattn

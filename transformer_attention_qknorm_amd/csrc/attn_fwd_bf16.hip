@@ -1,4 +1,4 @@
-// Attention forward, bf16 in/out, fp32 accumulation, head_dim 128, gfx950 MFMA.
+// Attention forward, bf16 in/out, fp32 accumulation, head_dim 64 or 128, gfx950 MFMA.
 //
 // Computes, per query head h (kv head h / G) and query row i,
 //   O_i = sum_j softmax_j(scale * q_i . k_j) v_j,  LSE_i = log sum_j exp(scale q_i . k_j)
@@ -42,25 +42,28 @@ namespace {
 constexpr int kBlockM = 128;
 constexpr float kSumLimit = 18446744073709551616.0f;  // 2^64
 
+template <int D>
 struct FwdState {
-  f32x16 oacc[4];
+  f32x16 oacc[Geom<D>::kDBlocks];
   float m_ref;  // exponent reference of the raw scores (both half-waves agree; -inf: none yet)
   float l_run;  // this lane's partial row sum (its 32 of every 64 keys)
 };
 
 // The K operands are read from LDS four MFMAs ahead of their use (the reads are
 // fenced in place, so their latency hides under the MFMAs in between).
-__device__ __forceinline__ void s_tile(f32x16 (&sacc)[2], const char *ks, const TileLane &L,
-                                       const bf16x8 (&qreg)[8]) {
+template <int D>
+__device__ __forceinline__ void s_tile(f32x16 (&sacc)[2], const char *ks, const TileLane<D> &L,
+                                       const bf16x8 (&qreg)[Geom<D>::kSteps]) {
   constexpr int kAhead = 4;
-  bf16x8 kop[16];
+  constexpr int kN = 2 * Geom<D>::kSteps;
+  bf16x8 kop[kN];
 #pragma unroll
   for (int i = 0; i < kAhead; ++i) kop[i] = row_operand(ks, L, i >> 1, i & 1);
   sacc[0] = f32x16{};
   sacc[1] = f32x16{};
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {  // i = 2 s + kb
-    if (i + kAhead < 16) kop[i + kAhead] = row_operand(ks, L, (i + kAhead) >> 1, (i + kAhead) & 1);
+  for (int i = 0; i < kN; ++i) {  // i = 2 s + kb
+    if (i + kAhead < kN) kop[i + kAhead] = row_operand(ks, L, (i + kAhead) >> 1, (i + kAhead) & 1);
     sacc[i & 1] = mfma32(kop[i], qreg[i >> 1], sacc[i & 1]);
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -107,7 +110,8 @@ __device__ __forceinline__ float tile_max(const f32x16 (&sacc)[2]) {
 
 // Gives rows without a reference yet (their O and l are still zero) the max of
 // this tile.
-__device__ __forceinline__ void init_ref(FwdState &st, const f32x16 (&sacc)[2]) {
+template <int D>
+__device__ __forceinline__ void init_ref(FwdState<D> &st, const f32x16 (&sacc)[2]) {
   if (__any(st.m_ref == -INFINITY)) {
     const float mt = tile_max(sacc);
     if (st.m_ref == -INFINITY) st.m_ref = mt;
@@ -116,7 +120,8 @@ __device__ __forceinline__ void init_ref(FwdState &st, const f32x16 (&sacc)[2]) 
 
 // Probabilities (in place) and the row-sum update; a row sum above 2^64 (or
 // infinite) raises `overflow`.
-__device__ __forceinline__ void softmax_exp(FwdState &st, f32x16 (&sacc)[2], float c, bool &overflow) {
+template <int D>
+__device__ __forceinline__ void softmax_exp(FwdState<D> &st, f32x16 (&sacc)[2], float c, bool &overflow) {
   const float nmc = (st.m_ref == -INFINITY) ? 0.f : -st.m_ref * c;
   float ls = 0.f;
 #pragma unroll
@@ -135,13 +140,15 @@ __device__ __forceinline__ void softmax_exp(FwdState &st, f32x16 (&sacc)[2], flo
 // a single bf16 P leaves O off by ~2^-9 relative before its own rounding, which
 // moves the stored O by an ulp often enough to matter downstream (the backward's
 // D = dO . O) and to miss 2e-2 where |O| >= 4.
-__device__ __forceinline__ void pv_tile(FwdState &st, const f32x16 (&pacc)[2], const char *vs, const TileLane &L) {
+template <int D>
+__device__ __forceinline__ void pv_tile(FwdState<D> &st, const f32x16 (&pacc)[2], const char *vs,
+                                        const TileLane<D> &L) {
 #pragma unroll
   for (int cs = 0; cs < 4; ++cs) {
     bf16x8 pb, pl;
     acc_to_operand_split(pacc[cs >> 1], cs & 1, pb, pl);
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
+    for (int db = 0; db < Geom<D>::kDBlocks; ++db) {
       const bf16x8 a = col_operand(vs, L, db, cs);
       st.oacc[db] = mfma32(a, pb, st.oacc[db]);
       st.oacc[db] = mfma32(a, pl, st.oacc[db]);
@@ -150,7 +157,7 @@ __device__ __forceinline__ void pv_tile(FwdState &st, const f32x16 (&pacc)[2], c
 }
 
 // QK-norm + RoPE of the query rows, for the fused forward: rotation turns per
-// position of pair j (base^(-2j/D) / 2 pi), epsilon, gain, position offsets.
+// position of pair j < D/2 (base^(-2j/D) / 2 pi), epsilon, gain, position offsets.
 struct QkNormRope {
   double turns[64];
   float eps, gain;
@@ -161,7 +168,7 @@ struct QkNormRope {
 // registers ("nanochat Admin & Developer Guide", section 3: weightless RMSNorm of
 // q, then rotary embedding) and writes them back through Qw (the same array as Q,
 // each row touched by the one lane pair that owns it).
-template <bool FUSE>
+template <int D, bool FUSE>
 __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const uint16_t *__restrict__ Q,
                                                                const uint16_t *__restrict__ K,
                                                                const uint16_t *__restrict__ V,
@@ -171,10 +178,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const uint16_t *_
                                                                uint16_t *Qw, QkNormRope qn) {
   // Two-slot rings for K and V, each slot its own LDS object so the compiler can
   // tell a copy into one slot from reads of the other.
-  __shared__ __attribute__((aligned(1024))) char kb0[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char kb1[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char vb0[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char vb1[kTileBytes];
+  using Gm = Geom<D>;
+  constexpr int kSteps = Gm::kSteps;
+  __shared__ __attribute__((aligned(1024))) char kb0[Gm::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char kb1[Gm::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char vb0[Gm::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char vb1[Gm::kTileBytes];
   __shared__ int overflow_flag;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -198,8 +207,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const uint16_t *_
   const int qw0 = q0 + 32 * wave;
   const int hh = lane >> 5;
   const float c = scale * kLog2e;
-  const long long q_stride = (long long)H * kD;
-  const long long kv_stride = (long long)KV * kD;
+  const long long q_stride = (long long)H * D;
+  const long long kv_stride = (long long)KV * D;
 
   // Query row r sits at position s0 + r of a sequence whose keys are rows
   // [0, s0 + Tq) of K / V (s0 = 0 for a whole sequence; the cache length before a
@@ -209,8 +218,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const uint16_t *_
     // invalid cache length: this block's rows of o and lse are NaN
     const int qr = qw0 + (lane & 31);
     if (qr < Tq) {
-      uint16_t *op = O + ((long long)b * Tq + qr) * q_stride + (long long)h * kD;
-      for (int d = 4 * hh; d < kD; d += 8) *(u32x2 *)(op + d) = u32x2{0x7fc07fc0u, 0x7fc07fc0u};
+      uint16_t *op = O + ((long long)b * Tq + qr) * q_stride + (long long)h * D;
+      for (int d = 4 * hh; d < D; d += 8) *(u32x2 *)(op + d) = u32x2{0x7fc07fc0u, 0x7fc07fc0u};
       if (hh == 0 && LSE) LSE[((long long)b * H + h) * Tq + qr] = __builtin_nanf("");
     }
     return;
@@ -218,11 +227,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const uint16_t *_
   const int nkeys = s0 + Tq;
   const int q_lane = s0 + qw0 + (lane & 31);  // position of this lane's query
   const int pw0 = s0 + qw0;                   // position of the wave's first query
-  const uint16_t *Kb = K + (long long)b * Tk * kv_stride + (long long)kvh * kD;
-  const uint16_t *Vb = V + (long long)b * Tk * kv_stride + (long long)kvh * kD;
+  const uint16_t *Kb = K + (long long)b * Tk * kv_stride + (long long)kvh * D;
+  const uint16_t *Vb = V + (long long)b * Tk * kv_stride + (long long)kvh * D;
   const TileSrc ksrc = make_tile_src(Kb, kv_stride, nkeys);
   const TileSrc vsrc = make_tile_src(Vb, kv_stride, nkeys);
-  const int voff = tile_lane_voff(ksrc.stride, tid);
+  const int voff = tile_lane_voff<D>(ksrc.stride, tid);
 
   // key tiles of the block, and the contiguous range of them this wave needs
   const int p_last_blk = s0 + min(q0 + kBlockM - 1, Tq - 1);
@@ -238,36 +247,37 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const uint16_t *_
     return !(k0 + kTileN - 1 <= pw0 && (W < 0 || pw_last - k0 <= W));
   };
 
-  tile_load_lds(kb0, ksrc, voff, t0 * kTileN);
-  tile_load_lds(vb0, vsrc, voff, t0 * kTileN);
-  if (t0 + 1 <= t1) tile_load_lds(kb1, ksrc, voff, (t0 + 1) * kTileN);
+  tile_load_lds<D>(kb0, ksrc, voff, t0 * kTileN);
+  tile_load_lds<D>(vb0, vsrc, voff, t0 * kTileN);
+  if (t0 + 1 <= t1) tile_load_lds<D>(kb1, ksrc, voff, (t0 + 1) * kTileN);
 
   // Q^T operand in registers: lane holds the query of row qw0 + l%32, d = 16 s + 8 hh + [0, 8).
-  bf16x8 qreg[8];
+  bf16x8 qreg[kSteps];
   if constexpr (!FUSE) {
     const int qr = min(qw0 + (lane & 31), Tq - 1);
-    const uint16_t *qp = Q + ((long long)b * Tq + qr) * q_stride + (long long)h * kD + 8 * hh;
+    const uint16_t *qp = Q + ((long long)b * Tq + qr) * q_stride + (long long)h * D + 8 * hh;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) qreg[s] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qp + 16 * s));
+    for (int s = 0; s < kSteps; ++s) qreg[s] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(qp + 16 * s));
   } else {
-    // The row's 128 elements are split between lanes l and l ^ 32 (64 each); the
-    // rotation pairs d and d + 64 are steps s and s + 4 of the same lane.
+    // The row's D elements are split between lanes l and l ^ 32 (D/2 each); the
+    // rotation pairs d and d + D/2 are steps s and s + kSteps/2 of the same lane.
     const int qrow = qw0 + (lane & 31);
     const int qr = min(qrow, Tq - 1);
-    uint16_t *qp = Qw + ((long long)b * Tq + qr) * q_stride + (long long)h * kD + 8 * hh;
-    u32x4 raw[8];
+    uint16_t *qp = Qw + ((long long)b * Tq + qr) * q_stride + (long long)h * D + 8 * hh;
+    u32x4 raw[kSteps];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) raw[s] = *(const u32x4 *)(qp + 16 * s);
+    for (int s = 0; s < kSteps; ++s) raw[s] = *(const u32x4 *)(qp + 16 * s);
     float ss = 0.f;
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
+    for (int s = 0; s < kSteps; ++s)
 #pragma unroll
       for (int i = 0; i < 4; ++i) ss += lo_bf16(raw[s][i]) * lo_bf16(raw[s][i]) + hi_bf16(raw[s][i]) * hi_bf16(raw[s][i]);
     ss += shfl_xor(ss, 32);
-    const float inv = qn.gain / sqrtf(ss / (float)kD + qn.eps);
+    const float inv = qn.gain / sqrtf(ss / (float)D + qn.eps);
     const double pos = (double)((qn.pos_offset ? qn.pos_offset[b] : 0) + qr);
+    constexpr int kHalf = kSteps / 2;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s = 0; s < kHalf; ++s) {
       u32x4 ya, yb;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -284,7 +294,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const uint16_t *_
           const float tf = (float)turns;
           const float sn = __builtin_amdgcn_sinf(tf), cs = __builtin_amdgcn_cosf(tf);
           const float a = (e ? hi_bf16(raw[s][i]) : lo_bf16(raw[s][i])) * inv;
-          const float bb = (e ? hi_bf16(raw[s + 4][i]) : lo_bf16(raw[s + 4][i])) * inv;
+          const float bb = (e ? hi_bf16(raw[s + kHalf][i]) : lo_bf16(raw[s + kHalf][i])) * inv;
           ra[e] = a * cs - bb * sn;
           rb[e] = a * sn + bb * cs;
         }
@@ -292,18 +302,18 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const uint16_t *_
         yb[i] = pack_bf16x2(rb[0], rb[1]);
       }
       raw[s] = ya;
-      raw[s + 4] = yb;
+      raw[s + kHalf] = yb;
     }
     if (qrow < Tq) {
 #pragma unroll
-      for (int s = 0; s < 8; ++s) *(u32x4 *)(qp + 16 * s) = raw[s];
+      for (int s = 0; s < kSteps; ++s) *(u32x4 *)(qp + 16 * s) = raw[s];
     }
 #pragma unroll
-    for (int s = 0; s < 8; ++s) qreg[s] = __builtin_bit_cast(bf16x8, raw[s]);
+    for (int s = 0; s < kSteps; ++s) qreg[s] = __builtin_bit_cast(bf16x8, raw[s]);
   }
-  const TileLane L = make_tile_lane(lane);
+  const TileLane<D> L = make_tile_lane<D>(lane);
 
-  FwdState st;
+  FwdState<D> st;
   float m_init = -INFINITY;
   if (tid == 0) overflow_flag = 0;
 
@@ -315,7 +325,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const uint16_t *_
       if (!overflow_flag) break;
 #pragma unroll 1
       for (int t = t0; t <= t1; ++t) {
-        tile_load_lds(kb0, ksrc, voff, t * kTileN);
+        tile_load_lds<D>(kb0, ksrc, voff, t * kTileN);
         lds_loads_done_barrier();
         if (in_range(t)) {
           f32x16 sx[2];
@@ -325,12 +335,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const uint16_t *_
         }
         __syncthreads();
       }
-      tile_load_lds(kb0, ksrc, voff, t0 * kTileN);
-      tile_load_lds(vb0, vsrc, voff, t0 * kTileN);
-      if (t0 + 1 <= t1) tile_load_lds(kb1, ksrc, voff, (t0 + 1) * kTileN);
+      tile_load_lds<D>(kb0, ksrc, voff, t0 * kTileN);
+      tile_load_lds<D>(vb0, vsrc, voff, t0 * kTileN);
+      if (t0 + 1 <= t1) tile_load_lds<D>(kb1, ksrc, voff, (t0 + 1) * kTileN);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) st.oacc[i] = f32x16{};
+    for (int i = 0; i < Gm::kDBlocks; ++i) st.oacc[i] = f32x16{};
     st.m_ref = m_init;
     st.l_run = 0.f;
     bool overflow = false;
@@ -343,8 +353,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const uint16_t *_
     // Step t: S of tile t+1 from kcur, softmax + PV of tile t from vcur; copies of
     // K(t+2) into kfill and V(t+1) into vfill run meanwhile.
     auto step = [&](const char *kcur, char *kfill, const char *vcur, char *vfill, int t) {
-      if (t + 2 <= t1) tile_load_lds(kfill, ksrc, voff, (t + 2) * kTileN);
-      if (t + 1 <= t1) tile_load_lds(vfill, vsrc, voff, (t + 1) * kTileN);
+      if (t + 2 <= t1) tile_load_lds<D>(kfill, ksrc, voff, (t + 2) * kTileN);
+      if (t + 1 <= t1) tile_load_lds<D>(vfill, vsrc, voff, (t + 1) * kTileN);
       const bool cur = in_range(t), next = in_range(t + 1);
       if (cur) {
         if (masked(t)) mask_tile(scur, t * kTileN, q_lane, W, hh);
@@ -380,9 +390,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const uint16_t *_
   const float inv_l = 1.f / l_tot;
   const int qr = qw0 + (lane & 31);
   if (qr < Tq) {
-    uint16_t *op = O + ((long long)b * Tq + qr) * q_stride + (long long)h * kD;
+    uint16_t *op = O + ((long long)b * Tq + qr) * q_stride + (long long)h * D;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+    for (int db = 0; db < Gm::kDBlocks; ++db)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int d = 32 * db + 8 * i + 4 * hh;
@@ -397,39 +407,50 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const uint16_t *_
 
 }  // namespace
 
-hipError_t launch_fwd_bf16_rows(const void *q, const void *k, const void *v, void *o, float *lse,
-                                const int32_t *q_pos0, int B, int Tq, int Tk, int H, int KV, int W, float scale,
-                                hipStream_t s) {
+template <int D, bool FUSE>
+hipError_t launch_fwd_kernel(const void *q, const void *k, const void *v, void *o, float *lse,
+                             const int32_t *q_pos0, int B, int Tq, int Tk, int H, int KV, int W, float scale,
+                             void *qw, const QkNormRope &qn, hipStream_t s) {
   const int nqb = (Tq + kBlockM - 1) / kBlockM;
   const long long blocks = (long long)nqb * B * H;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  QkNormRope none{};
-  hipLaunchKernelGGL(attn_fwd_bf16_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s, (const uint16_t *)q,
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, FUSE>), dim3((unsigned)blocks), dim3(256), 0, s, (const uint16_t *)q,
                      (const uint16_t *)k, (const uint16_t *)v, (uint16_t *)o, lse, q_pos0, B, Tq, Tk, H, KV, W, scale,
-                     nullptr, none);
+                     (uint16_t *)qw, qn);
   return hipGetLastError();
+}
+
+hipError_t launch_fwd_bf16_rows(const void *q, const void *k, const void *v, void *o, float *lse,
+                                const int32_t *q_pos0, int B, int Tq, int Tk, int H, int KV, int D, int W,
+                                float scale, hipStream_t s) {
+  const QkNormRope none{};
+  if (D == 64)
+    return launch_fwd_kernel<64, false>(q, k, v, o, lse, q_pos0, B, Tq, Tk, H, KV, W, scale, nullptr, none, s);
+  if (D == 128)
+    return launch_fwd_kernel<128, false>(q, k, v, o, lse, q_pos0, B, Tq, Tk, H, KV, W, scale, nullptr, none, s);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_fwd_bf16_qknorm_rope(void *q, const void *k, const void *v, void *o, float *lse,
                                        const AttnShape &sh, const int32_t *pos_offset,
                                        const double *inv_freq_host, float eps, float gain, hipStream_t s) {
-  const int nqb = (sh.T + kBlockM - 1) / kBlockM;
-  const long long blocks = (long long)nqb * sh.B * sh.H;
-  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  QkNormRope qn;
-  for (int j = 0; j < 64; ++j) qn.turns[j] = inv_freq_host[j] / 6.283185307179586;
+  QkNormRope qn{};
+  for (int j = 0; j < sh.D / 2; ++j) qn.turns[j] = inv_freq_host[j] / 6.283185307179586;
   qn.eps = eps;
   qn.gain = gain;
   qn.pos_offset = pos_offset;
-  hipLaunchKernelGGL(attn_fwd_bf16_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s, (const uint16_t *)q,
-                     (const uint16_t *)k, (const uint16_t *)v, (uint16_t *)o, lse, nullptr, sh.B, sh.T, sh.T, sh.H,
-                     sh.KV, sh.window, sh.scale, (uint16_t *)q, qn);
-  return hipGetLastError();
+  if (sh.D == 64)
+    return launch_fwd_kernel<64, true>(q, k, v, o, lse, nullptr, sh.B, sh.T, sh.T, sh.H, sh.KV, sh.window, sh.scale,
+                                       q, qn, s);
+  if (sh.D == 128)
+    return launch_fwd_kernel<128, true>(q, k, v, o, lse, nullptr, sh.B, sh.T, sh.T, sh.H, sh.KV, sh.window,
+                                        sh.scale, q, qn, s);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_fwd_bf16(const void *q, const void *k, const void *v, void *o, float *lse, const AttnShape &sh,
                            hipStream_t s) {
-  return launch_fwd_bf16_rows(q, k, v, o, lse, nullptr, sh.B, sh.T, sh.T, sh.H, sh.KV, sh.window, sh.scale, s);
+  return launch_fwd_bf16_rows(q, k, v, o, lse, nullptr, sh.B, sh.T, sh.T, sh.H, sh.KV, sh.D, sh.window, sh.scale, s);
 }
 
 }  // namespace ncattn

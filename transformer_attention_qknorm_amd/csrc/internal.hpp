@@ -31,7 +31,7 @@ constexpr int kBwdDelta = 1, kBwdDkDv = 2, kBwdDq = 4, kBwdAll = 7;
 // workspace: D [B][H][T] fp32 (padded to 256 B); bf16 adds LSE * log2(e) (same size)
 size_t bwd_workspace_bytes(int B, int T, int H, int W, bool bf16);
 
-// bf16, head_dim 128, MFMA kernels.
+// bf16, head_dim 64 or 128, MFMA kernels.
 hipError_t launch_fwd_bf16(const void *q, const void *k, const void *v, void *o, float *lse,
                            const AttnShape &sh, hipStream_t s);
 // The same forward with QK-norm + RoPE of q done in its prologue: each query row
@@ -46,8 +46,8 @@ hipError_t launch_fwd_bf16_qknorm_rope(void *q, const void *k, const void *v, vo
 // arrays with Tk rows per sequence; lse may be NULL.  Sequences whose offset
 // leaves the queries outside [0, Tk) get NaN rows.
 hipError_t launch_fwd_bf16_rows(const void *q, const void *k, const void *v, void *o, float *lse,
-                                const int32_t *q_pos0, int B, int Tq, int Tk, int H, int KV, int W, float scale,
-                                hipStream_t s);
+                                const int32_t *q_pos0, int B, int Tq, int Tk, int H, int KV, int D, int W,
+                                float scale, hipStream_t s);
 hipError_t launch_bwd_bf16(const void *q, const void *k, const void *v, const void *o,
                            const float *lse, const void *dout, void *dq, void *dk, void *dv,
                            void *workspace, const AttnShape &sh, int stages, hipStream_t s);
@@ -59,7 +59,7 @@ hipError_t launch_bwd_f32(const float *q, const float *k, const float *v, const 
                           const float *lse, const float *dout, float *dq, float *dk, float *dv,
                           float *delta, const AttnShape &sh, int stages, hipStream_t s);
 
-// Split-KV decode, bf16, head_dim 128.
+// Split-KV decode, bf16, head_dim 64 or 128.
 size_t decode_workspace_bytes(int B, int T_max, int H, int KV, int D, int window);
 hipError_t launch_decode_bf16(const void *q, const void *k_new, const void *v_new, void *k_cache,
                               void *v_cache, const int32_t *seqlens, void *o, float *lse, int B,
@@ -71,13 +71,13 @@ hipError_t launch_decode_bf16(const void *q, const void *k_new, const void *v_ne
 // device).  The array holds NCATTN_DECODE_SCRATCH_BYTES bytes.
 hipError_t decode_scratch_ptr(void **out);
 
-// Chunked prefill, bf16, head_dim 128: append k_new/v_new [B][Tn][KV][D] at
+// Chunked prefill, bf16, head_dim 64 or 128: append k_new/v_new [B][Tn][KV][D] at
 // cache rows seqlens[b].., then the forward of q [B][Tn][H][D] over the cache.
 hipError_t launch_cache_replicate(const void *k_src, const void *v_src, const int32_t *src_seqlen, void *k_dst,
                                   void *v_dst, int32_t *dst_seqlens, int N, int T_src, int T_max, int row_pieces,
                                   hipStream_t s);
 hipError_t launch_prefill_bf16(const void *q, const void *k_new, const void *v_new, void *k_cache, void *v_cache,
                                const int32_t *seqlens, void *o, float *lse, int B, int Tn, int T_max, int H,
-                               int KV, int window, float scale, hipStream_t s);
+                               int KV, int D, int window, float scale, hipStream_t s);
 
 }  // namespace ncattn

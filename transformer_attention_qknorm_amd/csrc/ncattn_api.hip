@@ -52,8 +52,8 @@ int check_dtype(const char *fn, int dtype) {
 }
 
 int check_attn_support(const char *fn, int dtype, int T, int H, int D) {
-  if (dtype == NCATTN_BF16 && D != 128)
-    return fail(NCATTN_EUNSUPPORTED, "%s: bf16 attention supports head_dim 128 only (got %d)", fn, D);
+  if (dtype == NCATTN_BF16 && D != 64 && D != 128)
+    return fail(NCATTN_EUNSUPPORTED, "%s: bf16 attention supports head_dim 64 or 128 (got %d)", fn, D);
   // the bf16 kernels address one (batch, head) slice of q/k/v/dO through 32-bit
   // byte offsets: (T + 64) rows of the token stride must stay below 2^31
   if (dtype == NCATTN_BF16 && ((double)T + 64.0) * H * D * 2.0 >= 2147483648.0)
@@ -307,7 +307,8 @@ int decode_check(const char *fn, const void *q, const void *k_new, const void *v
   NC_TRY(check_dtype(fn, dtype));
   if (window_left < -1) return fail(NCATTN_EINVAL, "%s: window_left must be >= -1 (got %d)", fn, window_left);
   if (dtype != NCATTN_BF16) return fail(NCATTN_EUNSUPPORTED, "%s: decode supports bf16 only", fn);
-  if (head_dim != 128) return fail(NCATTN_EUNSUPPORTED, "%s: decode supports head_dim 128 only (got %d)", fn, head_dim);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(NCATTN_EUNSUPPORTED, "%s: decode supports head_dim 64 or 128 (got %d)", fn, head_dim);
   if (!isfinite(softmax_scale)) return fail(NCATTN_EINVAL, "%s: softmax_scale must be finite", fn);
   if (k_cache == v_cache) return fail(NCATTN_EINVAL, "%s: k_cache and v_cache must differ", fn);
   if (o == q || o == k_cache || o == v_cache || o == k_new || o == v_new)
@@ -385,8 +386,8 @@ int ncattn_prefill(const void *q, const void *k_new, const void *v_new, void *k_
     return fail(NCATTN_EINVAL, "%s: o must not alias an input", fn);
   window_left = effective_window(window_left, T_max);
   hipError_t e = ncattn::launch_prefill_bf16(q, k_new, v_new, k_cache, v_cache, cache_seqlens, o, lse, B, Tn, T_max,
-                                             n_head, n_kv_head, window_left, resolve_scale(softmax_scale, head_dim),
-                                             (hipStream_t)stream);
+                                             n_head, n_kv_head, head_dim, window_left,
+                                             resolve_scale(softmax_scale, head_dim), (hipStream_t)stream);
   return hip_status(e, fn);
 }
 
