@@ -129,6 +129,11 @@ def test_bwd_validation_and_workspace(L):
     def rows(B, T, H):
         return (B * H * T * 4 + 255) // 256 * 256
     assert L.ncattn_bwd_workspace_bytes(2, 100, 4, 2, 128, -1, 1) == rows(2, 100, 4) == 3328
+    # shapes the calls refuse get 0, never a wrapped size
+    big = 2 ** 31 - 1
+    assert L.ncattn_bwd_workspace_bytes(big, big, big, 1, 128, -1, 0) == 0
+    assert L.ncattn_bwd_workspace_bytes(2, 100, 6, 4, 128, -1, 0) == 0        # n_head % n_kv_head
+    assert L.ncattn_decode_workspace_bytes(big, big, big, 1, 128, -1) == 0
     for B, T, H, W in [(2, 100, 4, -1), (2, 100, 4, 98), (1, 2048, 1, -1), (1, 2048, 1, 1024), (1, 2048, 1, 0),
                        (3, 777, 2, 256), (16, 4096, 12, 2048), (16, 4096, 12, -1), (1, 32768, 10, -1)]:
         assert L.ncattn_bwd_workspace_bytes(B, T, H, H, 128, W, 0) == 2 * rows(B, T, H), (B, T, H, W)

@@ -542,17 +542,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t *__restri
 
 }  // namespace
 
-size_t bwd_workspace_bytes(int B, int T, int H, int W, bool bf16) {
-  (void)W;
-  const size_t rows = ((size_t)B * H * T * sizeof(float) + 255) & ~(size_t)255;
-  return bf16 ? 2 * rows : rows;
-}
-
 template <int D>
 hipError_t launch_bwd_kernels(const void *q, const void *k, const void *v, const void *o, const float *lse,
                               const void *dout, void *dq, void *dk, void *dv, void *workspace, const AttnShape &sh,
                               int stages, hipStream_t s) {
-  const size_t row_bytes = ((size_t)sh.B * sh.H * sh.T * sizeof(float) + 255) & ~(size_t)255;
+  const size_t row_bytes = bwd_row_bytes(sh.B, sh.T, sh.H);
   float *delta = (float *)workspace;
   float *lse2 = (float *)((char *)workspace + row_bytes);
   const long long rows = (long long)sh.B * sh.T * sh.H;

@@ -32,12 +32,8 @@ namespace ncattn {
 
 namespace {
 
-constexpr int kCH = 128;   // keys per chunk
+constexpr int kCH = kDecodeChunk;  // keys per chunk
 
-int n_chunks_max(int T_max, int window) {
-  const int span = (window < 0 || window + 1 > T_max) ? T_max : window + 1;
-  return (span + kCH - 1) / kCH;
-}
 
 // Sum over each group of 8 lanes (DPP): xor-1 and xor-2 quad permutes, then the
 // half-row mirror, which pairs the two quads of the group.
@@ -253,18 +249,12 @@ hipError_t decode_scratch_ptr(void **out) {
   return hipSuccess;
 }
 
-size_t decode_workspace_bytes(int B, int T_max, int H, int KV, int D, int window) {
-  (void)KV;
-  const size_t parts = (size_t)B * H * n_chunks_max(T_max, window);
-  return parts * (D + 2) * sizeof(float) + 256;
-}
-
 namespace {
 template <int D>
 hipError_t launch_decode_kernels(const void *q, const void *k_new, const void *v_new, void *k_cache, void *v_cache,
                                  const int32_t *seqlens, void *o, float *lse, int B, int T_max, int H, int KV,
                                  int window, float scale, void *workspace, hipStream_t s) {
-  const int C_max = n_chunks_max(T_max, window);
+  const int C_max = decode_chunks_max(T_max, window);
   const size_t parts = (size_t)B * H * C_max;
   float *ws_o = (float *)workspace;
   float *ws_m = ws_o + parts * D;

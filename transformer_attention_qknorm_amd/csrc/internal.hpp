@@ -7,6 +7,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "sizing.hpp"
+
 namespace ncattn {
 
 struct AttnShape {
@@ -28,8 +30,7 @@ hipError_t launch_qknorm_rope_bwd(void *dq, void *dk, const void *q, const void 
 // Backward stages (bit mask): D_i = dO.O, then dK/dV, then dQ.
 constexpr int kBwdDelta = 1, kBwdDkDv = 2, kBwdDq = 4, kBwdAll = 7;
 
-// workspace: D [B][H][T] fp32 (padded to 256 B); bf16 adds LSE * log2(e) (same size)
-size_t bwd_workspace_bytes(int B, int T, int H, int W, bool bf16);
+// workspace: bwd_workspace_bytes() (sizing.hpp)
 
 // bf16, head_dim 64 or 128, MFMA kernels.
 hipError_t launch_fwd_bf16(const void *q, const void *k, const void *v, void *o, float *lse,
@@ -60,7 +61,6 @@ hipError_t launch_bwd_f32(const float *q, const float *k, const float *v, const 
                           float *delta, const AttnShape &sh, int stages, hipStream_t s);
 
 // Split-KV decode, bf16, head_dim 64 or 128.
-size_t decode_workspace_bytes(int B, int T_max, int H, int KV, int D, int window);
 hipError_t launch_decode_bf16(const void *q, const void *k_new, const void *v_new, void *k_cache,
                               void *v_cache, const int32_t *seqlens, void *o, float *lse, int B,
                               int T_max, int H, int KV, int D, int window, float scale,

@@ -34,6 +34,9 @@ int hip_status(hipError_t e, const char *what) {
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
+// The element-count limit of every tensor (see check_heads).
+bool too_large(int B, int T, int H, int D) { return (double)B * T * H * D > 4.0e15; }
+
 // Shape checks common to every attention call.
 int check_heads(const char *fn, int B, int T, int H, int KV, int D) {
   if (B <= 0 || T <= 0 || H <= 0 || KV <= 0 || D <= 0)
@@ -42,7 +45,7 @@ int check_heads(const char *fn, int B, int T, int H, int KV, int D) {
   if (H % KV != 0) return fail(NCATTN_EINVAL, "%s: n_head (%d) must be a multiple of n_kv_head (%d)", fn, H, KV);
   // every index used by the kernels is formed in 64-bit, but per-tensor element
   // counts must still fit the int64 address arithmetic comfortably
-  if ((double)B * T * H * D > 4.0e15) return fail(NCATTN_EINVAL, "%s: tensor too large", fn);
+  if (too_large(B, T, H, D)) return fail(NCATTN_EINVAL, "%s: tensor too large", fn);
   return NCATTN_OK;
 }
 
@@ -211,9 +214,9 @@ int ncattn_fwd_qknorm_rope(void *q, void *k, const void *v, void *o, float *lse,
 
 size_t ncattn_bwd_workspace_bytes(int B, int T, int n_head, int n_kv_head, int head_dim, int window_left,
                                   int dtype) {
-  (void)n_kv_head;
-  (void)head_dim;
-  if (B <= 0 || T <= 0 || n_head <= 0 || window_left < -1) return 0;
+  // 0 for any shape the backward refuses (never a wrapped size)
+  if (B <= 0 || T <= 0 || n_head <= 0 || n_kv_head <= 0 || head_dim <= 0 || window_left < -1) return 0;
+  if (n_head % n_kv_head != 0 || too_large(B, T, n_head, head_dim)) return 0;
   return ncattn::bwd_workspace_bytes(B, T, n_head, effective_window(window_left, T), dtype == NCATTN_BF16);
 }
 }  // extern "C"
@@ -281,7 +284,9 @@ int ncattn_bwd_dkdv(NC_BWD_PARAMS) { return bwd_common("ncattn_bwd_dkdv", ncattn
 int ncattn_bwd_dq(NC_BWD_PARAMS) { return bwd_common("ncattn_bwd_dq", ncattn::kBwdDq, NC_BWD_ARGS); }
 
 size_t ncattn_decode_workspace_bytes(int B, int T_max, int n_head, int n_kv_head, int head_dim, int window_left) {
+  // 0 for any shape decode refuses (never a wrapped size)
   if (B <= 0 || T_max <= 0 || n_head <= 0 || n_kv_head <= 0 || head_dim <= 0 || window_left < -1) return 0;
+  if (n_head % n_kv_head != 0 || too_large(B, T_max, n_head, head_dim)) return 0;
   return ncattn::decode_workspace_bytes(B, T_max, n_head, n_kv_head, head_dim, effective_window(window_left, T_max));
 }
 
@@ -407,10 +412,13 @@ int ncattn_cache_replicate(const void *k_src, const void *v_src, const int32_t *
     return fail(NCATTN_EINVAL, "%s: need N, T_src, n_kv_head, head_dim >= 1 (N=%d T_src=%d n_kv_head=%d head_dim=%d)",
                 fn, N, T_src, n_kv_head, head_dim);
   if (T_max < T_src) return fail(NCATTN_EINVAL, "%s: need T_src <= T_max (T_src=%d T_max=%d)", fn, T_src, T_max);
-  const long long row_bytes = (long long)n_kv_head * head_dim * (dtype == NCATTN_BF16 ? 2 : 4);
-  if (row_bytes % 16) return fail(NCATTN_EINVAL, "%s: a cache row (n_kv_head * head_dim elements) must be a multiple of 16 bytes", fn);
-  if (row_bytes / 16 > 0x7fffffffLL || (long long)N * T_max * row_bytes / 16 > (1LL << 60))
+  const int elem = dtype == NCATTN_BF16 ? 2 : 4;
+  // sizes checked in floating point before any integer product is formed
+  if ((double)n_kv_head * head_dim * elem / 16.0 > 2147483647.0 ||
+      (double)N * T_max * n_kv_head * head_dim * elem / 16.0 > 1152921504606846976.0 /* 2^60 */)
     return fail(NCATTN_EINVAL, "%s: sizes too large", fn);
+  const long long row_bytes = (long long)n_kv_head * head_dim * elem;
+  if (row_bytes % 16) return fail(NCATTN_EINVAL, "%s: a cache row (n_kv_head * head_dim elements) must be a multiple of 16 bytes", fn);
   if ((((uintptr_t)k_src | (uintptr_t)v_src | (uintptr_t)k_dst | (uintptr_t)v_dst) & 15u))
     return fail(NCATTN_EINVAL, "%s: cache pointers must be 16-byte aligned", fn);
   if (k_dst == v_dst || k_dst == k_src || k_dst == v_src || v_dst == k_src || v_dst == v_src)
