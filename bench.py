@@ -254,11 +254,13 @@ def time_config(nc, torch, cfg, dev, stream, iters=10):
 
 def qknorm_detail(nc, torch, cfg, dev, stream):
     """QK-norm + RoPE of a workload's q, k (GB/s), its backward, the logit-gain
-    variant, and the forward with QK-norm + RoPE fused into it against the two
-    calls it replaces, per window of the layer pattern."""
+    variant, the forward with QK-norm + RoPE fused into it and the backward with
+    the norm's backward fused into it, each against the two calls it replaces,
+    per window of the layer pattern."""
     from workloads import config_inputs
-    q0, k0, v0, _ = config_inputs(cfg)
+    q0, k0, v0, do0 = config_inputs(cfg)
     q, k, v = q0.to(dev), k0.to(dev), v0.to(dev)
+    del q0, k0, v0
     B, T, H, KV, D = cfg.B, cfg.T, cfg.H, cfg.KV, cfg.D
     base = cfg.rope_base
     qk_bytes = B * T * (H + KV) * D * 2 * 2
@@ -292,7 +294,32 @@ def qknorm_detail(nc, torch, cfg, dev, stream):
         fused["full" if W < 0 else f"w{W}"] = {"two_calls_us": round(t2, 2), "fused_us": round(t1, 2),
                                                "fused_fwd_TFLOPs": round(fl / (t1 * 1e-6) / 1e12, 1)}
     out["fwd_qknorm_rope"] = fused
-    del q, k, v, dq, dk, o, lse
+    # the backward with QK-norm + RoPE's backward folded into the dQ and dK/dV
+    # epilogues, against the attention backward followed by the norm's backward
+    do = do0.to(dev)
+    del do0
+    qn, kn = q.clone(), k.clone()
+    nc.qknorm_rope_(qn, kn, None, rope_base=base, eps=1e-6)
+    ws = nc.bwd_workspace(q, k, (-1, 0))
+    gq, gk, gv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    fb = {}
+    for W in sorted(set(cfg.windows)):
+        nc.fwd(qn, kn, v, window=(W, 0), out=(o, lse))
+
+        def two_calls_bwd():
+            nc.bwd(qn, kn, v, o, lse, do, window=(W, 0), out=(gq, gk, gv), workspace=ws)
+            nc.qknorm_rope_bwd_(gq, gk, q, k, None, rope_base=base, eps=1e-6)
+
+        def one_call_bwd():
+            nc.bwd_qknorm_rope(qn, kn, v, o, lse, do, q, k, None, rope_base=base, eps=1e-6, window=(W, 0),
+                               out=(gq, gk, gv), workspace=ws)
+        t2 = event_us(torch, stream, two_calls_bwd, 20)
+        t1 = event_us(torch, stream, one_call_bwd, 20)
+        fl = 8 * D * visible_pairs(T, W) * B * H
+        fb["full" if W < 0 else f"w{W}"] = {"two_calls_us": round(t2, 2), "fused_us": round(t1, 2),
+                                            "fused_bwd_TFLOPs": round(fl / (t1 * 1e-6) / 1e12, 1)}
+    out["bwd_qknorm_rope"] = fb
+    del q, k, v, dq, dk, o, lse, do, qn, kn, ws, gq, gk, gv
     torch.cuda.empty_cache()
     return out
 

@@ -184,6 +184,30 @@ int ncattn_bwd_dq(const void *q, const void *k, const void *v, const void *o, co
                   int window_left, int window_right, float softmax_scale, int dtype,
                   void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * The backward of QK-norm + RoPE followed by attention, in one call: the
+ * attention backward of ncattn_bwd whose dq and dk are carried back through
+ * QK-norm + RoPE ("nanochat Admin & Developer Guide", section 3: weightless
+ * RMSNorm of q and k, then rotary embedding; "nanochat (Python)" catalog,
+ * Backward pass: the chain rule through that forward) before they are stored.
+ *   q, k: the post-norm rows the forward attended with (ncattn_qknorm_rope's
+ *   output); q_raw [B][T][n_head][D], k_raw [B][T][n_kv_head][D]: its inputs,
+ *   before normalisation (the caller keeps them); pos_offset, rope_base, eps,
+ *   qk_gain as given to ncattn_qknorm_rope; the rest as ncattn_bwd.
+ *   Outputs: dq = d/dq_raw, dk = d/dk_raw (dtype), dv as ncattn_bwd.  Equal to
+ *   ncattn_bwd followed by ncattn_qknorm_rope_bwd, except that for bf16 the norm's
+ *   backward is applied to the fp32 gradients before their rounding to bf16
+ *   (one rounding instead of two) and dq, dk of the post-norm rows are never
+ *   written to memory.  dq / dk must not alias q, k, q_raw or k_raw.
+ *   workspace: ncattn_bwd_workspace_bytes(...) bytes.  bf16: head_dim 64 or 128;
+ *   fp32 (head_dim 64 or 128): the two calls in sequence.
+ */
+int ncattn_bwd_qknorm_rope(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                           const void *dout, const void *q_raw, const void *k_raw, const int32_t *pos_offset,
+                           float rope_base, float eps, float qk_gain, void *dq, void *dk, void *dv, int B, int T,
+                           int n_head, int n_kv_head, int head_dim, int window_left, int window_right,
+                           float softmax_scale, int dtype, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Bytes of workspace ncattn_decode needs (split-KV partial results). */
 size_t ncattn_decode_workspace_bytes(int B, int T_max, int n_head, int n_kv_head, int head_dim,
                                      int window_left);

@@ -134,6 +134,28 @@ static void test_bwd() {
   }
   CHECK(bwd(ncattn_bwd, 2, 300, 4, 2, 64, 17, NCATTN_F32, P(9), need) == NCATTN_OK);
   CHECK(strcmp(g_last.fn, "bwd_f32") == 0 && g_last.window == 17);
+
+  // the fused QK-norm + RoPE backward: the backward's checks, the norm's, and
+  // no gradient aliasing the raw rows
+  auto fb = [&](const void *qr, const void *kr, void *dq, float base, int D, int wl, int dt, void *ws, size_t wsb) {
+    return ncattn_bwd_qknorm_rope(P(0), P(1), P(2), P(3), F(4), P(5), qr, kr, nullptr, base, 1e-6f, 1.f, dq, P(7),
+                                  P(8), 2, 300, 4, 2, D, wl, 0, 0.f, dt, ws, wsb, nullptr);
+  };
+  CHECK(fb(nullptr, P(11), P(6), 1e5f, 128, -1, NCATTN_BF16, P(9), need) == NCATTN_EINVAL);
+  CHECK(fb(P(10), MIS(11), P(6), 1e5f, 128, -1, NCATTN_BF16, P(9), need) == NCATTN_EINVAL);
+  CHECK(fb(P(10), P(11), P(10), 1e5f, 128, -1, NCATTN_BF16, P(9), need) == NCATTN_EINVAL);   // dq aliases q_raw
+  CHECK(fb(P(10), P(11), P(0), 1e5f, 128, -1, NCATTN_BF16, P(9), need) == NCATTN_EINVAL);    // dq aliases q
+  CHECK(fb(P(10), P(11), P(6), 0.5f, 128, -1, NCATTN_BF16, P(9), need) == NCATTN_EINVAL);    // rope base
+  CHECK(fb(P(10), P(11), P(6), 1e5f, 96, -1, NCATTN_BF16, P(9), need) == NCATTN_EUNSUPPORTED);
+  CHECK(fb(P(10), P(11), P(6), 1e5f, 128, -1, NCATTN_BF16, P(9), need - 1) == NCATTN_EWORKSPACE);
+  const long before = g_last.count;
+  CHECK(fb(P(10), P(11), P(6), 1e5f, 128, -2, NCATTN_BF16, P(9), need) == NCATTN_EINVAL);
+  CHECK(g_last.count == before);  // nothing launched on a refusal
+  CHECK(fb(P(10), P(11), P(6), 1e5f, 64, INT_MAX, NCATTN_BF16, P(9), need) == NCATTN_OK);
+  CHECK(strcmp(g_last.fn, "bwd_bf16_qknorm_rope") == 0 && g_last.window == -1 && g_last.D == 64);
+  CHECK(g_last.stages == (int)(pow(1e5, -2.0 * 31 / 64) * 1e9));
+  CHECK(fb(P(10), P(11), P(6), 1e5f, 128, 5, NCATTN_F32, P(9), need) == NCATTN_OK);
+  CHECK(strcmp(g_last.fn, "qknorm_rope_bwd") == 0 && g_last.count == before + 3);  // bwd_f32, then the norm's
 }
 
 static int dec(bool noalloc, int B, int Tm, int H, int KV, int D, int wl, int dt, void *ws, size_t wsb,

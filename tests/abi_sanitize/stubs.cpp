@@ -61,6 +61,15 @@ hipError_t launch_bwd_bf16(const void *, const void *, const void *, const void 
   return hipSuccess;
 }
 
+hipError_t launch_bwd_bf16_qknorm_rope(const void *, const void *, const void *, const void *, const float *,
+                                       const void *, const void *, const void *, void *, void *, void *, void *,
+                                       const AttnShape &sh, const int32_t *, const double *inv, float, float,
+                                       hipStream_t) {
+  rec("bwd_bf16_qknorm_rope", sh.B, sh.T, sh.H, sh.KV, sh.D, sh.window, sh.scale);
+  g_last.stages = (int)(inv[sh.D / 2 - 1] * 1e9);
+  return hipSuccess;
+}
+
 hipError_t launch_fwd_f32(const float *, const float *, const float *, float *, float *, const AttnShape &sh,
                           hipStream_t) {
   rec("fwd_f32", sh.B, sh.T, sh.H, sh.KV, sh.D, sh.window, sh.scale);

@@ -119,6 +119,60 @@ def test_fwd_qknorm_rope(case):
     check(o, f64(o2), dtype, "o vs unfused")
 
 
+BWD_FUSED_CASES = [
+    # dtype, B, T, H, KV, D, W, base, gain, pos_offset
+    ("bf16", 2, 200, 4, 2, 128, -1, 100000.0, 1.0, False),
+    ("bf16", 2, 333, 8, 1, 128, 100, 100000.0, math.sqrt(1.2), True),
+    ("bf16", 1, 1, 2, 1, 128, -1, 100000.0, 1.0, True),
+    ("bf16", 3, 130, 6, 6, 128, 64, 10000.0, 1.0, True),
+    ("bf16", 1, 300, 6, 2, 64, 64, 10000.0, 1.0, True),
+    ("bf16", 3, 130, 4, 4, 64, -1, 100000.0, math.sqrt(1.2), False),
+    ("f32", 2, 100, 4, 2, 64, 17, 10000.0, math.sqrt(1.2), True),
+    ("f32", 1, 150, 3, 3, 128, -1, 100000.0, 1.0, False),
+]
+
+
+@pytest.mark.parametrize("case", BWD_FUSED_CASES, ids=lambda c: "-".join(str(x)[:6] for x in c))
+def test_bwd_qknorm_rope(case):
+    """The fused backward: gradients of the raw q, k (and of v) through QK-norm +
+    RoPE and attention, against the oracle's attention backward followed by its
+    QK-norm + RoPE backward, and against the two separate calls."""
+    dtype, B, T, H, KV, D, W, base, gain, offset = case
+    say(f"bwd_qknorm_rope {case}")
+    q, k, v, do = attn_inputs(B, T, H, KV, D, dtype, seed=400 + T)
+    pos = torch.from_numpy(np.random.default_rng(6).integers(0, 8192, size=B).astype(np.int32)) if offset else None
+    pn = None if pos is None else pos.numpy()
+    xq, xk = oracle.qknorm_rope(f64(q), f64(k), pn, base, 1e-6, gain)
+    sq, sk = stored(xq, dtype), stored(xk, dtype)
+    ro, _ = oracle.attn_fwd(sq, sk, f64(v), W)
+    rdy_q, rdy_k, rdv = oracle.attn_bwd(sq, sk, f64(v), f64(do), W, o=stored(ro, dtype))
+    rdq, rdk = oracle.qknorm_rope_bwd(f64(q), f64(k), rdy_q, rdy_k, pn, base, 1e-6, gain)
+    qr, kr, vd, dod = to_dev(q, k, v, do)
+    pd = None if pos is None else pos.to(DEV)
+    qn, kn = qr.clone(), kr.clone()
+    nc.qknorm_rope_(qn, kn, pd, rope_base=base, eps=1e-6, qk_gain=gain)
+    o, lse = nc.fwd(qn, kn, vd, window=(W, 0))
+    q_before, k_before = qr.clone(), kr.clone()
+    dq, dk, dv = nc.bwd_qknorm_rope(qn, kn, vd, o, lse, dod, qr, kr, pd, rope_base=base, eps=1e-6, qk_gain=gain,
+                                    window=(W, 0))
+    torch.cuda.synchronize()
+    check(dq, rdq, dtype, "dq_raw")
+    check(dk, rdk, dtype, "dk_raw")
+    check(dv, rdv, dtype, "dv")
+    assert torch.equal(qr, q_before) and torch.equal(kr, k_before)
+    # the attention backward followed by the norm's backward gives the same
+    # gradients up to rounding: dv bit for bit; dq, dk each within the bar of the
+    # exact values, so within twice the bar of each other (the two calls round the
+    # post-norm gradients to the I/O dtype in between, the fused call does not)
+    g = nc.bwd(qn, kn, vd, o, lse, dod, window=(W, 0))
+    nc.qknorm_rope_bwd_(g[0], g[1], qr, kr, pd, rope_base=base, eps=1e-6, qk_gain=gain)
+    torch.cuda.synchronize()
+    assert torch.equal(dv, g[2])
+    twice = {kk: 2 * vv for kk, vv in TOL[dtype].items()}
+    for name, a, b in (("dq_raw", dq, g[0]), ("dk_raw", dk, g[1])):
+        tol_check(f64(a), f64(b), what=f"{name} vs two calls", out_bf16=dtype == "bf16", **twice)
+
+
 # ------------------------------------------------------------------ forward / backward
 
 FWD_CASES = [

@@ -79,18 +79,25 @@ def _gpu_layer(cfg, W):
     say(f"{cfg.name}: W={W} generating inputs")
     q, k, v, do = config_inputs(cfg)
     qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    raw = None
     if not cfg.pre_normed:
+        raw = (qd.clone(), kd.clone())
         nc.qknorm_rope_(qd, kd, None, rope_base=cfg.rope_base, eps=1e-6, qk_gain=1.0)
     say(f"{cfg.name}: W={W} fwd/bwd on the GPU")
     o, lse = nc.fwd(qd, kd, vd, window=(W, 0))
     dq, dk, dv = nc.bwd(qd, kd, vd, o, lse, dod, window=(W, 0))
+    outs = [("q'", qd), ("k'", kd), ("o", o), ("lse", lse), ("dq", dq), ("dk", dk), ("dv", dv)]
+    if raw is not None:
+        # the fused backward: gradients of the raw q, k through QK-norm + RoPE
+        dqr, dkr, _ = nc.bwd_qknorm_rope(qd, kd, vd, o, lse, dod, raw[0], raw[1], None, rope_base=cfg.rope_base,
+                                         eps=1e-6, qk_gain=1.0, window=(W, 0))
+        outs += [("dq_raw", dqr), ("dk_raw", dkr)]
     torch.cuda.synchronize()
-    for name, t in (("q'", qd), ("k'", kd), ("o", o), ("lse", lse), ("dq", dq), ("dk", dk), ("dv", dv)):
+    for name, t in outs:
         assert bool(torch.isfinite(t).all()), f"{cfg.name} W={W}: non-finite values in {name}"
-    res = dict(inputs=(q, k, v, do), **{n: t.cpu() for n, t in
-                                        (("q", qd), ("k", kd), ("o", o), ("lse", lse), ("dq", dq), ("dk", dk),
-                                         ("dv", dv))})
-    del qd, kd, vd, dod, o, lse, dq, dk, dv
+    keys = {"q'": "q", "k'": "k"}
+    res = dict(inputs=(q, k, v, do), **{keys.get(n, n): t.cpu() for n, t in outs})
+    del qd, kd, vd, dod, o, lse, dq, dk, dv, outs, raw
     torch.cuda.empty_cache()
     _GPU_RESULTS[key] = res
     return res
@@ -124,6 +131,11 @@ def test_workload_layers(cfg, W):
         check(r["dq"][b:b + 1, :, hs], rdq, "bf16", f"dq W={W} b={b} g={g}")
         check(r["dk"][b:b + 1, :, g:g + 1], rdk, "bf16", f"dk W={W} b={b} g={g}")
         check(r["dv"][b:b + 1, :, g:g + 1], rdv, "bf16", f"dv W={W} b={b} g={g}")
+        if not cfg.pre_normed:
+            # the fused backward, through the norm to the raw inputs of the slice
+            rdq_raw, rdk_raw = oracle.qknorm_rope_bwd(f64(sq), f64(sk), rdq, rdk, None, cfg.rope_base, 1e-6, 1.0)
+            check(r["dq_raw"][b:b + 1, :, hs], rdq_raw, "bf16", f"dq_raw W={W} b={b} g={g}")
+            check(r["dk_raw"][b:b + 1, :, g:g + 1], rdk_raw, "bf16", f"dk_raw W={W} b={b} g={g}")
 
 
 @pytest.mark.parametrize("W", list(DECODE.windows))

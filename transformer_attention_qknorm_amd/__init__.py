@@ -25,7 +25,7 @@ import os
 
 import torch
 
-__all__ = ["qknorm_rope_", "qknorm_rope_bwd_", "fwd", "fwd_qknorm_rope_", "bwd", "decode", "decode_noalloc", "prefill",
+__all__ = ["qknorm_rope_", "qknorm_rope_bwd_", "fwd", "fwd_qknorm_rope_", "bwd", "bwd_qknorm_rope", "decode", "decode_noalloc", "prefill",
            "cache_replicate",
            "window_sizes", "lib", "NcattnError", "LIB_PATH",
            "BF16", "F32", "STATUS", "bwd_workspace", "decode_workspace", "BWD_STAGES"]
@@ -65,6 +65,8 @@ def lib():
     for fn in ("ncattn_bwd_preprocess", "ncattn_bwd_dkdv", "ncattn_bwd_dq"):
         getattr(L, fn).argtypes = L.ncattn_bwd.argtypes
         getattr(L, fn).restype = i32
+    L.ncattn_bwd_qknorm_rope.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, f32, f32, f32, vp, vp, vp, i32, i32,
+                                         i32, i32, i32, i32, i32, f32, i32, vp, sz, vp]
     L.ncattn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     L.ncattn_decode_workspace_bytes.restype = sz
     L.ncattn_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp, sz, vp]
@@ -74,6 +76,7 @@ def lib():
     L.ncattn_last_error.restype = ctypes.c_char_p
     L.ncattn_version.restype = ctypes.c_char_p
     for fn in ("ncattn_qknorm_rope", "ncattn_qknorm_rope_bwd", "ncattn_fwd", "ncattn_fwd_qknorm_rope", "ncattn_bwd",
+               "ncattn_bwd_qknorm_rope",
                "ncattn_decode", "ncattn_decode_noalloc",
                "ncattn_prefill", "ncattn_cache_replicate"):
         getattr(L, fn).restype = i32
@@ -263,6 +266,42 @@ def bwd(q, k, v, o, lse, do, window=(-1, 0), softmax_scale=None, out=None, works
         rc = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv),
                 B, T, H, KV, D, wl, wr, _scale(softmax_scale), dt, _ptr(ws), ws.numel(), _stream(dev))
     _check(BWD_STAGES[stage], rc)
+    return dq, dk, dv
+
+
+def bwd_qknorm_rope(q, k, v, o, lse, do, q_raw, k_raw, pos_offset=None, rope_base=100000.0, eps=1e-6,
+                    qk_gain=1.0, window=(-1, 0), softmax_scale=None, out=None, workspace=None):
+    """The backward of QK-norm + RoPE followed by attention, in one call: returns
+    (dq, dk, dv) with dq, dk the gradients of the raw rows q_raw, k_raw (q, k are
+    the post-norm rows the forward attended with).  ``out`` and ``workspace``
+    reuse preallocated buffers."""
+    dev = _dev(q, k, v, o, lse, do, q_raw, k_raw)
+    B, T, H, D = q.shape
+    KV = k.shape[2]
+    if o.shape != q.shape or do.shape != q.shape or lse.shape != (B, H, T) or lse.dtype != torch.float32:
+        raise ValueError("ncattn.bwd_qknorm_rope: o, do must match q and lse must be fp32 [B][H][T]")
+    if k.shape != v.shape or q_raw.shape != q.shape or k_raw.shape != k.shape \
+            or len({q.dtype, k.dtype, v.dtype, o.dtype, do.dtype, q_raw.dtype, k_raw.dtype}) != 1:
+        raise ValueError("ncattn.bwd_qknorm_rope: inconsistent shapes or dtypes")
+    if pos_offset is not None:
+        _dev(pos_offset)
+        if pos_offset.dtype != torch.int32 or pos_offset.numel() != B:
+            raise ValueError("ncattn.bwd_qknorm_rope: pos_offset must be int32 [B]")
+    wl, wr = _window(window)
+    ws = bwd_workspace(q, k, (wl, wr)) if workspace is None else workspace
+    if out is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    else:
+        dq, dk, dv = out
+        _dev(dq, dk, dv, ws)
+        if dq.shape != q.shape or dk.shape != k.shape or dv.shape != v.shape:
+            raise ValueError("ncattn.bwd_qknorm_rope: out must be (dq like q, dk like k, dv like v)")
+    with torch.cuda.device(dev):
+        rc = lib().ncattn_bwd_qknorm_rope(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(q_raw),
+                                          _ptr(k_raw), _ptr(pos_offset), float(rope_base), float(eps),
+                                          float(qk_gain), _ptr(dq), _ptr(dk), _ptr(dv), B, T, H, KV, D, wl, wr,
+                                          _scale(softmax_scale), _dtype_code(q), _ptr(ws), ws.numel(), _stream(dev))
+    _check("ncattn_bwd_qknorm_rope", rc)
     return dq, dk, dv
 
 

@@ -198,7 +198,73 @@ __device__ __forceinline__ void interleave_mfma_valu() {
   }
 }
 
+// ---------------------------------------------------------------- QK-norm + RoPE backward epilogue
+// For the fused backward (ncattn_bwd_qknorm_rope): the gradient that dK / dQ
+// hold for a post-norm row y = R(g x / r) is carried back to the raw row x
+// ("nanochat Admin & Developer Guide", section 3: weightless RMSNorm of q and k,
+// then rotary embedding; "nanochat (Python)" catalog, Backward pass: the chain
+// rule through that forward):
+//   dn = R^T dy (each pair (j, j + D/2) rotated by -theta_j),
+//   dx = (g / r) (dn - x (dn . x) / (D r^2)),  r = sqrt(mean(x^2) + eps).
+// The row is held by the lane pair (l, l ^ 32) in accumulator layout: element
+// 4 i + j of block db is d = 32 db + 8 i + 4 hh + j, so the pair partner d + D/2
+// is block db + D/64 of the same lane, and the two row sums need one exchange.
+struct NormRopeBwd {
+  const uint16_t *x;          // raw rows: q [B][T][H][D] (dQ) or k [B][T][KV][D] (dK)
+  const int32_t *pos_offset;  // device [B] or NULL
+  double turns[64];           // base^(-2j/D) / 2 pi for j < D/2: turns per position
+  float eps, gain;
+};
+
 template <int D>
+__device__ __forceinline__ void norm_rope_bwd_row(f32x16 (&g)[Geom<D>::kDBlocks], const uint16_t *xrow, double pos,
+                                                  const NormRopeBwd &nb, int hh) {
+  constexpr int NB = Geom<D>::kDBlocks, HB = NB / 2;
+  float x[NB][16];
+#pragma unroll
+  for (int db = 0; db < NB; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const u32x2 w = *(const u32x2 *)(xrow + 32 * db + 8 * i + 4 * hh);
+      x[db][4 * i + 0] = lo_bf16(w[0]);
+      x[db][4 * i + 1] = hi_bf16(w[0]);
+      x[db][4 * i + 2] = lo_bf16(w[1]);
+      x[db][4 * i + 3] = hi_bf16(w[1]);
+    }
+  float ss = 0.f, dot = 0.f;
+#pragma unroll
+  for (int db = 0; db < HB; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      // pair index 32 db + 8 (e >> 2) + 4 hh + (e & 3): both candidates as
+      // uniform loads of the argument block, then a per-lane select
+      const int p0 = 32 * db + 8 * (e >> 2) + (e & 3);
+      double f_lo = nb.turns[p0], f_hi = nb.turns[p0 + 4];
+      asm("" : "+s"(f_lo), "+s"(f_hi));
+      double turns = pos * (hh ? f_hi : f_lo);
+      turns -= rint(turns);
+      const float tf = (float)turns;
+      const float sn = __builtin_amdgcn_sinf(tf), cs = __builtin_amdgcn_cosf(tf);
+      const float ga = g[db][e], gb = g[db + HB][e];
+      const float na = ga * cs + gb * sn;  // rotation by -theta
+      const float nbv = gb * cs - ga * sn;
+      g[db][e] = na;
+      g[db + HB][e] = nbv;
+      ss += x[db][e] * x[db][e] + x[db + HB][e] * x[db + HB][e];
+      dot += na * x[db][e] + nbv * x[db + HB][e];
+    }
+  ss += shfl_xor(ss, 32);
+  dot += shfl_xor(dot, 32);
+  const float r2 = ss / (float)D + nb.eps;
+  const float g_r = nb.gain / sqrtf(r2);
+  const float coef = dot / ((float)D * r2);
+#pragma unroll
+  for (int db = 0; db < NB; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) g[db][e] = g_r * (g[db][e] - x[db][e] * coef);
+}
+
+template <int D, bool FUSE>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__restrict__ Q,
                                                           const uint16_t *__restrict__ K,
                                                           const uint16_t *__restrict__ V,
@@ -206,7 +272,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__rest
                                                           const float *__restrict__ lse2g,
                                                           const float *__restrict__ delta, uint16_t *__restrict__ dK,
                                                           uint16_t *__restrict__ dV, int B, int T, int H, int KV,
-                                                          int W, float scale) {
+                                                          int W, float scale, NormRopeBwd nb) {
   // Two separate LDS objects for the double buffer (Q | dO | lse2 | delta each),
   // so the compiler can tell the copy into one from the reads of the other.
   using Gm = Geom<D>;
@@ -352,14 +418,24 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__rest
   }
   if (!wave_active || key_lane >= T) return;
   const long long off = ((long long)b * T + key_lane) * kv_stride + (long long)kvh * D;
+  float kscale = scale;
+  if constexpr (FUSE) {
+#pragma unroll
+    for (int db = 0; db < Gm::kDBlocks; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) dkacc[db][e] *= scale;
+    const double pos = (double)((nb.pos_offset ? nb.pos_offset[b] : 0) + key_lane);
+    norm_rope_bwd_row<D>(dkacc, nb.x + off, pos, nb, hh);
+    kscale = 1.f;
+  }
 #pragma unroll
   for (int db = 0; db < Gm::kDBlocks; ++db)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int d = 32 * db + 8 * i + 4 * hh;
       u32x2 wk, wv;
-      wk[0] = pack_bf16x2(dkacc[db][4 * i + 0] * scale, dkacc[db][4 * i + 1] * scale);
-      wk[1] = pack_bf16x2(dkacc[db][4 * i + 2] * scale, dkacc[db][4 * i + 3] * scale);
+      wk[0] = pack_bf16x2(dkacc[db][4 * i + 0] * kscale, dkacc[db][4 * i + 1] * kscale);
+      wk[1] = pack_bf16x2(dkacc[db][4 * i + 2] * kscale, dkacc[db][4 * i + 3] * kscale);
       wv[0] = pack_bf16x2(dvacc[db][4 * i + 0], dvacc[db][4 * i + 1]);
       wv[1] = pack_bf16x2(dvacc[db][4 * i + 2], dvacc[db][4 * i + 3]);
       *(u32x2 *)(dK + off + d) = wk;
@@ -413,14 +489,15 @@ __device__ __forceinline__ void dq_mask_tile(f32x16 (&sacc)[2], int k0, int q_la
 // accumulators (K^T through transposing LDS reads).  Nothing is stored between
 // the stages, so the backward needs no O(T^2) workspace, and dS enters the dQ
 // product in fp32 precision (hi + lo).
-template <int D>
+template <int D, bool FUSE>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t *__restrict__ Q,
                                                         const uint16_t *__restrict__ K,
                                                         const uint16_t *__restrict__ V,
                                                         const uint16_t *__restrict__ dO,
                                                         const float *__restrict__ lse2g,
                                                         const float *__restrict__ ndelta, uint16_t *__restrict__ dQ,
-                                                        int B, int T, int H, int KV, int W, float scale) {
+                                                        int B, int T, int H, int KV, int W, float scale,
+                                                        NormRopeBwd nb) {
   using Gm = Geom<D>;
   constexpr int kSteps = Gm::kSteps;
   __shared__ __attribute__((aligned(1024))) char kb0[Gm::kTileBytes];
@@ -527,25 +604,35 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t *__restri
   }
 
   if (!wave_active || q_lane >= T) return;
-  uint16_t *dqp = dQ + ((long long)b * T + q_lane) * q_stride + (long long)h * D;
+  const long long qoff = ((long long)b * T + q_lane) * q_stride + (long long)h * D;
+  uint16_t *dqp = dQ + qoff;
+  float qscale = scale;
+  if constexpr (FUSE) {
+#pragma unroll
+    for (int db = 0; db < Gm::kDBlocks; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) dqacc[db][e] *= scale;
+    const double pos = (double)((nb.pos_offset ? nb.pos_offset[b] : 0) + q_lane);
+    norm_rope_bwd_row<D>(dqacc, nb.x + qoff, pos, nb, hh);
+    qscale = 1.f;
+  }
 #pragma unroll
   for (int db = 0; db < Gm::kDBlocks; ++db)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int d = 32 * db + 8 * i + 4 * hh;
       u32x2 w;
-      w[0] = pack_bf16x2(dqacc[db][4 * i + 0] * scale, dqacc[db][4 * i + 1] * scale);
-      w[1] = pack_bf16x2(dqacc[db][4 * i + 2] * scale, dqacc[db][4 * i + 3] * scale);
+      w[0] = pack_bf16x2(dqacc[db][4 * i + 0] * qscale, dqacc[db][4 * i + 1] * qscale);
+      w[1] = pack_bf16x2(dqacc[db][4 * i + 2] * qscale, dqacc[db][4 * i + 3] * qscale);
       *(u32x2 *)(dqp + d) = w;
     }
 }
 
-}  // namespace
 
-template <int D>
+template <int D, bool FUSE>
 hipError_t launch_bwd_kernels(const void *q, const void *k, const void *v, const void *o, const float *lse,
                               const void *dout, void *dq, void *dk, void *dv, void *workspace, const AttnShape &sh,
-                              int stages, hipStream_t s) {
+                              int stages, const NormRopeBwd &nq, const NormRopeBwd &nk, hipStream_t s) {
   const size_t row_bytes = bwd_row_bytes(sh.B, sh.T, sh.H);
   float *delta = (float *)workspace;
   float *lse2 = (float *)((char *)workspace + row_bytes);
@@ -560,21 +647,45 @@ hipError_t launch_bwd_kernels(const void *q, const void *k, const void *v, const
     hipLaunchKernelGGL(bwd_delta_kernel<D>, dim3((unsigned)dblocks), dim3(256), 0, s, (const uint16_t *)o,
                        (const uint16_t *)dout, lse, delta, lse2, sh.B, sh.T, sh.H);
   if (stages & kBwdDkDv)
-    hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)kvblocks), dim3(256), 0, s, (const uint16_t *)q,
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, FUSE>), dim3((unsigned)kvblocks), dim3(256), 0, s, (const uint16_t *)q,
                        (const uint16_t *)k, (const uint16_t *)v, (const uint16_t *)dout, lse2, delta, (uint16_t *)dk,
-                       (uint16_t *)dv, sh.B, sh.T, sh.H, sh.KV, sh.window, sh.scale);
+                       (uint16_t *)dv, sh.B, sh.T, sh.H, sh.KV, sh.window, sh.scale, nk);
   if (stages & kBwdDq)
-    hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)qblocks), dim3(256), 0, s, (const uint16_t *)q,
+    hipLaunchKernelGGL((bwd_dq_kernel<D, FUSE>), dim3((unsigned)qblocks), dim3(256), 0, s, (const uint16_t *)q,
                        (const uint16_t *)k, (const uint16_t *)v, (const uint16_t *)dout, lse2, delta, (uint16_t *)dq,
-                       sh.B, sh.T, sh.H, sh.KV, sh.window, sh.scale);
+                       sh.B, sh.T, sh.H, sh.KV, sh.window, sh.scale, nq);
   return hipGetLastError();
 }
+
+}  // namespace
 
 hipError_t launch_bwd_bf16(const void *q, const void *k, const void *v, const void *o, const float *lse,
                            const void *dout, void *dq, void *dk, void *dv, void *workspace, const AttnShape &sh,
                            int stages, hipStream_t s) {
-  if (sh.D == 64) return launch_bwd_kernels<64>(q, k, v, o, lse, dout, dq, dk, dv, workspace, sh, stages, s);
-  if (sh.D == 128) return launch_bwd_kernels<128>(q, k, v, o, lse, dout, dq, dk, dv, workspace, sh, stages, s);
+  const NormRopeBwd none{};
+  if (sh.D == 64)
+    return launch_bwd_kernels<64, false>(q, k, v, o, lse, dout, dq, dk, dv, workspace, sh, stages, none, none, s);
+  if (sh.D == 128)
+    return launch_bwd_kernels<128, false>(q, k, v, o, lse, dout, dq, dk, dv, workspace, sh, stages, none, none, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_bf16_qknorm_rope(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                                       const void *dout, const void *q_raw, const void *k_raw, void *dq, void *dk,
+                                       void *dv, void *workspace, const AttnShape &sh, const int32_t *pos_offset,
+                                       const double *inv_freq_host, float eps, float gain, hipStream_t s) {
+  NormRopeBwd nq{};
+  for (int j = 0; j < sh.D / 2; ++j) nq.turns[j] = inv_freq_host[j] / 6.283185307179586;
+  nq.pos_offset = pos_offset;
+  nq.eps = eps;
+  nq.gain = gain;
+  NormRopeBwd nk = nq;
+  nq.x = (const uint16_t *)q_raw;
+  nk.x = (const uint16_t *)k_raw;
+  if (sh.D == 64)
+    return launch_bwd_kernels<64, true>(q, k, v, o, lse, dout, dq, dk, dv, workspace, sh, kBwdAll, nq, nk, s);
+  if (sh.D == 128)
+    return launch_bwd_kernels<128, true>(q, k, v, o, lse, dout, dq, dk, dv, workspace, sh, kBwdAll, nq, nk, s);
   return hipErrorInvalidValue;
 }
 

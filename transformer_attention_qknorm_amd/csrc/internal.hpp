@@ -52,6 +52,13 @@ hipError_t launch_fwd_bf16_rows(const void *q, const void *k, const void *v, voi
 hipError_t launch_bwd_bf16(const void *q, const void *k, const void *v, const void *o,
                            const float *lse, const void *dout, void *dq, void *dk, void *dv,
                            void *workspace, const AttnShape &sh, int stages, hipStream_t s);
+// The full backward whose dq / dk are the gradients of the raw (pre-norm) q_raw /
+// k_raw: the dQ and dK/dV kernels carry their results back through QK-norm +
+// RoPE before storing them (q, k are the post-norm rows the forward used).
+hipError_t launch_bwd_bf16_qknorm_rope(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                                       const void *dout, const void *q_raw, const void *k_raw, void *dq, void *dk,
+                                       void *dv, void *workspace, const AttnShape &sh, const int32_t *pos_offset,
+                                       const double *inv_freq_host, float eps, float gain, hipStream_t s);
 
 // fp32 reference-precision kernels (head_dim 64 or 128).
 hipError_t launch_fwd_f32(const float *q, const float *k, const float *v, float *o, float *lse,

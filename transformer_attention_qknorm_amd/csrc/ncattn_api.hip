@@ -252,6 +252,7 @@ int bwd_common(const char *fn, int stages, const void *q, const void *k, const v
     return fail(NCATTN_EWORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
                 workspace == nullptr ? (size_t)0 : workspace_bytes);
   if (!aligned16(workspace)) return fail(NCATTN_EINVAL, "%s: workspace is not 16-byte aligned", fn);
+  if (stages == 0) return ok();  // validation only (the caller launches)
   window_left = effective_window(window_left, T);
   ncattn::AttnShape sh{B, T, n_head, n_kv_head, head_dim, window_left, resolve_scale(softmax_scale, head_dim)};
   hipError_t e =
@@ -267,6 +268,40 @@ int bwd_common(const char *fn, int stages, const void *q, const void *k, const v
 }  // namespace
 
 extern "C" {
+
+int ncattn_bwd_qknorm_rope(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                           const void *dout, const void *q_raw, const void *k_raw, const int32_t *pos_offset,
+                           float rope_base, float eps, float qk_gain, void *dq, void *dk, void *dv, int B, int T,
+                           int n_head, int n_kv_head, int head_dim, int window_left, int window_right,
+                           float softmax_scale, int dtype, void *workspace, size_t workspace_bytes, void *stream) {
+  const char *fn = "ncattn_bwd_qknorm_rope";
+  NC_PTR(q_raw, fn);
+  NC_PTR(k_raw, fn);
+  double inv_freq[64];
+  NC_TRY(check_qknorm(fn, B, T, n_head, n_kv_head, head_dim, pos_offset, rope_base, eps, qk_gain, dtype,
+                      inv_freq));
+  if (dq == q_raw || dq == k_raw || dk == q_raw || dk == k_raw || dv == q_raw || dv == k_raw)
+    return fail(NCATTN_EINVAL, "%s: gradients must not alias q_raw or k_raw", fn);
+  // every check of ncattn_bwd, with launching deferred to here
+  NC_TRY(bwd_common(fn, 0, q, k, v, o, lse, dout, dq, dk, dv, B, T, n_head, n_kv_head, head_dim, window_left,
+                    window_right, softmax_scale, dtype, workspace, workspace_bytes, stream));
+  window_left = effective_window(window_left, T);
+  ncattn::AttnShape sh{B, T, n_head, n_kv_head, head_dim, window_left, resolve_scale(softmax_scale, head_dim)};
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if (dtype == NCATTN_BF16) {
+    e = ncattn::launch_bwd_bf16_qknorm_rope(q, k, v, o, lse, dout, q_raw, k_raw, dq, dk, dv, workspace, sh,
+                                            pos_offset, inv_freq, eps, qk_gain, s);
+  } else {
+    e = ncattn::launch_bwd_f32((const float *)q, (const float *)k, (const float *)v, (const float *)o, lse,
+                               (const float *)dout, (float *)dq, (float *)dk, (float *)dv, (float *)workspace, sh,
+                               ncattn::kBwdAll, s);
+    if (e == hipSuccess)
+      e = ncattn::launch_qknorm_rope_bwd(dq, dk, q_raw, k_raw, B, T, n_head, n_kv_head, head_dim, pos_offset,
+                                         inv_freq, eps, qk_gain, false, s);
+  }
+  return hip_status(e, fn);
+}
 
 #define NC_BWD_ARGS                                                                                          \
   q, k, v, o, lse, dout, dq, dk, dv, B, T, n_head, n_kv_head, head_dim, window_left, window_right, softmax_scale, \
