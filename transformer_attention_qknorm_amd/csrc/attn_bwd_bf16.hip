@@ -11,11 +11,15 @@
 // Three kernels, no atomics (deterministic):
 //   1. bwd_delta: D_i per (b, h, i) into the workspace.
 //   2. bwd_dkdv: one workgroup per (b, kv head, 128-key block), wave w owns keys
-//      32w..32w+31 and keeps K, V for them in registers; it walks 64-row query
-//      tiles (Q, dO, LSE, D staged in LDS, double-buffered) for every query head of
-//      the group, computing S = Q K^T, dP = dO V^T (queries as MFMA rows, the
-//      wave's keys as columns), then dV^T += dO^T P and dK^T += Q^T dS with
-//      transposing LDS reads of dO and Q.
+//      32w..32w+31 and keeps K for them in registers, V of the block staged once
+//      in LDS; it walks 32-row query tiles (Q, dO, LSE, D staged in LDS,
+//      double-buffered) for every query head of the group, computing S = Q K^T,
+//      dP = dO V^T (queries as MFMA rows, the wave's keys as columns), then
+//      dV^T += dO^T P and dK^T += Q^T dS with transposing LDS reads of dO and Q.
+//      Sized for two workgroups per CU (at most 256 registers per wave, 67 KB of
+//      LDS at head_dim 128), so each SIMD runs waves of two workgroups that are
+//      not tied by a barrier: one's P/dS arithmetic runs beside the other's
+//      MFMAs.
 //   3. bwd_dq: one workgroup per (b, h, 128-row query block), like the forward:
 //      S^T = K Q^T and dP^T = V dO^T with Q, dO in registers, dQ^T += K^T dS^T.
 // Both contraction stages recompute S and dP; P and dS enter the dV, dK and dQ
@@ -30,10 +34,6 @@ namespace {
 
 constexpr int kBlockN = 128;  // keys per dkdv workgroup
 constexpr int kDqRows = 128;  // query rows per dq workgroup
-// VALU instructions placed after each MFMA where the P/dS arithmetic of one
-// query block runs under the MFMAs of the other (3 to 12 measured within noise)
-constexpr int kValuUnderSdP = 10;   // under the S/dP MFMAs of the second block
-constexpr int kValuUnderDkDv = 5;   // under the dV/dK MFMAs of the first block
 
 // ---------------------------------------------------------------- D_i = dO . O
 // Stores -D_i (the initial value of the dP - D accumulators of the dK/dV stage)
@@ -88,39 +88,6 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t *__restri
 }
 
 // ---------------------------------------------------------------- dK, dV
-template <int D>
-constexpr int kQBuf = 2 * Geom<D>::kTileBytes + 2 * kTileN * 4;  // Q tile, dO tile, lse2[64], delta[64]
-
-// S = Q K^T and dP - D = dO V^T - D for one 32-query block (rows 32 qb.. of the
-// staged tile) against this wave's 32 keys (queries as rows, the wave's keys as
-// columns).  The dP accumulator starts at -D of its query rows (staged next to
-// the tile), so it ends holding dP - D.
-template <int D>
-__device__ __forceinline__ void dkdv_sdp(f32x16 &sacc, f32x16 &dpacc, const char *qs, const char *dos,
-                                         const float *ndl, const TileLane<D> &L,
-                                         const bf16x8 (&kreg)[Geom<D>::kSteps],
-                                         const bf16x8 (&vreg)[Geom<D>::kSteps], int qb, int hh) {
-  constexpr int kSteps = Geom<D>::kSteps;
-  bf16x8 qa[kSteps], da[kSteps];
-#pragma unroll
-  for (int s = 0; s < kSteps; ++s) {
-    qa[s] = row_operand(qs, L, s, qb);
-    da[s] = row_operand(dos, L, s, qb);
-  }
-  sacc = f32x16{};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const f32x4 d4 = *(const f32x4 *)(ndl + 32 * qb + 8 * i + 4 * hh);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) dpacc[4 * i + j] = d4[j];
-  }
-#pragma unroll
-  for (int s = 0; s < kSteps; ++s) {
-    sacc = mfma32(qa[s], kreg[s], sacc);
-    dpacc = mfma32(da[s], vreg[s], dpacc);
-  }
-}
-
 // The bf16 value nearest x, and the bf16 value nearest the remainder: x is
 // carried into the dV and dK products as hi + lo, so those products see P and dS
 // to about 16 significant bits rather than bf16's 8 (only the final rounding of
@@ -184,17 +151,6 @@ __device__ __forceinline__ void dkdv_acc(f32x16 (&dkacc)[Geom<D>::kDBlocks], f32
       dvacc[db] = mfma32(a, pbl, dvacc[db]);
       dkacc[db] = mfma32(qa, dsl, dkacc[db]);
     }
-  }
-}
-
-// Interleave the next n MFMAs of the scheduling region with the vector ALU work
-// (k VALU instructions after each), so the matrix cores and the VALU run together.
-template <int N, int K>
-__device__ __forceinline__ void interleave_mfma_valu() {
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x002, K, 0);  // VALU
   }
 }
 
@@ -264,25 +220,68 @@ __device__ __forceinline__ void norm_rope_bwd_row(f32x16 (&g)[Geom<D>::kDBlocks]
     for (int e = 0; e < 16; ++e) g[db][e] = g_r * (g[db][e] - x[db][e] * coef);
 }
 
+// S = Q K^T and dP - D = dO V^T - D for the 32 query rows of block qb of the
+// staged tile against the wave's 32 keys (queries as rows, the wave's keys as
+// columns), with V^T read from the workgroup's V tile in LDS (key block kw).
+// The dP accumulator starts at -D of its query rows (staged next to the tile),
+// so it ends holding dP - D.  Operands are read two MFMA pairs ahead.
+template <int D>
+__device__ __forceinline__ void dkdv_sdp(f32x16 &sacc, f32x16 &dpacc, const char *qs, const char *dos,
+                                          const char *vs, const float *ndl, const TileLane<D> &L,
+                                          const bf16x8 (&kreg)[Geom<D>::kSteps], int qb, int kw, int hh) {
+  constexpr int kSteps = Geom<D>::kSteps;
+  constexpr int kAhead = 2;
+  bf16x8 qa[kSteps], da[kSteps], va[kSteps];
+#pragma unroll
+  for (int s = 0; s < kAhead; ++s) {
+    qa[s] = row_operand(qs, L, s, qb);
+    da[s] = row_operand(dos, L, s, qb);
+    va[s] = row_operand(vs, L, s, kw);
+  }
+  sacc = f32x16{};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f32x4 d4 = *(const f32x4 *)(ndl + 32 * qb + 8 * i + 4 * hh);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dpacc[4 * i + j] = d4[j];
+  }
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s) {
+    if (s + kAhead < kSteps) {
+      qa[s + kAhead] = row_operand(qs, L, s + kAhead, qb);
+      da[s + kAhead] = row_operand(dos, L, s + kAhead, qb);
+      va[s + kAhead] = row_operand(vs, L, s + kAhead, kw);
+    }
+    sacc = mfma32(qa[s], kreg[s], sacc);
+    dpacc = mfma32(da[s], va[s], dpacc);
+  }
+}
+
 template <int D, bool FUSE>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__restrict__ Q,
-                                                          const uint16_t *__restrict__ K,
-                                                          const uint16_t *__restrict__ V,
-                                                          const uint16_t *__restrict__ dO,
-                                                          const float *__restrict__ lse2g,
-                                                          const float *__restrict__ delta, uint16_t *__restrict__ dK,
-                                                          uint16_t *__restrict__ dV, int B, int T, int H, int KV,
-                                                          int W, float scale, NormRopeBwd nb) {
-  // Two separate LDS objects for the double buffer (Q | dO | lse2 | delta each),
-  // so the compiler can tell the copy into one from the reads of the other.
+__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t *__restrict__ Q,
+                                                        const uint16_t *__restrict__ K,
+                                                        const uint16_t *__restrict__ V,
+                                                        const uint16_t *__restrict__ dO,
+                                                        const float *__restrict__ lse2g,
+                                                        const float *__restrict__ delta, uint16_t *__restrict__ dK,
+                                                        uint16_t *__restrict__ dV, int B, int T, int H, int KV,
+                                                        int W, float scale, NormRopeBwd nb) {
   using Gm = Geom<D>;
   constexpr int kSteps = Gm::kSteps;
   constexpr int kTileBytes = Gm::kTileBytes;
-  __shared__ __attribute__((aligned(1024))) char buf0[kQBuf<D>];
-  __shared__ __attribute__((aligned(1024))) char buf1[kQBuf<D>];
+  // Q | dO | lse2 | delta of 32 query rows, double-buffered in two LDS objects
+  // (so the compiler can tell the copy into one from the reads of the other),
+  // and V of the block's 128 keys
+  constexpr int kR = 32;  // query rows per staged tile
+  constexpr int kHalfTile = kR * Gm::kRowBytes;
+  constexpr int kBuf = 2 * kHalfTile + 2 * 64 * 4;
+  __shared__ __attribute__((aligned(1024))) char buf0[kBuf];
+  __shared__ __attribute__((aligned(1024))) char buf1[kBuf];
+  __shared__ __attribute__((aligned(1024))) char vtile[kBlockN * Gm::kRowBytes];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int kw = wave;        // key sub-block (32 keys) of this wave
   const int hh = lane >> 5;
   const int G = H / KV;
   // key blocks near the start of the sequence see the most queries: launched
@@ -294,23 +293,20 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__rest
   const int b = bk / KV;
   const int kvh = bk % KV;
   const int k0 = kblk * kBlockN;
-  const int kw0 = k0 + 32 * wave;
-  const int key_lane = kw0 + (lane & 31);  // the key column this lane holds
+  const int kw0 = k0 + 32 * kw;
+  const int key_lane = kw0 + (lane & 31);
   const float c = scale * kLog2e;
 
   const long long q_stride = (long long)H * D;
   const long long kv_stride = (long long)KV * D;
   const int voff = tile_lane_voff<D>((int)(q_stride * 2), tid);
 
-  // Query tiles that can see any key of the block, times the G heads of the group.
   const int k_last_blk = min(k0 + kBlockN - 1, T - 1);
   const int q_hi = W < 0 ? T - 1 : min(T - 1, k_last_blk + W);
-  const int qt0 = k0 / kTileN;
-  const int nq = q_hi / kTileN - qt0 + 1;
+  const int qt0 = k0 / kR;
+  const int nq = q_hi / kR - qt0 + 1;
   const int n_iter = nq * G;
 
-  // Step order: query tile qt (outer) x head h = kvh G + g (inner), tracked
-  // incrementally (no division by G per step).
   struct Pos {
     int qt, g;
   };
@@ -321,33 +317,36 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__rest
     }
     return p;
   };
-  const long long qbase = (long long)b * T * q_stride + (long long)kvh * G * D;  // q/dO of (b, head kvh G)
-  const long long rbase = ((long long)b * H + (long long)kvh * G) * T;         // its lse / delta row
+  const long long qbase = (long long)b * T * q_stride + (long long)kvh * G * D;
+  const long long rbase = ((long long)b * H + (long long)kvh * G) * T;
 
   auto stage = [&](const Pos &p, char *base) {
     const long long hoff = qbase + (long long)p.g * D;
-    tile_load_lds<D>(base, make_tile_src(Q + hoff, q_stride, T), voff, p.qt * kTileN);
-    tile_load_lds<D>(base + kTileBytes, make_tile_src(dO + hoff, q_stride, T), voff, p.qt * kTileN);
+    tile_load_lds<D, 4, kR>(base, make_tile_src(Q + hoff, q_stride, T), voff, p.qt * kR);
+    tile_load_lds<D, 4, kR>(base + kHalfTile, make_tile_src(dO + hoff, q_stride, T), voff, p.qt * kR);
     if (wave < 2) {  // waves 0, 1: 64 lse rows and 64 delta rows, 4 bytes per lane (zeros past T)
       const float *row = (wave == 0 ? lse2g : delta) + rbase + (long long)p.g * T;
       const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void *)row, (short)0, T * 4, 0x00020000);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(base + 2 * kTileBytes + wave * kTileN * 4), 4,
-                                               lane * 4, p.qt * kTileN * 4, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(base + 2 * kHalfTile + wave * 64 * 4), 4,
+                                               lane * 4, p.qt * kR * 4, 0, 0);
     }
   };
 
+  {  // V of the block's 128 keys, rows past T as zeros
+    const TileSrc vsrc = make_tile_src(V + (long long)b * T * kv_stride + (long long)kvh * D, kv_stride, T);
+    const int vvoff = tile_lane_voff<D>(vsrc.stride, tid);
+    tile_load_lds<D, 4>(vtile, vsrc, vvoff, k0);
+    tile_load_lds<D, 4>(vtile + kTileBytes, vsrc, vvoff, k0 + kTileN);
+  }
   Pos pos{qt0, 0};
   stage(pos, buf0);
 
-  bf16x8 kreg[kSteps], vreg[kSteps];
+  bf16x8 kreg[kSteps];
   {
     const int kr = min(key_lane, T - 1);
     const long long off = ((long long)b * T + kr) * kv_stride + (long long)kvh * D + 8 * hh;
 #pragma unroll
-    for (int s = 0; s < kSteps; ++s) {
-      kreg[s] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(K + off + 16 * s));
-      vreg[s] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(V + off + 16 * s));
-    }
+    for (int s = 0; s < kSteps; ++s) kreg[s] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(K + off + 16 * s));
   }
   const TileLane<D> L = make_tile_lane<D>(lane);
   const int kw_last = min(kw0 + 31, T - 1);
@@ -364,50 +363,21 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__rest
 
   auto step = [&](char *cur, char *nxt, int it) {
     const char *qs = cur;
-    const char *dos = cur + kTileBytes;
-    const float *lse2 = (const float *)(cur + 2 * kTileBytes);
-    const float *ndl = lse2 + kTileN;
+    const char *dos = cur + kHalfTile;
+    const float *lse2 = (const float *)(cur + 2 * kHalfTile);
+    const float *ndl = lse2 + 64;
     const Pos p = pos;
     pos = advance(pos);
     if (it + 1 < n_iter) stage(pos, nxt);
-    const int qtile0 = p.qt * kTileN;
-    const bool skip = !wave_active || qtile0 + kTileN - 1 < kw0 || (W >= 0 && qtile0 - kw_last > W);
-    if (!skip) {
-      bool act[2], msk[2];
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const int qr0 = qtile0 + 32 * qb;
-        act[qb] = !(qr0 + 31 < kw0 || (W >= 0 && qr0 - kw_last > W));
-        msk[qb] = !(qr0 >= kw_last && (W < 0 || qr0 + 31 - kw0 <= W) && qr0 + 31 < T);
-      }
-      if (act[0] && act[1] && !msk[0] && !msk[1]) {
-        // steady state, one straight-line block: the S/dP MFMAs of query block 1
-        // run under the P/dS arithmetic of block 0, and the dV/dK MFMAs of block
-        // 0 under that of block 1
-        f32x16 s0, p0, s1, p1;
-        uint32_t pk0[8], pl0[8], dk0[8], dl0[8], pk1[8], pl1[8], dk1[8], dl1[8];
-        dkdv_sdp(s0, p0, qs, dos, ndl, L, kreg, vreg, 0, hh);
-        __builtin_amdgcn_sched_barrier(0);
-        dkdv_sdp(s1, p1, qs, dos, ndl, L, kreg, vreg, 1, hh);
-        dkdv_p_ds(s0, p0, lse2, false, 0, qtile0, key_lane, T, W, c, hh, pk0, pl0, dk0, dl0);
-        interleave_mfma_valu<2 * kSteps, kValuUnderSdP>();
-        __builtin_amdgcn_sched_barrier(0);
-        dkdv_acc(dkacc, dvacc, pk0, pl0, dk0, dl0, qs, dos, L, 0);
-        dkdv_p_ds(s1, p1, lse2, false, 1, qtile0, key_lane, T, W, c, hh, pk1, pl1, dk1, dl1);
-        interleave_mfma_valu<8 * Gm::kDBlocks, kValuUnderDkDv>();
-        __builtin_amdgcn_sched_barrier(0);
-        dkdv_acc(dkacc, dvacc, pk1, pl1, dk1, dl1, qs, dos, L, 1);
-      } else {
-#pragma unroll 1
-        for (int qb = 0; qb < 2; ++qb) {
-          if (!act[qb]) continue;
-          f32x16 s0, p0;
-          uint32_t pk0[8], pl0[8], dk0[8], dl0[8];
-          dkdv_sdp(s0, p0, qs, dos, ndl, L, kreg, vreg, qb, hh);
-          dkdv_p_ds(s0, p0, lse2, msk[qb], qb, qtile0, key_lane, T, W, c, hh, pk0, pl0, dk0, dl0);
-          dkdv_acc(dkacc, dvacc, pk0, pl0, dk0, dl0, qs, dos, L, qb);
-        }
-      }
+    const int qr0 = p.qt * kR;
+    const bool act = wave_active && !(qr0 + 31 < kw0 || (W >= 0 && qr0 - kw_last > W));
+    if (act) {
+      const bool msk = !(qr0 >= kw_last && (W < 0 || qr0 + 31 - kw0 <= W) && qr0 + 31 < T);
+      f32x16 s0, p0;
+      uint32_t pk0[8], pl0[8], dk0[8], dl0[8];
+      dkdv_sdp<D>(s0, p0, qs, dos, vtile, ndl, L, kreg, 0, kw, hh);
+      dkdv_p_ds(s0, p0, lse2, msk, 0, qr0, key_lane, T, W, c, hh, pk0, pl0, dk0, dl0);
+      dkdv_acc<D>(dkacc, dvacc, pk0, pl0, dk0, dl0, qs, dos, L, 0);
     }
     lds_loads_done_barrier();
   };
@@ -416,6 +386,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__rest
     if (it + 1 >= n_iter) break;
     step(buf1, buf0, it + 1);
   }
+
   if (!wave_active || key_lane >= T) return;
   const long long off = ((long long)b * T + key_lane) * kv_stride + (long long)kvh * D;
   float kscale = scale;
@@ -424,8 +395,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t *__rest
     for (int db = 0; db < Gm::kDBlocks; ++db)
 #pragma unroll
       for (int e = 0; e < 16; ++e) dkacc[db][e] *= scale;
-    const double pos = (double)((nb.pos_offset ? nb.pos_offset[b] : 0) + key_lane);
-    norm_rope_bwd_row<D>(dkacc, nb.x + off, pos, nb, hh);
+    const double posd = (double)((nb.pos_offset ? nb.pos_offset[b] : 0) + key_lane);
+    norm_rope_bwd_row<D>(dkacc, nb.x + off, posd, nb, hh);
     kscale = 1.f;
   }
 #pragma unroll

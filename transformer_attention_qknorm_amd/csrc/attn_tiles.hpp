@@ -89,13 +89,14 @@ __device__ __forceinline__ int tile_lane_voff(int row_stride_bytes, int tid) {
   return lane_row * row_stride_bytes + (((lane % Gm::kChunks) ^ swz_f<D>(lane_row)) << 4);
 }
 
-template <int D, int NW = 4>
+template <int D, int NW = 4, int ROWS = kTileN>
 __device__ __forceinline__ void tile_load_lds(char *lds_tile, const TileSrc &src, int voff, int row0) {
   using Gm = Geom<D>;
   constexpr int kRowsPerRound = Gm::kCopyRows * NW;
+  static_assert(ROWS % kRowsPerRound == 0, "whole copy rounds");
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
-  for (int i = 0; i < kTileN / kRowsPerRound; ++i)
+  for (int i = 0; i < ROWS / kRowsPerRound; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(src.rsrc,
                                              (lds_void *)(lds_tile + (kRowsPerRound * i + Gm::kCopyRows * w) *
                                                                          Gm::kRowBytes),
