@@ -299,7 +299,7 @@ def qknorm_detail(nc, torch, cfg, dev, stream):
     do = do0.to(dev)
     del do0
     qn, kn = q.clone(), k.clone()
-    nc.qknorm_rope_(qn, kn, None, rope_base=base, eps=1e-6)
+    _, _, rstd = nc.qknorm_rope_rstd_(qn, kn, None, rope_base=base, eps=1e-6)
     ws = nc.bwd_workspace(q, k, (-1, 0))
     gq, gk, gv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     fb = {}
@@ -311,7 +311,7 @@ def qknorm_detail(nc, torch, cfg, dev, stream):
             nc.qknorm_rope_bwd_(gq, gk, q, k, None, rope_base=base, eps=1e-6)
 
         def one_call_bwd():
-            nc.bwd_qknorm_rope(qn, kn, v, o, lse, do, q, k, None, rope_base=base, eps=1e-6, window=(W, 0),
+            nc.bwd_qknorm_rope(qn, kn, v, o, lse, do, rstd, None, rope_base=base, window=(W, 0),
                                out=(gq, gk, gv), workspace=ws)
         t2 = event_us(torch, stream, two_calls_bwd, 20)
         t1 = event_us(torch, stream, one_call_bwd, 20)
@@ -319,7 +319,7 @@ def qknorm_detail(nc, torch, cfg, dev, stream):
         fb["full" if W < 0 else f"w{W}"] = {"two_calls_us": round(t2, 2), "fused_us": round(t1, 2),
                                             "fused_bwd_TFLOPs": round(fl / (t1 * 1e-6) / 1e12, 1)}
     out["bwd_qknorm_rope"] = fb
-    del q, k, v, dq, dk, o, lse, do, qn, kn, ws, gq, gk, gv
+    del q, k, v, dq, dk, o, lse, do, qn, kn, ws, gq, gk, gv, rstd
     torch.cuda.empty_cache()
     return out
 

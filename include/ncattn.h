@@ -81,6 +81,18 @@ int ncattn_qknorm_rope(void *q, void *k, int B, int T, int n_head, int n_kv_head
                        int dtype, void *stream);
 
 /*
+ * ncattn_qknorm_rope that also stores each row's 1/r = 1/sqrt(mean_d(x_d^2) + eps)
+ * in fp32 (the statistic a backward needs besides the outputs, so that the raw
+ * q and k need not be kept; "nanochat Admin & Developer Guide", section 3).
+ *   rstd [B][T][n_head + n_kv_head] fp32, written: q rows at [b][t][h], k rows at
+ *   [b][t][n_head + kv head]; 4-byte aligned, not NULL.
+ *   Everything else as ncattn_qknorm_rope (same q, k results, bit for bit).
+ */
+int ncattn_qknorm_rope_rstd(void *q, void *k, float *rstd, int B, int T, int n_head, int n_kv_head,
+                            int head_dim, const int32_t *pos_offset, float rope_base, float eps, float qk_gain,
+                            int dtype, void *stream);
+
+/*
  * Backward of ncattn_qknorm_rope ("nanochat (Python)" catalog, Backward pass:
  * autograd of the forward; the forward is section 3 of the nanochat Admin &
  * Developer Guide).  With n = g x / r, r = sqrt(mean_d(x_d^2) + eps), y = R(pos) n:
@@ -121,14 +133,15 @@ int ncattn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
  * by a separate pass, which saves the separate read and write of q; for fp32 the
  * two calls run one after the other.
  *   q [B][T][n_head][D], k [B][T][n_kv_head][D]: raw on entry, normalised and
- *   rotated on return; v, o, lse as ncattn_fwd; pos_offset, rope_base, eps and
- *   qk_gain as ncattn_qknorm_rope; window and scale as ncattn_fwd.  o and v must
- *   not alias q, k or each other.  Validation and status codes as the two calls.
+ *   rotated on return; v, o, lse as ncattn_fwd; rstd NULL, or each row's 1/r as
+ *   ncattn_qknorm_rope_rstd writes it; pos_offset, rope_base, eps and qk_gain as
+ *   ncattn_qknorm_rope; window and scale as ncattn_fwd.  o and v must not alias
+ *   q, k or each other.  Validation and status codes as the two calls.
  */
-int ncattn_fwd_qknorm_rope(void *q, void *k, const void *v, void *o, float *lse, int B, int T, int n_head,
-                           int n_kv_head, int head_dim, const int32_t *pos_offset, float rope_base, float eps,
-                           float qk_gain, int window_left, int window_right, float softmax_scale, int dtype,
-                           void *stream);
+int ncattn_fwd_qknorm_rope(void *q, void *k, const void *v, void *o, float *lse, float *rstd, int B, int T,
+                           int n_head, int n_kv_head, int head_dim, const int32_t *pos_offset, float rope_base,
+                           float eps, float qk_gain, int window_left, int window_right, float softmax_scale,
+                           int dtype, void *stream);
 
 /*
  * Bytes of workspace ncattn_bwd needs for this shape: the per-row fp32
@@ -190,23 +203,25 @@ int ncattn_bwd_dq(const void *q, const void *k, const void *v, const void *o, co
  * QK-norm + RoPE ("nanochat Admin & Developer Guide", section 3: weightless
  * RMSNorm of q and k, then rotary embedding; "nanochat (Python)" catalog,
  * Backward pass: the chain rule through that forward) before they are stored.
- *   q, k: the post-norm rows the forward attended with (ncattn_qknorm_rope's
- *   output); q_raw [B][T][n_head][D], k_raw [B][T][n_kv_head][D]: its inputs,
- *   before normalisation (the caller keeps them); pos_offset, rope_base, eps,
- *   qk_gain as given to ncattn_qknorm_rope; the rest as ncattn_bwd.
- *   Outputs: dq = d/dq_raw, dk = d/dk_raw (dtype), dv as ncattn_bwd.  Equal to
- *   ncattn_bwd followed by ncattn_qknorm_rope_bwd, except that for bf16 the norm's
- *   backward is applied to the fp32 gradients before their rounding to bf16
- *   (one rounding instead of two) and dq, dk of the post-norm rows are never
- *   written to memory.  dq / dk must not alias q, k, q_raw or k_raw.
- *   workspace: ncattn_bwd_workspace_bytes(...) bytes.  bf16: head_dim 64 or 128;
- *   fp32 (head_dim 64 or 128): the two calls in sequence.
+ * With y = R(pos) g x / r the forward's output row:
+ *     dx = (g / r) R(pos)^T (dy - y sum_d(dy_d y_d) / (g^2 D))
+ * which is ncattn_qknorm_rope_bwd's dx written with y and 1/r in place of x.
+ *   q, k: the post-norm rows the forward attended with (ncattn_qknorm_rope_rstd's
+ *   or ncattn_fwd_qknorm_rope's output); rstd: their 1/r as those calls store it
+ *   ([B][T][n_head + n_kv_head] fp32); pos_offset, rope_base, qk_gain as given to
+ *   the forward; the rest as ncattn_bwd.  The raw q and k are not needed.
+ *   Outputs: dq = d/dq_raw, dk = d/dk_raw (dtype), dv as ncattn_bwd.  For bf16
+ *   the norm's backward is applied to the fp32 gradients in the dQ and dK/dV
+ *   kernels' epilogues, before the one rounding to bf16, and dq, dk of the
+ *   post-norm rows are never written to memory; for fp32 (head_dim 64 or 128)
+ *   ncattn_bwd runs, then the norm's backward in place.  dq, dk, dv must not
+ *   alias any input.  workspace: ncattn_bwd_workspace_bytes(...) bytes.
  */
 int ncattn_bwd_qknorm_rope(const void *q, const void *k, const void *v, const void *o, const float *lse,
-                           const void *dout, const void *q_raw, const void *k_raw, const int32_t *pos_offset,
-                           float rope_base, float eps, float qk_gain, void *dq, void *dk, void *dv, int B, int T,
-                           int n_head, int n_kv_head, int head_dim, int window_left, int window_right,
-                           float softmax_scale, int dtype, void *workspace, size_t workspace_bytes, void *stream);
+                           const void *dout, const float *rstd, const int32_t *pos_offset, float rope_base,
+                           float qk_gain, void *dq, void *dk, void *dv, int B, int T, int n_head, int n_kv_head,
+                           int head_dim, int window_left, int window_right, float softmax_scale, int dtype,
+                           void *workspace, size_t workspace_bytes, void *stream);
 
 /* Bytes of workspace ncattn_decode needs (split-KV partial results). */
 size_t ncattn_decode_workspace_bytes(int B, int T_max, int n_head, int n_kv_head, int head_dim,

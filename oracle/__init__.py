@@ -19,6 +19,7 @@ the kernels against this oracle is pinned.
 
 from .attention import (  # noqa: F401
     rms_norm,
+    rms_rstd,
     rope_angles,
     apply_rope,
     qknorm_rope,

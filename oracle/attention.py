@@ -66,6 +66,15 @@ def rms_norm(x, eps=1e-6, gain=1.0):
     return gain * x / np.sqrt(ms + eps)
 
 
+def rms_rstd(x, eps=1e-6):
+    """1 / sqrt(mean(x^2) + eps) of each row (last axis), the reciprocal RMS that
+    weightless RMSNorm divides by (section 3 of the nanochat Admin & Developer
+    Guide); the per-row statistic the QK-norm forward can store for its backward.
+    Returns shape x.shape[:-1]."""
+    x = np.asarray(x, dtype=np.float64)
+    return 1.0 / np.sqrt(np.mean(x * x, axis=-1) + eps)
+
+
 def rope_angles(pos, head_dim, base):
     """theta[p, j] = pos[p] * base ** (-2 j / head_dim), j < head_dim / 2 (float64)."""
     pos = np.asarray(pos, dtype=np.float64)

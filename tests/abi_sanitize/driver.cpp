@@ -92,11 +92,21 @@ static void test_qknorm() {
         NCATTN_EINVAL);
   CHECK(ncattn_qknorm_rope_bwd(P(0), P(1), P(2), P(3), 1, 4, 2, 2, 64, nullptr, 1e5f, 1e-6f, 1.f, 1, nullptr) ==
         NCATTN_OK);
-  CHECK(ncattn_fwd_qknorm_rope(P(0), P(0), P(2), P(3), F(4), 1, 4, 2, 2, 128, nullptr, 1e5f, 1e-6f, 1.f, -1, 0, 0,
-                               0, nullptr) == NCATTN_EINVAL);
-  CHECK(ncattn_fwd_qknorm_rope(P(0), P(1), P(2), P(3), F(4), 1, 40, 2, 2, 64, nullptr, 1e5f, 1e-6f, 1.f, INT_MAX, 0,
-                               0, 0, nullptr) == NCATTN_OK);
+  CHECK(ncattn_fwd_qknorm_rope(P(0), P(0), P(2), P(3), F(4), nullptr, 1, 4, 2, 2, 128, nullptr, 1e5f, 1e-6f, 1.f,
+                               -1, 0, 0, 0, nullptr) == NCATTN_EINVAL);
+  CHECK(ncattn_fwd_qknorm_rope(P(0), P(1), P(2), P(3), F(4), (float *)MIS(5), 1, 4, 2, 2, 128, nullptr, 1e5f, 1e-6f,
+                               1.f, -1, 0, 0, 0, nullptr) == NCATTN_EINVAL);
+  CHECK(ncattn_fwd_qknorm_rope(P(0), P(1), P(2), P(3), F(4), F(5), 1, 40, 2, 2, 64, nullptr, 1e5f, 1e-6f, 1.f,
+                               INT_MAX, 0, 0, 0, nullptr) == NCATTN_OK);
   CHECK(strcmp(g_last.fn, "fwd_bf16_qknorm_rope") == 0 && g_last.window == -1);
+  // the variant that also stores 1/r per row
+  CHECK(ncattn_qknorm_rope_rstd(P(0), P(1), nullptr, 1, 4, 2, 2, 128, nullptr, 1e5f, 1e-6f, 1.f, 0, nullptr) ==
+        NCATTN_EINVAL);
+  CHECK(ncattn_qknorm_rope_rstd(P(0), P(1), (float *)MIS(2), 1, 4, 2, 2, 128, nullptr, 1e5f, 1e-6f, 1.f, 0,
+                                nullptr) == NCATTN_EINVAL);
+  CHECK(ncattn_qknorm_rope_rstd(P(0), P(1), F(2), 1, 4, 6, 2, 128, nullptr, 1e5f, 1e-6f, 1.f, 0, nullptr) ==
+        NCATTN_OK);
+  CHECK(strcmp(g_last.fn, "qknorm_rope") == 0 && g_last.T_max == 8 && g_last.stages == 6);  // stride, k offset
 }
 
 static int bwd(int (*f)(const void *, const void *, const void *, const void *, const float *, const void *, void *,
@@ -137,25 +147,26 @@ static void test_bwd() {
 
   // the fused QK-norm + RoPE backward: the backward's checks, the norm's, and
   // no gradient aliasing the raw rows
-  auto fb = [&](const void *qr, const void *kr, void *dq, float base, int D, int wl, int dt, void *ws, size_t wsb) {
-    return ncattn_bwd_qknorm_rope(P(0), P(1), P(2), P(3), F(4), P(5), qr, kr, nullptr, base, 1e-6f, 1.f, dq, P(7),
-                                  P(8), 2, 300, 4, 2, D, wl, 0, 0.f, dt, ws, wsb, nullptr);
+  auto fb = [&](const void *rs, void *dq, float base, int D, int wl, int dt, void *ws, size_t wsb) {
+    return ncattn_bwd_qknorm_rope(P(0), P(1), P(2), P(3), F(4), P(5), (const float *)rs, nullptr, base, 1.f, dq,
+                                  P(7), P(8), 2, 300, 4, 2, D, wl, 0, 0.f, dt, ws, wsb, nullptr);
   };
-  CHECK(fb(nullptr, P(11), P(6), 1e5f, 128, -1, NCATTN_BF16, P(9), need) == NCATTN_EINVAL);
-  CHECK(fb(P(10), MIS(11), P(6), 1e5f, 128, -1, NCATTN_BF16, P(9), need) == NCATTN_EINVAL);
-  CHECK(fb(P(10), P(11), P(10), 1e5f, 128, -1, NCATTN_BF16, P(9), need) == NCATTN_EINVAL);   // dq aliases q_raw
-  CHECK(fb(P(10), P(11), P(0), 1e5f, 128, -1, NCATTN_BF16, P(9), need) == NCATTN_EINVAL);    // dq aliases q
-  CHECK(fb(P(10), P(11), P(6), 0.5f, 128, -1, NCATTN_BF16, P(9), need) == NCATTN_EINVAL);    // rope base
-  CHECK(fb(P(10), P(11), P(6), 1e5f, 96, -1, NCATTN_BF16, P(9), need) == NCATTN_EUNSUPPORTED);
-  CHECK(fb(P(10), P(11), P(6), 1e5f, 128, -1, NCATTN_BF16, P(9), need - 1) == NCATTN_EWORKSPACE);
+  CHECK(fb(nullptr, P(6), 1e5f, 128, -1, NCATTN_BF16, P(9), need) == NCATTN_EINVAL);
+  CHECK(fb(MIS(10), P(6), 1e5f, 128, -1, NCATTN_BF16, P(9), need) == NCATTN_EINVAL);
+  CHECK(fb(P(10), P(10), 1e5f, 128, -1, NCATTN_BF16, P(9), need) == NCATTN_EINVAL);   // dq aliases rstd
+  CHECK(fb(P(10), P(0), 1e5f, 128, -1, NCATTN_BF16, P(9), need) == NCATTN_EINVAL);    // dq aliases q
+  CHECK(fb(P(10), P(6), 0.5f, 128, -1, NCATTN_BF16, P(9), need) == NCATTN_EINVAL);    // rope base
+  CHECK(fb(P(10), P(6), 1e5f, 96, -1, NCATTN_BF16, P(9), need) == NCATTN_EUNSUPPORTED);
+  CHECK(fb(P(10), P(6), 1e5f, 128, -1, NCATTN_BF16, P(9), need - 1) == NCATTN_EWORKSPACE);
   const long before = g_last.count;
-  CHECK(fb(P(10), P(11), P(6), 1e5f, 128, -2, NCATTN_BF16, P(9), need) == NCATTN_EINVAL);
+  CHECK(fb(P(10), P(6), 1e5f, 128, -2, NCATTN_BF16, P(9), need) == NCATTN_EINVAL);
   CHECK(g_last.count == before);  // nothing launched on a refusal
-  CHECK(fb(P(10), P(11), P(6), 1e5f, 64, INT_MAX, NCATTN_BF16, P(9), need) == NCATTN_OK);
+  CHECK(fb(P(10), P(6), 1e5f, 64, INT_MAX, NCATTN_BF16, P(9), need) == NCATTN_OK);
   CHECK(strcmp(g_last.fn, "bwd_bf16_qknorm_rope") == 0 && g_last.window == -1 && g_last.D == 64);
   CHECK(g_last.stages == (int)(pow(1e5, -2.0 * 31 / 64) * 1e9));
-  CHECK(fb(P(10), P(11), P(6), 1e5f, 128, 5, NCATTN_F32, P(9), need) == NCATTN_OK);
+  CHECK(fb(P(10), P(6), 1e5f, 128, 5, NCATTN_F32, P(9), need) == NCATTN_OK);
   CHECK(strcmp(g_last.fn, "qknorm_rope_bwd") == 0 && g_last.count == before + 3);  // bwd_f32, then the norm's
+  CHECK(g_last.T_max == 6 && g_last.stages == 4);  // from y: 1/r with stride n_head + n_kv_head, k rows after q
 }
 
 static int dec(bool noalloc, int B, int Tm, int H, int KV, int D, int wl, int dt, void *ws, size_t wsb,

@@ -25,14 +25,19 @@ extern "C" const char *hipGetErrorString(hipError_t) { return "stub HIP error"; 
 namespace ncattn {
 
 hipError_t launch_qknorm_rope(void *, void *, int B, int T, int H, int KV, int D, const int32_t *, const double *inv,
-                              float, float, bool, hipStream_t) {
+                              float, float, bool, hipStream_t, float *rstd, long long rstd_stride, int rstd_k_off) {
   rec("qknorm_rope", B, T, H, KV, D, 0, (float)inv[D / 2 - 1]);
+  g_last.T_max = rstd ? (int)rstd_stride : -1;  // the 1/r layout, if any
+  g_last.stages = rstd ? rstd_k_off : -1;
   return hipSuccess;
 }
 
 hipError_t launch_qknorm_rope_bwd(void *, void *, const void *, const void *, int B, int T, int H, int KV, int D,
-                                  const int32_t *, const double *inv, float, float, bool, hipStream_t) {
+                                  const int32_t *, const double *inv, float, float, bool, hipStream_t,
+                                  const float *rstd, long long rstd_stride, int rstd_k_off) {
   rec("qknorm_rope_bwd", B, T, H, KV, D, 0, (float)inv[D / 2 - 1]);
+  g_last.T_max = rstd ? (int)rstd_stride : -1;
+  g_last.stages = rstd ? rstd_k_off : -1;
   return hipSuccess;
 }
 
@@ -43,7 +48,8 @@ hipError_t launch_fwd_bf16(const void *, const void *, const void *, void *, flo
 }
 
 hipError_t launch_fwd_bf16_qknorm_rope(void *, const void *, const void *, void *, float *, const AttnShape &sh,
-                                       const int32_t *, const double *, float, float, hipStream_t) {
+                                       const int32_t *, const double *, float, float, hipStream_t, float *,
+                                       long long) {
   rec("fwd_bf16_qknorm_rope", sh.B, sh.T, sh.H, sh.KV, sh.D, sh.window, sh.scale);
   return hipSuccess;
 }
@@ -62,8 +68,8 @@ hipError_t launch_bwd_bf16(const void *, const void *, const void *, const void 
 }
 
 hipError_t launch_bwd_bf16_qknorm_rope(const void *, const void *, const void *, const void *, const float *,
-                                       const void *, const void *, const void *, void *, void *, void *, void *,
-                                       const AttnShape &sh, const int32_t *, const double *inv, float, float,
+                                       const void *, const float *, void *, void *, void *, void *,
+                                       const AttnShape &sh, const int32_t *, const double *inv, float,
                                        hipStream_t) {
   rec("bwd_bf16_qknorm_rope", sh.B, sh.T, sh.H, sh.KV, sh.D, sh.window, sh.scale);
   g_last.stages = (int)(inv[sh.D / 2 - 1] * 1e9);

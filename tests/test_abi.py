@@ -93,11 +93,12 @@ def test_fwd_validation(L):
 
 def test_fwd_qknorm_rope_validation(L):
     f = L.ncattn_fwd_qknorm_rope
-    def call(q=P, k=P + 16, v=P + 32, o=P + 48, lse=P + 64, B=1, T=4, H=2, KV=2, D=128, pos=None, base=1e5,
-             eps=1e-6, gain=1.0, wl=-1, wr=0, scale=0.0, dt=0):
-        return f(q, k, v, o, lse, B, T, H, KV, D, pos, base, eps, gain, wl, wr, scale, dt, None)
+    def call(q=P, k=P + 16, v=P + 32, o=P + 48, lse=P + 64, rstd=None, B=1, T=4, H=2, KV=2, D=128, pos=None,
+             base=1e5, eps=1e-6, gain=1.0, wl=-1, wr=0, scale=0.0, dt=0):
+        return f(q, k, v, o, lse, rstd, B, T, H, KV, D, pos, base, eps, gain, wl, wr, scale, dt, None)
     assert call(q=None) == EINVAL
     assert call(lse=MIS) == EINVAL
+    assert call(rstd=P + 2) == EINVAL         # rstd misaligned
     assert call(k=P) == EINVAL                # q and k must be distinct
     assert call(o=P + 16) == EINVAL           # o aliases k
     assert call(v=P) == EINVAL                # v aliases q
@@ -110,6 +111,33 @@ def test_fwd_qknorm_rope_validation(L):
     assert call(D=96) == EUNSUP               # head_dim 64 or 128
     assert call(D=96, dt=1) == EUNSUP
     assert call(scale=float("inf")) == EINVAL
+
+
+def test_qknorm_rope_rstd_validation(L):
+    f = L.ncattn_qknorm_rope_rstd
+    assert f(P, P + 16, None, 1, 4, 2, 2, 128, None, 1e5, 1e-6, 1.0, 0, None) == EINVAL   # rstd NULL
+    assert f(P, P + 16, P + 34, 1, 4, 2, 2, 128, None, 1e5, 1e-6, 1.0, 0, None) == EINVAL  # rstd misaligned
+    assert f(None, P + 16, P + 32, 1, 4, 2, 2, 128, None, 1e5, 1e-6, 1.0, 0, None) == EINVAL
+    assert f(P, P + 16, P + 32, 1, 4, 2, 2, 96, None, 1e5, 1e-6, 1.0, 0, None) == EUNSUP
+    assert f(P, P + 16, P + 32, 1, 4, 2, 2, 128, None, 0.5, 1e-6, 1.0, 0, None) == EINVAL
+    assert "ncattn_qknorm_rope_rstd" in L.ncattn_last_error().decode()
+
+
+def test_bwd_qknorm_rope_validation(L):
+    f = L.ncattn_bwd_qknorm_rope
+    need = L.ncattn_bwd_workspace_bytes(1, 8, 2, 2, 128, -1, 0)
+
+    def call(rstd=P + 160, dq=P + 96, base=1e5, D=128, wl=-1, ws=P + 192, wsb=None):
+        return f(P, P + 16, P + 32, P + 48, P + 64, P + 80, rstd, None, base, 1.0, dq, P + 112, P + 128, 1, 8, 2, 2,
+                 D, wl, 0, 0.0, 0, ws, need if wsb is None else wsb, None)
+    assert call(rstd=None) == EINVAL
+    assert call(rstd=P + 162) == EINVAL
+    assert call(dq=P + 160) == EINVAL          # dq aliases rstd
+    assert call(dq=P) == EINVAL                # dq aliases q
+    assert call(base=1.0) == EINVAL
+    assert call(D=96) == EUNSUP
+    assert call(wl=-2) == EINVAL
+    assert call(wsb=need - 1) == EWS
 
 
 def test_qknorm_rope_validation(L):

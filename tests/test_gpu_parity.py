@@ -76,6 +76,23 @@ def test_qknorm_rope_bwd(dtype, B, T, H, KV, D, base, gain, offset):
     assert torch.equal(qd, q_before) and torch.equal(kd, k_before)
 
 
+@pytest.mark.parametrize("dtype,B,T,H,KV,D", [("bf16", 2, 100, 4, 2, 128), ("bf16", 1, 77, 6, 6, 64),
+                                               ("f32", 2, 50, 3, 1, 64), ("f32", 1, 9, 2, 2, 128)])
+def test_qknorm_rope_rstd(dtype, B, T, H, KV, D):
+    """The variant that also stores 1/r: q', k' bit-equal to ncattn_qknorm_rope's,
+    1/r of every row against the oracle (q rows, then k rows, per token)."""
+    q, k, _, _ = attn_inputs(B, T, H, KV, D, dtype, seed=60 + T)
+    pos = torch.arange(B, dtype=torch.int32) * 1000 + 3
+    qa, ka = to_dev(q, k)
+    qb, kb = to_dev(q, k)
+    nc.qknorm_rope_(qa, ka, pos.to(DEV), rope_base=1e4, eps=1e-6, qk_gain=math.sqrt(1.2))
+    _, _, rstd = nc.qknorm_rope_rstd_(qb, kb, pos.to(DEV), rope_base=1e4, eps=1e-6, qk_gain=math.sqrt(1.2))
+    torch.cuda.synchronize()
+    assert torch.equal(qa, qb) and torch.equal(ka, kb)
+    ref = np.concatenate([oracle.rms_rstd(f64(q), 1e-6), oracle.rms_rstd(f64(k), 1e-6)], axis=2)
+    np.testing.assert_allclose(f64(rstd), ref, rtol=1e-5)
+
+
 FUSED_CASES = [
     # dtype, B, T, H, KV, D, W, base, gain, pos_offset
     ("bf16", 2, 200, 4, 2, 128, -1, 100000.0, 1.0, False),
@@ -102,11 +119,14 @@ def test_fwd_qknorm_rope(case):
     ro, rlse = oracle.attn_fwd(stored(xq, dtype), stored(xk, dtype), f64(v), W)
     qd, kd, vd = to_dev(q, k, v)
     v_before = vd.clone()
+    rstd = nc.rstd_like(qd, kd)
     o, lse = nc.fwd_qknorm_rope_(qd, kd, vd, None if pos is None else pos.to(DEV), rope_base=base, eps=1e-6,
-                                 qk_gain=gain, window=(W, 0))
+                                 qk_gain=gain, window=(W, 0), rstd=rstd)
     torch.cuda.synchronize()
     check(qd, xq, dtype, "q'")
     check(kd, xk, dtype, "k'")
+    ref_rstd = np.concatenate([oracle.rms_rstd(f64(q), 1e-6), oracle.rms_rstd(f64(k), 1e-6)], axis=2)
+    np.testing.assert_allclose(f64(rstd), ref_rstd, rtol=1e-5)
     check(o, ro, dtype, "o")
     check_lse(lse, rlse, dtype, "lse")
     assert torch.equal(vd, v_before)
@@ -150,16 +170,16 @@ def test_bwd_qknorm_rope(case):
     qr, kr, vd, dod = to_dev(q, k, v, do)
     pd = None if pos is None else pos.to(DEV)
     qn, kn = qr.clone(), kr.clone()
-    nc.qknorm_rope_(qn, kn, pd, rope_base=base, eps=1e-6, qk_gain=gain)
+    _, _, rstd = nc.qknorm_rope_rstd_(qn, kn, pd, rope_base=base, eps=1e-6, qk_gain=gain)
     o, lse = nc.fwd(qn, kn, vd, window=(W, 0))
-    q_before, k_before = qr.clone(), kr.clone()
-    dq, dk, dv = nc.bwd_qknorm_rope(qn, kn, vd, o, lse, dod, qr, kr, pd, rope_base=base, eps=1e-6, qk_gain=gain,
-                                    window=(W, 0))
+    before = [t.clone() for t in (qn, kn, rstd)]
+    # from the post-norm rows and their 1/r only: the raw rows are not passed
+    dq, dk, dv = nc.bwd_qknorm_rope(qn, kn, vd, o, lse, dod, rstd, pd, rope_base=base, qk_gain=gain, window=(W, 0))
     torch.cuda.synchronize()
     check(dq, rdq, dtype, "dq_raw")
     check(dk, rdk, dtype, "dk_raw")
     check(dv, rdv, dtype, "dv")
-    assert torch.equal(qr, q_before) and torch.equal(kr, k_before)
+    assert all(torch.equal(a, b) for a, b in zip((qn, kn, rstd), before))
     # the attention backward followed by the norm's backward gives the same
     # gradients up to rounding: dv bit for bit; dq, dk each within the bar of the
     # exact values, so within twice the bar of each other (the two calls round the

@@ -79,25 +79,25 @@ def _gpu_layer(cfg, W):
     say(f"{cfg.name}: W={W} generating inputs")
     q, k, v, do = config_inputs(cfg)
     qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
-    raw = None
+    rstd = None
     if not cfg.pre_normed:
-        raw = (qd.clone(), kd.clone())
-        nc.qknorm_rope_(qd, kd, None, rope_base=cfg.rope_base, eps=1e-6, qk_gain=1.0)
+        _, _, rstd = nc.qknorm_rope_rstd_(qd, kd, None, rope_base=cfg.rope_base, eps=1e-6, qk_gain=1.0)
     say(f"{cfg.name}: W={W} fwd/bwd on the GPU")
     o, lse = nc.fwd(qd, kd, vd, window=(W, 0))
     dq, dk, dv = nc.bwd(qd, kd, vd, o, lse, dod, window=(W, 0))
     outs = [("q'", qd), ("k'", kd), ("o", o), ("lse", lse), ("dq", dq), ("dk", dk), ("dv", dv)]
-    if raw is not None:
-        # the fused backward: gradients of the raw q, k through QK-norm + RoPE
-        dqr, dkr, _ = nc.bwd_qknorm_rope(qd, kd, vd, o, lse, dod, raw[0], raw[1], None, rope_base=cfg.rope_base,
-                                         eps=1e-6, qk_gain=1.0, window=(W, 0))
+    if rstd is not None:
+        # the fused backward: gradients of the raw q, k through QK-norm + RoPE,
+        # from the post-norm rows and their 1/r
+        dqr, dkr, _ = nc.bwd_qknorm_rope(qd, kd, vd, o, lse, dod, rstd, None, rope_base=cfg.rope_base, qk_gain=1.0,
+                                         window=(W, 0))
         outs += [("dq_raw", dqr), ("dk_raw", dkr)]
     torch.cuda.synchronize()
     for name, t in outs:
         assert bool(torch.isfinite(t).all()), f"{cfg.name} W={W}: non-finite values in {name}"
     keys = {"q'": "q", "k'": "k"}
     res = dict(inputs=(q, k, v, do), **{keys.get(n, n): t.cpu() for n, t in outs})
-    del qd, kd, vd, dod, o, lse, dq, dk, dv, outs, raw
+    del qd, kd, vd, dod, o, lse, dq, dk, dv, outs, rstd
     torch.cuda.empty_cache()
     _GPU_RESULTS[key] = res
     return res

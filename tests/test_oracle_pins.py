@@ -64,6 +64,17 @@ def test_rmsnorm_closed_forms():
     np.testing.assert_allclose(oracle.rms_norm(7.0 * x, eps=0.0), oracle.rms_norm(x, eps=0.0), rtol=1e-13)
 
 
+def test_rms_rstd_against_torch_rms_norm_and_closed_forms():
+    """x * rstd(x) is torch's rms_norm of x; a constant row c gives 1/sqrt(c^2 + eps)."""
+    x = rand(3, 5, 2, 128)
+    r = oracle.rms_rstd(x, eps=1e-6)
+    assert r.shape == x.shape[:-1]
+    ref = F.rms_norm(torch.from_numpy(x), (128,), eps=1e-6).numpy()
+    np.testing.assert_allclose(x * r[..., None], ref, rtol=1e-13, atol=1e-13)
+    c = np.full((2, 64), -3.5)
+    np.testing.assert_allclose(oracle.rms_rstd(c, eps=0.25), 1.0 / math.sqrt(3.5 ** 2 + 0.25), rtol=1e-15)
+
+
 # ----------------------------------------------------------------- RoPE
 
 def test_rope_golden_hand_values():

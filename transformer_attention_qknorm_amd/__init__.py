@@ -25,7 +25,7 @@ import os
 
 import torch
 
-__all__ = ["qknorm_rope_", "qknorm_rope_bwd_", "fwd", "fwd_qknorm_rope_", "bwd", "bwd_qknorm_rope", "decode", "decode_noalloc", "prefill",
+__all__ = ["qknorm_rope_", "qknorm_rope_rstd_", "rstd_like", "qknorm_rope_bwd_", "fwd", "fwd_qknorm_rope_", "bwd", "bwd_qknorm_rope", "decode", "decode_noalloc", "prefill",
            "cache_replicate",
            "window_sizes", "lib", "NcattnError", "LIB_PATH",
            "BF16", "F32", "STATUS", "bwd_workspace", "decode_workspace", "BWD_STAGES"]
@@ -56,7 +56,8 @@ def lib():
     L.ncattn_qknorm_rope.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, f32, f32, f32, i32, vp]
     L.ncattn_qknorm_rope_bwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, f32, f32, f32, i32, vp]
     L.ncattn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp]
-    L.ncattn_fwd_qknorm_rope.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, f32, f32, f32, i32, i32,
+    L.ncattn_qknorm_rope_rstd.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp, f32, f32, f32, i32, vp]
+    L.ncattn_fwd_qknorm_rope.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, f32, f32, f32, i32, i32,
                                          f32, i32, vp]
     L.ncattn_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
     L.ncattn_bwd_workspace_bytes.restype = sz
@@ -65,8 +66,8 @@ def lib():
     for fn in ("ncattn_bwd_preprocess", "ncattn_bwd_dkdv", "ncattn_bwd_dq"):
         getattr(L, fn).argtypes = L.ncattn_bwd.argtypes
         getattr(L, fn).restype = i32
-    L.ncattn_bwd_qknorm_rope.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, f32, f32, f32, vp, vp, vp, i32, i32,
-                                         i32, i32, i32, i32, i32, f32, i32, vp, sz, vp]
+    L.ncattn_bwd_qknorm_rope.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, f32, f32, vp, vp, vp, i32, i32, i32, i32,
+                                         i32, i32, i32, f32, i32, vp, sz, vp]
     L.ncattn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     L.ncattn_decode_workspace_bytes.restype = sz
     L.ncattn_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp, sz, vp]
@@ -76,7 +77,7 @@ def lib():
     L.ncattn_last_error.restype = ctypes.c_char_p
     L.ncattn_version.restype = ctypes.c_char_p
     for fn in ("ncattn_qknorm_rope", "ncattn_qknorm_rope_bwd", "ncattn_fwd", "ncattn_fwd_qknorm_rope", "ncattn_bwd",
-               "ncattn_bwd_qknorm_rope",
+               "ncattn_bwd_qknorm_rope", "ncattn_qknorm_rope_rstd",
                "ncattn_decode", "ncattn_decode_noalloc",
                "ncattn_prefill", "ncattn_cache_replicate"):
         getattr(L, fn).restype = i32
@@ -128,23 +129,53 @@ def _scale(softmax_scale):
     return 0.0 if softmax_scale is None else float(softmax_scale)
 
 
-def qknorm_rope_(q, k, pos_offset=None, rope_base=100000.0, eps=1e-6, qk_gain=1.0):
-    """In-place QK-norm + RoPE of q [B][T][H][D] and k [B][T][KV][D]; returns (q, k)."""
+def _qk_shapes(fn, q, k, pos_offset):
     dev = _dev(q, k)
     if q.dtype != k.dtype or q.dim() != 4 or k.dim() != 4:
-        raise ValueError("ncattn.qknorm_rope_: q and k must be 4-D tensors of one dtype")
+        raise ValueError(f"ncattn.{fn}: q and k must be 4-D tensors of one dtype")
     B, T, H, D = q.shape
     if k.shape[0] != B or k.shape[1] != T or k.shape[3] != D:
-        raise ValueError("ncattn.qknorm_rope_: k must be [B][T][n_kv_head][D] matching q")
+        raise ValueError(f"ncattn.{fn}: k must be [B][T][n_kv_head][D] matching q")
     if pos_offset is not None:
         _dev(pos_offset)
         if pos_offset.dtype != torch.int32 or pos_offset.numel() != B:
-            raise ValueError("ncattn.qknorm_rope_: pos_offset must be int32 [B]")
+            raise ValueError(f"ncattn.{fn}: pos_offset must be int32 [B]")
+    return dev, B, T, H, k.shape[2], D
+
+
+def rstd_like(q, k):
+    """An fp32 [B][T][n_head + n_kv_head] tensor for the rows' 1/r."""
+    return torch.empty((q.shape[0], q.shape[1], q.shape[2] + k.shape[2]), dtype=torch.float32, device=q.device)
+
+
+def _check_rstd(fn, rstd, q, k):
+    _dev(rstd)
+    if rstd.dtype != torch.float32 or tuple(rstd.shape) != (q.shape[0], q.shape[1], q.shape[2] + k.shape[2]) \
+            or not rstd.is_contiguous():
+        raise ValueError(f"ncattn.{fn}: rstd must be contiguous fp32 [B][T][n_head + n_kv_head]")
+
+
+def qknorm_rope_(q, k, pos_offset=None, rope_base=100000.0, eps=1e-6, qk_gain=1.0):
+    """In-place QK-norm + RoPE of q [B][T][H][D] and k [B][T][KV][D]; returns (q, k)."""
+    dev, B, T, H, KV, D = _qk_shapes("qknorm_rope_", q, k, pos_offset)
     with torch.cuda.device(dev):
-        rc = lib().ncattn_qknorm_rope(_ptr(q), _ptr(k), B, T, H, k.shape[2], D, _ptr(pos_offset),
+        rc = lib().ncattn_qknorm_rope(_ptr(q), _ptr(k), B, T, H, KV, D, _ptr(pos_offset),
                                       float(rope_base), float(eps), float(qk_gain), _dtype_code(q), _stream(dev))
     _check("ncattn_qknorm_rope", rc)
     return q, k
+
+
+def qknorm_rope_rstd_(q, k, pos_offset=None, rope_base=100000.0, eps=1e-6, qk_gain=1.0, rstd=None):
+    """qknorm_rope_ that also returns each row's 1/r (fp32 [B][T][H + KV], q rows
+    first), what bwd_qknorm_rope needs instead of the raw rows; returns (q, k, rstd)."""
+    dev, B, T, H, KV, D = _qk_shapes("qknorm_rope_rstd_", q, k, pos_offset)
+    rstd = rstd_like(q, k) if rstd is None else rstd
+    _check_rstd("qknorm_rope_rstd_", rstd, q, k)
+    with torch.cuda.device(dev):
+        rc = lib().ncattn_qknorm_rope_rstd(_ptr(q), _ptr(k), _ptr(rstd), B, T, H, KV, D, _ptr(pos_offset),
+                                           float(rope_base), float(eps), float(qk_gain), _dtype_code(q), _stream(dev))
+    _check("ncattn_qknorm_rope_rstd", rc)
+    return q, k, rstd
 
 
 def qknorm_rope_bwd_(dq, dk, q, k, pos_offset=None, rope_base=100000.0, eps=1e-6, qk_gain=1.0):
@@ -195,9 +226,10 @@ def fwd(q, k, v, window=(-1, 0), softmax_scale=None, out=None):
 
 
 def fwd_qknorm_rope_(q, k, v, pos_offset=None, rope_base=100000.0, eps=1e-6, qk_gain=1.0, window=(-1, 0),
-                     softmax_scale=None, out=None):
+                     softmax_scale=None, out=None, rstd=None):
     """QK-norm + RoPE of q and k, in place, fused with the attention forward:
-    the same as qknorm_rope_(q, k, ...) then fwd(q, k, v, ...).  Returns (o, lse)."""
+    the same as qknorm_rope_(q, k, ...) then fwd(q, k, v, ...).  Returns (o, lse).
+    ``rstd`` (fp32 [B][T][H + KV], see rstd_like) also receives each row's 1/r."""
     dev = _dev(q, k, v)
     if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or len({q.dtype, k.dtype, v.dtype}) != 1:
         raise ValueError("ncattn.fwd_qknorm_rope_: q, k, v must be 4-D of one dtype, k and v alike")
@@ -217,8 +249,11 @@ def fwd_qknorm_rope_(q, k, v, pos_offset=None, rope_base=100000.0, eps=1e-6, qk_
         _dev(o, lse)
         if o.shape != q.shape or o.dtype != q.dtype or lse.shape != (B, H, T) or lse.dtype != torch.float32:
             raise ValueError("ncattn.fwd_qknorm_rope_: out must be (o like q, lse fp32 [B][H][T])")
+    if rstd is not None:
+        _check_rstd("fwd_qknorm_rope_", rstd, q, k)
     with torch.cuda.device(dev):
-        rc = lib().ncattn_fwd_qknorm_rope(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, T, H, k.shape[2], D,
+        rc = lib().ncattn_fwd_qknorm_rope(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(rstd), B, T, H,
+                                          k.shape[2], D,
                                           _ptr(pos_offset), float(rope_base), float(eps), float(qk_gain), wl, wr,
                                           _scale(softmax_scale), _dtype_code(q), _stream(dev))
     _check("ncattn_fwd_qknorm_rope", rc)
@@ -269,20 +304,21 @@ def bwd(q, k, v, o, lse, do, window=(-1, 0), softmax_scale=None, out=None, works
     return dq, dk, dv
 
 
-def bwd_qknorm_rope(q, k, v, o, lse, do, q_raw, k_raw, pos_offset=None, rope_base=100000.0, eps=1e-6,
-                    qk_gain=1.0, window=(-1, 0), softmax_scale=None, out=None, workspace=None):
+def bwd_qknorm_rope(q, k, v, o, lse, do, rstd, pos_offset=None, rope_base=100000.0, qk_gain=1.0, window=(-1, 0),
+                    softmax_scale=None, out=None, workspace=None):
     """The backward of QK-norm + RoPE followed by attention, in one call: returns
-    (dq, dk, dv) with dq, dk the gradients of the raw rows q_raw, k_raw (q, k are
-    the post-norm rows the forward attended with).  ``out`` and ``workspace``
+    (dq, dk, dv) with dq, dk the gradients of the raw (pre-norm) rows.  q, k are
+    the post-norm rows the forward attended with and rstd their 1/r as
+    qknorm_rope_rstd_ or fwd_qknorm_rope_ stored it.  ``out`` and ``workspace``
     reuse preallocated buffers."""
-    dev = _dev(q, k, v, o, lse, do, q_raw, k_raw)
+    dev = _dev(q, k, v, o, lse, do)
     B, T, H, D = q.shape
     KV = k.shape[2]
     if o.shape != q.shape or do.shape != q.shape or lse.shape != (B, H, T) or lse.dtype != torch.float32:
         raise ValueError("ncattn.bwd_qknorm_rope: o, do must match q and lse must be fp32 [B][H][T]")
-    if k.shape != v.shape or q_raw.shape != q.shape or k_raw.shape != k.shape \
-            or len({q.dtype, k.dtype, v.dtype, o.dtype, do.dtype, q_raw.dtype, k_raw.dtype}) != 1:
+    if k.shape != v.shape or len({q.dtype, k.dtype, v.dtype, o.dtype, do.dtype}) != 1:
         raise ValueError("ncattn.bwd_qknorm_rope: inconsistent shapes or dtypes")
+    _check_rstd("bwd_qknorm_rope", rstd, q, k)
     if pos_offset is not None:
         _dev(pos_offset)
         if pos_offset.dtype != torch.int32 or pos_offset.numel() != B:
@@ -297,10 +333,10 @@ def bwd_qknorm_rope(q, k, v, o, lse, do, q_raw, k_raw, pos_offset=None, rope_bas
         if dq.shape != q.shape or dk.shape != k.shape or dv.shape != v.shape:
             raise ValueError("ncattn.bwd_qknorm_rope: out must be (dq like q, dk like k, dv like v)")
     with torch.cuda.device(dev):
-        rc = lib().ncattn_bwd_qknorm_rope(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(q_raw),
-                                          _ptr(k_raw), _ptr(pos_offset), float(rope_base), float(eps),
-                                          float(qk_gain), _ptr(dq), _ptr(dk), _ptr(dv), B, T, H, KV, D, wl, wr,
-                                          _scale(softmax_scale), _dtype_code(q), _ptr(ws), ws.numel(), _stream(dev))
+        rc = lib().ncattn_bwd_qknorm_rope(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(rstd),
+                                          _ptr(pos_offset), float(rope_base), float(qk_gain), _ptr(dq), _ptr(dk),
+                                          _ptr(dv), B, T, H, KV, D, wl, wr, _scale(softmax_scale), _dtype_code(q),
+                                          _ptr(ws), ws.numel(), _stream(dev))
     _check("ncattn_bwd_qknorm_rope", rc)
     return dq, dk, dv
 

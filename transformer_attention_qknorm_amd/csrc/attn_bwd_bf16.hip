@@ -155,39 +155,51 @@ __device__ __forceinline__ void dkdv_acc(f32x16 (&dkacc)[Geom<D>::kDBlocks], f32
 }
 
 // ---------------------------------------------------------------- QK-norm + RoPE backward epilogue
-// For the fused backward (ncattn_bwd_qknorm_rope): the gradient that dK / dQ
+// For the fused backward (ncattn_bwd_qknorm_rope): the gradient dy that dK / dQ
 // hold for a post-norm row y = R(g x / r) is carried back to the raw row x
 // ("nanochat Admin & Developer Guide", section 3: weightless RMSNorm of q and k,
 // then rotary embedding; "nanochat (Python)" catalog, Backward pass: the chain
-// rule through that forward):
-//   dn = R^T dy (each pair (j, j + D/2) rotated by -theta_j),
-//   dx = (g / r) (dn - x (dn . x) / (D r^2)),  r = sqrt(mean(x^2) + eps).
+// rule through that forward).  With n = R^T y = g x / r the gradient
+//   dx = (g / r) (R^T dy - (x / r) ((R^T dy) . (x / r)) / D)
+// becomes, since the rotation keeps dot products,
+//   dx = (g / r) R^T (dy - y (dy . y) / (g^2 D)):
+// it needs the post-norm row y (the attention's own input) and 1/r, which the
+// forward stored, not the raw row.  Each pair (j, j + D/2) is rotated by -theta_j.
 // The row is held by the lane pair (l, l ^ 32) in accumulator layout: element
 // 4 i + j of block db is d = 32 db + 8 i + 4 hh + j, so the pair partner d + D/2
-// is block db + D/64 of the same lane, and the two row sums need one exchange.
+// is block db + D/64 of the same lane, and the row sum needs one exchange.
 struct NormRopeBwd {
-  const uint16_t *x;          // raw rows: q [B][T][H][D] (dQ) or k [B][T][KV][D] (dK)
+  const float *rstd;          // 1/r per row: [B][T][rstd_stride], q rows at head h, k rows at rstd_k_off + kv head
+  long long rstd_stride;
+  int rstd_k_off;
   const int32_t *pos_offset;  // device [B] or NULL
   double turns[64];           // base^(-2j/D) / 2 pi for j < D/2: turns per position
-  float eps, gain;
+  float gain;
 };
 
 template <int D>
-__device__ __forceinline__ void norm_rope_bwd_row(f32x16 (&g)[Geom<D>::kDBlocks], const uint16_t *xrow, double pos,
-                                                  const NormRopeBwd &nb, int hh) {
+__device__ __forceinline__ void norm_rope_bwd_row(f32x16 (&g)[Geom<D>::kDBlocks], const uint16_t *yrow, float rs,
+                                                  double pos, const NormRopeBwd &nb, int hh) {
   constexpr int NB = Geom<D>::kDBlocks, HB = NB / 2;
-  float x[NB][16];
+  float y[NB][16];
 #pragma unroll
   for (int db = 0; db < NB; ++db)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const u32x2 w = *(const u32x2 *)(xrow + 32 * db + 8 * i + 4 * hh);
-      x[db][4 * i + 0] = lo_bf16(w[0]);
-      x[db][4 * i + 1] = hi_bf16(w[0]);
-      x[db][4 * i + 2] = lo_bf16(w[1]);
-      x[db][4 * i + 3] = hi_bf16(w[1]);
+      const u32x2 w = *(const u32x2 *)(yrow + 32 * db + 8 * i + 4 * hh);
+      y[db][4 * i + 0] = lo_bf16(w[0]);
+      y[db][4 * i + 1] = hi_bf16(w[0]);
+      y[db][4 * i + 2] = lo_bf16(w[1]);
+      y[db][4 * i + 3] = hi_bf16(w[1]);
     }
-  float ss = 0.f, dot = 0.f;
+  float dot = 0.f;
+#pragma unroll
+  for (int db = 0; db < NB; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) dot += g[db][e] * y[db][e];
+  dot += shfl_xor(dot, 32);
+  const float coef = nb.gain == 0.f ? 0.f : dot / (nb.gain * nb.gain * (float)D);
+  const float g_r = nb.gain * rs;
 #pragma unroll
   for (int db = 0; db < HB; ++db)
 #pragma unroll
@@ -201,23 +213,10 @@ __device__ __forceinline__ void norm_rope_bwd_row(f32x16 (&g)[Geom<D>::kDBlocks]
       turns -= rint(turns);
       const float tf = (float)turns;
       const float sn = __builtin_amdgcn_sinf(tf), cs = __builtin_amdgcn_cosf(tf);
-      const float ga = g[db][e], gb = g[db + HB][e];
-      const float na = ga * cs + gb * sn;  // rotation by -theta
-      const float nbv = gb * cs - ga * sn;
-      g[db][e] = na;
-      g[db + HB][e] = nbv;
-      ss += x[db][e] * x[db][e] + x[db + HB][e] * x[db + HB][e];
-      dot += na * x[db][e] + nbv * x[db + HB][e];
+      const float ua = g[db][e] - y[db][e] * coef, ub = g[db + HB][e] - y[db + HB][e] * coef;
+      g[db][e] = g_r * (ua * cs + ub * sn);  // rotation by -theta
+      g[db + HB][e] = g_r * (ub * cs - ua * sn);
     }
-  ss += shfl_xor(ss, 32);
-  dot += shfl_xor(dot, 32);
-  const float r2 = ss / (float)D + nb.eps;
-  const float g_r = nb.gain / sqrtf(r2);
-  const float coef = dot / ((float)D * r2);
-#pragma unroll
-  for (int db = 0; db < NB; ++db)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) g[db][e] = g_r * (g[db][e] - x[db][e] * coef);
 }
 
 // S = Q K^T and dP - D = dO V^T - D for the 32 query rows of block qb of the
@@ -396,7 +395,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t *__rest
 #pragma unroll
       for (int e = 0; e < 16; ++e) dkacc[db][e] *= scale;
     const double posd = (double)((nb.pos_offset ? nb.pos_offset[b] : 0) + key_lane);
-    norm_rope_bwd_row<D>(dkacc, nb.x + off, posd, nb, hh);
+    const float rs = nb.rstd[((long long)b * T + key_lane) * nb.rstd_stride + nb.rstd_k_off + kvh];
+    norm_rope_bwd_row<D>(dkacc, K + off, rs, posd, nb, hh);
     kscale = 1.f;
   }
 #pragma unroll
@@ -584,7 +584,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t *__restri
 #pragma unroll
       for (int e = 0; e < 16; ++e) dqacc[db][e] *= scale;
     const double pos = (double)((nb.pos_offset ? nb.pos_offset[b] : 0) + q_lane);
-    norm_rope_bwd_row<D>(dqacc, nb.x + qoff, pos, nb, hh);
+    const float rs = nb.rstd[((long long)b * T + q_lane) * nb.rstd_stride + h];
+    norm_rope_bwd_row<D>(dqacc, Q + qoff, rs, pos, nb, hh);
     qscale = 1.f;
   }
 #pragma unroll
@@ -642,21 +643,20 @@ hipError_t launch_bwd_bf16(const void *q, const void *k, const void *v, const vo
 }
 
 hipError_t launch_bwd_bf16_qknorm_rope(const void *q, const void *k, const void *v, const void *o, const float *lse,
-                                       const void *dout, const void *q_raw, const void *k_raw, void *dq, void *dk,
-                                       void *dv, void *workspace, const AttnShape &sh, const int32_t *pos_offset,
-                                       const double *inv_freq_host, float eps, float gain, hipStream_t s) {
-  NormRopeBwd nq{};
-  for (int j = 0; j < sh.D / 2; ++j) nq.turns[j] = inv_freq_host[j] / 6.283185307179586;
-  nq.pos_offset = pos_offset;
-  nq.eps = eps;
-  nq.gain = gain;
-  NormRopeBwd nk = nq;
-  nq.x = (const uint16_t *)q_raw;
-  nk.x = (const uint16_t *)k_raw;
+                                       const void *dout, const float *rstd, void *dq, void *dk, void *dv,
+                                       void *workspace, const AttnShape &sh, const int32_t *pos_offset,
+                                       const double *inv_freq_host, float gain, hipStream_t s) {
+  NormRopeBwd nb{};
+  for (int j = 0; j < sh.D / 2; ++j) nb.turns[j] = inv_freq_host[j] / 6.283185307179586;
+  nb.rstd = rstd;
+  nb.rstd_stride = (long long)sh.H + sh.KV;
+  nb.rstd_k_off = sh.H;
+  nb.pos_offset = pos_offset;
+  nb.gain = gain;
   if (sh.D == 64)
-    return launch_bwd_kernels<64, true>(q, k, v, o, lse, dout, dq, dk, dv, workspace, sh, kBwdAll, nq, nk, s);
+    return launch_bwd_kernels<64, true>(q, k, v, o, lse, dout, dq, dk, dv, workspace, sh, kBwdAll, nb, nb, s);
   if (sh.D == 128)
-    return launch_bwd_kernels<128, true>(q, k, v, o, lse, dout, dq, dk, dv, workspace, sh, kBwdAll, nq, nk, s);
+    return launch_bwd_kernels<128, true>(q, k, v, o, lse, dout, dq, dk, dv, workspace, sh, kBwdAll, nb, nb, s);
   return hipErrorInvalidValue;
 }
 

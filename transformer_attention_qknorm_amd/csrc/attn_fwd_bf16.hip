@@ -162,6 +162,8 @@ struct QkNormRope {
   double turns[64];
   float eps, gain;
   const int32_t *pos_offset;  // device [B] or NULL
+  float *rstd;                // NULL, or each query row's 1/r at rstd[token * rstd_stride + head]
+  long long rstd_stride;
 };
 
 // FUSE: the query rows arrive raw; the prologue normalises and rotates them in
@@ -273,7 +275,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const uint16_t *_
 #pragma unroll
       for (int i = 0; i < 4; ++i) ss += lo_bf16(raw[s][i]) * lo_bf16(raw[s][i]) + hi_bf16(raw[s][i]) * hi_bf16(raw[s][i]);
     ss += shfl_xor(ss, 32);
-    const float inv = qn.gain / sqrtf(ss / (float)D + qn.eps);
+    const float rs = 1.f / sqrtf(ss / (float)D + qn.eps);
+    const float inv = qn.gain * rs;
+    if (qn.rstd != nullptr && hh == 0 && qrow < Tq) qn.rstd[((long long)b * Tq + qrow) * qn.rstd_stride + h] = rs;
     const double pos = (double)((qn.pos_offset ? qn.pos_offset[b] : 0) + qr);
     constexpr int kHalf = kSteps / 2;
 #pragma unroll
@@ -433,12 +437,15 @@ hipError_t launch_fwd_bf16_rows(const void *q, const void *k, const void *v, voi
 
 hipError_t launch_fwd_bf16_qknorm_rope(void *q, const void *k, const void *v, void *o, float *lse,
                                        const AttnShape &sh, const int32_t *pos_offset,
-                                       const double *inv_freq_host, float eps, float gain, hipStream_t s) {
+                                       const double *inv_freq_host, float eps, float gain, hipStream_t s,
+                                       float *rstd, long long rstd_stride) {
   QkNormRope qn{};
   for (int j = 0; j < sh.D / 2; ++j) qn.turns[j] = inv_freq_host[j] / 6.283185307179586;
   qn.eps = eps;
   qn.gain = gain;
   qn.pos_offset = pos_offset;
+  qn.rstd = rstd;
+  qn.rstd_stride = rstd_stride;
   if (sh.D == 64)
     return launch_fwd_kernel<64, true>(q, k, v, o, lse, nullptr, sh.B, sh.T, sh.T, sh.H, sh.KV, sh.window, sh.scale,
                                        q, qn, s);

@@ -18,14 +18,20 @@ struct AttnShape {
 };
 
 // QK-norm + RoPE in place; inv_freq[j] = base^(-2j/D) computed on the host in fp64.
+// rstd (optional): each row's 1/sqrt(mean(x^2) + eps) at rstd[token * rstd_stride +
+// head] (q rows) and [token * rstd_stride + rstd_k_off + kv head] (k rows).
 hipError_t launch_qknorm_rope(void *q, void *k, int B, int T, int H, int KV, int D,
                               const int32_t *pos_offset, const double *inv_freq_host, float eps,
-                              float gain, bool bf16, hipStream_t s);
+                              float gain, bool bf16, hipStream_t s, float *rstd = nullptr,
+                              long long rstd_stride = 0, int rstd_k_off = 0);
 
-// Its backward: dq/dk hold dy on entry and dx on return; q/k are the forward's inputs.
+// Its backward: dq/dk hold dy on entry and dx on return; q/k are the forward's
+// inputs x, or, when rstd is given, its outputs y with the rows' 1/r in rstd
+// (layout as launch_qknorm_rope's).
 hipError_t launch_qknorm_rope_bwd(void *dq, void *dk, const void *q, const void *k, int B, int T, int H, int KV,
                                   int D, const int32_t *pos_offset, const double *inv_freq_host, float eps,
-                                  float gain, bool bf16, hipStream_t s);
+                                  float gain, bool bf16, hipStream_t s, const float *rstd = nullptr,
+                                  long long rstd_stride = 0, int rstd_k_off = 0);
 
 // Backward stages (bit mask): D_i = dO.O, then dK/dV, then dQ.
 constexpr int kBwdDelta = 1, kBwdDkDv = 2, kBwdDq = 4, kBwdAll = 7;
@@ -41,7 +47,8 @@ hipError_t launch_fwd_bf16(const void *q, const void *k, const void *v, void *o,
 // base^(-2j/D) in fp64.
 hipError_t launch_fwd_bf16_qknorm_rope(void *q, const void *k, const void *v, void *o, float *lse,
                                        const AttnShape &sh, const int32_t *pos_offset,
-                                       const double *inv_freq_host, float eps, float gain, hipStream_t s);
+                                       const double *inv_freq_host, float eps, float gain, hipStream_t s,
+                                       float *rstd = nullptr, long long rstd_stride = 0);
 // The same forward for Tq query rows per sequence at positions q_pos0[b] + r
 // (q_pos0 device int32 [B], NULL for 0) over key rows [0, q_pos0[b] + Tq) of K/V
 // arrays with Tk rows per sequence; lse may be NULL.  Sequences whose offset
@@ -52,13 +59,14 @@ hipError_t launch_fwd_bf16_rows(const void *q, const void *k, const void *v, voi
 hipError_t launch_bwd_bf16(const void *q, const void *k, const void *v, const void *o,
                            const float *lse, const void *dout, void *dq, void *dk, void *dv,
                            void *workspace, const AttnShape &sh, int stages, hipStream_t s);
-// The full backward whose dq / dk are the gradients of the raw (pre-norm) q_raw /
-// k_raw: the dQ and dK/dV kernels carry their results back through QK-norm +
-// RoPE before storing them (q, k are the post-norm rows the forward used).
+// The full backward whose dq / dk are the gradients of the raw (pre-norm) rows:
+// the dQ and dK/dV kernels carry their results back through QK-norm + RoPE
+// before storing them, from the post-norm q, k and each row's 1/r (rstd
+// [B][T][H + KV], q rows first).
 hipError_t launch_bwd_bf16_qknorm_rope(const void *q, const void *k, const void *v, const void *o, const float *lse,
-                                       const void *dout, const void *q_raw, const void *k_raw, void *dq, void *dk,
-                                       void *dv, void *workspace, const AttnShape &sh, const int32_t *pos_offset,
-                                       const double *inv_freq_host, float eps, float gain, hipStream_t s);
+                                       const void *dout, const float *rstd, void *dq, void *dk, void *dv,
+                                       void *workspace, const AttnShape &sh, const int32_t *pos_offset,
+                                       const double *inv_freq_host, float gain, hipStream_t s);
 
 // fp32 reference-precision kernels (head_dim 64 or 128).
 hipError_t launch_fwd_f32(const float *q, const float *k, const float *v, float *o, float *lse,

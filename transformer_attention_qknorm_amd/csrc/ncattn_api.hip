@@ -131,6 +131,23 @@ int ncattn_qknorm_rope(void *q, void *k, int B, int T, int n_head, int n_kv_head
                     fn);
 }
 
+int ncattn_qknorm_rope_rstd(void *q, void *k, float *rstd, int B, int T, int n_head, int n_kv_head, int head_dim,
+                            const int32_t *pos_offset, float rope_base, float eps, float qk_gain, int dtype,
+                            void *stream) {
+  const char *fn = "ncattn_qknorm_rope_rstd";
+  NC_PTR(q, fn);
+  NC_PTR(k, fn);
+  if (rstd == nullptr) return fail(NCATTN_EINVAL, "%s: rstd is NULL", fn);
+  if ((uintptr_t)rstd & 3u) return fail(NCATTN_EINVAL, "%s: rstd is not 4-byte aligned", fn);
+  double inv_freq[64];
+  NC_TRY(check_qknorm(fn, B, T, n_head, n_kv_head, head_dim, pos_offset, rope_base, eps, qk_gain, dtype,
+                      inv_freq));
+  return hip_status(ncattn::launch_qknorm_rope(q, k, B, T, n_head, n_kv_head, head_dim, pos_offset, inv_freq, eps,
+                                               qk_gain, dtype == NCATTN_BF16, (hipStream_t)stream, rstd,
+                                               (long long)n_head + n_kv_head, n_head),
+                    fn);
+}
+
 int ncattn_qknorm_rope_bwd(void *dq, void *dk, const void *q, const void *k, int B, int T, int n_head,
                            int n_kv_head, int head_dim, const int32_t *pos_offset, float rope_base, float eps,
                            float qk_gain, int dtype, void *stream) {
@@ -175,16 +192,17 @@ int ncattn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
   return hip_status(e, fn);
 }
 
-int ncattn_fwd_qknorm_rope(void *q, void *k, const void *v, void *o, float *lse, int B, int T, int n_head,
-                           int n_kv_head, int head_dim, const int32_t *pos_offset, float rope_base, float eps,
-                           float qk_gain, int window_left, int window_right, float softmax_scale, int dtype,
-                           void *stream) {
+int ncattn_fwd_qknorm_rope(void *q, void *k, const void *v, void *o, float *lse, float *rstd, int B, int T,
+                           int n_head, int n_kv_head, int head_dim, const int32_t *pos_offset, float rope_base,
+                           float eps, float qk_gain, int window_left, int window_right, float softmax_scale,
+                           int dtype, void *stream) {
   const char *fn = "ncattn_fwd_qknorm_rope";
   NC_PTR(q, fn);
   NC_PTR(k, fn);
   NC_PTR(v, fn);
   NC_PTR(o, fn);
   NC_PTR(lse, fn);
+  if (rstd != nullptr && ((uintptr_t)rstd & 3u)) return fail(NCATTN_EINVAL, "%s: rstd is not 4-byte aligned", fn);
   double inv_freq[64];
   NC_TRY(check_qknorm(fn, B, T, n_head, n_kv_head, head_dim, pos_offset, rope_base, eps, qk_gain, dtype,
                       inv_freq));
@@ -198,14 +216,17 @@ int ncattn_fwd_qknorm_rope(void *q, void *k, const void *v, void *o, float *lse,
   ncattn::AttnShape sh{B, T, n_head, n_kv_head, head_dim, window_left, resolve_scale(softmax_scale, head_dim)};
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
+  const long long rstride = (long long)n_head + n_kv_head;
   if (dtype == NCATTN_BF16) {
     // k alone (no query rows), then the forward that normalises q in its prologue
-    e = ncattn::launch_qknorm_rope(k, k, B, T, 0, n_kv_head, head_dim, pos_offset, inv_freq, eps, qk_gain, true, s);
+    e = ncattn::launch_qknorm_rope(k, k, B, T, 0, n_kv_head, head_dim, pos_offset, inv_freq, eps, qk_gain, true, s,
+                                   rstd, rstride, n_head);
     if (e == hipSuccess)
-      e = ncattn::launch_fwd_bf16_qknorm_rope(q, k, v, o, lse, sh, pos_offset, inv_freq, eps, qk_gain, s);
+      e = ncattn::launch_fwd_bf16_qknorm_rope(q, k, v, o, lse, sh, pos_offset, inv_freq, eps, qk_gain, s, rstd,
+                                              rstride);
   } else {
     e = ncattn::launch_qknorm_rope(q, k, B, T, n_head, n_kv_head, head_dim, pos_offset, inv_freq, eps, qk_gain,
-                                   false, s);
+                                   false, s, rstd, rstride, n_head);
     if (e == hipSuccess)
       e = ncattn::launch_fwd_f32((const float *)q, (const float *)k, (const float *)v, (float *)o, lse, sh, s);
   }
@@ -270,18 +291,18 @@ int bwd_common(const char *fn, int stages, const void *q, const void *k, const v
 extern "C" {
 
 int ncattn_bwd_qknorm_rope(const void *q, const void *k, const void *v, const void *o, const float *lse,
-                           const void *dout, const void *q_raw, const void *k_raw, const int32_t *pos_offset,
-                           float rope_base, float eps, float qk_gain, void *dq, void *dk, void *dv, int B, int T,
-                           int n_head, int n_kv_head, int head_dim, int window_left, int window_right,
-                           float softmax_scale, int dtype, void *workspace, size_t workspace_bytes, void *stream) {
+                           const void *dout, const float *rstd, const int32_t *pos_offset, float rope_base,
+                           float qk_gain, void *dq, void *dk, void *dv, int B, int T, int n_head, int n_kv_head,
+                           int head_dim, int window_left, int window_right, float softmax_scale, int dtype,
+                           void *workspace, size_t workspace_bytes, void *stream) {
   const char *fn = "ncattn_bwd_qknorm_rope";
-  NC_PTR(q_raw, fn);
-  NC_PTR(k_raw, fn);
+  if (rstd == nullptr) return fail(NCATTN_EINVAL, "%s: rstd is NULL", fn);
+  if ((uintptr_t)rstd & 3u) return fail(NCATTN_EINVAL, "%s: rstd is not 4-byte aligned", fn);
   double inv_freq[64];
-  NC_TRY(check_qknorm(fn, B, T, n_head, n_kv_head, head_dim, pos_offset, rope_base, eps, qk_gain, dtype,
+  NC_TRY(check_qknorm(fn, B, T, n_head, n_kv_head, head_dim, pos_offset, rope_base, 0.f, qk_gain, dtype,
                       inv_freq));
-  if (dq == q_raw || dq == k_raw || dk == q_raw || dk == k_raw || dv == q_raw || dv == k_raw)
-    return fail(NCATTN_EINVAL, "%s: gradients must not alias q_raw or k_raw", fn);
+  if ((const void *)rstd == dq || (const void *)rstd == dk || (const void *)rstd == dv)
+    return fail(NCATTN_EINVAL, "%s: gradients must not alias rstd", fn);
   // every check of ncattn_bwd, with launching deferred to here
   NC_TRY(bwd_common(fn, 0, q, k, v, o, lse, dout, dq, dk, dv, B, T, n_head, n_kv_head, head_dim, window_left,
                     window_right, softmax_scale, dtype, workspace, workspace_bytes, stream));
@@ -290,15 +311,15 @@ int ncattn_bwd_qknorm_rope(const void *q, const void *k, const void *v, const vo
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   if (dtype == NCATTN_BF16) {
-    e = ncattn::launch_bwd_bf16_qknorm_rope(q, k, v, o, lse, dout, q_raw, k_raw, dq, dk, dv, workspace, sh,
-                                            pos_offset, inv_freq, eps, qk_gain, s);
+    e = ncattn::launch_bwd_bf16_qknorm_rope(q, k, v, o, lse, dout, rstd, dq, dk, dv, workspace, sh, pos_offset,
+                                            inv_freq, qk_gain, s);
   } else {
     e = ncattn::launch_bwd_f32((const float *)q, (const float *)k, (const float *)v, (const float *)o, lse,
                                (const float *)dout, (float *)dq, (float *)dk, (float *)dv, (float *)workspace, sh,
                                ncattn::kBwdAll, s);
     if (e == hipSuccess)
-      e = ncattn::launch_qknorm_rope_bwd(dq, dk, q_raw, k_raw, B, T, n_head, n_kv_head, head_dim, pos_offset,
-                                         inv_freq, eps, qk_gain, false, s);
+      e = ncattn::launch_qknorm_rope_bwd(dq, dk, q, k, B, T, n_head, n_kv_head, head_dim, pos_offset, inv_freq, 0.f,
+                                         qk_gain, false, s, rstd, (long long)n_head + n_kv_head, n_head);
   }
   return hip_status(e, fn);
 }

@@ -28,6 +28,16 @@ struct InvFreq {
   double v[64];  // base^(-2j/D) / (2 pi): turns of the rotation per position
 };
 
+// Optional output of the forward: 1/r = 1/sqrt(mean(x^2) + eps) of every row,
+// at rstd[token * stride + head] for q rows and [token * stride + k_off + kv head]
+// for k rows (stride = n_head + n_kv_head, k_off = n_head for the layout
+// [B][T][n_head + n_kv_head]).
+struct RstdOut {
+  float *rstd;
+  long long stride;
+  int k_off;
+};
+
 // Loads the lane's 4 pairs (x_j, x_{j+D/2}), j = j0..j0+3, of a row as fp32.
 template <int D, bool BF16>
 __device__ __forceinline__ void load_pairs(const void *base, long long off, int j0, float (&a)[4], float (&b)[4]) {
@@ -103,7 +113,7 @@ constexpr int kPasses = 4;
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void qknorm_rope_kernel(void *__restrict__ qp, void *__restrict__ kp, int B, int T,
                                                           int H, int KV, const int32_t *__restrict__ pos_offset,
-                                                          InvFreq inv_freq, float eps, float gain) {
+                                                          InvFreq inv_freq, float eps, float gain, RstdOut ro) {
   constexpr int R = D / 8;          // lanes per row
   constexpr int ROWS = 64 / R;      // rows per wave pass
   const int lane = threadIdx.x & 63;
@@ -140,7 +150,10 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(void *__restrict__ qp,
 #pragma unroll
         for (int i = 0; i < 4; ++i) ss += a[p][i] * a[p][i] + bb[p][i] * bb[p][i];
         ss = row_sum<R>(ss);
-        const float inv = gain / sqrtf(ss / (float)D + eps);
+        const float rs = 1.f / sqrtf(ss / (float)D + eps);
+        const float inv = gain * rs;
+        if (ro.rstd != nullptr && r == 0 && row < nrows)
+          ro.rstd[tok * ro.stride + (row < H ? row : ro.k_off + row - H)] = rs;
         float ya[4], yb[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -154,12 +167,16 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(void *__restrict__ qp,
   }
 }
 
-template <int D, bool BF16>
+// FROM_Y: qp / kp hold the forward's outputs y (not its inputs x) and rs.rstd
+// each row's 1/r.  With n = R^T y = g x / r the same gradient is
+//   dx = (g / r) R^T (dy - y (dy . y) / (g^2 D))
+// (dn . x / r = (R^T dy) . (R^T y) / g = dy . y / g: the rotation keeps dot products).
+template <int D, bool BF16, bool FROM_Y>
 __global__ __launch_bounds__(256) void qknorm_rope_bwd_kernel(void *__restrict__ dqp, void *__restrict__ dkp,
                                                               const void *__restrict__ qp,
                                                               const void *__restrict__ kp, int B, int T, int H,
                                                               int KV, const int32_t *__restrict__ pos_offset,
-                                                              InvFreq inv_freq, float eps, float gain) {
+                                                              InvFreq inv_freq, float eps, float gain, RstdOut rs) {
   constexpr int R = D / 8;
   constexpr int ROWS = 64 / R;
   const int lane = threadIdx.x & 63;
@@ -193,25 +210,42 @@ __global__ __launch_bounds__(256) void qknorm_rope_bwd_kernel(void *__restrict__
 #pragma unroll
       for (int p = 0; p < kPasses; ++p) {
         const int row = row0 + p * ROWS + slot;
-        float na[4], nb[4];
-        float ss = 0.f, dot = 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          na[i] = ga[p][i] * c[i] + gb[p][i] * s[i];  // rotation by -theta
-          nb[i] = gb[p][i] * c[i] - ga[p][i] * s[i];
-          ss += xa[p][i] * xa[p][i] + xb[p][i] * xb[p][i];
-          dot += na[i] * xa[p][i] + nb[i] * xb[p][i];
-        }
-        ss = row_sum<R>(ss);
-        dot = row_sum<R>(dot);
-        const float r2 = ss / (float)D + eps;
-        const float g_r = gain / sqrtf(r2);
-        const float coef = dot / ((float)D * r2);
         float da[4], db[4];
+        if constexpr (!FROM_Y) {
+          float na[4], nb[4];
+          float ss = 0.f, dot = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          da[i] = g_r * (na[i] - xa[p][i] * coef);
-          db[i] = g_r * (nb[i] - xb[p][i] * coef);
+          for (int i = 0; i < 4; ++i) {
+            na[i] = ga[p][i] * c[i] + gb[p][i] * s[i];  // rotation by -theta
+            nb[i] = gb[p][i] * c[i] - ga[p][i] * s[i];
+            ss += xa[p][i] * xa[p][i] + xb[p][i] * xb[p][i];
+            dot += na[i] * xa[p][i] + nb[i] * xb[p][i];
+          }
+          ss = row_sum<R>(ss);
+          dot = row_sum<R>(dot);
+          const float r2 = ss / (float)D + eps;
+          const float g_r = gain / sqrtf(r2);
+          const float coef = dot / ((float)D * r2);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            da[i] = g_r * (na[i] - xa[p][i] * coef);
+            db[i] = g_r * (nb[i] - xb[p][i] * coef);
+          }
+        } else {
+          // xa / xb hold y here
+          float dot = 0.f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dot += ga[p][i] * xa[p][i] + gb[p][i] * xb[p][i];
+          dot = row_sum<R>(dot);
+          const int rr = min(row, nrows - 1);
+          const float g_r = gain * rs.rstd[tok * rs.stride + (rr < H ? rr : rs.k_off + rr - H)];
+          const float coef = gain == 0.f ? 0.f : dot / (gain * gain * (float)D);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float ua = ga[p][i] - xa[p][i] * coef, ub = gb[p][i] - xb[p][i] * coef;
+            da[i] = g_r * (ua * c[i] + ub * s[i]);  // rotation by -theta
+            db[i] = g_r * (ub * c[i] - ua * s[i]);
+          }
         }
         if (row < nrows) store_pairs<D, BF16>(row < H ? dqp : dkp, off[p], j0, da, db);
       }
@@ -221,27 +255,36 @@ __global__ __launch_bounds__(256) void qknorm_rope_bwd_kernel(void *__restrict__
 
 hipError_t launch_qknorm_rope_bwd(void *dq, void *dk, const void *q, const void *k, int B, int T, int H, int KV,
                                   int D, const int32_t *pos_offset, const double *inv_freq_host, float eps,
-                                  float gain, bool bf16, hipStream_t s) {
+                                  float gain, bool bf16, hipStream_t s, const float *rstd, long long rstd_stride,
+                                  int rstd_k_off) {
   InvFreq f;
   for (int j = 0; j < 64; ++j) f.v[j] = j < D / 2 ? inv_freq_host[j] / 6.283185307179586 : 0.0;
+  const RstdOut rs{(float *)rstd, rstd_stride, rstd_k_off};
   const long long ntok = (long long)B * T;
   long long blocks = (ntok + 3) / 4;
   if (blocks > 4096) blocks = 4096;
   dim3 grid((unsigned)blocks), block(256);
+#define NC_QKB(DD, BF, FY)                                                                                     \
+  hipLaunchKernelGGL((qknorm_rope_bwd_kernel<DD, BF, FY>), grid, block, 0, s, dq, dk, q, k, B, T, H, KV, pos_offset, \
+                     f, eps, gain, rs)
+  const bool fy = rstd != nullptr;
   if (D == 128) {
-    if (bf16) hipLaunchKernelGGL((qknorm_rope_bwd_kernel<128, true>), grid, block, 0, s, dq, dk, q, k, B, T, H, KV, pos_offset, f, eps, gain);
-    else hipLaunchKernelGGL((qknorm_rope_bwd_kernel<128, false>), grid, block, 0, s, dq, dk, q, k, B, T, H, KV, pos_offset, f, eps, gain);
+    if (bf16) { if (fy) NC_QKB(128, true, true); else NC_QKB(128, true, false); }
+    else { if (fy) NC_QKB(128, false, true); else NC_QKB(128, false, false); }
   } else {
-    if (bf16) hipLaunchKernelGGL((qknorm_rope_bwd_kernel<64, true>), grid, block, 0, s, dq, dk, q, k, B, T, H, KV, pos_offset, f, eps, gain);
-    else hipLaunchKernelGGL((qknorm_rope_bwd_kernel<64, false>), grid, block, 0, s, dq, dk, q, k, B, T, H, KV, pos_offset, f, eps, gain);
+    if (bf16) { if (fy) NC_QKB(64, true, true); else NC_QKB(64, true, false); }
+    else { if (fy) NC_QKB(64, false, true); else NC_QKB(64, false, false); }
   }
+#undef NC_QKB
   return hipGetLastError();
 }
 
 hipError_t launch_qknorm_rope(void *q, void *k, int B, int T, int H, int KV, int D, const int32_t *pos_offset,
-                              const double *inv_freq_host, float eps, float gain, bool bf16, hipStream_t s) {
+                              const double *inv_freq_host, float eps, float gain, bool bf16, hipStream_t s,
+                              float *rstd, long long rstd_stride, int rstd_k_off) {
   InvFreq f;
   for (int j = 0; j < 64; ++j) f.v[j] = j < D / 2 ? inv_freq_host[j] / 6.283185307179586 : 0.0;
+  const RstdOut ro{rstd, rstd_stride, rstd_k_off};
   const long long ntok = (long long)B * T;
   // 4 waves per block; enough blocks to fill 256 CUs several times, each wave
   // then walks several tokens so its per-lane setup is amortised.
@@ -249,11 +292,11 @@ hipError_t launch_qknorm_rope(void *q, void *k, int B, int T, int H, int KV, int
   if (blocks > 4096) blocks = 4096;
   dim3 grid((unsigned)blocks), block(256);
   if (D == 128) {
-    if (bf16) hipLaunchKernelGGL((qknorm_rope_kernel<128, true>), grid, block, 0, s, q, k, B, T, H, KV, pos_offset, f, eps, gain);
-    else hipLaunchKernelGGL((qknorm_rope_kernel<128, false>), grid, block, 0, s, q, k, B, T, H, KV, pos_offset, f, eps, gain);
+    if (bf16) hipLaunchKernelGGL((qknorm_rope_kernel<128, true>), grid, block, 0, s, q, k, B, T, H, KV, pos_offset, f, eps, gain, ro);
+    else hipLaunchKernelGGL((qknorm_rope_kernel<128, false>), grid, block, 0, s, q, k, B, T, H, KV, pos_offset, f, eps, gain, ro);
   } else {
-    if (bf16) hipLaunchKernelGGL((qknorm_rope_kernel<64, true>), grid, block, 0, s, q, k, B, T, H, KV, pos_offset, f, eps, gain);
-    else hipLaunchKernelGGL((qknorm_rope_kernel<64, false>), grid, block, 0, s, q, k, B, T, H, KV, pos_offset, f, eps, gain);
+    if (bf16) hipLaunchKernelGGL((qknorm_rope_kernel<64, true>), grid, block, 0, s, q, k, B, T, H, KV, pos_offset, f, eps, gain, ro);
+    else hipLaunchKernelGGL((qknorm_rope_kernel<64, false>), grid, block, 0, s, q, k, B, T, H, KV, pos_offset, f, eps, gain, ro);
   }
   return hipGetLastError();
 }
