@@ -495,7 +495,7 @@ def main():
 
     import torch
     import transformer_attention_qknorm_amd as nc
-    from workloads import D12, D20, DECODE, GQA, decode_inputs
+    from workloads import D12, D20, DECODE, GQA, HD64, decode_inputs
 
     nc.lib()  # fail loudly if the HIP library is missing
     dev = torch.device("cuda:0")
@@ -593,6 +593,9 @@ def main():
     configs = None
     if not args.no_configs:
         configs = {c.name: time_config(nc, torch, c, dev, stream) for c in (GQA, D12, D20) if c is not cfg}
+        # the head_dim-64 kernels on a layer of GPT-2's head size (not one of the
+        # workloads above: reported as detail)
+        detail["head_dim_64"] = time_config(nc, torch, HD64, dev, stream)
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,

@@ -20,7 +20,7 @@ import torch
 import oracle
 import transformer_attention_qknorm_amd as nc
 from parity_util import check, check_lse, f64, group_slice, stored
-from workloads import D12, D20, DECODE, GQA, TINY, config_inputs, decode_inputs
+from workloads import D12, D20, DECODE, GQA, HD64, TINY, config_inputs, decode_inputs
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -103,7 +103,7 @@ def _gpu_layer(cfg, W):
     return res
 
 
-LAYER_CASES = [(cfg, W) for cfg in (D12, D20, GQA) for W in sorted(set(cfg.windows))]
+LAYER_CASES = [(cfg, W) for cfg in (D12, D20, GQA, HD64) for W in sorted(set(cfg.windows))]
 
 
 @pytest.mark.parametrize("cfg,W", LAYER_CASES, ids=[f"{c.name}-W{W}" for c, W in LAYER_CASES])

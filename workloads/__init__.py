@@ -84,6 +84,11 @@ D20 = AttnConfig("d20_b32_t2048_h10_d128_bf16", B=32, T=2048, H=10, KV=10, D=128
 GQA = AttnConfig("gqa_b16_t4096_h12_kv4_d128_bf16", B=16, T=4096, H=12, KV=4, D=128, dtype="bf16",
                  short_window=2048, windows=(2048, 2048, 2048, -1),
                  pre_normed=True, seed=4)
+# head_dim 64 (GPT-2's n_embd / n_head = 768 / 12, "nanoGPT Administrator & Developer
+# Guide", sections 3 and 6) at the d12 layer's token count per batch: a measurement
+# and parity case for the head_dim-64 kernels, inputs taken as post-norm.
+HD64 = AttnConfig("hd64_b16_t2048_h12_d64_bf16", B=16, T=2048, H=12, KV=12, D=64, dtype="bf16",
+                  short_window=1024, windows=(1024, 1024, 1024, -1), pre_normed=True, seed=7)
 DECODE = DecodeConfig("decode_b64_h10_d128_bf16", B=64, H=10, KV=10, D=128,
                       min_len=256, max_len=8192, T_max=8320)
 
