@@ -319,6 +319,18 @@ def qknorm_detail(nc, torch, cfg, dev, stream):
         fb["full" if W < 0 else f"w{W}"] = {"two_calls_us": round(t2, 2), "fused_us": round(t1, 2),
                                             "fused_bwd_TFLOPs": round(fl / (t1 * 1e-6) / 1e12, 1)}
     out["bwd_qknorm_rope"] = fb
+    # fwd+bwd including QK-norm + RoPE and its backward, over the layer pattern:
+    # the separate calls, and the fused forward + fused backward
+    tot_f = tot_sep = tot_fused = 0.0
+    for W in cfg.windows:
+        key = "full" if W < 0 else f"w{W}"
+        tot_f += 12 * D * visible_pairs(T, W) * B * H
+        tot_sep += (fused[key]["two_calls_us"] + fb[key]["two_calls_us"]) * 1e-6
+        tot_fused += (fused[key]["fused_us"] + fb[key]["fused_us"]) * 1e-6
+    out["fwd_bwd_incl_qknorm_rope"] = {
+        "layers": list(cfg.windows), "separate_calls_tflops": round(tot_f / tot_sep / 1e12, 1),
+        "fused_calls_tflops": round(tot_f / tot_fused / 1e12, 1),
+        "note": "algorithmic attention FLOPs of the layers / time of QK-norm + RoPE, fwd, bwd and the norm's bwd"}
     del q, k, v, dq, dk, o, lse, do, qn, kn, ws, gq, gk, gv, rstd
     torch.cuda.empty_cache()
     return out
