@@ -508,6 +508,41 @@ def test_decode_random_shapes(case):
         assert torch.equal(a[mask].view(torch.int16), b_[mask].view(torch.int16))
 
 
+@pytest.mark.parametrize("W,D", [(0, 128), (100, 128), (511, 128), (-1, 128), (300, 64)])
+def test_decode_many_groups(W, D):
+    """512 (sequence, kv head) pairs with grouped query heads (G = 2): lengths across
+    the whole cache (0 and T_max - 1 included), NaN-poisoned slots past them, two
+    invalid lengths in the same batch (NaN rows, cache untouched)."""
+    B, H, KV, Tm = 64, 16, 8, 700
+    say(f"decode many groups W={W} D={D}")
+    q, kn, vn, kc, vc, lens = decode_inputs(B, H, KV, D, 0, Tm - 1, Tm, seed=70 + D, poison=True)
+    lens[0], lens[1] = 0, Tm - 1
+    kc[1] = torch.nan_to_num(kc[1].float(), nan=0.5).to(kc.dtype)   # every slot of row 1 is read
+    vc[1] = torch.nan_to_num(vc[1].float(), nan=-0.25).to(vc.dtype)
+    lens[2], lens[3] = -1, Tm      # invalid
+    ok = torch.ones(B, dtype=torch.bool)
+    ok[2] = ok[3] = False
+    ro, rlse, _, _ = oracle.decode(f64(q[ok]), f64(kn[ok]), f64(vn[ok]), f64(kc[ok]), f64(vc[ok]),
+                                   lens[ok].numpy(), W)
+    qd, knd, vnd, kcd, vcd, ld = to_dev(q, kn, vn, kc, vc, lens)
+    o, lse = nc.decode(qd, knd, vnd, kcd, vcd, ld, window=W, return_lse=True)
+    torch.cuda.synchronize()
+    o, lse = o.cpu(), lse.cpu()
+    check(o[ok], ro, "bf16", "o")
+    check_lse(lse[ok], rlse, "bf16", "lse")
+    assert torch.isnan(o[~ok].float()).all() and torch.isnan(lse[~ok]).all()
+    kc_after = kcd.cpu()
+    for b in range(B):
+        s_ = int(lens[b])
+        if 0 <= s_ < Tm:
+            assert torch.equal(kc_after[b, s_], kn[b, 0])
+            keep = torch.ones(Tm, dtype=torch.bool)
+            keep[s_] = False
+            assert torch.equal(kc_after[b, keep].view(torch.int16), kc[b, keep].view(torch.int16))
+        else:
+            assert torch.equal(kc_after[b].view(torch.int16), kc[b].view(torch.int16))
+
+
 @pytest.mark.parametrize("D", [128, 64])
 def test_decode_matches_fwd_row(D):
     """Decode at position s equals row s of the forward over the prefix (the
