@@ -33,3 +33,14 @@ def test_traffic_lookup_requires_matching_source():
     assert h == bench.kernel_source_hash("attn_bwd_bf16.hip") and len(h) == 16
     tr = bench.measured_traffic("bwd_dkdv", "gqa_b16_t4096_h12_kv4_d128_bf16")
     assert tr is None or (isinstance(tr, int) and tr > 0)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """Nothing here uses a second GPU: --gpus N > 1 (or a multi-rank launch)
+    exits with a message before touching any device."""
+    import subprocess
+    for extra_env, argv in (({}, ["--gpus", "2"]), ({"WORLD_SIZE": "8"}, [])):
+        env = dict(os.environ, **extra_env)
+        r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *argv], capture_output=True, text=True,
+                           env=env, timeout=120)
+        assert r.returncode == 2 and "one GPU only" in r.stderr, (r.returncode, r.stderr)
