@@ -97,13 +97,29 @@ __device__ __forceinline__ void split_bf16x2(float x0, float x1, uint32_t &hi, u
   lo = pack_bf16x2(x0 - __uint_as_float(hi << 16), x1 - __uint_as_float(hi & 0xffff0000u));
 }
 
+// -inf on the scores of a straddling tile that are not visible (a query row past
+// T, a key after the query, or one further back than the window): element e of
+// the lane holds query row qtile0 + 32 qb + 8 (e / 4) + 4 hh + e % 4 against key
+// key_lane.  Applied before the exponentials, so their block stays free of
+// branches.
+__device__ __forceinline__ void dkdv_mask(f32x16 &sacc, int qb, int qtile0, int key_lane, int T, int W, int hh) {
+  const int r0 = qtile0 + 32 * qb + 4 * hh;  // query row of element 0
+  const int d0 = r0 - key_lane;
+  const int rlim = T - r0;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int off = 8 * (e >> 2) + (e & 3);
+    const bool vis = (off < rlim) & (d0 + off >= 0) & ((W < 0) | (d0 + off <= W));
+    sacc[e] = vis ? sacc[e] : -INFINITY;
+  }
+}
+
 // P = exp2(S c - LSE log2 e) and dS = P (dP - D) as bf16 MFMA operands, each as
 // a hi + lo pair (pk/pl, dk/dl: element pairs of accumulator rows 8 i + 4 hh + j,
-// the layout acc_to_operand gives).
-__device__ __forceinline__ void dkdv_p_ds(const f32x16 &sacc, const f32x16 &dmd, const float *lse2, bool need_mask,
-                                          int qb, int qtile0, int key_lane, int T, int W, float c, int hh,
-                                          uint32_t (&pk)[8], uint32_t (&pl)[8], uint32_t (&dk)[8],
-                                          uint32_t (&dl)[8]) {
+// the layout acc_to_operand gives).  Scores masked to -inf give P = 0 (c > 0).
+__device__ __forceinline__ void dkdv_p_ds(const f32x16 &sacc, const f32x16 &dmd, const float *lse2, int qb,
+                                          float c, int hh, uint32_t (&pk)[8], uint32_t (&pl)[8],
+                                          uint32_t (&dk)[8], uint32_t (&dl)[8]) {
   // rows of this lane's accumulator elements: 32 qb + 8 i + 4 hh + j
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -114,11 +130,6 @@ __device__ __forceinline__ void dkdv_p_ds(const f32x16 &sacc, const f32x16 &dmd,
     for (int j = 0; j < 4; ++j) {
       const int e = 4 * i + j;
       p[j] = fast_exp2(__builtin_fmaf(sacc[e], c, -l4[j]));
-      if (need_mask) {
-        const int qi = qtile0 + r0 + j;
-        const bool vis = qi < T && key_lane <= qi && (W < 0 || qi - key_lane <= W);
-        if (!vis) p[j] = 0.f;
-      }
       ds[j] = p[j] * dmd[e];
     }
     split_bf16x2(p[0], p[1], pk[2 * i], pl[2 * i]);
@@ -177,9 +188,34 @@ struct NormRopeBwd {
   float gain;
 };
 
+// The norm's arguments as a fused kernel keeps them: copied into LDS at its
+// start and read back by its epilogue, so that none of them occupies registers
+// through the main loop (the loop needs all of them).
+template <int D>
+struct NormRopeLds {
+  double turns[D / 2];
+  const float *rstd;
+  const int32_t *pos_offset;
+  long long rstd_stride;
+  int rstd_k_off;
+  float gain;
+};
+
+template <int D>
+__device__ __forceinline__ void stage_norm_rope(NormRopeLds<D> &s, const NormRopeBwd &nb, int tid) {
+  if (tid < D / 2) s.turns[tid] = nb.turns[tid];
+  if (tid == 0) {
+    s.rstd = nb.rstd;
+    s.pos_offset = nb.pos_offset;
+    s.rstd_stride = nb.rstd_stride;
+    s.rstd_k_off = nb.rstd_k_off;
+    s.gain = nb.gain;
+  }
+}
+
 template <int D>
 __device__ __forceinline__ void norm_rope_bwd_row(f32x16 (&g)[Geom<D>::kDBlocks], const uint16_t *yrow, float rs,
-                                                  double pos, const NormRopeBwd &nb, int hh) {
+                                                  double pos, const NormRopeLds<D> &nb, int hh) {
   constexpr int NB = Geom<D>::kDBlocks, HB = NB / 2;
   float y[NB][16];
 #pragma unroll
@@ -204,12 +240,8 @@ __device__ __forceinline__ void norm_rope_bwd_row(f32x16 (&g)[Geom<D>::kDBlocks]
   for (int db = 0; db < HB; ++db)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      // pair index 32 db + 8 (e >> 2) + 4 hh + (e & 3): both candidates as
-      // uniform loads of the argument block, then a per-lane select
-      const int p0 = 32 * db + 8 * (e >> 2) + (e & 3);
-      double f_lo = nb.turns[p0], f_hi = nb.turns[p0 + 4];
-      asm("" : "+s"(f_lo), "+s"(f_hi));
-      double turns = pos * (hh ? f_hi : f_lo);
+      // pair index 32 db + 8 (e >> 2) + 4 hh + (e & 3)
+      double turns = pos * nb.turns[32 * db + 8 * (e >> 2) + 4 * hh + (e & 3)];
       turns -= rint(turns);
       const float tf = (float)turns;
       const float sn = __builtin_amdgcn_sinf(tf), cs = __builtin_amdgcn_cosf(tf);
@@ -277,7 +309,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t *__rest
   __shared__ __attribute__((aligned(1024))) char buf0[kBuf];
   __shared__ __attribute__((aligned(1024))) char buf1[kBuf];
   __shared__ __attribute__((aligned(1024))) char vtile[kBlockN * Gm::kRowBytes];
+  __shared__ NormRopeLds<D> nrs;  // fused only
   const int tid = threadIdx.x;
+  if constexpr (FUSE) stage_norm_rope<D>(nrs, nb, tid);  // read after the loop's barriers
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int kw = wave;        // key sub-block (32 keys) of this wave
@@ -324,7 +358,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t *__rest
     tile_load_lds<D, 4, kR>(base, make_tile_src(Q + hoff, q_stride, T), voff, p.qt * kR);
     tile_load_lds<D, 4, kR>(base + kHalfTile, make_tile_src(dO + hoff, q_stride, T), voff, p.qt * kR);
     if (wave < 2) {  // waves 0, 1: 64 lse rows and 64 delta rows, 4 bytes per lane (zeros past T)
-      const float *row = (wave == 0 ? lse2g : delta) + rbase + (long long)p.g * T;
+      // the row address is the same on every lane: taken from the first (both
+      // 32-bit halves; the builtin moves one dword), so the buffer resource is
+      // built in scalar registers
+      const unsigned long long ra =
+          (unsigned long long)((wave == 0 ? lse2g : delta) + rbase + (long long)p.g * T);
+      const unsigned ra_lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)ra);
+      const unsigned ra_hi = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)(ra >> 32));
+      const float *row = (const float *)(((unsigned long long)ra_hi << 32) | ra_lo);
       const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void *)row, (short)0, T * 4, 0x00020000);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(base + 2 * kHalfTile + wave * 64 * 4), 4,
                                                lane * 4, p.qt * kR * 4, 0, 0);
@@ -375,7 +416,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t *__rest
       f32x16 s0, p0;
       uint32_t pk0[8], pl0[8], dk0[8], dl0[8];
       dkdv_sdp<D>(s0, p0, qs, dos, vtile, ndl, L, kreg, 0, kw, hh);
-      dkdv_p_ds(s0, p0, lse2, msk, 0, qr0, key_lane, T, W, c, hh, pk0, pl0, dk0, dl0);
+      if (msk) dkdv_mask(s0, 0, qr0, key_lane, T, W, hh);
+      dkdv_p_ds(s0, p0, lse2, 0, c, hh, pk0, pl0, dk0, dl0);
       dkdv_acc<D>(dkacc, dvacc, pk0, pl0, dk0, dl0, qs, dos, L, 0);
     }
     lds_loads_done_barrier();
@@ -394,9 +436,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t *__rest
     for (int db = 0; db < Gm::kDBlocks; ++db)
 #pragma unroll
       for (int e = 0; e < 16; ++e) dkacc[db][e] *= scale;
-    const double posd = (double)((nb.pos_offset ? nb.pos_offset[b] : 0) + key_lane);
-    const float rs = nb.rstd[((long long)b * T + key_lane) * nb.rstd_stride + nb.rstd_k_off + kvh];
-    norm_rope_bwd_row<D>(dkacc, K + off, rs, posd, nb, hh);
+    // the norm's arguments read from here on, through a pointer the compiler
+    // cannot trace back, so that none of them is held in registers through the
+    // loop above
+    const double posd = (double)((nrs.pos_offset ? nrs.pos_offset[b] : 0) + key_lane);
+    const float rs = nrs.rstd[((long long)b * T + key_lane) * nrs.rstd_stride + nrs.rstd_k_off + kvh];
+    norm_rope_bwd_row<D>(dkacc, K + off, rs, posd, nrs, hh);
     kscale = 1.f;
   }
 #pragma unroll
@@ -475,7 +520,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t *__restri
   __shared__ __attribute__((aligned(1024))) char kb1[Gm::kTileBytes];
   __shared__ __attribute__((aligned(1024))) char vb0[Gm::kTileBytes];
   __shared__ __attribute__((aligned(1024))) char vb1[Gm::kTileBytes];
+  __shared__ NormRopeLds<D> nrs;  // fused only
   const int tid = threadIdx.x;
+  if constexpr (FUSE) stage_norm_rope<D>(nrs, nb, tid);  // read after the loop's barriers
   const int lane = tid & 63;
   const int wave = tid >> 6;
   // launch order as the forward's: heaviest query blocks first, the G heads of a
@@ -583,9 +630,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t *__restri
     for (int db = 0; db < Gm::kDBlocks; ++db)
 #pragma unroll
       for (int e = 0; e < 16; ++e) dqacc[db][e] *= scale;
-    const double pos = (double)((nb.pos_offset ? nb.pos_offset[b] : 0) + q_lane);
-    const float rs = nb.rstd[((long long)b * T + q_lane) * nb.rstd_stride + h];
-    norm_rope_bwd_row<D>(dqacc, Q + qoff, rs, pos, nb, hh);
+    const double pos = (double)((nrs.pos_offset ? nrs.pos_offset[b] : 0) + q_lane);
+    const float rs = nrs.rstd[((long long)b * T + q_lane) * nrs.rstd_stride + h];
+    norm_rope_bwd_row<D>(dqacc, Q + qoff, rs, pos, nrs, hh);
     qscale = 1.f;
   }
 #pragma unroll
