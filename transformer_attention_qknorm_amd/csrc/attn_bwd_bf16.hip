@@ -592,6 +592,17 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t *__restri
       f32x16 sacc[2], dpacc[2];
       dq_st_tile(sacc, ks, L, qreg);
       dq_st_tile(dpacc, vs, L, dreg);
+      // scheduling of the 32 MFMAs above and their 32 LDS operand reads: each
+      // read four MFMAs ahead of its use
+#pragma unroll
+      for (int i = 0; i < 4; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+      for (int i = 0; i < 28; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       if (!(k0 + kTileN - 1 <= qw0 && (W < 0 || qw_last - k0 <= W))) dq_mask_tile(sacc, k0, q_lane, W, hh);
       // dS^T in place of S^T: P = exp2(S c - LSE log2 e), dS = P (dP - D)
 #pragma unroll
