@@ -114,53 +114,62 @@ __device__ __forceinline__ void dkdv_mask(f32x16 &sacc, int qb, int qtile0, int 
   }
 }
 
-// P = exp2(S c - LSE log2 e) and dS = P (dP - D) as bf16 MFMA operands, each as
-// a hi + lo pair (pk/pl, dk/dl: element pairs of accumulator rows 8 i + 4 hh + j,
-// the layout acc_to_operand gives).  Scores masked to -inf give P = 0 (c > 0).
-__device__ __forceinline__ void dkdv_p_ds(const f32x16 &sacc, const f32x16 &dmd, const float *lse2, int qb,
-                                          float c, int hh, uint32_t (&pk)[8], uint32_t (&pl)[8],
-                                          uint32_t (&dk)[8], uint32_t (&dl)[8]) {
-  // rows of this lane's accumulator elements: 32 qb + 8 i + 4 hh + j
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r0 = 32 * qb + 8 * i + 4 * hh;
-    const f32x4 l4 = *(const f32x4 *)(lse2 + r0);
-    float p[4], ds[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = 4 * i + j;
-      p[j] = fast_exp2(__builtin_fmaf(sacc[e], c, -l4[j]));
-      ds[j] = p[j] * dmd[e];
-    }
-    split_bf16x2(p[0], p[1], pk[2 * i], pl[2 * i]);
-    split_bf16x2(p[2], p[3], pk[2 * i + 1], pl[2 * i + 1]);
-    split_bf16x2(ds[0], ds[1], dk[2 * i], dl[2 * i]);
-    split_bf16x2(ds[2], ds[3], dk[2 * i + 1], dl[2 * i + 1]);
-  }
+// P = exp2(S c - LSE log2 e) and dS = P (dP - D) of one element pair (row i of
+// 8, pair jp of 2: accumulator elements 4 i + 2 jp, + 1) as bf16 MFMA operands,
+// each as a hi + lo pair (pk/pl, dk/dl[2 i + jp]: the layout acc_to_operand
+// gives).  Scores masked to -inf give P = 0 (c > 0).
+__device__ __forceinline__ void dkdv_p_ds_pair(const f32x16 &sacc, const f32x16 &dmd, const f32x4 (&l4)[4],
+                                               float c, int i, int jp, uint32_t (&pk)[8], uint32_t (&pl)[8],
+                                               uint32_t (&dk)[8], uint32_t (&dl)[8]) {
+  const int e = 4 * i + 2 * jp;
+  const float p0 = fast_exp2(__builtin_fmaf(sacc[e], c, -l4[i][2 * jp]));
+  const float p1 = fast_exp2(__builtin_fmaf(sacc[e + 1], c, -l4[i][2 * jp + 1]));
+  split_bf16x2(p0, p1, pk[2 * i + jp], pl[2 * i + jp]);
+  split_bf16x2(p0 * dmd[e], p1 * dmd[e + 1], dk[2 * i + jp], dl[2 * i + jp]);
 }
 
-// dV^T += dO^T (P_hi + P_lo) and dK^T += Q^T (dS_hi + dS_lo), contraction over the
-// 32 query rows of block qb.
+// From S and dP - D of the 32 query rows of the staged tile (rows 8 i + 4 hh + j
+// of the lane's accumulators, i < 4): P and dS, then dV^T += dO^T (P_hi + P_lo)
+// and dK^T += Q^T (dS_hi + dS_lo), contraction over those rows in two halves of
+// 16.  The second half's exponentials and splits are placed among the first
+// half's MFMAs (each group fenced), so that one wave's arithmetic runs while its
+// own MFMAs execute.
 template <int D>
-__device__ __forceinline__ void dkdv_acc(f32x16 (&dkacc)[Geom<D>::kDBlocks], f32x16 (&dvacc)[Geom<D>::kDBlocks],
-                                         const uint32_t (&pk)[8], const uint32_t (&pl)[8], const uint32_t (&dk)[8],
-                                         const uint32_t (&dl)[8], const char *qs, const char *dos,
-                                         const TileLane<D> &L, int qb) {
+__device__ __forceinline__ void dkdv_p_ds_acc(f32x16 (&dkacc)[Geom<D>::kDBlocks], f32x16 (&dvacc)[Geom<D>::kDBlocks],
+                                              const f32x16 &sacc, const f32x16 &dmd, const float *lse2, float c,
+                                              int hh, const char *qs, const char *dos, const TileLane<D> &L) {
+  constexpr int NB = Geom<D>::kDBlocks;
+  constexpr int kPer = 4 / NB;  // element pairs of the second half per block of the first
+  f32x4 l4[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) l4[i] = *(const f32x4 *)(lse2 + 8 * i + 4 * hh);
+  uint32_t pk[8], pl[8], dk[8], dl[8];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int jp = 0; jp < 2; ++jp) dkdv_p_ds_pair(sacc, dmd, l4, c, i, jp, pk, pl, dk, dl);
 #pragma unroll
   for (int c2 = 0; c2 < 2; ++c2) {
-    const int cs = 2 * qb + c2;
     const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pk[4 * c2], pk[4 * c2 + 1], pk[4 * c2 + 2], pk[4 * c2 + 3]});
     const bf16x8 pbl = __builtin_bit_cast(bf16x8, u32x4{pl[4 * c2], pl[4 * c2 + 1], pl[4 * c2 + 2], pl[4 * c2 + 3]});
     const bf16x8 dsb = __builtin_bit_cast(bf16x8, u32x4{dk[4 * c2], dk[4 * c2 + 1], dk[4 * c2 + 2], dk[4 * c2 + 3]});
     const bf16x8 dsl = __builtin_bit_cast(bf16x8, u32x4{dl[4 * c2], dl[4 * c2 + 1], dl[4 * c2 + 2], dl[4 * c2 + 3]});
 #pragma unroll
-    for (int db = 0; db < Geom<D>::kDBlocks; ++db) {
-      const bf16x8 a = col_operand(dos, L, db, cs);
-      const bf16x8 qa = col_operand(qs, L, db, cs);
+    for (int db = 0; db < NB; ++db) {
+      const bf16x8 a = col_operand(dos, L, db, c2);
+      const bf16x8 qa = col_operand(qs, L, db, c2);
+      if (c2 == 0) {
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+          const int q = db * kPer + k;
+          dkdv_p_ds_pair(sacc, dmd, l4, c, 2 + q / 2, q % 2, pk, pl, dk, dl);
+        }
+      }
       dvacc[db] = mfma32(a, pb, dvacc[db]);
       dkacc[db] = mfma32(qa, dsb, dkacc[db]);
       dvacc[db] = mfma32(a, pbl, dvacc[db]);
       dkacc[db] = mfma32(qa, dsl, dkacc[db]);
+      if (c2 == 0) __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
@@ -414,11 +423,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t *__rest
     if (act) {
       const bool msk = !(qr0 >= kw_last && (W < 0 || qr0 + 31 - kw0 <= W) && qr0 + 31 < T);
       f32x16 s0, p0;
-      uint32_t pk0[8], pl0[8], dk0[8], dl0[8];
       dkdv_sdp<D>(s0, p0, qs, dos, vtile, ndl, L, kreg, 0, kw, hh);
       if (msk) dkdv_mask(s0, 0, qr0, key_lane, T, W, hh);
-      dkdv_p_ds(s0, p0, lse2, 0, c, hh, pk0, pl0, dk0, dl0);
-      dkdv_acc<D>(dkacc, dvacc, pk0, pl0, dk0, dl0, qs, dos, L, 0);
+      dkdv_p_ds_acc<D>(dkacc, dvacc, s0, p0, lse2, c, hh, qs, dos, L);
     }
     lds_loads_done_barrier();
   };

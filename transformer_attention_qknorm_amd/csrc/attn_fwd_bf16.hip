@@ -69,6 +69,40 @@ __device__ __forceinline__ void s_tile(f32x16 (&sacc)[2], const char *ks, const 
   }
 }
 
+// s_tile for tile t+1 with tile t's exponentials (softmax_exp below) placed
+// among its MFMAs, 32 / (2 D / 16) of them after each MFMA, so that one wave's
+// exponentials run while its own MFMAs execute.
+template <int D>
+__device__ __forceinline__ void s_tile_exp(f32x16 (&snext)[2], const char *ks, const TileLane<D> &L,
+                                           const bf16x8 (&qreg)[Geom<D>::kSteps], FwdState<D> &st,
+                                           f32x16 (&scur)[2], float c, bool &overflow) {
+  constexpr int kAhead = 4;
+  constexpr int kN = 2 * Geom<D>::kSteps;
+  constexpr int kPer = 32 / kN;
+  const float nmc = (st.m_ref == -INFINITY) ? 0.f : -st.m_ref * c;
+  float ls = 0.f;
+  bf16x8 kop[kN];
+#pragma unroll
+  for (int i = 0; i < kAhead; ++i) kop[i] = row_operand(ks, L, i >> 1, i & 1);
+  snext[0] = f32x16{};
+  snext[1] = f32x16{};
+#pragma unroll
+  for (int i = 0; i < kN; ++i) {  // i = 2 s + kb
+    if (i + kAhead < kN) kop[i + kAhead] = row_operand(ks, L, (i + kAhead) >> 1, (i + kAhead) & 1);
+    snext[i & 1] = mfma32(kop[i], qreg[i >> 1], snext[i & 1]);
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int x = i * kPer + k;
+      const float p = fast_exp2(__builtin_fmaf(scur[x >> 4][x & 15], c, nmc));
+      scur[x >> 4][x & 15] = p;
+      ls += p;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  overflow |= ls > kSumLimit;
+  st.l_run += ls;
+}
+
 // Masks a tile that straddles the causal diagonal or the window edge.  Element e
 // of sacc[kb] is key k0 + 32 kb + 8 (e >> 2) + 4 hh + (e & 3) of query q_lane.
 // With d0 = k0 + 4 hh - q_lane, element (kb, e) has key - query = d0 + off(kb, e)
@@ -367,8 +401,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const uint16_t *_
       if (cur && next) {
         // steady state: one straight-line block holding the S MFMAs of tile t+1,
         // then the exponentials and the PV MFMAs of tile t
-        s_tile(snext, kcur, L, qreg);
-        softmax_exp(st, scur, c, overflow);
+        s_tile_exp(snext, kcur, L, qreg, st, scur, c, overflow);
         pv_tile(st, scur, vcur, L);
         scur[0] = snext[0];
         scur[1] = snext[1];
