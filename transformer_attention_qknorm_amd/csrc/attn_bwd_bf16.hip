@@ -487,6 +487,35 @@ __device__ __forceinline__ void dq_st_tile(f32x16 (&acc)[2], const char *tile, c
   }
 }
 
+// dP^T = V dO^T for the tile (as dq_st_tile), with the exponentials of the
+// tile's scores placed among its MFMAs (P = exp2(S c - LSE log2 e) in place of
+// S^T, 32 / (2 D / 16) after each MFMA), so that one wave's exponentials run
+// while its own MFMAs execute.  Operands read four MFMAs ahead.
+template <int D>
+__device__ __forceinline__ void dq_dp_tile_exp(f32x16 (&dpacc)[2], const char *vs, const TileLane<D> &L,
+                                               const bf16x8 (&dreg)[Geom<D>::kSteps], f32x16 (&sacc)[2], float c,
+                                               float lse2_q) {
+  constexpr int kAhead = 4;
+  constexpr int kN = 2 * Geom<D>::kSteps;
+  constexpr int kPer = 32 / kN;
+  bf16x8 op[kN];
+#pragma unroll
+  for (int i = 0; i < kAhead; ++i) op[i] = row_operand(vs, L, i >> 1, i & 1);
+  dpacc[0] = f32x16{};
+  dpacc[1] = f32x16{};
+#pragma unroll
+  for (int i = 0; i < kN; ++i) {  // i = 2 s + kb
+    if (i + kAhead < kN) op[i + kAhead] = row_operand(vs, L, (i + kAhead) >> 1, (i + kAhead) & 1);
+    dpacc[i & 1] = mfma32(op[i], dreg[i >> 1], dpacc[i & 1]);
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int x = i * kPer + k;
+      sacc[x >> 4][x & 15] = fast_exp2(__builtin_fmaf(sacc[x >> 4][x & 15], c, -lse2_q));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // -inf on the elements of a straddling tile that are not visible: with
 // d0 = k0 + 4 hh - q_lane, element (kb, e) has key - query = d0 + off(kb, e).
 __device__ __forceinline__ void dq_mask_tile(f32x16 (&sacc)[2], int k0, int q_lane, int W, int hh) {
@@ -598,27 +627,24 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const uint16_t *__restri
       const int k0 = t * kTileN;
       f32x16 sacc[2], dpacc[2];
       dq_st_tile(sacc, ks, L, qreg);
-      dq_st_tile(dpacc, vs, L, dreg);
-      // scheduling of the 32 MFMAs above and their 32 LDS operand reads: each
-      // read four MFMAs ahead of its use
+      // scheduling of those 16 MFMAs and their LDS operand reads: each read four
+      // MFMAs ahead of its use
 #pragma unroll
       for (int i = 0; i < 4; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
 #pragma unroll
-      for (int i = 0; i < 28; ++i) {
+      for (int i = 0; i < 12; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       if (!(k0 + kTileN - 1 <= qw0 && (W < 0 || qw_last - k0 <= W))) dq_mask_tile(sacc, k0, q_lane, W, hh);
-      // dS^T in place of S^T: P = exp2(S c - LSE log2 e), dS = P (dP - D)
+      // P in place of S^T (among the dP MFMAs), then dS^T = P (dP - D)
+      dq_dp_tile_exp(dpacc, vs, L, dreg, sacc, c, lse2_q);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float p = fast_exp2(__builtin_fmaf(sacc[kb][e], c, -lse2_q));
-          sacc[kb][e] = p * (dpacc[kb][e] + nd_q);
-        }
+        for (int e = 0; e < 16; ++e) sacc[kb][e] *= dpacc[kb][e] + nd_q;
 #pragma unroll
       for (int cs = 0; cs < 4; ++cs) {
         bf16x8 dh, dl;
