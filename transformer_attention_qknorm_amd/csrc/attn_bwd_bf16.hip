@@ -443,9 +443,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t *__rest
     for (int db = 0; db < Gm::kDBlocks; ++db)
 #pragma unroll
       for (int e = 0; e < 16; ++e) dkacc[db][e] *= scale;
-    // the norm's arguments read from here on, through a pointer the compiler
-    // cannot trace back, so that none of them is held in registers through the
-    // loop above
+    // the norm's arguments, from their copy in LDS
     const double posd = (double)((nrs.pos_offset ? nrs.pos_offset[b] : 0) + key_lane);
     const float rs = nrs.rstd[((long long)b * T + key_lane) * nrs.rstd_stride + nrs.rstd_k_off + kvh];
     norm_rope_bwd_row<D>(dkacc, K + off, rs, posd, nrs, hh);

@@ -399,8 +399,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(const uint16_t *_
         init_ref(st, scur);
       }
       if (cur && next) {
-        // steady state: one straight-line block holding the S MFMAs of tile t+1,
-        // then the exponentials and the PV MFMAs of tile t
+        // steady state: one straight-line block holding the S MFMAs of tile t+1
+        // with the exponentials of tile t among them, then the PV MFMAs of tile t
         s_tile_exp(snext, kcur, L, qreg, st, scur, c, overflow);
         pv_tile(st, scur, vcur, L);
         scur[0] = snext[0];
