@@ -17,12 +17,11 @@
 // (V^T comes from LDS with transposing reads).
 //
 // Software pipeline: in step t a wave issues the S^T MFMAs of tile t+1 (their K
-// operands read four MFMAs ahead), then the softmax of tile t, then O += P V for
-// tile t; two workgroups share a CU, so a SIMD runs two such waves.  K therefore
-// runs one tile ahead of V: step t reads K(t+1) and V(t) while K(t+2) and V(t+1)
-// are being copied into the other halves of two LDS rings.  (Placing the
-// softmax's exponentials between the S MFMAs of the same wave was measured too:
-// no faster on this chip.)
+// operands read four MFMAs ahead) with the softmax exponentials of tile t placed
+// among them, then O += P V for tile t; two workgroups share a CU, so a SIMD runs
+// two such waves.  K therefore runs one tile ahead of V: step t reads K(t+1) and
+// V(t) while K(t+2) and V(t+1) are being copied into the other halves of two LDS
+// rings.
 // Tiles entirely outside a wave's window are skipped; masks are applied only on
 // tiles that straddle the causal diagonal or the window edge.
 //
