@@ -39,6 +39,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 FLOP/clk)
+PEAK_FP8_TFLOPS = 5033.2    # MI355X dense fp8 MFMA (twice the bf16 rate)
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 METRIC = "attn fwd+bwd TFLOP/s (unmasked FLOPs) & % bf16 MFMA peak; decode GB/s"
 
@@ -250,6 +251,33 @@ def time_config(nc, torch, cfg, dev, stream, iters=10):
     torch.cuda.empty_cache()
     return {"workload": cfg.name, "layers": layers, "sssl_fwd_bwd_tflops": round(tot_f / tot_t / 1e12, 1),
             "sssl_frac_bf16_peak": round(tot_f / tot_t / 1e12 / PEAK_BF16_TFLOPS, 4), "timed_calls": iters}
+
+
+def fp8_detail(nc, torch, cfg, dev, stream, iters=10):
+    """The fp8 forward on a workload's shape (inputs drawn as its bf16 ones and
+    stored as e4m3 with per-tensor descales), per window of its layer pattern,
+    beside the bf16 forward on the same shape: TFLOP/s (the same algorithmic
+    4 D flops per visible pair) and the fraction of the fp8 MFMA peak."""
+    from workloads import config_inputs, fp8_inputs
+    (q8, k8, v8), (dq, dk, dv) = fp8_inputs(cfg.B, cfg.T, cfg.H, cfg.KV, cfg.D, seed=cfg.seed)
+    q8, k8, v8 = q8.to(dev), k8.to(dev), v8.to(dev)
+    q0, k0, v0, _ = config_inputs(cfg)
+    q, k, v = q0.to(dev), k0.to(dev), v0.to(dev)
+    del q0, k0, v0
+    o = torch.empty(cfg.B, cfg.T, cfg.H, cfg.D, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(cfg.B, cfg.H, cfg.T, dtype=torch.float32, device=dev)
+    out = {"workload": cfg.name, "descales": [round(x, 8) for x in (dq, dk, dv)]}
+    for W in sorted(set(cfg.windows)):
+        fl = 4 * cfg.D * visible_pairs(cfg.T, W) * cfg.B * cfg.H
+        t8 = event_us(torch, stream, lambda: nc.fwd_fp8(q8, k8, v8, dq, dk, dv, window=(W, 0), out=(o, lse)), iters)
+        tb = event_us(torch, stream, lambda: nc.fwd(q, k, v, window=(W, 0), out=(o, lse)), iters)
+        out["full" if W < 0 else f"w{W}"] = {
+            "fp8_us": round(t8, 2), "fp8_tflops": round(fl / (t8 * 1e-6) / 1e12, 1),
+            "frac_fp8_peak": round(fl / (t8 * 1e-6) / 1e12 / PEAK_FP8_TFLOPS, 4),
+            "bf16_us": round(tb, 2), "bf16_tflops": round(fl / (tb * 1e-6) / 1e12, 1)}
+    del q8, k8, v8, q, k, v, o, lse
+    torch.cuda.empty_cache()
+    return out
 
 
 def qknorm_detail(nc, torch, cfg, dev, stream):
@@ -608,6 +636,9 @@ def main():
         # the head_dim-64 kernels on a layer of GPT-2's head size (not one of the
         # workloads above: reported as detail)
         detail["head_dim_64"] = time_config(nc, torch, HD64, dev, stream)
+        # the fp8 forward on the grouped-query layer's shape (reported as detail:
+        # the step above is bf16)
+        detail["fp8_fwd"] = fp8_detail(nc, torch, GQA, dev, stream)
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,

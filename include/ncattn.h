@@ -123,6 +123,26 @@ int ncattn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
                int window_left, int window_right, float softmax_scale, int dtype, void *stream);
 
 /*
+ * Attention forward with fp8 inputs ("nanochat Admin & Developer Guide", section
+ * 6, Attention: FA3 with SDPA fallback, which runs attention in bf16 or fp8).
+ *   q [B][T][n_head][128], k, v [B][T][n_kv_head][128]: OCP e4m3 bytes (FP8 E4M3FN:
+ *     1 sign, 4 exponent bits with bias 7, 3 fraction bits, no infinities, 0x7f /
+ *     0xff NaN); the value an element stands for is its byte's value times the
+ *     tensor's descale (q_descale, k_descale, v_descale: finite, > 0).
+ *   o [B][T][n_head][128] bf16 (written); lse [B][n_head][T] fp32 as ncattn_fwd's.
+ *   Computes ncattn_fwd's function of those values (window and softmax_scale as
+ *   there).  P enters the P V contraction rounded to e4m3 (scaled by 2^8 first,
+ *   after the running row maximum has made it <= 1), so o carries a relative
+ *   error of up to 2^-4 per probability: |o - o_exact| <= max|v| (2^-4 +
+ *   n 2^-18) + the bf16 rounding of o, n the row's visible keys.
+ * head_dim must be 128 (NCATTN_EUNSUPPORTED otherwise); pointers 16-byte
+ * aligned; o must not alias an input (NCATTN_EINVAL).
+ */
+int ncattn_fwd_fp8(const void *q, const void *k, const void *v, float q_descale, float k_descale, float v_descale,
+                   void *o, float *lse, int B, int T, int n_head, int n_kv_head, int head_dim, int window_left,
+                   int window_right, float softmax_scale, void *stream);
+
+/*
  * QK-norm + RoPE fused into the attention forward ("nanochat Admin & Developer
  * Guide", section 3: q and k are RMS-normalised and rotated before attention;
  * sections 3 and 6 for the attention).  Exactly ncattn_qknorm_rope(q, k, ...)

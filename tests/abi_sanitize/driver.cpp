@@ -68,6 +68,30 @@ static void test_fwd() {
   CHECK(g_last.window == 0 && g_last.scale == 0.25f);
 }
 
+static int fwd8(void *q, void *k, void *v, float qd, float kd, float vd, void *o, float *lse, int B, int T, int H,
+                int KV, int D, int wl, int wr, float sc) {
+  return ncattn_fwd_fp8(q, k, v, qd, kd, vd, o, lse, B, T, H, KV, D, wl, wr, sc, nullptr);
+}
+
+static void test_fwd_fp8() {
+  CHECK(fwd8(nullptr, P(1), P(2), 1, 1, 1, P(3), F(4), 1, 64, 2, 2, 128, -1, 0, 0) == NCATTN_EINVAL && err_ok());
+  CHECK(fwd8(P(0), P(1), MIS(2), 1, 1, 1, P(3), F(4), 1, 64, 2, 2, 128, -1, 0, 0) == NCATTN_EINVAL);
+  CHECK(fwd8(P(0), P(1), P(2), 1, 1, 1, P(3), F(4), 1, 64, 2, 2, 64, -1, 0, 0) == NCATTN_EUNSUPPORTED);
+  CHECK(fwd8(P(0), P(1), P(2), 1, 1, 1, P(3), F(4), 1, 64, 6, 4, 128, -1, 0, 0) == NCATTN_EINVAL);
+  CHECK(fwd8(P(0), P(1), P(2), 0.f, 1, 1, P(3), F(4), 1, 64, 2, 2, 128, -1, 0, 0) == NCATTN_EINVAL);
+  CHECK(fwd8(P(0), P(1), P(2), 1, -1.f, 1, P(3), F(4), 1, 64, 2, 2, 128, -1, 0, 0) == NCATTN_EINVAL);
+  CHECK(fwd8(P(0), P(1), P(2), 1, 1, NAN, P(3), F(4), 1, 64, 2, 2, 128, -1, 0, 0) == NCATTN_EINVAL);
+  CHECK(fwd8(P(0), P(1), P(2), 1, 1, INFINITY, P(3), F(4), 1, 64, 2, 2, 128, -1, 0, 0) == NCATTN_EINVAL);
+  CHECK(fwd8(P(0), P(1), P(2), 1, 1, 1, P(1), F(4), 1, 64, 2, 2, 128, -1, 0, 0) == NCATTN_EINVAL);
+  CHECK(fwd8(P(0), P(1), P(2), 1, 1, 1, P(3), F(4), 1, 64, 2, 2, 128, -1, 1, 0) == NCATTN_EINVAL);
+  CHECK(fwd8(P(0), P(1), P(2), 1, 1, 1, P(3), F(4), INT_MAX, INT_MAX, INT_MAX, INT_MAX, INT_MAX, -1, 0, 0) ==
+        NCATTN_EINVAL);
+  CHECK(fwd8(P(0), P(1), P(2), 1, 1, 1, P(3), F(4), 1, INT_MAX, 1, 1, 128, -1, 0, 0) == NCATTN_EUNSUPPORTED);
+  CHECK(fwd8(P(0), P(1), P(2), 0.5f, 0.25f, 2.f, P(3), F(4), 2, 300, 4, 2, 128, INT_MAX, 0, 0) == NCATTN_OK);
+  CHECK(strcmp(g_last.fn, "fwd_fp8") == 0 && g_last.window == -1 && g_last.D == 128);
+  CHECK(fabsf(g_last.scale - 0.25f / sqrtf(128.f)) < 1e-7f);
+}
+
 static void test_qknorm() {
   double dummy = 0;
   (void)dummy;
@@ -244,6 +268,7 @@ static void test_replicate() {
 
 int main() {
   test_fwd();
+  test_fwd_fp8();
   test_qknorm();
   test_bwd();
   test_decode();

@@ -47,6 +47,12 @@ hipError_t launch_fwd_bf16(const void *, const void *, const void *, void *, flo
   return hipSuccess;
 }
 
+hipError_t launch_fwd_fp8(const void *, const void *, const void *, float qd, float kd, float vd, void *, float *,
+                          const AttnShape &sh, hipStream_t) {
+  rec("fwd_fp8", sh.B, sh.T, sh.H, sh.KV, sh.D, sh.window, sh.scale * qd * kd * vd);
+  return hipSuccess;
+}
+
 hipError_t launch_fwd_bf16_qknorm_rope(void *, const void *, const void *, void *, float *, const AttnShape &sh,
                                        const int32_t *, const double *, float, float, hipStream_t, float *,
                                        long long) {

@@ -52,3 +52,32 @@ def check_lse(got, ref, dtype, what, tol=None):
     assert np.all(np.isfinite(g)), f"{what}: non-finite lse"
     assert err <= tol, f"{what}: lse max_abs={err:.3e} > {tol:.3e}"
     return err
+
+
+def check_fp8_o(got, ref, ref_abs, v, window, what):
+    """Element-wise bar of the fp8 forward's o (derived in the header of its
+    kernel): each probability P_ij enters P V rounded to e4m3 after scaling by
+    2^8, a relative error of at most 2^-4, or an absolute 2^-18 (relative to the
+    row max) below e4m3's normal range; the row sum is exact fp32.  So
+        |o_id - o_exact,id| <= 2^-4 sum_j P_ij |v_jd| + n_i 2^-18 max_j |v_jd|
+    for row i with n_i visible keys, plus the bf16 rounding of o (one ulp of the
+    exact value: half an ulp of a value that may sit a binade higher) and 1e-6 of
+    fp32 accumulation.  ref_abs = sum_j P_ij |v_jd| is the oracle's forward of the
+    same q, k with |v| in place of v; v: the float64 values [B][T][KV][D]."""
+    import sys
+    g = f64(got) if isinstance(got, torch.Tensor) else got
+    B, T, H, D = ref.shape
+    vmax = np.abs(v).max(axis=(0, 1, 2))  # per column d
+    i = np.arange(T)
+    n = i + 1 if window < 0 else np.minimum(i + 1, window + 1)
+    e = np.floor(np.log2(np.maximum(np.abs(ref), 1e-30)))
+    bound = 2.0 ** -4 * ref_abs + n[None, :, None, None] * 2.0 ** -18 * vmax[None, None, None, :] \
+        + 2.0 ** (e - 7) + 1e-6
+    err = np.abs(g - ref)
+    rel_fro = float(np.linalg.norm(g - ref) / max(np.linalg.norm(ref), 1e-30))
+    worst = float((err / bound).max()) if err.size else 0.0
+    print(f"  {what}: max_abs={float(err.max()):.3e} rel_fro={rel_fro:.3e} worst err/bound={worst:.3f}",
+          file=sys.stderr, flush=True)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite values"
+    assert worst <= 1.0, f"{what}: error {float(err.max()):.3e} exceeds the fp8 bound (ratio {worst:.3f})"
+    return err

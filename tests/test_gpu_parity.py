@@ -14,8 +14,8 @@ import torch
 import oracle
 import transformer_attention_qknorm_amd as nc
 from conftest import tol_check
-from parity_util import LSE_TOL, TOL, check, check_lse, f64, stored
-from workloads import attn_inputs, decode_inputs, prefill_inputs, replicate_inputs
+from parity_util import LSE_TOL, TOL, check, check_fp8_o, check_lse, f64, stored
+from workloads import attn_inputs, decode_inputs, fp8_inputs, prefill_inputs, replicate_inputs
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -91,6 +91,49 @@ def test_qknorm_rope_rstd(dtype, B, T, H, KV, D):
     assert torch.equal(qa, qb) and torch.equal(ka, kb)
     ref = np.concatenate([oracle.rms_rstd(f64(q), 1e-6), oracle.rms_rstd(f64(k), 1e-6)], axis=2)
     np.testing.assert_allclose(f64(rstd), ref, rtol=1e-5)
+
+
+# ------------------------------------------------------------------ fp8 forward
+FP8_CASES = [
+    # B, T, H, KV, W, softmax_scale
+    (2, 200, 4, 2, -1, None),
+    (1, 333, 8, 1, 100, None),
+    (3, 130, 6, 6, 64, 0.05),
+    (1, 1, 2, 1, -1, None),
+    (2, 64, 4, 4, 0, None),
+    (2, 129, 4, 2, 63, None),
+    (1, 1000, 4, 2, 511, None),
+    (1, 2048, 6, 2, -1, None),
+]
+
+
+@pytest.mark.parametrize("case", FP8_CASES, ids=lambda c: "-".join(str(x) for x in c))
+def test_fwd_fp8(case):
+    """fp8 (OCP e4m3) q, k, v with per-tensor descales: o against the oracle's
+    forward on the values they stand for, within the bound the fp8 rounding of P
+    allows (check_fp8_o); lse to the fp32 bar; and the same o and lse on a second
+    run."""
+    B, T, H, KV, W, sc = case
+    say(f"fwd_fp8 {case}")
+    (q8, k8, v8), (dq, dk, dv) = fp8_inputs(B, T, H, KV, 128, seed=500 + T)
+    qv, kv, vv = (x.to(torch.float64).numpy() * d for x, d in ((q8, dq), (k8, dk), (v8, dv)))
+    ro, rlse = oracle.attn_fwd(qv, kv, vv, W, sc)
+    ra, _ = oracle.attn_fwd(qv, kv, np.abs(vv), W, sc)
+    qd, kd, vd = to_dev(q8, k8, v8)
+    o, lse = nc.fwd_fp8(qd, kd, vd, dq, dk, dv, window=(W, 0), softmax_scale=sc)
+    torch.cuda.synchronize()
+    assert o.dtype == torch.bfloat16
+    check_fp8_o(o, ro, ra, vv, W, "o")
+    check_lse(lse, rlse, "bf16", "lse")
+    o2, lse2 = nc.fwd_fp8(qd, kd, vd, dq, dk, dv, window=(W, 0), softmax_scale=sc)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2), "fp8 forward not deterministic"
+
+
+def test_fwd_fp8_unsupported_head_dim():
+    q8 = torch.zeros(1, 8, 2, 64, dtype=torch.float8_e4m3fn, device=DEV)
+    with pytest.raises(nc.NcattnError, match="EUNSUPPORTED"):
+        nc.fwd_fp8(q8, q8, q8, 1.0, 1.0, 1.0)
 
 
 FUSED_CASES = [

@@ -19,8 +19,8 @@ import torch
 
 import oracle
 import transformer_attention_qknorm_amd as nc
-from parity_util import check, check_lse, f64, group_slice, stored
-from workloads import D12, D20, DECODE, GQA, HD64, TINY, config_inputs, decode_inputs
+from parity_util import check, check_fp8_o, check_lse, f64, group_slice, stored
+from workloads import D12, D20, DECODE, GQA, HD64, TINY, config_inputs, decode_inputs, fp8_inputs
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -136,6 +136,33 @@ def test_workload_layers(cfg, W):
             rdq_raw, rdk_raw = oracle.qknorm_rope_bwd(f64(sq), f64(sk), rdq, rdk, None, cfg.rope_base, 1e-6, 1.0)
             check(r["dq_raw"][b:b + 1, :, hs], rdq_raw, "bf16", f"dq_raw W={W} b={b} g={g}")
             check(r["dk_raw"][b:b + 1, :, g:g + 1], rdk_raw, "bf16", f"dk_raw W={W} b={b} g={g}")
+
+
+@pytest.mark.parametrize("W", sorted(set(GQA.windows)))
+def test_workload_fp8_forward(W):
+    """The fp8 forward at the grouped-query layer's full size (its inputs drawn as
+    the bf16 layer's and stored as e4m3 with per-tensor descales), on the six
+    sampled (sequence, kv-group) slices, against the oracle's forward on the
+    values the fp8 tensors stand for."""
+    cfg = GQA
+    say(f"{cfg.name} fp8: W={W} generating inputs")
+    (q8, k8, v8), (dq, dk, dv) = fp8_inputs(cfg.B, cfg.T, cfg.H, cfg.KV, cfg.D, seed=cfg.seed)
+    say(f"{cfg.name} fp8: W={W} forward on the GPU")
+    o, lse = nc.fwd_fp8(q8.to(DEV), k8.to(DEV), v8.to(DEV), dq, dk, dv, window=(W, 0))
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
+    o, lse = o.cpu(), lse.cpu()
+    G = cfg.H // cfg.KV
+    for b, g in _samples(cfg):
+        say(f"{cfg.name} fp8: W={W} oracle on slice b={b} kv-group={g}")
+        hs = slice(g * G, (g + 1) * G)
+        sq = q8[b:b + 1, :, hs].to(torch.float64).numpy() * dq
+        sk = k8[b:b + 1, :, g:g + 1].to(torch.float64).numpy() * dk
+        sv = v8[b:b + 1, :, g:g + 1].to(torch.float64).numpy() * dv
+        ro, rlse = oracle.attn_fwd(sq, sk, sv, W)
+        ra, _ = oracle.attn_fwd(sq, sk, np.abs(sv), W)
+        check_fp8_o(o[b:b + 1, :, hs], ro, ra, sv, W, f"o W={W} b={b} g={g}")
+        check_lse(lse[b:b + 1, hs], rlse, "bf16", f"lse W={W} b={b} g={g}")
 
 
 @pytest.mark.parametrize("W", list(DECODE.windows))

@@ -2,6 +2,7 @@
 and it only replaces the 2e-2 bar where a correctly rounded value cannot meet it."""
 
 import numpy as np
+import pytest
 import torch
 
 from conftest import elementwise_bound, half_ulp_bf16, tol_check
@@ -39,3 +40,49 @@ def test_tol_check_rejects_real_errors():
         except AssertionError:
             continue
         raise AssertionError("tolerance check accepted a real error")
+
+
+def _fp8_round_p(p):
+    """P rounded as the fp8 forward rounds it: times 2^8, to OCP e4m3 (torch's
+    round to nearest), back, divided by 2^8."""
+    t = torch.from_numpy(np.ascontiguousarray(p * 256.0, dtype=np.float32)).to(torch.float8_e4m3fn)
+    return t.to(torch.float64).numpy() / 256.0
+
+
+def test_fp8_o_bound_holds_for_simulated_rounding_and_is_not_vacuous():
+    """The fp8 forward's bar (parity_util.check_fp8_o) against a CPU model of its
+    rounding: P relative to the exact row max, rounded to e4m3 after scaling by
+    2^8, the row sum over the unrounded P.  The model meets the bar; the same
+    model with each row's previous key dropped, or with the values of
+    neighbouring keys swapped (P and V paired on different keys), exceeds it."""
+    from parity_util import check_fp8_o
+    from workloads import fp8_inputs
+    import oracle
+    B, T, H, KV, D, W = 1, 300, 2, 1, 128, 100
+    (q8, k8, v8), (dq, dk, dv) = fp8_inputs(B, T, H, KV, D, seed=3)
+    q, k, v = (x.to(torch.float64).numpy() * d for x, d in ((q8, dq), (k8, dk), (v8, dv)))
+    ro, _ = oracle.attn_fwd(q, k, v, W)
+    ra, _ = oracle.attn_fwd(q, k, np.abs(v), W)
+
+    def model(drop_prev=False, swap_keys=False):
+        o = np.zeros_like(ro)
+        for h in range(H):
+            s = q[0, :, h] @ k[0, :, h // (H // KV)].T / np.sqrt(D)
+            i, j = np.meshgrid(np.arange(T), np.arange(T), indexing="ij")
+            vis = (j <= i) & (i - j <= W)
+            if drop_prev:
+                vis &= j != i - 1
+            s = np.where(vis, s, -np.inf)
+            p = np.exp(s - s.max(axis=1, keepdims=True))
+            l = p.sum(axis=1, keepdims=True)
+            vh = v[0, :, h // (H // KV)]
+            if swap_keys:
+                vh = vh[np.arange(T) ^ 1 if T % 2 == 0 else np.minimum(np.arange(T) ^ 1, T - 1)]
+            o[0, :, h] = (_fp8_round_p(p) @ vh) / l
+        return torch.from_numpy(o).to(torch.bfloat16).double().numpy()
+
+    check_fp8_o(model(), ro, ra, v, W, "model")
+    with pytest.raises(AssertionError):
+        check_fp8_o(model(drop_prev=True), ro, ra, v, W, "model missing each row's previous key")
+    with pytest.raises(AssertionError):
+        check_fp8_o(model(swap_keys=True), ro, ra, v, W, "model with neighbouring keys' values swapped")

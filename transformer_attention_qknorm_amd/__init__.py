@@ -57,6 +57,7 @@ def lib():
     L.ncattn_qknorm_rope_bwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, f32, f32, f32, i32, vp]
     L.ncattn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp]
     L.ncattn_qknorm_rope_rstd.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp, f32, f32, f32, i32, vp]
+    L.ncattn_fwd_fp8.argtypes = [vp, vp, vp, f32, f32, f32, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, vp]
     L.ncattn_fwd_qknorm_rope.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, f32, f32, f32, i32, i32,
                                          f32, i32, vp]
     L.ncattn_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
@@ -77,7 +78,7 @@ def lib():
     L.ncattn_last_error.restype = ctypes.c_char_p
     L.ncattn_version.restype = ctypes.c_char_p
     for fn in ("ncattn_qknorm_rope", "ncattn_qknorm_rope_bwd", "ncattn_fwd", "ncattn_fwd_qknorm_rope", "ncattn_bwd",
-               "ncattn_bwd_qknorm_rope", "ncattn_qknorm_rope_rstd",
+               "ncattn_bwd_qknorm_rope", "ncattn_qknorm_rope_rstd", "ncattn_fwd_fp8",
                "ncattn_decode", "ncattn_decode_noalloc",
                "ncattn_prefill", "ncattn_cache_replicate"):
         getattr(L, fn).restype = i32
@@ -222,6 +223,34 @@ def fwd(q, k, v, window=(-1, 0), softmax_scale=None, out=None):
         rc = lib().ncattn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, T, H, k.shape[2], D, wl, wr,
                               _scale(softmax_scale), _dtype_code(q), _stream(dev))
     _check("ncattn_fwd", rc)
+    return o, lse
+
+
+def fwd_fp8(q, k, v, q_descale, k_descale, v_descale, window=(-1, 0), softmax_scale=None, out=None):
+    """Attention forward on fp8 inputs: q [B][T][H][128], k, v [B][T][KV][128] as
+    torch.float8_e4m3fn (OCP e4m3), each standing for its values times a per-tensor
+    descale (positive floats).  Returns (o bf16 [B][T][H][128], lse fp32
+    [B][H][T]); ``out=(o, lse)`` reuses preallocated outputs."""
+    dev = _dev(q, k, v)
+    if q.dim() != 4 or k.dim() != 4 or q.dtype != torch.float8_e4m3fn or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("ncattn.fwd_fp8: q, k, v must be 4-D torch.float8_e4m3fn")
+    B, T, H, D = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[1] != T or k.shape[3] != D:
+        raise ValueError("ncattn.fwd_fp8: k, v must be [B][T][n_kv_head][D] matching q")
+    wl, wr = _window(window)
+    if out is None:
+        o = torch.empty((B, T, H, D), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    else:
+        o, lse = out
+        _dev(o, lse)
+        if o.shape != q.shape or o.dtype != torch.bfloat16 or lse.shape != (B, H, T) or lse.dtype != torch.float32:
+            raise ValueError("ncattn.fwd_fp8: out must be (o bf16 shaped like q, lse fp32 [B][H][T])")
+    with torch.cuda.device(dev):
+        rc = lib().ncattn_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), float(q_descale), float(k_descale), float(v_descale),
+                                  _ptr(o), _ptr(lse), B, T, H, k.shape[2], D, wl, wr, _scale(softmax_scale),
+                                  _stream(dev))
+    _check("ncattn_fwd_fp8", rc)
     return o, lse
 
 

@@ -68,6 +68,10 @@ hipError_t launch_bwd_bf16_qknorm_rope(const void *q, const void *k, const void 
                                        void *workspace, const AttnShape &sh, const int32_t *pos_offset,
                                        const double *inv_freq_host, float gain, hipStream_t s);
 
+// fp8 (OCP e4m3) q, k, v with per-tensor descales, bf16 o, head_dim 128.
+hipError_t launch_fwd_fp8(const void *q, const void *k, const void *v, float q_descale, float k_descale,
+                          float v_descale, void *o, float *lse, const AttnShape &sh, hipStream_t s);
+
 // fp32 reference-precision kernels (head_dim 64 or 128).
 hipError_t launch_fwd_f32(const float *q, const float *k, const float *v, float *o, float *lse,
                           const AttnShape &sh, hipStream_t s);

@@ -192,6 +192,33 @@ int ncattn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
   return hip_status(e, fn);
 }
 
+int ncattn_fwd_fp8(const void *q, const void *k, const void *v, float q_descale, float k_descale, float v_descale,
+                   void *o, float *lse, int B, int T, int n_head, int n_kv_head, int head_dim, int window_left,
+                   int window_right, float softmax_scale, void *stream) {
+  const char *fn = "ncattn_fwd_fp8";
+  NC_PTR(q, fn);
+  NC_PTR(k, fn);
+  NC_PTR(v, fn);
+  NC_PTR(o, fn);
+  NC_PTR(lse, fn);
+  NC_TRY(check_heads(fn, B, T, n_head, n_kv_head, head_dim));
+  NC_TRY(check_window(fn, window_left, window_right));
+  if (head_dim != 128)
+    return fail(NCATTN_EUNSUPPORTED, "%s: fp8 attention supports head_dim 128 (got %d)", fn, head_dim);
+  // one (batch, head) slice of k / v is addressed through 32-bit byte offsets
+  if (((double)T + 64.0) * n_kv_head * head_dim >= 2147483648.0)
+    return fail(NCATTN_EUNSUPPORTED, "%s: seq_len x n_kv_head too large (T=%d n_kv_head=%d)", fn, T, n_kv_head);
+  if (!isfinite(softmax_scale)) return fail(NCATTN_EINVAL, "%s: softmax_scale must be finite", fn);
+  if (!(isfinite(q_descale) && q_descale > 0.f && isfinite(k_descale) && k_descale > 0.f && isfinite(v_descale) &&
+        v_descale > 0.f))
+    return fail(NCATTN_EINVAL, "%s: descales must be finite and > 0", fn);
+  if (o == q || o == k || o == v) return fail(NCATTN_EINVAL, "%s: o must not alias an input", fn);
+  window_left = effective_window(window_left, T);
+  ncattn::AttnShape sh{B, T, n_head, n_kv_head, head_dim, window_left, resolve_scale(softmax_scale, head_dim)};
+  return hip_status(ncattn::launch_fwd_fp8(q, k, v, q_descale, k_descale, v_descale, o, lse, sh, (hipStream_t)stream),
+                    fn);
+}
+
 int ncattn_fwd_qknorm_rope(void *q, void *k, const void *v, void *o, float *lse, float *rstd, int B, int T,
                            int n_head, int n_kv_head, int head_dim, const int32_t *pos_offset, float rope_base,
                            float eps, float qk_gain, int window_left, int window_right, float softmax_scale,

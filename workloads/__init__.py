@@ -116,6 +116,25 @@ def attn_inputs(B, T, H, KV, D, dtype="bf16", seed=0):
     return tuple(_to_dtype(x, dtype) for x in (q, k, v, do))
 
 
+def fp8_inputs(B, T, H, KV, D, seed=0):
+    """q [B][T][H][D], k, v [B][T][KV][D] drawn as attn_inputs draws them (fp32
+    N(0, 1), in that order) and stored as OCP e4m3 (torch.float8_e4m3fn, round to
+    nearest) with one descale per tensor, amax / 448, so that each tensor's largest
+    magnitude lands on e4m3's largest finite value.  Returns ((q8, k8, v8),
+    (q_descale, k_descale, v_descale)): CPU tensors and Python floats; x8 times its
+    descale is the value the test's reference sees."""
+    rng = np.random.default_rng(seed)
+    xs = (rng.standard_normal((B, T, H, D), dtype=np.float32),
+          rng.standard_normal((B, T, KV, D), dtype=np.float32),
+          rng.standard_normal((B, T, KV, D), dtype=np.float32))
+    out, scales = [], []
+    for x in xs:
+        descale = float(np.abs(x).max()) / 448.0
+        out.append((torch.from_numpy(x) / descale).to(torch.float8_e4m3fn))
+        scales.append(descale)
+    return tuple(out), tuple(scales)
+
+
 def config_inputs(cfg: AttnConfig):
     return attn_inputs(cfg.B, cfg.T, cfg.H, cfg.KV, cfg.D, cfg.dtype, cfg.seed)
 
