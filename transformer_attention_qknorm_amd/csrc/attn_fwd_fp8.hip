@@ -30,12 +30,17 @@
 // 16 (lane group) + 8 e .. + 8 of the head, and four such reads (r = 0..3) fill
 // the 32 bytes.
 //
-// Softmax: the running row max is kept (O and the row sum are rescaled when it
-// grows), so P <= 1; P is multiplied by 2^8 before its conversion to fp8 (round
-// to nearest), which keeps P >= 2^-14 in e4m3's normal range, and the 2^-8 is
-// folded into the output scale.  The row sum is taken over the fp32 P.  Each
-// probability thus enters O with a relative error of at most 2^-4 (e4m3 keeps 3
-// fraction bits), or an absolute one of at most 2^-18 below the normal range.
+// Softmax: each row keeps an exponent reference m (O and the row sum are
+// rescaled when it moves) that trails the running row max by less than 0.8 in
+// base-2 exponent units, so P = exp2((s - m) c) < 2^0.8 = 1.74; P is computed
+// already multiplied by 2^8 (2^8 P <= 446 fits e4m3's largest finite value, 448)
+// and converted to fp8 by rounding to nearest, which keeps P >= 2^-14 in e4m3's
+// normal range; the row sum is taken over the same fp32 2^8 P, so the factor
+// cancels in O.  Moving m only when the max has grown by 0.8 spares most tiles
+// the rescale once a row's first tiles have been seen.  Each probability thus
+// enters O with a relative error of at most 2^-4 (e4m3 keeps 3 fraction bits),
+// or an absolute one of at most 2^-18 (relative to the reference) below the
+// normal range.
 #include "attn_tiles.hpp"
 #include "internal.hpp"
 
@@ -79,7 +84,7 @@ __device__ __forceinline__ void mask_tile_fp8(f32x16 (&sacc)[2], int k0, int q_l
 }
 
 // c: scale dq dk log2 e (raw scores to exponent base 2); lse_scale: scale dq dk;
-// o_scale: dv / 2^8.
+// o_scale: dv.
 __global__ __launch_bounds__(256, 2) void attn_fwd_fp8_kernel(const uint8_t *__restrict__ Q,
                                                              const uint8_t *__restrict__ K,
                                                              const uint8_t *__restrict__ V,
@@ -169,8 +174,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_fp8_kernel(const uint8_t *__r
   f32x16 oacc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) oacc[i] = f32x16{};
-  float m_run = -INFINITY;  // running max of the raw scores (both halves of a row agree)
-  float l_run = 0.f;        // this lane's partial row sum (its 32 of every 64 keys)
+  float m_run = -INFINITY;  // exponent reference of the raw scores (both halves of a row agree)
+  float l_run = 0.f;        // this lane's partial row sum of 2^8 P (its 32 of every 64 keys)
 
   lds_loads_done_barrier();
 
@@ -198,18 +203,20 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_fp8_kernel(const uint8_t *__r
 #pragma unroll
         for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, sacc[kb][e]);
       tmax = fmaxf(tmax, shfl_xor(tmax, 32));
-      const float m_new = fmaxf(m_run, tmax);
-      if (__any(m_new > m_run)) {
-        // the first visible tile gives alpha = exp2(-inf) = 0 on zeros
-        const float alpha = m_new > m_run ? fast_exp2((m_run - m_new) * c) : 1.f;
+      // move the reference when the max has grown by 0.8 (base-2 units) or more,
+      // or on the first visible tile (alpha = exp2(-inf) = 0 on zeros)
+      const bool move = (tmax - m_run) * c >= 0.8f;
+      if (__any(move)) {
+        const float alpha = move ? fast_exp2((m_run - tmax) * c) : 1.f;
 #pragma unroll
         for (int db = 0; db < 4; ++db)
 #pragma unroll
           for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
         l_run *= alpha;
-        m_run = m_new;
+        m_run = move ? tmax : m_run;
       }
-      const float nmc = m_run == -INFINITY ? 0.f : -m_run * c;
+      // 2^8 P = exp2((s - m) c + 8)
+      const float nmc = m_run == -INFINITY ? 0.f : 8.f - m_run * c;
       i32x8 pop;
       float ls = 0.f;
 #pragma unroll
@@ -221,8 +228,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_fp8_kernel(const uint8_t *__r
           p[j] = fast_exp2(__builtin_fmaf(sacc[kb][e0 + j], c, nmc));
           ls += p[j];
         }
-        int x = __builtin_amdgcn_cvt_pk_fp8_f32(p[0] * 256.f, p[1] * 256.f, 0, false);
-        x = __builtin_amdgcn_cvt_pk_fp8_f32(p[2] * 256.f, p[3] * 256.f, x, true);
+        int x = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+        x = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], x, true);
         pop[w] = x;
       }
       l_run += ls;
@@ -260,7 +267,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_fp8_kernel(const uint8_t *__r
       w[1] = pack_bf16x2(oacc[db][4 * i + 2] * inv, oacc[db][4 * i + 3] * inv);
       *(u32x2 *)(op + d) = w;
     }
-  if (hh == 0 && LSE) LSE[((long long)b * H + h) * T + q_lane] = m_run * lse_scale + logf(l_tot);
+  if (hh == 0 && LSE) LSE[((long long)b * H + h) * T + q_lane] = m_run * lse_scale + logf(l_tot) - 8.f * kLn2;
 }
 
 }  // namespace
@@ -273,7 +280,7 @@ hipError_t launch_fwd_fp8(const void *q, const void *k, const void *v, float q_d
   const float sc = sh.scale * q_descale * k_descale;
   hipLaunchKernelGGL(attn_fwd_fp8_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (const uint8_t *)q,
                      (const uint8_t *)k, (const uint8_t *)v, (uint16_t *)o, lse, sh.B, sh.T, sh.H, sh.KV,
-                     sh.window, sc * kLog2e, sc, v_descale * (1.f / 256.f));
+                     sh.window, sc * kLog2e, sc, v_descale);
   return hipGetLastError();
 }
 
