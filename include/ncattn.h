@@ -131,10 +131,11 @@ int ncattn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
  *     tensor's descale (q_descale, k_descale, v_descale: finite, > 0).
  *   o [B][T][n_head][128] bf16 (written); lse [B][n_head][T] fp32 as ncattn_fwd's.
  *   Computes ncattn_fwd's function of those values (window and softmax_scale as
- *   there).  P enters the P V contraction rounded to e4m3 (scaled by 2^8 first,
- *   after the running row maximum has made it <= 1), so o carries a relative
- *   error of up to 2^-4 per probability: |o - o_exact| <= max|v| (2^-4 +
- *   n 2^-18) + the bf16 rounding of o, n the row's visible keys.
+ *   there).  P enters the P V contraction rounded to e4m3 (as 2^8 P against an
+ *   exponent reference within 0.8, base 2, of the running row maximum, so below
+ *   e4m3's 448), so o carries a relative error of up to 2^-4 per probability:
+ *   |o_id - o_exact,id| <= 2^-4 sum_j P_ij |v_jd| + n 2^-18 max_j |v_jd| + the
+ *   bf16 rounding of o, n the row's visible keys.
  * head_dim must be 128 (NCATTN_EUNSUPPORTED otherwise); pointers 16-byte
  * aligned; o must not alias an input (NCATTN_EINVAL).
  */
