@@ -130,6 +130,35 @@ def test_fwd_fp8(case):
     assert torch.equal(o, o2) and torch.equal(lse, lse2), "fp8 forward not deterministic"
 
 
+@pytest.mark.parametrize("W", [-1, 300])
+def test_fwd_fp8_scores_growing_along_the_keys(W):
+    """Scores that rise by about 0.23 (natural units) per key, so that every
+    64-key tile's row max exceeds the exponent reference by far more than 0.8 in
+    base 2 and the reference moves (O and the row sum rescaled) on every tile:
+    o and lse against the oracle on the values the fp8 bytes stand for."""
+    B, T, H, KV, D = 1, 700, 2, 1, 128
+    say(f"fwd_fp8 growing scores W={W}")
+    q = np.zeros((B, T, H, D), np.float32)
+    q[..., :64] = 2.0
+    k = np.zeros((B, T, KV, D), np.float32)
+    k[..., :64] = (0.02 * np.arange(T, dtype=np.float32))[None, :, None, None]
+    rng = np.random.default_rng(77)
+    v = rng.standard_normal((B, T, KV, D), dtype=np.float32)
+    v8 = (torch.from_numpy(v) / (float(np.abs(v).max()) / 448.0)).to(torch.float8_e4m3fn)
+    q8 = torch.from_numpy(q).to(torch.float8_e4m3fn)
+    k8 = torch.from_numpy(k).to(torch.float8_e4m3fn)
+    dq, dk, dv = 1.0, 1.0, float(np.abs(v).max()) / 448.0
+    qv, kv, vv = (x.to(torch.float64).numpy() * d for x, d in ((q8, dq), (k8, dk), (v8, dv)))
+    assert float(kv.max()) > 12.0  # e4m3 keeps the growth: scores reach ~150
+    ro, rlse = oracle.attn_fwd(qv, kv, vv, W, None)
+    ra, _ = oracle.attn_fwd(qv, kv, np.abs(vv), W, None)
+    qd, kd, vd = to_dev(q8, k8, v8)
+    o, lse = nc.fwd_fp8(qd, kd, vd, dq, dk, dv, window=(W, 0))
+    torch.cuda.synchronize()
+    check_fp8_o(o, ro, ra, vv, W, "o")
+    check_lse(lse, rlse, "bf16", "lse")
+
+
 def test_fwd_fp8_unsupported_head_dim():
     q8 = torch.zeros(1, 8, 2, 64, dtype=torch.float8_e4m3fn, device=DEV)
     with pytest.raises(nc.NcattnError, match="EUNSUPPORTED"):
