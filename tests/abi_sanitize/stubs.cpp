@@ -1,7 +1,7 @@
 // Stand-ins for the kernel launchers behind the C ABI, for a host-only build of
 // the validation layer (ncattn_api.hip compiled as plain C++ under AddressSanitizer
 // and UndefinedBehaviorSanitizer).  Each launcher records what it was asked to
-// do and enqueues nothing; the driver checks the records.
+// do and enqueues nothing; driver.cpp checks the records.
 #include "stubs.hpp"
 
 #include <string.h>
